@@ -1,0 +1,313 @@
+"""Plain float64 CPU oracle for KV-cached grouped-query attention.
+
+TEST INFRASTRUCTURE. Only tests/, the package smoke check and the CPU-baseline
+leg of bench.py may import or run this module. It shares no code with the HIP
+path (no kernels, headers, helpers or tables) and imports nothing from it.
+
+What it computes, and where the pages define it:
+
+* Storage. A preallocated cache of shape (L, B, H_kv, max_len, d_h) for K and
+  for V, zero before anything is written ("kv-cache-decoding", shapes table:
+  unfilled slots are zeros; "Generation and the KV Cache", the KVCache
+  paragraph: k, v of shape (L, B, H, max_len, d_head)).
+* Per-layer fill counts and the committed length s = min over layers
+  ("KV cache, incremental decode, ...", section 2.3). Rows of a batch carry
+  their own counts (the per-request length of "kv-cache-decoding",
+  "Batching caches of different lengths").
+* append: write a chunk of T positions at slots [fill, fill+T) after
+  rounding to the storage dtype, and advance that layer's fill
+  ("KV cache, ...", sections 2.5 and 4, update; "kv-cache-decoding", step 5).
+  On any error nothing changes ("KV cache, ...", section 4 test table,
+  test_update_copies_and_checks).
+* attend: softmax(q K^T / sqrt(d_h)) V for every query head h of every row,
+  over the keys that head's K/V head g = h // G holds, with query i of the
+  chunk at absolute position s + i seeing keys j <= s + i
+  ("KV cache, ...", section 2.3, the mask equation; "Heads, GQA and K/V
+  cache", "Four queries, two sets of K/V": heads map in order [0,0,1,1];
+  "kv-cache-decoding", shapes table: scores = q k^T / sqrt(d_head)).
+  It is the definition written out: every call recomputes from storage,
+  in float64, with masked keys excluded from the sum.
+* truncate(n): every layer's fill becomes n; storage is untouched
+  ("KV cache, ...", section 2.4).
+* nbytes = 2 L B H_kv max_len d_h itemsize ("KV cache, ...", section 2.5;
+  "Heads, GQA and K/V cache", "Memory and the window limit").
+
+Readings where the pages are silent (each one is listed with its reason in the
+design notes of the repository):
+
+* Rounding to fp16/bf16 is IEEE round-to-nearest-even from the float32 value
+  the caller hands in. NaN becomes a canonical quiet NaN that keeps the sign
+  (fp16: 0x7E00, bf16: 0x7FC0); overflow rounds to infinity.
+* The query is rounded to the storage dtype before the product when the
+  cache is fp16/bf16 and q arrives as float32 (a 16-bit q is used as is).
+* Truncating to n > s (extending) or n < 0 is an error; appending past
+  max_len is an error that changes nothing; T < 1 is an error; attend
+  needs fill >= T for every row.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+DTYPES = ("fp32", "fp16", "bf16")
+_ITEMSIZE = {"fp32": 4, "fp16": 2, "bf16": 2}
+
+
+class OracleError(ValueError):
+    """A call the cache contract rejects; the oracle state is unchanged."""
+
+
+class OracleCapacityError(OracleError):
+    """An append that would run past max_len."""
+
+
+# ---------------------------------------------------------------------------
+# Rounding to the storage dtype ("KV cache, ...", section 2.5: values are
+# converted on the way in and the stored values are what is returned).
+# ---------------------------------------------------------------------------
+
+def round_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+
+    bfloat16 keeps the top 16 bits of the float32 pattern; rounding to nearest
+    with ties to even adds 0x7FFF plus the lowest kept bit before the shift.
+    Overflow carries into the exponent and gives infinity, as IEEE asks.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    sign = (u >> 31) & 1
+    is_nan = (u & 0x7FFFFFFF) > 0x7F800000
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF
+    r = np.where(is_nan, (sign << 15) | 0x7FC0, r)
+    return r.astype(np.uint16)
+
+
+def round_f16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns (uint16), round-to-nearest-even.
+
+    NumPy's float32 -> float16 cast is RNE with subnormals and overflow to
+    infinity; NaN is replaced by the canonical quiet NaN of the same sign.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        h = x.astype(np.float16).view(np.uint16).astype(np.uint32)
+    sign = (x.view(np.uint32) >> 31).astype(np.uint32)
+    h = np.where(np.isnan(x), (sign << 15) | 0x7E00, h)
+    return h.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> the float32 values they denote (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """binary16 bit patterns -> the float32 values they denote (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The float32 array of values a cache of `dtype` stores for input x."""
+    if dtype == "fp32":
+        return np.array(x, dtype=np.float32, copy=True)
+    if dtype == "fp16":
+        return f16_bits_to_f32(round_f16_bits(x))
+    if dtype == "bf16":
+        return bf16_bits_to_f32(round_bf16_bits(x))
+    raise OracleError(f"unknown dtype {dtype!r}")
+
+
+def storage_bits(values_f32: np.ndarray, dtype: str) -> np.ndarray:
+    """Raw storage pattern of already-rounded values (uint32 for fp32, uint16 else)."""
+    v = np.ascontiguousarray(values_f32, dtype=np.float32)
+    if dtype == "fp32":
+        return v.view(np.uint32).copy()
+    if dtype == "bf16":
+        return (v.view(np.uint32) >> 16).astype(np.uint16)
+    if dtype == "fp16":
+        return v.astype(np.float16).view(np.uint16).copy()
+    raise OracleError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# Mask and byte count, as closed forms.
+# ---------------------------------------------------------------------------
+
+def causal_mask(T: int, n_keys: int, q_offset: int) -> np.ndarray:
+    """Boolean [T, n_keys]: query i (absolute position q_offset + i) may see key j
+    exactly when j <= q_offset + i ("KV cache, ...", section 2.3 equation;
+    "kv-cache-decoding", step 3)."""
+    i = np.arange(T)[:, None]
+    j = np.arange(n_keys)[None, :]
+    return j <= q_offset + i
+
+
+def kv_bytes(layers: int, heads: int, head_dim: int, seq_len: int,
+             batch: int = 1, bytes_per_value: int = 2) -> int:
+    """2 * layers * batch * heads * seq_len * head_dim * bytes: K and V of every
+    layer and KV head ("kv-cache-decoding", "What is cached, what is not, and
+    what it costs"; "Heads, GQA and K/V cache", "Memory and the window limit")."""
+    return 2 * layers * batch * heads * seq_len * head_dim * bytes_per_value
+
+
+# ---------------------------------------------------------------------------
+# The cache.
+# ---------------------------------------------------------------------------
+
+class OracleCache:
+    """Float64 reference of the KV-cache contract (append / attend / seq_len /
+    truncate / nbytes), with its own bookkeeping and its own rounding.
+
+    K and V hold the dtype-rounded values as float32 (every fp16/bf16 value
+    is exact in float32); arithmetic upcasts them to float64.
+    """
+
+    def __init__(self, n_layers: int, batch: int, n_q_heads: int, n_kv_heads: int,
+                 d_head: int, max_len: int, dtype: str = "fp32"):
+        for name, val in (("n_layers", n_layers), ("batch", batch), ("n_q_heads", n_q_heads),
+                          ("n_kv_heads", n_kv_heads), ("d_head", d_head), ("max_len", max_len)):
+            if int(val) < 1:
+                raise OracleError(f"{name} must be positive, got {val}")
+        if n_q_heads % n_kv_heads:
+            raise OracleError("n_q_heads must be a multiple of n_kv_heads")
+        if dtype not in DTYPES:
+            raise OracleError(f"unknown dtype {dtype!r}")
+        self.L, self.B = int(n_layers), int(batch)
+        self.Hq, self.Hkv, self.D = int(n_q_heads), int(n_kv_heads), int(d_head)
+        self.G = self.Hq // self.Hkv
+        self.max_len = int(max_len)
+        self.dtype = dtype
+        shape = (self.L, self.B, self.Hkv, self.max_len, self.D)
+        self.K = np.zeros(shape, dtype=np.float32)
+        self.V = np.zeros(shape, dtype=np.float32)
+        self.fill = np.zeros((self.L, self.B), dtype=np.int64)
+
+    # -- bookkeeping ("KV cache, ...", sections 2.3 and 2.4) ---------------
+
+    def seq_len(self, layer: int = -1) -> np.ndarray:
+        """Per-row committed length min over layers (layer = -1), or one layer's fill."""
+        if layer == -1:
+            return self.fill.min(axis=0).copy()
+        if not 0 <= layer < self.L:
+            raise OracleError(f"layer {layer} out of range")
+        return self.fill[layer].copy()
+
+    def positions(self, T: int) -> np.ndarray:
+        """[B, T] absolute positions s_b + i of the next chunk (what RoPE rotates by)."""
+        s = self.seq_len(-1)
+        return s[:, None] + np.arange(T)[None, :]
+
+    def mask(self, T: int, row: int = 0) -> np.ndarray:
+        """causal_mask(T, s + T, q_offset=s) for one row of the batch."""
+        s = int(self.seq_len(-1)[row])
+        return causal_mask(T, s + T, s)
+
+    def truncate(self, n) -> None:
+        """Set every layer's fill of each row to n (scalar: all rows). Storage is
+        not touched; the next append overwrites from n."""
+        n = np.asarray(n, dtype=np.int64)
+        if n.ndim == 0:
+            n = np.full(self.B, int(n), dtype=np.int64)
+        if n.shape != (self.B,):
+            raise OracleError("truncate takes one length or one per row")
+        s = self.seq_len(-1)
+        if (n < 0).any() or (n > s).any():
+            raise OracleError("truncate length must lie in [0, committed length]")
+        self.fill[:, :] = n[None, :]
+
+    def nbytes(self) -> int:
+        return kv_bytes(self.L, self.Hkv, self.D, self.max_len, self.B, _ITEMSIZE[self.dtype])
+
+    # -- append ("KV cache, ...", sections 2.5 and 4; "kv-cache-decoding", step 5)
+
+    def append(self, layer: int, k_new: np.ndarray, v_new: np.ndarray) -> None:
+        """Store k_new, v_new [B, H_kv, T, d_h] (float32 or an already 16-bit
+        array's float32 values) at slots [fill, fill + T) of `layer`."""
+        if not 0 <= layer < self.L:
+            raise OracleError(f"layer {layer} out of range")
+        k_new = np.asarray(k_new)
+        v_new = np.asarray(v_new)
+        if k_new.ndim != 4 or k_new.shape != v_new.shape or k_new.shape[:2] != (self.B, self.Hkv) \
+                or k_new.shape[3] != self.D:
+            raise OracleError(f"k/v must be [B={self.B}, H_kv={self.Hkv}, T, d_h={self.D}]")
+        T = k_new.shape[2]
+        if T < 1:
+            raise OracleError("T must be at least 1")
+        f = self.fill[layer]
+        if (f + T > self.max_len).any():
+            raise OracleCapacityError("append would run past max_len")
+        kr = round_to_storage(k_new.astype(np.float32), self.dtype)
+        vr = round_to_storage(v_new.astype(np.float32), self.dtype)
+        for b in range(self.B):
+            fb = int(f[b])
+            self.K[layer, b, :, fb:fb + T] = kr[b]
+            self.V[layer, b, :, fb:fb + T] = vr[b]
+        self.fill[layer] += T
+
+    # -- attend (the plain definition) --------------------------------------
+
+    def query_values(self, q: np.ndarray) -> np.ndarray:
+        """The values of q the product uses: rounded to the storage dtype when
+        the cache is 16-bit and q is float32 (a 16-bit q is already exact)."""
+        q = np.asarray(q)
+        if self.dtype != "fp32" and q.dtype == np.float32:
+            return round_to_storage(q, self.dtype)
+        return q.astype(np.float32)
+
+    def attend(self, layer: int, q: np.ndarray, rows=None) -> np.ndarray:
+        """out[b, h, i] = sum_j w_j V[g, j] / sum_j w_j over visible keys j,
+        w_j = exp(z_j - max z), z_j = q[b, h, i] . K[g, j] / sqrt(d_h), g = h // G.
+
+        q is [B, H_q, T, d_h]; the chunk is the last T slots of the layer, so row
+        b's query offset is s_b = fill[layer][b] - T. Returns float64
+        [B, H_q, T, d_h]; with rows = [(b, h, i), ...] only those are computed
+        (others stay NaN).
+        """
+        if not 0 <= layer < self.L:
+            raise OracleError(f"layer {layer} out of range")
+        q = np.asarray(q)
+        if q.ndim != 4 or q.shape[:2] != (self.B, self.Hq) or q.shape[3] != self.D:
+            raise OracleError(f"q must be [B={self.B}, H_q={self.Hq}, T, d_h={self.D}]")
+        T = q.shape[2]
+        if T < 1:
+            raise OracleError("T must be at least 1")
+        if (self.fill[layer] < T).any():
+            raise OracleError("attend needs the chunk appended first (fill >= T)")
+        qv = self.query_values(q).astype(np.float64)
+        out = np.full((self.B, self.Hq, T, self.D), np.nan)
+        inv_sqrt_d = 1.0 / math.sqrt(self.D)
+        wanted = None
+        if rows is not None:
+            wanted = {}
+            for (b, h, i) in rows:
+                wanted.setdefault((int(b), int(h) // self.G), set()).add((int(h), int(i)))
+        for b in range(self.B):
+            n = int(self.fill[layer, b])
+            s = n - T
+            visible = causal_mask(T, n, s)
+            for g in range(self.Hkv):
+                if wanted is not None and (b, g) not in wanted:
+                    continue
+                Kg = self.K[layer, b, g, :n].astype(np.float64)
+                Vg = self.V[layer, b, g, :n].astype(np.float64)
+                for h in range(g * self.G, (g + 1) * self.G):
+                    if wanted is not None:
+                        idx = sorted(i for (hh, i) in wanted[(b, g)] if hh == h)
+                        if not idx:
+                            continue
+                    else:
+                        idx = list(range(T))
+                    z = (qv[b, h, idx] @ Kg.T) * inv_sqrt_d          # [len(idx), n]
+                    vis = visible[idx]
+                    z = np.where(vis, z, -np.inf)                     # masked keys drop out
+                    m = z.max(axis=1, keepdims=True)
+                    w = np.where(vis, np.exp(z - m), 0.0)
+                    out[b, h, idx] = (w @ Vg) / w.sum(axis=1, keepdims=True)
+        return out
+
+    # -- raw views for bit-exact comparison ---------------------------------
+
+    def stored_bits(self, which: str = "K") -> np.ndarray:
+        arr = self.K if which == "K" else self.V
+        return storage_bits(arr, self.dtype)

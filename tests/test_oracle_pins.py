@@ -1,0 +1,571 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print, closed forms, invariants the pages state, a library routine on a
+special case, or brute force on tiny inputs. The mutant tests at the end plant
+the pages' own pitfalls in a copy of the oracle and show that a pin fails.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (OracleCache, OracleCapacityError, OracleError, bf16_bits_to_f32, causal_mask,
+                    f16_bits_to_f32, kv_bytes, round_bf16_bits, round_f16_bits, round_to_storage)
+from kv_cached_gqa_amd import work
+
+
+def _rand(rng, *shape, scale=1.0):
+    return (rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Printed values
+# ---------------------------------------------------------------------------
+
+def test_hand_example(golden_dir):
+    """The worked example of "KV cache, incremental decode, ...", section 3."""
+    g = json.load(open(os.path.join(golden_dir, "hand_example.json")))
+    c = g["config"]
+    oc = OracleCache(c["n_layers"], c["batch"], c["n_q_heads"], c["n_kv_heads"], c["d_head"],
+                     c["max_len"], c["dtype"])
+    k1 = np.array(g["prefill_keys"], dtype=np.float32)[None, None]
+    oc.append(0, k1, k1)
+    assert int(oc.seq_len()[0]) == g["after_prefill"]["seq_len"]
+    assert oc.positions(1)[0].tolist() == g["after_prefill"]["next_positions"]
+    n = int(oc.seq_len()[0])
+    assert oc.K[0, 0, 0, :n].tolist() == g["after_prefill"]["stored_rows"]
+    k2 = np.array(g["decode_key"], dtype=np.float32)[None, None]
+    oc.append(0, k2, k2)
+    a = g["after_decode"]
+    assert int(oc.seq_len()[0]) == a["seq_len"]
+    n = int(oc.seq_len()[0])
+    assert oc.K[0, 0, 0, :n].tolist() == a["stored_rows"]
+    assert int(oc.positions(1)[0, 0]) == a["next_query_position"]
+    assert oc.mask(1)[0].astype(int).tolist() == a["next_mask_row"]
+    assert oc.nbytes() == g["nbytes"]
+    # slots past the fill are still the zeros the cache started with
+    assert (oc.K[0, 0, 0, n:] == 0).all()
+
+
+def test_memory_figures(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "memory_figures.json")))
+    c0, c1, c2, c3, c4 = g["cases"]
+    oc = OracleCache(c0["layers"], c0["batch"], c0["kv_heads"], c0["kv_heads"], c0["head_dim"],
+                     c0["positions"], "fp32")
+    assert oc.nbytes() == c0["bytes"]["fp32"]
+    assert oc.nbytes() // 4 == c0["elements"]
+    assert kv_bytes(c0["layers"], c0["kv_heads"], c0["head_dim"], c0["positions"], 1, 8) == c0["bytes"]["fp64"]
+    b = kv_bytes(c1["layers"], c1["kv_heads"], c1["head_dim"], c1["positions"], 1, 4)
+    assert int(b // 10 ** 6) == c1["bytes_fp32_megabytes_floor"]
+    oc16 = OracleCache(c1["layers"], 1, 9, c1["kv_heads"], c1["head_dim"], c1["positions"], "fp16")
+    assert 2 * oc16.nbytes() == b                     # "a float16 cache halves it"
+    assert kv_bytes(c2["layers"], c2["kv_heads"], c2["head_dim"], 1, 1, 8) == c2["bytes"]
+    per_tok = kv_bytes(c3["layers"], c3["kv_heads"], c3["head_dim"], 1, 1, 2)
+    assert per_tok == c3["bytes"]
+    assert round(per_tok * 4000 / 1e9, 1) == c3["positions_4000_gigabytes_rounded"]
+    oc4 = OracleCache(1, 1, 1, 1, 2, 4, "fp32")
+    assert oc4.nbytes() == c4["bytes"]
+
+
+def test_work_counters(golden_dir):
+    """The score counters of the tiny-decoder self-check of "kv-cache-decoding"."""
+    g = json.load(open(os.path.join(golden_dir, "work_counters.json")))
+    L, H, P, N = g["layers"], g["heads"], g["prompt"], g["new_tokens"]
+    # without a cache: step i reruns all P + i positions at t = 0
+    unc = sum(L * work.rectangle_scores(H, P + i, 0) for i in range(N))
+    # with a cache: one prefill of P at t = 0, then N - 1 single-token steps at t = P .. P + N - 2
+    cac = L * work.rectangle_scores(H, P, 0) + sum(L * work.rectangle_scores(H, 1, P + i - 1)
+                                                    for i in range(1, N))
+    assert unc == g["scores_uncached"]
+    assert cac == g["scores_cached"]
+    P2, N2 = g["long_prompt"], g["long_new_tokens"]
+    assert sum(P2 + i for i in range(N2)) == g["positions_uncached_long"]
+    assert P2 + N2 - 1 == g["positions_cached_long"]
+    # visible pairs: the rectangle minus the strictly upper triangle of the last T keys
+    for T, s in [(1, 0), (1, 37), (16, 0), (5, 9), (512, 15872)]:
+        brute = int(causal_mask(T, s + T, s).sum())
+        assert work.visible_pairs(T, s) == brute
+        assert work.rectangle_scores(1, T, s) == T * (s + T)
+
+
+# ---------------------------------------------------------------------------
+# Mask
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("s", [0, 1, 7, 30])
+def test_mask_single_query_is_all_true(s):
+    m = causal_mask(1, s + 1, s)
+    assert m.shape == (1, s + 1) and m.all()
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 16])
+def test_mask_at_zero_offset_is_lower_triangle(T):
+    assert np.array_equal(causal_mask(T, T, 0), np.tril(np.ones((T, T), dtype=bool)))
+
+
+@pytest.mark.parametrize("T,s", [(3, 4), (5, 2), (1, 9), (4, 0)])
+def test_mask_is_triangle_shifted_by_offset(T, s):
+    m = causal_mask(T, s + T, s)
+    assert np.array_equal(m, np.tril(np.ones((T, s + T), dtype=bool), k=s))
+    # the oracle's per-row mask follows the committed length
+    oc = OracleCache(1, 1, 1, 1, 2, s + T + 1)
+    if s:
+        oc.append(0, np.ones((1, 1, s, 2), np.float32), np.ones((1, 1, s, 2), np.float32))
+    assert np.array_equal(oc.mask(T), m)
+
+
+# ---------------------------------------------------------------------------
+# Rounding ("KV cache, ...", section 2.5)
+# ---------------------------------------------------------------------------
+
+def _edge_f32():
+    rng = np.random.default_rng(1)
+    vals = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 1e5, -1e5, 6.1e-5, 5.96e-8, 2.98e-8, 1e-9,
+            3.0e38, -3.3895e38, 1.0 + 2.0 ** -8, 1.0 + 2.0 ** -9, 1.0 + 3 * 2.0 ** -9,
+            np.inf, -np.inf]
+    x = np.array(vals, dtype=np.float32)
+    bits = rng.integers(0, 2 ** 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    rnd = bits.view(np.float32)
+    rnd = rnd[~np.isnan(rnd)]
+    return np.concatenate([x, rnd, _rand(rng, 5000), _rand(rng, 2000, scale=1e-6)])
+
+
+def test_f16_rounding_matches_torch_and_is_nearest_even():
+    x = _edge_f32()
+    bits = round_f16_bits(x)
+    ref = torch.from_numpy(x.copy()).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, ref)
+    # nearest-even property on finite, in-range values, computed in float64
+    fin = np.isfinite(x) & (np.abs(x) < 65504.0)
+    r = f16_bits_to_f32(bits[fin]).astype(np.float64)
+    xs = x[fin].astype(np.float64)
+    up = np.nextafter(bits[fin].view(np.float16), np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(bits[fin].view(np.float16), np.float16(-np.inf)).astype(np.float64)
+    err = np.abs(r - xs)
+    assert (err <= np.abs(up - xs)).all() and (err <= np.abs(dn - xs)).all()
+    tie = (err == np.abs(up - xs)) | (err == np.abs(dn - xs))
+    assert ((bits[fin][tie & (err > 0)] & 1) == 0).all()
+
+
+def test_bf16_rounding_matches_torch_and_is_nearest_even():
+    x = _edge_f32()
+    bits = round_bf16_bits(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, ref)
+    fin = np.isfinite(x) & np.isfinite(bf16_bits_to_f32(bits))
+    r = bf16_bits_to_f32(bits[fin]).astype(np.float64)
+    xs = x[fin].astype(np.float64)
+    b = bits[fin].astype(np.int64)
+    # neighbours one unit in the last place away, in magnitude, as float64 values
+    nb_hi = bf16_bits_to_f32(((b + 1) & 0xFFFF).astype(np.uint16)).astype(np.float64)
+    nb_lo = bf16_bits_to_f32(np.where((b & 0x7FFF) > 0, b - 1, b).astype(np.uint16)).astype(np.float64)
+    err = np.abs(r - xs)
+    ok_hi = ~np.isfinite(nb_hi) | (err <= np.abs(nb_hi - xs))
+    ok_lo = err <= np.abs(nb_lo - xs)
+    assert ok_hi.all() and ok_lo.all()
+    tie = (err > 0) & ((err == np.abs(nb_hi - xs)) | (err == np.abs(nb_lo - xs)))
+    assert ((b[tie] & 1) == 0).all()
+
+
+def test_nan_becomes_canonical_quiet_nan():
+    x = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF812345], dtype=np.uint32).view(np.float32)
+    assert round_bf16_bits(x).tolist() == [0x7FC0, 0xFFC0, 0x7FC0, 0xFFC0]
+    assert round_f16_bits(x).tolist() == [0x7E00, 0xFE00, 0x7E00, 0xFE00]
+
+
+def test_every_f16_and_bf16_value_rounds_to_itself():
+    allbits = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16)
+    for to_f32, rnd in ((f16_bits_to_f32, round_f16_bits), (bf16_bits_to_f32, round_bf16_bits)):
+        vals = to_f32(allbits)
+        keep = ~np.isnan(vals)
+        assert np.array_equal(rnd(vals[keep]), allbits[keep])
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_cache_returns_what_it_stores(dtype):
+    """test_float16_cache_rounds_what_it_stores: the stored values, the new chunk
+    included, are the rounded inputs ("KV cache, ...", section 2.5)."""
+    rng = np.random.default_rng(5)
+    oc = OracleCache(2, 2, 4, 2, 8, 16, dtype)
+    k1, v1 = _rand(rng, 2, 2, 5, 8), _rand(rng, 2, 2, 5, 8)
+    oc.append(0, k1, v1)
+    k2, v2 = _rand(rng, 2, 2, 3, 8), _rand(rng, 2, 2, 3, 8)
+    oc.append(0, k2, v2)
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    want = torch.from_numpy(np.concatenate([k1, k2], axis=2)).to(tdt).float().numpy()
+    assert np.array_equal(oc.K[0, :, :, :8], want)
+    assert oc.nbytes() * 2 == OracleCache(2, 2, 4, 2, 8, 16, "fp32").nbytes()
+
+
+# ---------------------------------------------------------------------------
+# Attention values: brute force, a library routine, closed forms
+# ---------------------------------------------------------------------------
+
+def _brute_attend(K, V, q, s, T, G, shift):
+    """Explicit loops with math.exp; shift=True subtracts the row max first."""
+    B, Hq, _, D = q.shape
+    out = np.zeros(q.shape)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for i in range(T):
+                n = s[b] + i + 1
+                z = []
+                for j in range(n):
+                    acc = 0.0
+                    for c in range(D):
+                        acc += float(q[b, h, i, c]) * float(K[b, g, j, c])
+                    z.append(acc / math.sqrt(D))
+                mx = max(z) if shift else 0.0
+                w = [math.exp(zj - mx) for zj in z]
+                tot = sum(w)
+                for c in range(D):
+                    out[b, h, i, c] = sum(w[j] * float(V[b, g, j, c]) for j in range(n)) / tot
+    return out
+
+
+@pytest.mark.parametrize("shift", [True, False])
+@pytest.mark.parametrize("G,T", [(1, 1), (2, 1), (2, 3), (3, 2)])
+def test_attend_brute_force_tiny(shift, G, T):
+    rng = np.random.default_rng(11 + G * 7 + T)
+    B, Hkv, D = 2, 2, 4
+    pre = [2, 3]
+    oc = OracleCache(1, B, Hkv * G, Hkv, D, 8)
+    # rows of different lengths: append the common part, truncate row 0 back
+    kp, vp = _rand(rng, B, Hkv, 3, D), _rand(rng, B, Hkv, 3, D)
+    oc.append(0, kp, vp)
+    oc.truncate(np.array(pre))
+    k, v, q = _rand(rng, B, Hkv, T, D), _rand(rng, B, Hkv, T, D), _rand(rng, B, Hkv * G, T, D)
+    oc.append(0, k, v)
+    got = oc.attend(0, q)
+    want = _brute_attend(oc.K[0], oc.V[0], q, pre, T, G, shift)
+    assert np.max(np.abs(got - want)) < 1e-13
+
+
+def test_attend_matches_torch_sdpa_with_explicit_mask():
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, D, s, T = 2, 6, 2, 16, 5, 3
+    G = Hq // Hkv
+    oc = OracleCache(1, B, Hq, Hkv, D, 12)
+    oc.append(0, _rand(rng, B, Hkv, s, D), _rand(rng, B, Hkv, s, D))
+    oc.append(0, _rand(rng, B, Hkv, T, D), _rand(rng, B, Hkv, T, D))
+    q = _rand(rng, B, Hq, T, D)
+    got = oc.attend(0, q)
+    Kt = torch.from_numpy(oc.K[0, :, :, :s + T].astype(np.float64)).repeat_interleave(G, dim=1)
+    Vt = torch.from_numpy(oc.V[0, :, :, :s + T].astype(np.float64)).repeat_interleave(G, dim=1)
+    mask = torch.from_numpy(np.tril(np.ones((T, s + T), dtype=bool), k=s))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64)), Kt.contiguous(), Vt.contiguous(), attn_mask=mask)
+    assert np.max(np.abs(got - ref.numpy())) < 1e-13
+    # at s = 0 the top-left causal mask of the library is the right one
+    oc0 = OracleCache(1, B, Hq, Hkv, D, 8)
+    k0, v0 = _rand(rng, B, Hkv, 4, D), _rand(rng, B, Hkv, 4, D)
+    oc0.append(0, k0, v0)
+    q0 = _rand(rng, B, Hq, 4, D)
+    ref0 = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q0.astype(np.float64)),
+        torch.from_numpy(k0.astype(np.float64)).repeat_interleave(G, 1).contiguous(),
+        torch.from_numpy(v0.astype(np.float64)).repeat_interleave(G, 1).contiguous(), is_causal=True)
+    assert np.max(np.abs(oc0.attend(0, q0) - ref0.numpy())) < 1e-13
+
+
+def test_closed_forms():
+    rng = np.random.default_rng(4)
+    B, Hq, Hkv, D = 1, 4, 2, 8
+    # q = 0: uniform weights, the output of query i is the mean of V over keys 0 .. s + i
+    oc = OracleCache(1, B, Hq, Hkv, D, 16)
+    oc.append(0, _rand(rng, B, Hkv, 6, D), _rand(rng, B, Hkv, 6, D))
+    oc.append(0, _rand(rng, B, Hkv, 3, D), _rand(rng, B, Hkv, 3, D))
+    out = oc.attend(0, np.zeros((B, Hq, 3, D), np.float32))
+    for h in range(Hq):
+        for i in range(3):
+            mean = oc.V[0, 0, h // 2, :6 + i + 1].astype(np.float64).mean(axis=0)
+            assert np.allclose(out[0, h, i], mean, atol=1e-15, rtol=0)
+    # s = 0, T = 1: the only key is the token itself, so out = v_0 exactly
+    oc1 = OracleCache(1, B, Hq, Hkv, D, 4)
+    k, v = _rand(rng, B, Hkv, 1, D), _rand(rng, B, Hkv, 1, D)
+    oc1.append(0, k, v)
+    o1 = oc1.attend(0, _rand(rng, B, Hq, 1, D))
+    for h in range(Hq):
+        assert np.array_equal(o1[0, h, 0], v[0, h // 2, 0].astype(np.float64))
+    # V constant c: out = c whatever the weights
+    oc2 = OracleCache(1, B, Hq, Hkv, D, 16)
+    kk = _rand(rng, B, Hkv, 7, D, scale=3.0)
+    oc2.append(0, kk, np.full((B, Hkv, 7, D), 0.375, np.float32))
+    o2 = oc2.attend(0, _rand(rng, B, Hq, 7, D, scale=3.0))
+    assert np.allclose(o2, 0.375, atol=1e-15, rtol=0)
+    # identical q within one group gives identical outputs; across groups it does not
+    qq = np.repeat(_rand(rng, B, 1, 7, D), Hq, axis=1)
+    oc3 = OracleCache(1, B, Hq, Hkv, D, 16)
+    oc3.append(0, _rand(rng, B, Hkv, 7, D), _rand(rng, B, Hkv, 7, D))
+    o3 = oc3.attend(0, qq)
+    assert np.array_equal(o3[0, 0], o3[0, 1]) and np.array_equal(o3[0, 2], o3[0, 3])
+    assert not np.allclose(o3[0, 0], o3[0, 2])
+
+
+def test_group_of_one_is_multi_head_attention():
+    """With H_q = H_kv every head has its own K/V; compare with torch's MHA math."""
+    rng = np.random.default_rng(8)
+    B, H, D, n = 2, 3, 8, 9
+    oc = OracleCache(1, B, H, H, D, 12)
+    k, v, q = _rand(rng, B, H, n, D), _rand(rng, B, H, n, D), _rand(rng, B, H, n, D)
+    oc.append(0, k, v)
+    got = oc.attend(0, q)
+    sc = torch.from_numpy(q.astype(np.float64)) @ torch.from_numpy(k.astype(np.float64)).transpose(-1, -2)
+    sc = sc / math.sqrt(D)
+    sc = sc.masked_fill(~torch.ones(n, n, dtype=torch.bool).tril(), float("-inf"))
+    ref = torch.softmax(sc, -1) @ torch.from_numpy(v.astype(np.float64))
+    assert np.max(np.abs(got - ref.numpy())) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Invariants the pages state
+# ---------------------------------------------------------------------------
+
+def _run_schedule(chunks, k, v, q, dtype="fp32", max_len=None):
+    B, Hkv, N, D = k.shape
+    oc = OracleCache(1, B, q.shape[1], Hkv, D, max_len or N, dtype)
+    outs, t = [], 0
+    for m in chunks:
+        oc.append(0, k[:, :, t:t + m], v[:, :, t:t + m])
+        outs.append(oc.attend(0, q[:, :, t:t + m]))
+        t += m
+    return oc, np.concatenate(outs, axis=2)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_cached_equals_full_recompute(dtype):
+    """test_cached_logits_equal_full_recompute: a prefill then one token per call
+    equals one pass over the whole sequence ("KV cache, ...", sections 2.2-2.3)."""
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, D, N = 2, 4, 2, 16, 24
+    k, v, q = _rand(rng, B, Hkv, N, D), _rand(rng, B, Hkv, N, D), _rand(rng, B, Hq, N, D)
+    _, inc = _run_schedule([8] + [1] * 16, k, v, q, dtype)
+    _, full = _run_schedule([N], k, v, q, dtype)
+    assert np.max(np.abs(inc - full)) < 1e-13
+
+
+def test_chunked_prefill_equals_whole():
+    """Chunks of 3, 1, 5, 2 and of 30 + 18 and single tokens build the same cache and
+    the same outputs ("KV cache, ...", section 4; "kv-cache-decoding", tests)."""
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, D = 1, 4, 2, 8
+    for schedules in ([[3, 1, 5, 2], [11], [1] * 11], [[30, 18], [48], [1] * 48]):
+        N = sum(schedules[0])
+        k, v, q = _rand(rng, B, Hkv, N, D), _rand(rng, B, Hkv, N, D), _rand(rng, B, Hq, N, D)
+        ref_c, ref_o = _run_schedule(schedules[1], k, v, q)
+        for sch in (schedules[0], schedules[2]):
+            c, o = _run_schedule(sch, k, v, q)
+            assert np.array_equal(c.K, ref_c.K) and np.array_equal(c.V, ref_c.V)
+            assert np.max(np.abs(o - ref_o)) < 1e-13
+
+
+def test_appending_leaves_earlier_slots_unchanged():
+    rng = np.random.default_rng(23)
+    oc = OracleCache(2, 2, 4, 2, 8, 64, "bf16")
+    for layer in range(2):
+        oc.append(layer, _rand(rng, 2, 2, 30, 8), _rand(rng, 2, 2, 30, 8))
+    before_k, before_v = oc.K[:, :, :, :30].copy(), oc.V[:, :, :, :30].copy()
+    for _ in range(20):
+        for layer in range(2):
+            oc.append(layer, _rand(rng, 2, 2, 1, 8), _rand(rng, 2, 2, 1, 8))
+    assert np.array_equal(oc.K[:, :, :, :30], before_k) and np.array_equal(oc.V[:, :, :, :30], before_v)
+
+
+def test_truncate_then_append_equals_never_appended():
+    """test_truncate_rolls_back ("KV cache, ...", section 2.4): every layer rolls back."""
+    rng = np.random.default_rng(24)
+    L, B, Hq, Hkv, D = 3, 2, 4, 2, 8
+    pre = [(_rand(rng, B, Hkv, 6, D), _rand(rng, B, Hkv, 6, D)) for _ in range(L)]
+    draft = [(_rand(rng, B, Hkv, 4, D), _rand(rng, B, Hkv, 4, D)) for _ in range(L)]
+    final = [(_rand(rng, B, Hkv, 2, D), _rand(rng, B, Hkv, 2, D)) for _ in range(L)]
+    q = _rand(rng, B, Hq, 2, D)
+    a = OracleCache(L, B, Hq, Hkv, D, 16, "fp16")
+    b = OracleCache(L, B, Hq, Hkv, D, 16, "fp16")
+    for layer in range(L):
+        a.append(layer, *pre[layer])
+        b.append(layer, *pre[layer])
+        a.append(layer, *draft[layer])
+    a.truncate(6)
+    assert a.seq_len().tolist() == [6, 6] and all(a.seq_len(layer).tolist() == [6, 6] for layer in range(L))
+    outs_a, outs_b = [], []
+    for layer in range(L):
+        a.append(layer, *final[layer])
+        b.append(layer, *final[layer])
+        outs_a.append(a.attend(layer, q))
+        outs_b.append(b.attend(layer, q))
+    assert np.array_equal(a.K[:, :, :, :8], b.K[:, :, :, :8])
+    assert np.array_equal(np.stack(outs_a), np.stack(outs_b))
+    # storage past the new fill keeps the stale draft values: nothing was freed
+    assert np.array_equal(a.K[0, :, :, 8:10], round_to_storage(draft[0][0][:, :, 2:4], "fp16"))
+
+
+def test_seq_len_commits_after_every_layer():
+    rng = np.random.default_rng(25)
+    L, B = 4, 2
+    oc = OracleCache(L, B, 4, 2, 8, 32)
+    for layer in range(L):
+        oc.append(layer, _rand(rng, B, 2, 5, 8), _rand(rng, B, 2, 5, 8))
+    for layer in range(L - 1):
+        oc.append(layer, _rand(rng, B, 2, 3, 8), _rand(rng, B, 2, 3, 8))
+        assert oc.seq_len().tolist() == [5, 5]                 # not yet committed
+        assert oc.seq_len(layer).tolist() == [8, 8]
+        assert oc.positions(3)[0].tolist() == [5, 6, 7]         # positions read before the pass
+    oc.append(L - 1, _rand(rng, B, 2, 3, 8), _rand(rng, B, 2, 3, 8))
+    assert oc.seq_len().tolist() == [8, 8]
+
+
+def test_errors_change_nothing():
+    """test_update_copies_and_checks: errors leave the cache as it was."""
+    rng = np.random.default_rng(26)
+    oc = OracleCache(2, 2, 4, 2, 8, 10, "bf16")
+    oc.append(0, _rand(rng, 2, 2, 8, 8), _rand(rng, 2, 2, 8, 8))
+    snap = (oc.K.copy(), oc.V.copy(), oc.fill.copy())
+
+    def same():
+        return np.array_equal(oc.K, snap[0]) and np.array_equal(oc.V, snap[1]) and np.array_equal(oc.fill, snap[2])
+
+    with pytest.raises(OracleCapacityError):
+        oc.append(0, _rand(rng, 2, 2, 3, 8), _rand(rng, 2, 2, 3, 8))
+    assert same()
+    with pytest.raises(OracleError):
+        oc.append(2, _rand(rng, 2, 2, 1, 8), _rand(rng, 2, 2, 1, 8))
+    with pytest.raises(OracleError):
+        oc.append(0, np.zeros((2, 2, 0, 8), np.float32), np.zeros((2, 2, 0, 8), np.float32))
+    with pytest.raises(OracleError):
+        oc.append(0, _rand(rng, 2, 3, 1, 8), _rand(rng, 2, 3, 1, 8))
+    with pytest.raises(OracleError):
+        oc.attend(1, _rand(rng, 2, 4, 1, 8))                 # nothing appended to layer 1
+    with pytest.raises(OracleError):
+        oc.truncate(1)                                       # committed length is 0 (layer 1 empty)
+    assert same()
+    oc.append(1, _rand(rng, 2, 2, 8, 8), _rand(rng, 2, 2, 8, 8))
+    snap = (oc.K.copy(), oc.V.copy(), oc.fill.copy())
+    with pytest.raises(OracleError):
+        oc.truncate(9)                                       # cannot extend
+    with pytest.raises(OracleError):
+        oc.truncate(-1)
+    assert same()
+    with pytest.raises(OracleError):
+        OracleCache(1, 1, 3, 2, 8, 4)                        # 3 query heads over 2 KV heads
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each pitfall of "KV cache, ...", section 5 fails a pin
+# ---------------------------------------------------------------------------
+
+class _NoOffsetMask(OracleCache):
+    """Pitfall 3: a decode mask without the offset (q_offset = 0)."""
+
+    def attend(self, layer, q, rows=None):
+        T = q.shape[2]
+        saved = self.fill[layer].copy()
+        out = np.zeros((self.B, self.Hq, T, self.D))
+        for b in range(self.B):
+            n = int(saved[b])
+            Kg = self.K[layer, b].astype(np.float64)
+            for h in range(self.Hq):
+                g = h // self.G
+                z = q[b, h].astype(np.float64) @ Kg[g, :n].T / math.sqrt(self.D)
+                vis = causal_mask(T, n, 0)
+                z = np.where(vis, z, -np.inf)
+                w = np.exp(z - z.max(axis=1, keepdims=True))
+                out[b, h] = (w @ self.V[layer, b, g, :n].astype(np.float64)) / w.sum(1, keepdims=True)
+        return out
+
+
+class _NewChunkOnly(OracleCache):
+    """Pitfall 4: attention over the new chunk only (the cache is ignored)."""
+
+    def attend(self, layer, q, rows=None):
+        T = q.shape[2]
+        keep = self.fill[layer].copy()
+        sub = OracleCache(1, self.B, self.Hq, self.Hkv, self.D, T, self.dtype)
+        for b in range(self.B):
+            n = int(keep[b])
+            sub.K[0, b, :, :T] = self.K[layer, b, :, n - T:n]
+            sub.V[0, b, :, :T] = self.V[layer, b, :, n - T:n]
+        sub.fill[:] = T
+        return sub.attend(0, q)
+
+
+class _CommitPerLayer(OracleCache):
+    """Pitfall 2: the committed length moves after the first layer's append."""
+
+    def seq_len(self, layer=-1):
+        if layer == -1:
+            return self.fill.max(axis=0).copy()
+        return super().seq_len(layer)
+
+
+class _TruncateOneLayer(OracleCache):
+    """Pitfall 6: truncate rolls back layer 0 only."""
+
+    def truncate(self, n):
+        self.fill[0, :] = n
+
+
+class _RawChunk(OracleCache):
+    """Pitfall 8: a 16-bit cache whose newest chunk is used unrounded."""
+
+    def append(self, layer, k_new, v_new):
+        super().append(layer, k_new, v_new)
+        T = k_new.shape[2]
+        for b in range(self.B):
+            n = int(self.fill[layer, b])
+            self.K[layer, b, :, n - T:n] = k_new[b]
+            self.V[layer, b, :, n - T:n] = v_new[b]
+
+
+def test_planted_mask_without_offset_fails_recompute_pin():
+    rng = np.random.default_rng(31)
+    k, v, q = _rand(rng, 1, 2, 12, 8), _rand(rng, 1, 2, 12, 8), _rand(rng, 1, 4, 12, 8)
+    _, full = _run_schedule([12], k, v, q)
+    oc = _NoOffsetMask(1, 1, 4, 2, 8, 12)
+    outs, t = [], 0
+    for m in [4] + [1] * 8:
+        oc.append(0, k[:, :, t:t + m], v[:, :, t:t + m])
+        outs.append(oc.attend(0, q[:, :, t:t + m]))
+        t += m
+    assert np.max(np.abs(np.concatenate(outs, axis=2) - full)) > 1e-3
+
+
+def test_planted_new_chunk_only_fails_hand_example_pin():
+    k = np.array([[[[1, 2], [3, 4]]]], np.float32)
+    oc = _NewChunkOnly(1, 1, 1, 1, 2, 4)
+    oc.append(0, k, k)
+    oc.append(0, np.array([[[[5, 6]]]], np.float32), np.array([[[[5, 6]]]], np.float32))
+    out = oc.attend(0, np.array([[[[0, 0]]]], np.float32))
+    # q = 0 must average all three stored values: [3, 4]
+    assert not np.allclose(out[0, 0, 0], [3.0, 4.0])
+    good = OracleCache(1, 1, 1, 1, 2, 4)
+    good.append(0, k, k)
+    good.append(0, np.array([[[[5, 6]]]], np.float32), np.array([[[[5, 6]]]], np.float32))
+    assert np.allclose(good.attend(0, np.zeros((1, 1, 1, 2), np.float32))[0, 0, 0], [3.0, 4.0])
+
+
+def test_planted_commit_per_layer_fails_commit_pin():
+    oc = _CommitPerLayer(2, 1, 2, 1, 4, 8)
+    oc.append(0, np.ones((1, 1, 3, 4), np.float32), np.ones((1, 1, 3, 4), np.float32))
+    assert oc.seq_len().tolist() != [0]        # the pin expects 0 until the last layer appends
+
+
+def test_planted_one_layer_truncate_fails_rollback_pin():
+    oc = _TruncateOneLayer(2, 1, 2, 1, 4, 8)
+    for layer in range(2):
+        oc.append(layer, np.ones((1, 1, 5, 4), np.float32), np.ones((1, 1, 5, 4), np.float32))
+    oc.truncate(2)
+    assert not all(oc.seq_len(layer).tolist() == [2] for layer in range(2))
+
+
+def test_planted_raw_chunk_fails_rounding_pin():
+    rng = np.random.default_rng(32)
+    k = _rand(rng, 1, 1, 3, 8)
+    oc = _RawChunk(1, 1, 1, 1, 8, 4, "fp16")
+    oc.append(0, k, k)
+    want = torch.from_numpy(k).to(torch.float16).float().numpy()
+    assert not np.array_equal(oc.K[0, :, :, :3], want)
