@@ -1,0 +1,210 @@
+"""Batched-decode benchmark on one MI355X.
+
+Workload: one Llama-3-8B-shaped attention layer decoding a batch of 32
+sequences: H_q=32, H_kv=8, d_h=128, bf16 cache with max_len 4096, per-row
+committed lengths drawn uniformly from {1024..4095} (seed 0), T=1.
+
+One step = the whole hot path for one token of every row: truncate the cache
+back to its drawn lengths (host bookkeeping), append the step's k/v (append
+kernel), attend (split-K decode kernel + combine kernel). Inputs are resident
+in HBM before timing starts. Steps rotate over --instances independent caches
+(default 4, 2.1 GB of K/V in all) so the 256 MB Infinity Cache cannot hold the
+working set between steps.
+
+Prints one JSON line. `value` is the step's algorithmic HBM traffic (K and V of
+every visible position, q, the float32 output, and the append's read+write)
+divided by the step time. The roofline object times the decode attention
+(partial + combine kernels) alone with HIP events on the stream it runs on.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn HBM GB/s (% peak) + tokens/s, GQA 32q/8kv d128 ctx4k B=32"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+B, HQ, HKV, D, MAX_LEN = 32, 32, 8, 128, 4096
+WORKLOAD = ("batched decode, one Llama-3-8B-shaped layer: B=32, H_q=32, H_kv=8, d_h=128, "
+            "bf16 cache max_len 4096, lengths U{1024..4095} seed 0, T=1")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time budget of the oracle sample")
+    return ap.parse_args()
+
+
+def lengths_seed0() -> np.ndarray:
+    from kv_cached_gqa_amd.workloads import batched_lengths
+    return batched_lengths(np.random.default_rng(0), B, 1024, MAX_LEN - 1)
+
+
+def step_bytes(lengths) -> tuple[int, int]:
+    from kv_cached_gqa_amd import work
+    att = work.attend_bytes(lengths, 1, HQ, HKV, D, "bf16", "bf16")
+    app = work.append_bytes(B, HKV, 1, D, "bf16", "bf16")
+    return att, app
+
+
+def gpu_bench(args, lengths):
+    import torch
+    from kv_cached_gqa_amd.kvc import KVCache
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    caches = []
+    for c in range(args.instances):
+        gen.manual_seed(1000 + c)
+        cache = KVCache(1, HKV, D, MAX_LEN, batch=B, n_q_heads=HQ, dtype="bf16", device=dev)
+        k = torch.randn((B, HKV, MAX_LEN - 1, D), generator=gen, device=dev, dtype=torch.bfloat16)
+        v = torch.randn((B, HKV, MAX_LEN - 1, D), generator=gen, device=dev, dtype=torch.bfloat16)
+        cache.append(0, k, v)
+        del k, v
+        cache.truncate(lengths)
+        caches.append(cache)
+    n_in = 8
+    gen.manual_seed(7)
+    qs = [torch.randn((B, HQ, 1, D), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(n_in)]
+    ks = [torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(n_in)]
+    vs = [torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(n_in)]
+    outs = [torch.empty((B, HQ, 1, D), device=dev, dtype=torch.float32) for _ in range(args.instances)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        c = i % args.instances
+        cache = caches[c]
+        cache.truncate(lengths)
+        cache.append(0, ks[i % n_in], vs[i % n_in])
+        cache.attend(0, qs[i % n_in], out=outs[c])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # decode attention alone (split-K partial + combine), events on the same stream
+    for c in caches:
+        c.truncate(lengths)
+        c.append(0, ks[0], vs[0])
+    torch.cuda.synchronize()
+    reps = max(50, args.steps)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for i in range(reps):
+        c = i % args.instances
+        caches[c].attend(0, qs[i % n_in], out=outs[c])
+    a1.record(stream)
+    torch.cuda.synchronize()
+    us_attend = a0.elapsed_time(a1) * 1e3 / reps
+    for c in caches:
+        c.close()
+    return ms_step, us_attend, wall
+
+
+def cpu_baseline(lengths, seconds: float) -> dict:
+    """The oracle, as it stands, on the same workload: whole steps (truncate,
+    append, attend of all 32 rows) until `seconds` of CPU time are spent, with
+    BLAS limited to one thread. The preload is not timed."""
+    from threadpoolctl import threadpool_limits
+    from oracle import OracleCache
+    from kv_cached_gqa_amd.workloads import draw_kv, draw_qkv, SHAPES
+
+    shape = SHAPES["llama3_8b_layer_decode_bf16"]
+    oc = OracleCache(1, B, HQ, HKV, D, MAX_LEN, "bf16")
+    rng = np.random.default_rng(0)
+    rng.integers(1024, MAX_LEN, size=B)          # the lengths draw (already known)
+    k, v = draw_kv(rng, shape, MAX_LEN - 1)
+    oc.append(0, k, v)
+    del k, v
+    oc.truncate(lengths)
+    inputs = [draw_qkv(rng, shape, 1) for _ in range(4)]
+    att, app = step_bytes(lengths)
+    steps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            q, k, v = inputs[steps % len(inputs)]
+            oc.truncate(lengths)
+            oc.append(0, k, v)
+            oc.attend(0, q)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    t_step = el / steps
+    return {"value": round((att + app) / t_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole decode steps of the same workload (all 32 rows), float64 NumPy, "
+                      f"1 BLAS thread, {el:.1f} s",
+            "tokens_per_s": round(B / t_step, 2), "s_per_step": round(t_step, 4)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path shards by (row, KV head) with no exchange, so no multi-GPU figure is produced.",
+              file=sys.stderr)
+        sys.exit(2)
+    lengths = lengths_seed0()
+    att, app = step_bytes(lengths)
+    ms_step, us_attend, wall = gpu_bench(args, lengths)
+    gbs = (att + app) / (ms_step * 1e-3) / 1e9
+    att_gbs = att / (us_attend * 1e-6) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": B, "n_q_heads": HQ, "n_kv_heads": HKV, "d_head": D,
+                   "max_len": MAX_LEN, "T": 1, "cache_instances": args.instances,
+                   "mean_context": float(np.mean(lengths) + 1)},
+        "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "bytes_per_step": att + app,
+        "roofline": {"bound": "hbm", "kernel": "decode attention: decode_partial + decode_combine",
+                     "achieved": round(att_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(att_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": att, "launch_us": round(us_attend, 3)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(lengths, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

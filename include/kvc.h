@@ -1,0 +1,146 @@
+/*
+ * kvc.h - C ABI of libkvc: a preallocated KV cache with grouped-query
+ * attention over it, for AMD Instinct MI355X (gfx950).
+ *
+ * The contract follows the KVCache interface of "KV cache, incremental
+ * decode, incremental UTF-8 detokenizer, generate" (section 4, The interface;
+ * section 2.3 for the committed length, positions and mask; section 2.4 for
+ * rollback; section 2.5 for the storage dtype and nbytes). Storage layout is
+ * the (L, B, H, max_len, d_head) cache of "Generation and the KV Cache"
+ * (the KVCache paragraph) with H = the number of KV heads; query heads share
+ * KV heads in consecutive groups as in "Heads, GQA and K/V cache"
+ * ("Four queries, two sets of K/V").
+ *
+ * Conventions for every call:
+ *  - Return value: KVC_OK (0) or a negative kvc_status. On any error the
+ *    cache state (fill counts and storage) is unchanged; arguments are
+ *    validated before any device work is enqueued.
+ *  - Device pointers are HIP device addresses on the device that holds the
+ *    cache storage; they must stay valid until the work enqueued on
+ *    `stream` has run. Host pointers are read during the call only.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream). All calls
+ *    on one handle must be issued in stream order by one thread: the host
+ *    metadata advances when a call returns, the device work runs later in
+ *    stream order. A handle is not thread-safe.
+ *  - Tensors are dense, row-major (C order), with the shapes stated.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. fp32 = IEEE binary32, fp16 = IEEE binary16, bf16 = bfloat16. */
+typedef enum kvc_dtype { KVC_F32 = 0, KVC_F16 = 1, KVC_BF16 = 2 } kvc_dtype;
+
+typedef enum kvc_status {
+    KVC_OK = 0,
+    KVC_ERR_ARG = -1,         /* a bad argument: null pointer, shape, layer index, T < 1 */
+    KVC_ERR_CAPACITY = -2,    /* an append would write past max_len */
+    KVC_ERR_STATE = -3,       /* attend before the chunk was appended; truncate past the committed length */
+    KVC_ERR_DTYPE = -4,       /* unknown dtype code */
+    KVC_ERR_STORAGE = -5,     /* storage null, too small or not 16-byte aligned */
+    KVC_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
+    KVC_ERR_NOMEM = -7,       /* host or device allocation failed */
+    KVC_ERR_UNSUPPORTED = -8  /* a shape outside what the kernels handle (d_head not 32, 64 or 128) */
+} kvc_status;
+
+/* Shape of a cache. n_q_heads must be a multiple of n_kv_heads (G = n_q_heads /
+ * n_kv_heads query heads share each KV head; query head h reads KV head h / G).
+ * d_head is 32, 64 or 128. max_len * d_head must be below 2^31. */
+typedef struct kvc_config {
+    int32_t n_layers;
+    int32_t batch;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t d_head;
+    int32_t dtype;      /* kvc_dtype of the stored keys and values */
+    int64_t max_len;    /* preallocated positions per row, N_max */
+} kvc_config;
+
+typedef struct kvc_cache kvc_cache;
+
+/* Create a handle over caller-owned storage.
+ *  k_store, v_store: device buffers, each at least store_bytes_each bytes,
+ *    holding [n_layers][batch][n_kv_heads][max_len][d_head] elements of
+ *    cfg->dtype, 16-byte aligned, ZERO-FILLED by the caller (never-written
+ *    slots read as zero, as in the shapes table of "kv-cache-decoding").
+ *    store_bytes_each must be >= nbytes / 2. The caller keeps ownership and
+ *    must keep both buffers alive for the life of the handle.
+ *  out: receives the handle. Every fill count starts at 0.
+ * The library also owns a device workspace for split-K partial results,
+ * allocated on the storage's device at the first kvc_attend and freed by
+ * kvc_destroy. No device work is done here.
+ * Errors: KVC_ERR_ARG (null cfg/out, nonpositive dims, n_q_heads not a multiple
+ * of n_kv_heads, max_len * d_head >= 2^31), KVC_ERR_DTYPE, KVC_ERR_UNSUPPORTED,
+ * KVC_ERR_STORAGE, KVC_ERR_NOMEM. */
+int kvc_create(const kvc_config* cfg, void* k_store, void* v_store,
+               uint64_t store_bytes_each, kvc_cache** out);
+
+/* Free the handle and its workspace (never the caller's storage). Waits for
+ * the device to finish work that may use the workspace. NULL is a no-op. */
+void kvc_destroy(kvc_cache* cache);
+
+/* Append a chunk of T positions to one layer ("KV cache, ...", section 4,
+ * update; "kv-cache-decoding", step 5).
+ *  k_new, v_new: device [batch][n_kv_heads][T][d_head] of in_dtype.
+ *  Row b's chunk is written at slots [fill[layer][b], fill[layer][b] + T),
+ *  converted to the storage dtype with IEEE round-to-nearest-even (NaN becomes
+ *  the canonical quiet NaN of its sign; overflow becomes infinity), and then
+ *  fill[layer][b] += T. The inputs are copied: the caller may reuse them once
+ *  the stream has passed this call. Earlier slots are never touched, so the
+ *  stored values the cache hands back are exactly the rounded inputs.
+ *  The committed length (kvc_seq_len with layer -1) moves only when every
+ *  layer has appended ("KV cache, ...", section 2.3).
+ * Errors: KVC_ERR_ARG (null handle or pointer, layer out of range, T < 1),
+ * KVC_ERR_DTYPE, KVC_ERR_CAPACITY (fill + T > max_len for some row), KVC_ERR_HIP. */
+int kvc_append(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+               int32_t in_dtype, int32_t T, void* stream);
+
+/* Attention of a chunk's queries over everything a layer holds
+ * ("KV cache, ...", section 2.3; "kv-cache-decoding", shapes table).
+ *  q: device [batch][n_q_heads][T][d_head] of q_dtype. For an fp16/bf16 cache
+ *     an fp32 q is first rounded to the storage dtype (round-to-nearest-even);
+ *     a q already in a 16-bit type, or any q for an fp32 cache, is used exactly.
+ *  out: device float32 [batch][n_q_heads][T][d_head].
+ *  The chunk is the last T positions appended to the layer: row b's queries sit
+ *  at absolute positions s_b + i, s_b = fill[layer][b] - T, i < T, and query i
+ *  sees keys j <= s_b + i (causal_mask(T, s_b + T, q_offset = s_b)). Query head
+ *  h reads KV head h / G. out = softmax(q K^T / sqrt(d_head)) V with float32
+ *  accumulation. Read-only on the cache; fills are unchanged.
+ * Errors: KVC_ERR_ARG (null pointer, layer out of range, T < 1), KVC_ERR_DTYPE,
+ * KVC_ERR_STATE (fill[layer][b] < T for some row), KVC_ERR_NOMEM, KVC_ERR_HIP. */
+int kvc_attend(kvc_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
+               int32_t T, float* out, void* stream);
+
+/* Per-row lengths ("KV cache, ...", section 2.3, seq_len).
+ *  layer = -1: the committed length s_b = min over layers of fill[layer][b];
+ *  0 <= layer < n_layers: that layer's fill count.
+ *  out_lens: host int64 [batch]. Host metadata only; no device work, no sync.
+ * Errors: KVC_ERR_ARG. */
+int kvc_seq_len(const kvc_cache* cache, int32_t layer, int64_t* out_lens);
+
+/* Roll back ("KV cache, ...", section 2.4): set EVERY layer's fill of each row
+ * to n. n: host int64, count = 1 (one length for all rows) or count = batch
+ * (one per row). Each n_b must satisfy 0 <= n_b <= committed length s_b.
+ * Storage is not cleared or copied; the next append overwrites from n_b.
+ * Host metadata only. Errors: KVC_ERR_ARG (null, count), KVC_ERR_STATE (n out of
+ * range). */
+int kvc_truncate(kvc_cache* cache, const int64_t* n, int32_t count);
+
+/* Storage bytes, 2 * L * B * H_kv * max_len * d_head * itemsize
+ * ("KV cache, ...", section 2.5). Workspace and metadata are not counted.
+ * out: host uint64. Errors: KVC_ERR_ARG. */
+int kvc_nbytes(const kvc_cache* cache, uint64_t* out);
+
+/* A static, human-readable text for a kvc_status code. */
+const char* kvc_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

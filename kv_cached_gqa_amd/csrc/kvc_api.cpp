@@ -1,0 +1,305 @@
+// Host core and C ABI of libkvc (declared in include/kvc.h).
+//
+// The host side owns the bookkeeping the pages' KVCache contract defines
+// ("KV cache, incremental decode, ...", sections 2.3-2.5 and 4): a fill count
+// per (layer, batch row), the committed length as the minimum over layers,
+// truncate as a metadata-only rollback of every layer, and the exact byte
+// count. Every call validates all of its arguments before it touches state or
+// enqueues device work, so an error leaves the cache unchanged.
+//
+// Device work is enqueued on the caller's stream; metadata advances when the
+// enqueue succeeded, which keeps host state and stream order consistent
+// without any synchronisation.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kvc.h"
+#include "kvc_kernels.h"
+
+using kvc::kMaxDecodeBlocks;
+using kvc::kMaxDecodeRows;
+using kvc::kMaxRowsPerLaunch;
+
+struct kvc_cache {
+    kvc_config cfg;
+    void* k_store;
+    void* v_store;
+    std::vector<int64_t> fill;    // [n_layers][batch]
+    // split-K workspace, allocated on first attend on the storage's device
+    int device;
+    float* ws_o;
+    float* ws_ml;
+    int64_t ws_segments;
+};
+
+namespace {
+
+bool dtype_ok(int32_t dt) { return dt == KVC_F32 || dt == KVC_F16 || dt == KVC_BF16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+uint64_t storage_bytes(const kvc_config& c) {
+    return 2ull * static_cast<uint64_t>(c.n_layers) * c.batch * c.n_kv_heads * static_cast<uint64_t>(c.max_len) *
+           c.d_head * kvc::itemsize(c.dtype);
+}
+
+int64_t committed(const kvc_cache* c, int b) {
+    int64_t s = c->fill[b];
+    for (int l = 1; l < c->cfg.n_layers; ++l) s = std::min(s, c->fill[static_cast<size_t>(l) * c->cfg.batch + b]);
+    return s;
+}
+
+// Segments the decode workspace must hold: one per work-group plus one per unit
+// boundary inside a launch.
+int64_t workspace_segments(const kvc_config& c) {
+    const int64_t units = static_cast<int64_t>(std::min(c.batch, kMaxRowsPerLaunch)) * c.n_kv_heads;
+    return kMaxDecodeBlocks + units;
+}
+
+int ensure_workspace(kvc_cache* c) {
+    if (c->ws_o) return KVC_OK;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, c->k_store) != hipSuccess) return KVC_ERR_HIP;
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return KVC_ERR_HIP;
+    const int dev = attr.device;
+    if (dev != prev && hipSetDevice(dev) != hipSuccess) return KVC_ERR_HIP;
+    const int64_t segs = workspace_segments(c->cfg);
+    const size_t o_bytes = static_cast<size_t>(segs) * kMaxDecodeRows * c->cfg.d_head * sizeof(float);
+    const size_t ml_bytes = static_cast<size_t>(segs) * kMaxDecodeRows * 2 * sizeof(float);
+    void* o = nullptr;
+    void* ml = nullptr;
+    int rc = KVC_OK;
+    if (hipMalloc(&o, o_bytes) != hipSuccess) rc = KVC_ERR_NOMEM;
+    else if (hipMalloc(&ml, ml_bytes) != hipSuccess) {
+        (void)hipFree(o);
+        rc = KVC_ERR_NOMEM;
+    }
+    if (dev != prev) (void)hipSetDevice(prev);
+    if (rc != KVC_OK) {
+        (void)hipGetLastError();
+        return rc;
+    }
+    c->device = dev;
+    c->ws_o = static_cast<float*>(o);
+    c->ws_ml = static_cast<float*>(ml);
+    c->ws_segments = segs;
+    return KVC_OK;
+}
+
+// Work-groups for a decode launch: enough to fill the GPU (256 CUs, several
+// work-groups each) but never slices shorter than a few key tiles.
+void decode_split(int64_t total_keys, int32_t* n_blocks, int64_t* keys_per_block) {
+    constexpr int64_t kTarget = 1024;
+    constexpr int64_t kMinKeys = 64;
+    int64_t nb = (total_keys + kMinKeys - 1) / kMinKeys;
+    nb = std::max<int64_t>(1, std::min<int64_t>(nb, kTarget));
+    int64_t kpb = (total_keys + nb - 1) / nb;
+    nb = (total_keys + kpb - 1) / kpb;
+    *n_blocks = static_cast<int32_t>(nb);
+    *keys_per_block = kpb;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvc_strerror(int status) {
+    switch (status) {
+        case KVC_OK: return "ok";
+        case KVC_ERR_ARG: return "invalid argument";
+        case KVC_ERR_CAPACITY: return "append would exceed max_len";
+        case KVC_ERR_STATE: return "call not valid in the current cache state";
+        case KVC_ERR_DTYPE: return "unknown dtype";
+        case KVC_ERR_STORAGE: return "storage buffer null, too small or misaligned";
+        case KVC_ERR_HIP: return "HIP runtime error";
+        case KVC_ERR_NOMEM: return "out of memory";
+        case KVC_ERR_UNSUPPORTED: return "shape not supported by the kernels";
+        default: return "unknown status";
+    }
+}
+
+int kvc_create(const kvc_config* cfg, void* k_store, void* v_store, uint64_t store_bytes_each, kvc_cache** out) {
+    if (!cfg || !out) return KVC_ERR_ARG;
+    const kvc_config c = *cfg;
+    if (c.n_layers < 1 || c.batch < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.d_head < 1 || c.max_len < 1)
+        return KVC_ERR_ARG;
+    if (c.n_q_heads % c.n_kv_heads) return KVC_ERR_ARG;
+    if (c.max_len * static_cast<int64_t>(c.d_head) >= (int64_t(1) << 31)) return KVC_ERR_ARG;
+    if (!dtype_ok(c.dtype)) return KVC_ERR_DTYPE;
+    if (!kvc::decode_supported(c.d_head, c.dtype)) return KVC_ERR_UNSUPPORTED;
+    if (!k_store || !v_store || !aligned16(k_store) || !aligned16(v_store)) return KVC_ERR_STORAGE;
+    if (store_bytes_each < storage_bytes(c) / 2) return KVC_ERR_STORAGE;
+    kvc_cache* h = new (std::nothrow) kvc_cache();
+    if (!h) return KVC_ERR_NOMEM;
+    try {
+        h->fill.assign(static_cast<size_t>(c.n_layers) * c.batch, 0);
+    } catch (...) {
+        delete h;
+        return KVC_ERR_NOMEM;
+    }
+    h->cfg = c;
+    h->k_store = k_store;
+    h->v_store = v_store;
+    h->device = -1;
+    h->ws_o = nullptr;
+    h->ws_ml = nullptr;
+    h->ws_segments = 0;
+    *out = h;
+    return KVC_OK;
+}
+
+void kvc_destroy(kvc_cache* c) {
+    if (!c) return;
+    if (c->ws_o) {
+        int prev = 0;
+        (void)hipGetDevice(&prev);
+        (void)hipSetDevice(c->device);
+        (void)hipDeviceSynchronize();
+        (void)hipFree(c->ws_o);
+        (void)hipFree(c->ws_ml);
+        (void)hipSetDevice(prev);
+    }
+    delete c;
+}
+
+int kvc_append(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new, int32_t in_dtype, int32_t T,
+               void* stream) {
+    if (!c || !k_new || !v_new) return KVC_ERR_ARG;
+    const kvc_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || T < 1) return KVC_ERR_ARG;
+    if (!dtype_ok(in_dtype)) return KVC_ERR_DTYPE;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVC_ERR_ARG;
+    int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
+    for (int b = 0; b < cf.batch; ++b)
+        if (f[b] + T > cf.max_len) return KVC_ERR_CAPACITY;
+
+    const int64_t head_stride = cf.max_len * cf.d_head;
+    const int64_t row_stride = head_stride * cf.n_kv_heads;
+    const int64_t in_row = static_cast<int64_t>(cf.n_kv_heads) * T * cf.d_head * kvc::itemsize(in_dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
+        kvc::AppendArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.rows = std::min(kMaxRowsPerLaunch, cf.batch - row0);
+        a.k_cache = c->k_store;
+        a.v_cache = c->v_store;
+        a.k_in = static_cast<const char*>(k_new) + row0 * in_row;
+        a.v_in = static_cast<const char*>(v_new) + row0 * in_row;
+        a.layer_off = (static_cast<int64_t>(layer) * cf.batch + row0) * row_stride;
+        a.row_stride = row_stride;
+        a.head_stride = head_stride;
+        a.H = cf.n_kv_heads;
+        a.T = T;
+        a.D = cf.d_head;
+        a.in_dtype = in_dtype;
+        a.st_dtype = cf.dtype;
+        for (int b = 0; b < a.rows; ++b) a.fill[b] = static_cast<int32_t>(f[row0 + b]);
+        if (kvc::launch_append(a, s) != hipSuccess) return KVC_ERR_HIP;
+    }
+    for (int b = 0; b < cf.batch; ++b) f[b] += T;
+    return KVC_OK;
+}
+
+int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int32_t T, float* out, void* stream) {
+    if (!c || !q || !out) return KVC_ERR_ARG;
+    const kvc_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || T < 1) return KVC_ERR_ARG;
+    if (!dtype_ok(q_dtype)) return KVC_ERR_DTYPE;
+    if (!aligned16(q) || !aligned16(out)) return KVC_ERR_ARG;
+    const int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
+    for (int b = 0; b < cf.batch; ++b)
+        if (f[b] < T) return KVC_ERR_STATE;
+    const int rc = ensure_workspace(c);
+    if (rc != KVC_OK) return rc;
+
+    const int G = cf.n_q_heads / cf.n_kv_heads;
+    const int64_t head_stride = cf.max_len * cf.d_head;
+    const int64_t row_stride = head_stride * cf.n_kv_heads;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    // Slabs of at most kMaxDecodeRows query rows per KV head: Gc query heads
+    // of the group times Tc query positions.
+    const int Gc = std::min(G, kMaxDecodeRows);
+    const int Tc = std::max(1, kMaxDecodeRows / Gc);
+    for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
+        const int rows = std::min(kMaxRowsPerLaunch, cf.batch - row0);
+        for (int r0 = 0; r0 < G; r0 += Gc) {
+            for (int i0 = 0; i0 < T; i0 += Tc) {
+                kvc::DecodeArgs a;
+                std::memset(&a, 0, sizeof(a));
+                a.k_cache = c->k_store;
+                a.v_cache = c->v_store;
+                a.q = q;
+                a.out = out;
+                a.ws_o = c->ws_o;
+                a.ws_ml = c->ws_ml;
+                a.layer_off = (static_cast<int64_t>(layer) * cf.batch + row0) * row_stride;
+                a.row_stride = row_stride;
+                a.head_stride = head_stride;
+                a.row0 = row0;
+                a.rows = rows;
+                a.Hq = cf.n_q_heads;
+                a.Hkv = cf.n_kv_heads;
+                a.G = G;
+                a.T = T;
+                a.D = cf.d_head;
+                a.r0 = r0;
+                a.Gc = std::min(Gc, G - r0);
+                a.i0 = i0;
+                a.Tc = std::min(Tc, T - i0);
+                a.q_dtype = q_dtype;
+                a.st_dtype = cf.dtype;
+                a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.d_head)));
+                int64_t acc = 0;
+                for (int b = 0; b < rows; ++b) {
+                    a.prefix[b] = acc;
+                    const int64_t n_b = f[row0 + b] - T + i0 + a.Tc;   // keys the slab's last query sees
+                    acc += n_b * cf.n_kv_heads;
+                }
+                a.prefix[rows] = acc;
+                a.total_keys = acc;
+                decode_split(acc, &a.n_blocks, &a.keys_per_block);
+                if (kvc::launch_decode(a, s) != hipSuccess) return KVC_ERR_HIP;
+            }
+        }
+    }
+    return KVC_OK;
+}
+
+int kvc_seq_len(const kvc_cache* c, int32_t layer, int64_t* out_lens) {
+    if (!c || !out_lens) return KVC_ERR_ARG;
+    if (layer < -1 || layer >= c->cfg.n_layers) return KVC_ERR_ARG;
+    for (int b = 0; b < c->cfg.batch; ++b)
+        out_lens[b] = layer == -1 ? committed(c, b) : c->fill[static_cast<size_t>(layer) * c->cfg.batch + b];
+    return KVC_OK;
+}
+
+int kvc_truncate(kvc_cache* c, const int64_t* n, int32_t count) {
+    if (!c || !n) return KVC_ERR_ARG;
+    const int B = c->cfg.batch;
+    if (count != 1 && count != B) return KVC_ERR_ARG;
+    for (int b = 0; b < B; ++b) {
+        const int64_t nb = n[count == 1 ? 0 : b];
+        if (nb < 0 || nb > committed(c, b)) return KVC_ERR_STATE;
+    }
+    for (int b = 0; b < B; ++b) {
+        const int64_t nb = n[count == 1 ? 0 : b];
+        for (int l = 0; l < c->cfg.n_layers; ++l) c->fill[static_cast<size_t>(l) * B + b] = nb;
+    }
+    return KVC_OK;
+}
+
+int kvc_nbytes(const kvc_cache* c, uint64_t* out) {
+    if (!c || !out) return KVC_ERR_ARG;
+    *out = storage_bytes(c->cfg);
+    return KVC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal interface between the host core (kvc_api.cpp) and the HIP kernels.
+// Plain structs passed by value as kernel arguments (kept under 4 KB), and the
+// launch functions each kernel file defines.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace kvc {
+
+// Rows of the batch one launch covers; larger batches are split into several
+// launches so that per-row tables fit in the kernel argument block.
+constexpr int kMaxRowsPerLaunch = 256;
+// Query rows (query heads of one group x query positions) one decode work item
+// carries in registers.
+constexpr int kMaxDecodeRows = 8;
+// Upper bound on decode work-groups per launch (sizes the split-K workspace).
+constexpr int kMaxDecodeBlocks = 2048;
+
+enum Dtype : int32_t { F32 = 0, F16 = 1, BF16 = 2 };
+
+inline int itemsize(int dt) { return dt == F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------
+// Append: copy a [rows][H_kv][T][D] chunk into the cache with rounding.
+// ---------------------------------------------------------------------------
+struct AppendArgs {
+    void* k_cache;           // storage base (element type = st_dtype)
+    void* v_cache;
+    const void* k_in;        // chunk base for row `row0` (element type = in_dtype)
+    const void* v_in;
+    int64_t layer_off;       // element offset of (layer, row0, head 0, slot 0)
+    int64_t row_stride;      // elements between rows: H_kv * max_len * D
+    int64_t head_stride;     // elements between heads: max_len * D
+    int32_t rows, H, T, D;
+    int32_t in_dtype, st_dtype;
+    int32_t fill[kMaxRowsPerLaunch];   // first slot written, per row
+};
+
+// ---------------------------------------------------------------------------
+// Split-K decode attention over a flattened key axis ("stream-K"):
+// work unit u = (row b, KV head g) owns n_b keys; the units are laid end to
+// end (b-major) and each work-group takes an equal slice of that axis.
+// A slab is a set of query rows of one unit: query heads g*G + r0 .. + Gc and
+// query positions i0 .. i0 + Tc of the chunk (Gc * Tc <= kMaxDecodeRows).
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+    const void* k_cache;
+    const void* v_cache;
+    const void* q;           // [B][Hq][T][D], q_dtype, whole-batch base
+    float* out;              // [B][Hq][T][D] float32, whole-batch base
+    float* ws_o;             // [segments][kMaxDecodeRows][D] unnormalised partial outputs
+    float* ws_ml;            // [segments][kMaxDecodeRows][2] running max (log2 units) and sum
+    int64_t layer_off;       // element offset of (layer, row0, 0, 0, 0)
+    int64_t row_stride;
+    int64_t head_stride;
+    int64_t total_keys;      // sum over rows of n_b * H_kv
+    int64_t keys_per_block;  // slice of the key axis per work-group
+    int32_t row0, rows;      // batch rows of this launch
+    int32_t Hq, Hkv, G, T;   // T = query positions in the chunk
+    int32_t D;
+    int32_t r0, Gc, i0, Tc;  // the slab
+    int32_t q_dtype, st_dtype;
+    int32_t n_blocks;        // work-groups in the partial pass
+    float scale_log2;        // log2(e) / sqrt(D)
+    int64_t prefix[kMaxRowsPerLaunch + 1];  // exclusive prefix of n_b * H_kv
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Which decode kernel shapes exist (d_head x storage dtype).
+bool decode_supported(int D, int st_dtype);
+
+}  // namespace kvc

@@ -1,0 +1,258 @@
+"""Thin ctypes binding of libkvc (include/kvc.h).
+
+Argument marshalling only: every step of append and attention runs in the
+HIP kernels of libkvc.so. PyTorch supplies device memory and streams.
+Importing this module loads the library and raises ImportError when it has
+not been built (there is no fallback).
+
+    cache = KVCache(n_layers, n_kv_heads, d_head, max_len, batch=B,
+                    n_q_heads=Hq, dtype="bf16")
+    cache.append(layer, k, v)        # k, v: [B, H_kv, T, d_h] device tensors
+    out = cache.attend(layer, q)     # q: [B, H_q, T, d_h] -> float32 [B, H_q, T, d_h]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m kv_cached_gqa_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---- dtypes and status codes (kvc.h) --------------------------------------
+F32, F16, BF16 = 0, 1, 2
+DTYPE_CODES = {"fp32": F32, "fp16": F16, "bf16": BF16}
+ITEMSIZE = {"fp32": 4, "fp16": 2, "bf16": 2}
+
+OK = 0
+ERR_ARG, ERR_CAPACITY, ERR_STATE, ERR_DTYPE = -1, -2, -3, -4
+ERR_STORAGE, ERR_HIP, ERR_NOMEM, ERR_UNSUPPORTED = -5, -6, -7, -8
+
+EXPORTED = ("kvc_create", "kvc_destroy", "kvc_append", "kvc_attend", "kvc_seq_len",
+            "kvc_truncate", "kvc_nbytes", "kvc_strerror")
+
+
+class KVCConfig(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("d_head", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("max_len", ctypes.c_int64)]
+
+
+_vp, _i32, _i64, _u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+_lib.kvc_create.argtypes = [ctypes.POINTER(KVCConfig), _vp, _vp, _u64, ctypes.POINTER(_vp)]
+_lib.kvc_create.restype = ctypes.c_int
+_lib.kvc_destroy.argtypes = [_vp]
+_lib.kvc_destroy.restype = None
+_lib.kvc_append.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _vp]
+_lib.kvc_append.restype = ctypes.c_int
+_lib.kvc_attend.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp, _vp]
+_lib.kvc_attend.restype = ctypes.c_int
+_lib.kvc_seq_len.argtypes = [_vp, _i32, ctypes.POINTER(_i64)]
+_lib.kvc_seq_len.restype = ctypes.c_int
+_lib.kvc_truncate.argtypes = [_vp, ctypes.POINTER(_i64), _i32]
+_lib.kvc_truncate.restype = ctypes.c_int
+_lib.kvc_nbytes.argtypes = [_vp, ctypes.POINTER(_u64)]
+_lib.kvc_nbytes.restype = ctypes.c_int
+_lib.kvc_strerror.argtypes = [ctypes.c_int]
+_lib.kvc_strerror.restype = ctypes.c_char_p
+
+
+class KVCError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {strerror(status)} ({status})")
+
+
+class KVCArgumentError(KVCError, ValueError):
+    """Bad argument, dtype, storage or unsupported shape."""
+
+
+class ContextLimitError(KVCError):
+    """An append would run past max_len (the cache is unchanged)."""
+
+
+class KVCStateError(KVCError):
+    """Attend before append, or truncate past the committed length."""
+
+
+def strerror(status: int) -> str:
+    return _lib.kvc_strerror(int(status)).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status == OK:
+        return
+    if status == ERR_CAPACITY:
+        raise ContextLimitError(status, call)
+    if status == ERR_STATE:
+        raise KVCStateError(status, call)
+    if status in (ERR_ARG, ERR_DTYPE, ERR_STORAGE, ERR_UNSUPPORTED):
+        raise KVCArgumentError(status, call)
+    raise KVCError(status, call)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkvc (for tests that call the C ABI directly)."""
+    return _lib
+
+
+# ---- torch plumbing ----------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def torch_dtype(name: str):
+    torch = _torch()
+    return {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[name]
+
+
+def dtype_name(t) -> str:
+    torch = _torch()
+    m = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
+    if t.dtype not in m:
+        raise KVCArgumentError(ERR_DTYPE, f"dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class KVCache:
+    """Owns zero-filled device storage (two torch tensors shaped
+    (L, B, H_kv, max_len, d_h)) and a libkvc handle over it.
+
+    The method names follow the KVCache interface of "KV cache, incremental
+    decode, incremental UTF-8 detokenizer, generate" (section 4).
+    """
+
+    def __init__(self, n_layers: int, n_kv_heads: int, d_head: int, max_len: int, batch: int = 1,
+                 n_q_heads: Optional[int] = None, dtype: str = "fp32", device=None):
+        torch = _torch()
+        if dtype not in DTYPE_CODES:
+            raise KVCArgumentError(ERR_DTYPE, f"dtype {dtype!r}")
+        self.n_layers, self.batch = int(n_layers), int(batch)
+        self.n_kv_heads, self.d_head, self.max_len = int(n_kv_heads), int(d_head), int(max_len)
+        self.n_q_heads = int(n_q_heads if n_q_heads is not None else n_kv_heads)
+        self.dtype = dtype
+        self.device = torch.device(device if device is not None else "cuda")
+        shape = (self.n_layers, self.batch, self.n_kv_heads, self.max_len, self.d_head)
+        tdt = torch_dtype(dtype)
+        self.k_storage = torch.zeros(shape, dtype=tdt, device=self.device)
+        self.v_storage = torch.zeros(shape, dtype=tdt, device=self.device)
+        cfg = KVCConfig(self.n_layers, self.batch, self.n_q_heads, self.n_kv_heads, self.d_head,
+                        DTYPE_CODES[dtype], self.max_len)
+        h = _vp()
+        each = self.k_storage.numel() * self.k_storage.element_size()
+        _check(_lib.kvc_create(ctypes.byref(cfg), self.k_storage.data_ptr(), self.v_storage.data_ptr(),
+                               each, ctypes.byref(h)), "kvc_create")
+        self._h = h
+
+    # -- lifetime --
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _lib.kvc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    # -- the contract --
+    def append(self, layer: int, k_new, v_new, stream=None) -> None:
+        """Store k_new, v_new [B, H_kv, T, d_h] (device, contiguous) at slots
+        [fill, fill + T) of `layer`, rounded to the storage dtype."""
+        self._check_chunk(k_new, self.n_kv_heads, "k_new")
+        self._check_chunk(v_new, self.n_kv_heads, "v_new")
+        if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
+            raise KVCArgumentError(ERR_ARG, "k_new and v_new differ in shape or dtype")
+        _check(_lib.kvc_append(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
+                               DTYPE_CODES[dtype_name(k_new)], int(k_new.shape[2]), _stream_ptr(stream)),
+               "kvc_append")
+
+    def attend(self, layer: int, q, out=None, stream=None):
+        """softmax(q K^T / sqrt(d_h)) V over everything `layer` holds, with the
+        chunk's queries at positions [s, s + T). Returns float32 [B, H_q, T, d_h]."""
+        torch = _torch()
+        self._check_chunk(q, self.n_q_heads, "q")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
+            raise KVCArgumentError(ERR_ARG, "out must be contiguous float32 shaped like q")
+        _check(_lib.kvc_attend(self._h, int(layer), q.data_ptr(), DTYPE_CODES[dtype_name(q)],
+                               int(q.shape[2]), out.data_ptr(), _stream_ptr(stream)), "kvc_attend")
+        return out
+
+    def update(self, layer: int, k_new, v_new, stream=None):
+        """Append, then return views of everything the layer stores (the pages'
+        update): [B, H_kv, n, d_h] up to the longest row's fill."""
+        self.append(layer, k_new, v_new, stream)
+        n = int(self.seq_len(layer).max())
+        return self.k_storage[layer, :, :, :n], self.v_storage[layer, :, :, :n]
+
+    def seq_len(self, layer: Optional[int] = None) -> np.ndarray:
+        """Per-row committed length (layer None) or one layer's fill count."""
+        out = (_i64 * self.batch)()
+        _check(_lib.kvc_seq_len(self._h, -1 if layer is None else int(layer), out), "kvc_seq_len")
+        return np.frombuffer(out, dtype=np.int64).copy()
+
+    def positions(self, t_new: int) -> np.ndarray:
+        """[B, T] absolute positions s_b + i of the next chunk."""
+        s = self.seq_len()
+        return s[:, None] + np.arange(int(t_new))[None, :]
+
+    def mask(self, t_new: int, row: int = 0) -> np.ndarray:
+        """causal_mask(T, s + T, q_offset=s) for one row (boolean [T, s + T])."""
+        s = int(self.seq_len()[row])
+        i = np.arange(int(t_new))[:, None]
+        j = np.arange(s + int(t_new))[None, :]
+        return j <= s + i
+
+    def truncate(self, n) -> None:
+        arr = np.ascontiguousarray(np.atleast_1d(np.asarray(n, dtype=np.int64)))
+        _check(_lib.kvc_truncate(self._h, arr.ctypes.data_as(ctypes.POINTER(_i64)), int(arr.size)),
+               "kvc_truncate")
+
+    def nbytes(self) -> int:
+        out = _u64()
+        _check(_lib.kvc_nbytes(self._h, ctypes.byref(out)), "kvc_nbytes")
+        return int(out.value)
+
+    # -- helpers --
+    def _check_chunk(self, t, heads: int, name: str) -> None:
+        if t.dim() != 4 or t.shape[0] != self.batch or t.shape[1] != heads or t.shape[3] != self.d_head:
+            raise KVCArgumentError(ERR_ARG, f"{name} must be [B={self.batch}, H={heads}, T, d_h={self.d_head}], "
+                                            f"got {tuple(t.shape)}")
+        if not t.is_contiguous() or t.device != self.k_storage.device:
+            raise KVCArgumentError(ERR_ARG, f"{name} must be contiguous and on {self.k_storage.device}")
+
+
+def exported_symbols(names: Sequence[str] = EXPORTED) -> dict:
+    """Which of the C ABI's names the loaded library exports."""
+    found = {}
+    for n in names:
+        try:
+            getattr(_lib, n)
+            found[n] = True
+        except AttributeError:
+            found[n] = False
+    return found

@@ -74,13 +74,15 @@ def round_bf16_bits(x: np.ndarray) -> np.ndarray:
     with ties to even adds 0x7FFF plus the lowest kept bit before the shift.
     Overflow carries into the exponent and gives infinity, as IEEE asks.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    sign = (u >> 31) & 1
-    is_nan = (u & 0x7FFFFFFF) > 0x7F800000
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF
-    r = np.where(is_nan, (sign << 15) | 0x7FC0, r)
-    return r.astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    is_nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    # only NaN patterns can wrap around 2^32 here, and those are replaced below
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    r = r.astype(np.uint16)
+    if is_nan.any():
+        sign = (u[is_nan] >> np.uint32(31)).astype(np.uint16)
+        r[is_nan] = (sign << np.uint16(15)) | np.uint16(0x7FC0)
+    return r
 
 
 def round_f16_bits(x: np.ndarray) -> np.ndarray:
