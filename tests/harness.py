@@ -40,8 +40,9 @@ class Report:
 def to_device(x: np.ndarray, dtype: str, device):
     import torch
     from kv_cached_gqa_amd.kvc import torch_dtype
-    t = torch.from_numpy(np.ascontiguousarray(x))
-    return t.to(device=device).to(torch_dtype(dtype)).contiguous()
+    # convert on the host, so the device gets exactly the bits input_values() describes
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch_dtype(dtype)).contiguous()
+    return t.to(device=device)
 
 
 def input_values(x: np.ndarray, dtype: str) -> np.ndarray:
