@@ -196,7 +196,7 @@ def main():
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
         "bytes_per_step": att + app,
-        "roofline": {"bound": "hbm", "kernel": "decode attention: decode_partial + decode_combine",
+        "roofline": {"bound": "hbm", "kernel": "decode attention: decode_attn + decode_combine",
                      "achieved": round(att_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(att_gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "bytes_per_launch": att, "launch_us": round(us_attend, 3)},

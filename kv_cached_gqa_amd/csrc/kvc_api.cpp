@@ -76,34 +76,19 @@ int ensure_workspace(kvc_cache* c) {
     void* o = nullptr;
     void* ml = nullptr;
     int rc = KVC_OK;
-    if (hipMalloc(&o, o_bytes) != hipSuccess) rc = KVC_ERR_NOMEM;
-    else if (hipMalloc(&ml, ml_bytes) != hipSuccess) {
-        (void)hipFree(o);
+    if (hipMalloc(&o, o_bytes) != hipSuccess || hipMalloc(&ml, ml_bytes) != hipSuccess) {
         rc = KVC_ERR_NOMEM;
+        if (o) (void)hipFree(o);
+        if (ml) (void)hipFree(ml);
+        (void)hipGetLastError();
     }
     if (dev != prev) (void)hipSetDevice(prev);
-    if (rc != KVC_OK) {
-        (void)hipGetLastError();
-        return rc;
-    }
+    if (rc != KVC_OK) return rc;
     c->device = dev;
     c->ws_o = static_cast<float*>(o);
     c->ws_ml = static_cast<float*>(ml);
     c->ws_segments = segs;
     return KVC_OK;
-}
-
-// Work-groups for a decode launch: enough to fill the GPU (256 CUs, several
-// work-groups each) but never slices shorter than a few key tiles.
-void decode_split(int64_t total_keys, int32_t* n_blocks, int64_t* keys_per_block) {
-    constexpr int64_t kTarget = 1024;
-    constexpr int64_t kMinKeys = 64;
-    int64_t nb = (total_keys + kMinKeys - 1) / kMinKeys;
-    nb = std::max<int64_t>(1, std::min<int64_t>(nb, kTarget));
-    int64_t kpb = (total_keys + nb - 1) / nb;
-    nb = (total_keys + kpb - 1) / kpb;
-    *n_blocks = static_cast<int32_t>(nb);
-    *keys_per_block = kpb;
 }
 
 }  // namespace
@@ -265,7 +250,6 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
                 }
                 a.prefix[rows] = acc;
                 a.total_keys = acc;
-                decode_split(acc, &a.n_blocks, &a.keys_per_block);
                 if (kvc::launch_decode(a, s) != hipSuccess) return KVC_ERR_HIP;
             }
         }

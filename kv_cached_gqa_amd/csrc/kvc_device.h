@@ -110,6 +110,30 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm(2,3,0,1)
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
+// In-place sums of M independent values over aligned groups of N lanes
+// (N in 1..16). The steps go across all M values before the next step, so a
+// DPP read never directly follows the write it depends on.
+template <int N, int M>
+__device__ __forceinline__ void group_sum_n(float (&x)[M]) {
+    if constexpr (N >= 2) {
+#pragma unroll
+        for (int i = 0; i < M; ++i) x[i] += dpp_f<kDppXor1>(x[i]);
+    }
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int i = 0; i < M; ++i) x[i] += dpp_f<kDppXor2>(x[i]);
+    }
+    if constexpr (N >= 8) {
+#pragma unroll
+        for (int i = 0; i < M; ++i) x[i] += dpp_f<kDppHalfMirror>(x[i]);
+    }
+    if constexpr (N >= 16) {
+#pragma unroll
+        for (int i = 0; i < M; ++i) x[i] += dpp_f<kDppMirror>(x[i]);
+    }
+    static_assert(N <= 16, "group_sum_n works inside one 16-lane DPP row");
+}
+
 // Sum over aligned groups of N lanes (N in 1..64, power of two); every lane of
 // a group gets the group's sum.
 template <int N>

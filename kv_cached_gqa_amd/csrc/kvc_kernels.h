@@ -15,7 +15,7 @@ constexpr int kMaxRowsPerLaunch = 256;
 // carries in registers.
 constexpr int kMaxDecodeRows = 8;
 // Upper bound on decode work-groups per launch (sizes the split-K workspace).
-constexpr int kMaxDecodeBlocks = 2048;
+constexpr int kMaxDecodeBlocks = 8192;
 
 enum Dtype : int32_t { F32 = 0, F16 = 1, BF16 = 2 };
 
@@ -50,7 +50,7 @@ struct DecodeArgs {
     const void* q;           // [B][Hq][T][D], q_dtype, whole-batch base
     float* out;              // [B][Hq][T][D] float32, whole-batch base
     float* ws_o;             // [segments][kMaxDecodeRows][D] unnormalised partial outputs
-    float* ws_ml;            // [segments][kMaxDecodeRows][2] running max (log2 units) and sum
+    float* ws_ml;            // [segments][kMaxDecodeRows][2] running max (raw q.k units) and sum
     int64_t layer_off;       // element offset of (layer, row0, 0, 0, 0)
     int64_t row_stride;
     int64_t head_stride;
@@ -61,13 +61,14 @@ struct DecodeArgs {
     int32_t D;
     int32_t r0, Gc, i0, Tc;  // the slab
     int32_t q_dtype, st_dtype;
-    int32_t n_blocks;        // work-groups in the partial pass
+    int32_t n_blocks;        // work-groups (set by launch_decode)
     float scale_log2;        // log2(e) / sqrt(D)
     int64_t prefix[kMaxRowsPerLaunch + 1];  // exclusive prefix of n_b * H_kv
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Fills in n_blocks and keys_per_block from the device's resident capacity.
+hipError_t launch_decode(DecodeArgs& a, hipStream_t stream);
 
 // Which decode kernel shapes exist (d_head x storage dtype).
 bool decode_supported(int D, int st_dtype);
