@@ -208,6 +208,46 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
     const int64_t head_stride = cf.max_len * cf.d_head;
     const int64_t row_stride = head_stride * cf.n_kv_heads;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.d_head)));
+
+    // Dispatch: a 16-bit cache with more than 32 query rows per KV head (a prefill
+    // chunk) runs on the matrix cores; everything else on the split-K decode kernel.
+    if (cf.dtype != KVC_F32 && static_cast<int64_t>(T) * G > 32 && kvc::prefill_supported(cf.d_head, cf.dtype)) {
+        const int Gc = std::min(G, 32);
+        for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
+            const int rows = std::min(kMaxRowsPerLaunch, cf.batch - row0);
+            for (int r0 = 0; r0 < G; r0 += Gc) {
+                kvc::PrefillArgs a;
+                std::memset(&a, 0, sizeof(a));
+                a.k_cache = c->k_store;
+                a.v_cache = c->v_store;
+                a.q = q;
+                a.out = out;
+                a.layer_off = (static_cast<int64_t>(layer) * cf.batch + row0) * row_stride;
+                a.row_stride = row_stride;
+                a.head_stride = head_stride;
+                a.row0 = row0;
+                a.rows = rows;
+                a.Hq = cf.n_q_heads;
+                a.Hkv = cf.n_kv_heads;
+                a.G = G;
+                a.T = T;
+                a.D = cf.d_head;
+                a.r0 = r0;
+                a.Gc = std::min(Gc, G - r0);
+                a.i0 = 0;
+                a.Ti = T;
+                a.qpt = 32 / a.Gc;
+                a.q_per_block = a.qpt * (kvc::prefill_columns_per_block() / 32);
+                a.q_dtype = q_dtype;
+                a.st_dtype = cf.dtype;
+                a.scale_log2 = scale_log2;
+                for (int b = 0; b < rows; ++b) a.offset[b] = static_cast<int32_t>(f[row0 + b] - T);
+                if (kvc::launch_prefill(a, s) != hipSuccess) return KVC_ERR_HIP;
+            }
+        }
+        return KVC_OK;
+    }
 
     // Slabs of at most kMaxDecodeRows query rows per KV head: Gc query heads
     // of the group times Tc query positions.
@@ -241,7 +281,7 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
                 a.Tc = std::min(Tc, T - i0);
                 a.q_dtype = q_dtype;
                 a.st_dtype = cf.dtype;
-                a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.d_head)));
+                a.scale_log2 = scale_log2;
                 int64_t acc = 0;
                 for (int b = 0; b < rows; ++b) {
                     a.prefix[b] = acc;

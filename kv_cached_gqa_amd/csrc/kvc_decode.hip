@@ -56,8 +56,6 @@ struct Layout {
     static constexpr int epl = 16 / esz;   // elements per lane per 16-byte load
 };
 
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 template <int ST>
 __device__ __forceinline__ float dot16(const uint32_t (&q)[4], const uint4& k, float acc) {
     const uint32_t kw[4] = {k.x, k.y, k.z, k.w};

@@ -93,6 +93,9 @@ __device__ __forceinline__ void store8(void* base, int64_t elem, const float (&v
     }
 }
 
+// Hardware base-2 exponential (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---- cross-lane reductions --------------------------------------------------
 // DPP row operations act within rows of 16 lanes. quad_perm [1,0,3,2] and
 // [2,3,0,1] exchange with lanes 1 and 2 away; after those a whole quad holds

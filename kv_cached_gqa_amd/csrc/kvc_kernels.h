@@ -66,11 +66,39 @@ struct DecodeArgs {
     int64_t prefix[kMaxRowsPerLaunch + 1];  // exclusive prefix of n_b * H_kv
 };
 
+// ---------------------------------------------------------------------------
+// Prefill-chunk attention on matrix cores (fp16/bf16 caches): one work-group per
+// (row, KV head, block of queries); columns are (query, head-in-group) pairs.
+// ---------------------------------------------------------------------------
+struct PrefillArgs {
+    const void* k_cache;
+    const void* v_cache;
+    const void* q;           // [B][Hq][T][D], q_dtype, whole-batch base
+    float* out;              // [B][Hq][T][D] float32, whole-batch base
+    int64_t layer_off;       // element offset of (layer, row0, 0, 0, 0)
+    int64_t row_stride;
+    int64_t head_stride;
+    int32_t row0, rows;
+    int32_t Hq, Hkv, G, T, D;
+    int32_t r0, Gc;          // query heads g*G + r0 .. + Gc of each group
+    int32_t i0, Ti;          // queries i0 .. i0 + Ti of the chunk
+    int32_t qpt;             // queries per 32-column tile (Gc * qpt <= 32)
+    int32_t q_per_block;     // queries per work-group
+    int32_t q_dtype, st_dtype;
+    float scale_log2;
+    int32_t offset[kMaxRowsPerLaunch];   // per row: s_b, the chunk's query offset
+};
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // Fills in n_blocks and keys_per_block from the device's resident capacity.
 hipError_t launch_decode(DecodeArgs& a, hipStream_t stream);
 
-// Which decode kernel shapes exist (d_head x storage dtype).
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Which kernel shapes exist (d_head x storage dtype).
 bool decode_supported(int D, int st_dtype);
+bool prefill_supported(int D, int st_dtype);
+// Query-head columns of one prefill work-group (tiles of 32 columns).
+int prefill_columns_per_block();
 
 }  // namespace kvc

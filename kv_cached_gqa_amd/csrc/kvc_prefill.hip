@@ -1,0 +1,394 @@
+// Prefill-chunk attention on CDNA4 matrix cores (fp16/bf16 caches, chunks of
+// many query rows): out = softmax(q K^T / sqrt(D)) V with the bottom-right
+// causal mask of a chunk that sits at offset s ("KV cache, incremental decode,
+// ...", section 2.3; "kv-cache-decoding", "Prefill and decode": one parallel
+// pass with a score matrix per head). A chunk of T queries against s + T keys
+// is a dense contraction, so both products run on v_mfma_f32_32x32x16.
+//
+// Shapes and layouts (32x32x16 MFMA: A 32x16, B 16x32, C 32x32 fp32):
+//  * Columns. A work-group owns one (batch row b, KV head g) and a block of the
+//    chunk's queries. Its columns are (query i, query head r) pairs, query-major
+//    (c = i * G + r), so all G heads that share K/V sit in the same tiles and
+//    every K/V tile staged in LDS serves all of them ("Heads, GQA and K/V
+//    cache": a group of queries shares the same keys and values). Each wave
+//    owns NT tiles of 32 columns.
+//  * S^T = K Q^T. A = K tile rows from LDS (16 bytes per lane), B = Q^T held in
+//    registers for the whole launch. The C layout gives each lane one column
+//    (lane % 32) and 16 of the 32 keys; the other 16 are in lane ^ 32, so the
+//    softmax reductions are in-lane plus one exchange.
+//  * O^T = V^T P^T. The probabilities in S^T's C registers are already the B
+//    operand of this product when the 32 keys of a tile are taken in the order
+//    the C layout holds them; V^T's A operand uses the same order, read from a
+//    transposed copy of the V tile in LDS. O^T's C layout again gives each lane
+//    its own column, so rescaling needs no data movement.
+//  * Online softmax in base 2 with a lazily moved reference max (moved only
+//    when a score passes it by 2^8); P is rounded to the storage type for the
+//    MFMA and the normaliser sums the rounded values.
+//  * Masking. Key tiles entirely visible to the work-group's queries skip the
+//    mask; tiles past the last query's diagonal are never loaded.
+#include <type_traits>
+
+#include "kvc_device.h"
+
+namespace kvc {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+#ifndef KVC_PF_NT
+#define KVC_PF_NT 1           // 32-column tiles per wave
+#endif
+#ifndef KVC_PF_WAVES_PER_EU
+#define KVC_PF_WAVES_PER_EU 2   // two work-groups per CU: one softmax overlaps the other's MFMAs
+#endif
+#ifndef KVC_PF_STAGES
+#define KVC_PF_STAGES 3       // key/value tiles in the LDS ring
+#endif
+
+constexpr int kPWaves = 4;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kNT = KVC_PF_NT;
+constexpr int kNB = KVC_PF_STAGES;
+constexpr int kBN = 32;                // keys per tile
+constexpr float kPRescaleLog2 = 8.f;
+
+template <int ST>
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+    if constexpr (ST == BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                     __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+template <int ST>
+__device__ __forceinline__ uint32_t to_st(float x) {
+    return ST == BF16 ? f32_to_bf16_rne(x) : f32_to_f16_rne(x);
+}
+
+template <int ST>
+__device__ __forceinline__ float from_st(uint32_t h) {
+    return ST == BF16 ? bf16_to_f32(h) : f16_to_f32(h);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and all LDS operations are done (gfx9 s_waitcnt encoding; expcnt not waited).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | ((N >> 4) << 14));
+}
+
+template <int D>
+struct PCfg {
+    static constexpr int CPR = D / 8;           // 16-byte chunks per key row
+    static constexpr int DS = D / 16;           // MFMA k-steps over the head dimension
+    static constexpr int DT = D / 32;           // 32-wide tiles of the head dimension
+    static constexpr int TILE = kBN * D;        // elements per K (or V) tile
+    static constexpr int NLD = TILE * 2 / 1024; // 1 KB LDS-DMA instructions per tile and tensor
+    static constexpr int LPW = 2 * ((NLD + kPWaves - 1) / kPWaves);   // DMA loads per wave per stage
+    // element offset of (key r, head element d) in a K tile: rows of D elements,
+    // 16-byte chunks XOR-swizzled by the row so the 32 lanes reading one chunk of
+    // 32 different rows hit distinct banks. V tiles are plain rows: their reads
+    // take one element of one row per lane, consecutive lanes consecutive elements.
+    __device__ static constexpr int koff(int r, int d) {
+        return r * D + (((d >> 3) ^ (r & (CPR - 1))) << 3) + (d & 7);
+    }
+};
+
+template <int D, int ST>
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(KVC_PF_WAVES_PER_EU)))
+void prefill_attn(PrefillArgs a) {
+    using P = PCfg<D>;
+    // One LDS object per ring stage: with compile-time stage indices the compiler
+    // can tell that a DMA into one stage does not touch the stage being read, and
+    // does not wait for it.
+    __shared__ __attribute__((aligned(16))) uint16_t sk0[P::TILE], sk1[P::TILE], sk2[P::TILE], sk3[P::TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t sv0[P::TILE], sv1[P::TILE], sv2[P::TILE], sv3[P::TILE];
+    static_assert(kNB >= 2 && kNB <= 4, "the ring has two to four stages");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col32 = lane & 31;
+    const int hl = lane >> 5;                   // which half of the k-dimension this lane feeds
+
+    // -- which (row, KV head, query block) this work-group owns; consecutive query
+    //    blocks of one unit stay on one XCD when the unit count is a multiple of 8
+    const int n_units = a.rows * a.Hkv;
+    const int unit = blockIdx.x % n_units;
+    const int qblk = blockIdx.x / n_units;
+    const int b = unit / a.Hkv;
+    const int g = unit - b * a.Hkv;
+    const int s = a.offset[b];                  // the chunk's query offset for this row
+    const int qpt = a.qpt;                      // queries per 32-column tile
+    const int q_lo = a.i0 + qblk * a.q_per_block;   // first query of this work-group
+    if (q_lo >= a.i0 + a.Ti) return;
+    int q_hi = q_lo + a.q_per_block - 1;
+    if (q_hi > a.i0 + a.Ti - 1) q_hi = a.i0 + a.Ti - 1;
+
+    const int64_t head_base = a.layer_off + b * a.row_stride + g * a.head_stride;
+    const uint16_t* kg = static_cast<const uint16_t*>(a.k_cache) + head_base;
+    const uint16_t* vg = static_cast<const uint16_t*>(a.v_cache) + head_base;
+
+    // -- this lane's columns: query i and head r of each of its tiles
+    int col_i[kNT], col_r[kNT];
+    bool col_ok[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int tile = wave * kNT + nt;
+        const int i = q_lo + tile * qpt + col32 / a.Gc;
+        const int r = col32 % a.Gc;
+        col_ok[nt] = col32 < qpt * a.Gc && i <= q_hi;
+        col_i[nt] = col_ok[nt] ? i : q_lo;
+        col_r[nt] = r;
+    }
+
+    // -- key range: the last query of the work-group sees keys [0, s + q_hi]
+    const int n_keys = s + q_hi + 1;
+    const int n_tiles = (n_keys + kBN - 1) / kBN;
+    const int vis_all = s + q_lo;               // keys <= this are visible to every column
+
+    // -- the LDS ring: stage = one K tile and one V tile, moved by LDS-DMA loads
+    //    (16 bytes per lane, lane i at byte 16 * i of the instruction's 1 KB).
+    //    Tiles past the range are issued too, clamped to the last key, so every
+    //    wave issues the same number of loads per stage.
+    auto kstage = [&](auto slot_c) -> uint16_t* {
+        constexpr int S = decltype(slot_c)::value;
+        if constexpr (S == 0) return sk0;
+        else if constexpr (S == 1) return sk1;
+        else if constexpr (S == 2) return sk2;
+        else return sk3;
+    };
+    auto vstage = [&](auto slot_c) -> uint16_t* {
+        constexpr int S = decltype(slot_c)::value;
+        if constexpr (S == 0) return sv0;
+        else if constexpr (S == 1) return sv1;
+        else if constexpr (S == 2) return sv2;
+        else return sv3;
+    };
+    auto issue = [&](auto slot_c, int t) {
+        uint16_t* kd = kstage(slot_c);
+        uint16_t* vd = vstage(slot_c);
+#pragma unroll
+        for (int n = wave; n < P::NLD; n += kPWaves) {
+            const int e = n * 512 + lane * 8;       // element offset inside the tile
+            const int r = e / D;
+            const int phys = (e % D) >> 3;
+            const int chunk = phys ^ (r & (P::CPR - 1));
+            int j = t * kBN + r;
+            j = j < n_keys ? j : n_keys - 1;
+            const int64_t row = static_cast<int64_t>(j) * D;
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kg + row + chunk * 8),
+                                             (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vg + row + phys * 8),
+                                             (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0, 0);
+        }
+    };
+    issue(std::integral_constant<int, 0>{}, 0);
+    if constexpr (kNB > 2) issue(std::integral_constant<int, 1>{}, 1);
+    if constexpr (kNB > 3) issue(std::integral_constant<int, 2>{}, 2);
+
+    // -- Q^T as the B operand, rounded as the storage type: 8 consecutive head
+    //    elements of this lane's column per k-step
+    uint4 qb[kNT][P::DS];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int h = g * a.G + a.r0 + col_r[nt];
+        const int64_t qrow = ((static_cast<int64_t>(a.row0 + b) * a.Hq + h) * a.T + col_i[nt]) * D;
+#pragma unroll
+        for (int ds = 0; ds < P::DS; ++ds) {
+            const int64_t e0 = qrow + ds * 16 + hl * 8;
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x0, x1;
+                if (a.q_dtype == F32) {
+                    x0 = static_cast<const float*>(a.q)[e0 + 2 * e];
+                    x1 = static_cast<const float*>(a.q)[e0 + 2 * e + 1];
+                } else if (a.q_dtype == BF16) {
+                    x0 = bf16_to_f32(static_cast<const uint16_t*>(a.q)[e0 + 2 * e]);
+                    x1 = bf16_to_f32(static_cast<const uint16_t*>(a.q)[e0 + 2 * e + 1]);
+                } else {
+                    x0 = f16_to_f32(static_cast<const uint16_t*>(a.q)[e0 + 2 * e]);
+                    x1 = f16_to_f32(static_cast<const uint16_t*>(a.q)[e0 + 2 * e + 1]);
+                }
+                w[e] = to_st<ST>(x0) | (to_st<ST>(x1) << 16);
+            }
+            qb[nt][ds] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+
+    // -- per-column softmax state and the O^T accumulators
+    float m[kNT], lsum[kNT];
+    f32x16_t o[kNT][P::DT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        m[nt] = -INFINITY;
+        lsum[nt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < P::DT; ++dt) o[nt][dt] = f32x16_t{};
+    }
+    const float c = a.scale_log2;
+    const float thresh = kPRescaleLog2 / c;
+
+    auto step = [&](auto slot_c, int t) {
+        constexpr int S = decltype(slot_c)::value;
+        // this wave's loads of tile t are done (the kNB - 2 later stages may still
+        // be in flight); then every wave's are, and every wave is done with tile t - 1
+        wait_vm_lgkm0<(kNB - 2) * P::LPW>();
+        __builtin_amdgcn_s_barrier();
+        issue(std::integral_constant<int, (S + kNB - 1) % kNB>{}, t + kNB - 1);
+
+        const int j0 = t * kBN;
+        const bool plain = j0 + kBN - 1 <= vis_all && j0 + kBN <= n_keys;
+        const uint16_t* ks_ = kstage(slot_c);
+        const uint16_t* vs_ = vstage(slot_c);
+
+        // S^T tile per column tile: 32 keys x 32 columns
+        f32x16_t sacc[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) sacc[nt] = f32x16_t{};
+#pragma unroll
+        for (int ds = 0; ds < P::DS; ++ds) {
+            const uint4 ka = *reinterpret_cast<const uint4*>(&ks_[P::koff(col32, ds * 16 + hl * 8)]);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) sacc[nt] = mfma32<ST>(ka, qb[nt][ds], sacc[nt]);
+        }
+
+        // scores -> probabilities, in the C layout: value jj is key
+        // j0 + (jj / 4) * 8 + hl * 4 + jj % 4 of this lane's column
+        uint4 pb[kNT][2];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            float sv_[16];
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) sv_[jj] = sacc[nt][jj];
+            if (!plain) {
+                const int lim = s + col_i[nt];
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                    const int j = j0 + (jj >> 2) * 8 + hl * 4 + (jj & 3);
+                    if (j > lim || j >= n_keys) sv_[jj] = -INFINITY;
+                }
+            }
+            float mt = sv_[0];
+#pragma unroll
+            for (int jj = 1; jj < 16; ++jj) mt = fmaxf(mt, sv_[jj]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const bool need = mt - m[nt] > thresh;
+            if (__any(need)) {
+                if (need) {
+                    const float alpha = m[nt] == -INFINITY ? 0.f : fexp2((m[nt] - mt) * c);
+                    m[nt] = mt;
+                    lsum[nt] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < P::DT; ++dt) o[nt][dt] *= alpha;
+                }
+            }
+            const float nmc = m[nt] == -INFINITY ? 0.f : -m[nt] * c;
+            uint32_t h16[16];
+            float ls = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                const float p = fexp2(fmaf(sv_[jj], c, nmc));
+                h16[jj] = to_st<ST>(p);
+                ls += from_st<ST>(h16[jj]);
+            }
+            lsum[nt] += ls;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                pb[nt][kk] = make_uint4(h16[kk * 8 + 0] | (h16[kk * 8 + 1] << 16), h16[kk * 8 + 2] | (h16[kk * 8 + 3] << 16),
+                                        h16[kk * 8 + 4] | (h16[kk * 8 + 5] << 16), h16[kk * 8 + 6] | (h16[kk * 8 + 7] << 16));
+        }
+
+        // O^T += V^T P^T: A = V^T rows (head elements) with the keys in the order
+        // of P^T's registers: for k-step kk, element e is key kk * 16 + (e / 4) * 8 + hl * 4 + e % 4
+#pragma unroll
+        for (int dt = 0; dt < P::DT; ++dt) {
+            const int d = dt * 32 + col32;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int e = 2 * e2;
+                    const int key0 = kk * 16 + (e >> 2) * 8 + hl * 4 + (e & 3);
+                    w[e2] = static_cast<uint32_t>(vs_[key0 * D + d]) |
+                            (static_cast<uint32_t>(vs_[(key0 + 1) * D + d]) << 16);
+                }
+                const uint4 va = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) o[nt][dt] = mfma32<ST>(va, pb[nt][kk], o[nt][dt]);
+            }
+        }
+    };
+    for (int t0 = 0; t0 < n_tiles; t0 += kNB) {
+        step(std::integral_constant<int, 0>{}, t0);
+        if (t0 + 1 >= n_tiles) break;
+        step(std::integral_constant<int, 1>{}, t0 + 1);
+        if constexpr (kNB > 2) {
+            if (t0 + 2 >= n_tiles) break;
+            step(std::integral_constant<int, 2>{}, t0 + 2);
+        }
+        if constexpr (kNB > 3) {
+            if (t0 + 3 >= n_tiles) break;
+            step(std::integral_constant<int, 3>{}, t0 + 3);
+        }
+    }
+    wait_vm_lgkm0<0>();   // drain the ring's clamped tail loads before the work-group ends
+
+    // -- normalise and write: lane holds column col32, head elements
+    //    dt * 32 + (jj / 4) * 8 + hl * 4 + jj % 4
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const float l_all = lsum[nt] + __shfl_xor(lsum[nt], 32);
+        if (!col_ok[nt]) continue;
+        const float inv = 1.f / l_all;
+        const int h = g * a.G + a.r0 + col_r[nt];
+        float* dst = a.out + ((static_cast<int64_t>(a.row0 + b) * a.Hq + h) * a.T + col_i[nt]) * D;
+#pragma unroll
+        for (int dt = 0; dt < P::DT; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = dt * 32 + q4 * 8 + hl * 4;
+                *reinterpret_cast<float4*>(dst + d) =
+                    make_float4(o[nt][dt][q4 * 4 + 0] * inv, o[nt][dt][q4 * 4 + 1] * inv,
+                                o[nt][dt][q4 * 4 + 2] * inv, o[nt][dt][q4 * 4 + 3] * inv);
+            }
+    }
+}
+
+template <int D>
+hipError_t run_p(const PrefillArgs& a, hipStream_t s, unsigned grid) {
+    if (a.st_dtype == BF16) prefill_attn<D, BF16><<<grid, kPThreads, 0, s>>>(a);
+    else if (a.st_dtype == F16) prefill_attn<D, F16><<<grid, kPThreads, 0, s>>>(a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_columns_per_block() { return kPWaves * kNT * 32; }
+
+bool prefill_supported(int D, int st_dtype) {
+    return (D == 32 || D == 64 || D == 128) && (st_dtype == F16 || st_dtype == BF16);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    if (a.Gc < 1 || a.Gc > 32 || a.qpt < 1 || a.qpt * a.Gc > 32) return hipErrorInvalidValue;
+    const int n_qblk = (a.Ti + a.q_per_block - 1) / a.q_per_block;
+    const int64_t grid = static_cast<int64_t>(n_qblk) * a.rows * a.Hkv;
+    if (grid < 1 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    switch (a.D) {
+        case 32: return run_p<32>(a, s, static_cast<unsigned>(grid));
+        case 64: return run_p<64>(a, s, static_cast<unsigned>(grid));
+        case 128: return run_p<128>(a, s, static_cast<unsigned>(grid));
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvc

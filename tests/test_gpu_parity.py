@@ -266,3 +266,60 @@ def test_errors_leave_gpu_state_unchanged():
     torch.cuda.synchronize()
     assert np.array_equal(gpu_bits(cache.k_storage), snap)
     assert [cache.seq_len(layer).tolist() for layer in range(2)] == fills
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_prefill_chunks_matrix_core_path(dtype, D):
+    """Chunks with more than 32 query rows per KV head (the matrix-core kernel):
+    group sizes 1..40 (40 > 32 splits the group), chunk lengths that leave ragged
+    query blocks, rows with different offsets, and offsets that are not multiples
+    of the key tile."""
+    log(f"prefill matrix-core path dtype={dtype} D={D}")
+    rng = np.random.default_rng(600 + D)
+    for (Hq, Hkv, T) in ((2, 2, 40), (4, 1, 33), (9, 3, 100), (32, 8, 64), (16, 2, 17), (40, 1, 9), (8, 8, 300)):
+        B, max_len = 3, 700
+        cache, orc = _new((1, B, Hq, Hkv, D, max_len), dtype)
+        pre = np.array([0, 17, 301])
+        k, v = (rng.standard_normal((B, Hkv, 301, D), dtype=np.float32) for _ in range(2))
+        cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
+        orc.append(0, k, v)
+        cache.truncate(pre)
+        orc.truncate(pre)
+        q, k, v = (rng.standard_normal(s, dtype=np.float32) for s in ((B, Hq, T, D), (B, Hkv, T, D), (B, Hkv, T, D)))
+        cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
+        orc.append(0, k, v)
+        for q_in in ("fp32", dtype):
+            got = cache.attend(0, to_device(q, q_in, DEV)).cpu().numpy()
+            want = orc.attend(0, input_values(q, q_in))
+            mabs, rel = compare_out(got, want, dtype)
+            log(f"  Hq={Hq} Hkv={Hkv} T={T} q={q_in}: rel {rel:.2e} max abs {mabs:.2e}")
+            assert np.isfinite(got).all()
+            assert rel <= HALF_REL_FROB, (Hq, Hkv, T, rel)
+
+
+def test_chunked_prefill_bf16_full_size():
+    """All 32 chunks of T=512 (offsets 0 .. 15872) at B=4, H_q=32, H_kv=8, d_h=128:
+    sampled query rows of two (row, head) pairs per chunk against the oracle."""
+    log("chunked prefill bf16 full size: 32 chunks of 512")
+    shape, calls = W.script_chunked_prefill()
+    from kv_cached_gqa_amd.kvc import KVCache
+    cache = KVCache(shape.n_layers, shape.n_kv_heads, shape.d_head, shape.max_len, batch=shape.batch,
+                    n_q_heads=shape.n_q_heads, dtype=shape.dtype, device=DEV)
+    orc = OracleCache(shape.n_layers, shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.d_head,
+                      shape.max_len, shape.dtype)
+    rng = np.random.default_rng(7)
+    worst = 0.0
+    for n, call in enumerate(calls):
+        cache.append(0, to_device(call.k, "fp32", DEV), to_device(call.v, "fp32", DEV))
+        orc.append(0, call.k, call.v)
+        got = cache.attend(0, to_device(call.q, "bf16", DEV)).cpu().numpy()
+        pairs = [(int(rng.integers(shape.batch)), int(rng.integers(shape.n_q_heads))) for _ in range(2)]
+        rows = sorted({(b, h, int(i)) for (b, h) in pairs for i in rng.integers(0, call.T, 24)} |
+                      {(b, h, call.T - 1) for (b, h) in pairs})
+        want = orc.attend(0, input_values(call.q, "bf16"), rows=rows)
+        mabs, rel = compare_out(got, want, "bf16", rows)
+        worst = max(worst, rel)
+        assert rel <= HALF_REL_FROB, (n, rel)
+        assert np.isfinite(got).all()
+    log(f"  worst rel {worst:.3e}")
