@@ -36,6 +36,9 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 #ifndef KVC_PF_NT
 #define KVC_PF_NT 1           // 32-column tiles per wave
@@ -69,9 +72,29 @@ __device__ __forceinline__ uint32_t to_st(float x) {
     return ST == BF16 ? f32_to_bf16_rne(x) : f32_to_f16_rne(x);
 }
 
+// Two probabilities rounded to the storage type (round to nearest even) and
+// packed low-then-high into one word: one v_cvt_pk_bf16_f32 for bf16. The
+// values are finite and non-negative, so no NaN case is needed.
 template <int ST>
-__device__ __forceinline__ float from_st(uint32_t h) {
-    return ST == BF16 ? bf16_to_f32(h) : f16_to_f32(h);
+__device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
+    if constexpr (ST == BF16) {
+        const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        const f16x2_t v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+// Sum of the two values of a packed pair, exactly as stored.
+template <int ST>
+__device__ __forceinline__ float sum_pair(uint32_t w) {
+    if constexpr (ST == BF16) {
+        return __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
+    } else {
+        const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
+        return static_cast<float>(v[0]) + static_cast<float>(v[1]);
+    }
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding
@@ -252,12 +275,14 @@ void prefill_attn(PrefillArgs a) {
         f32x16_t sacc[kNT];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) sacc[nt] = f32x16_t{};
+        uint4 ka[P::DS];
 #pragma unroll
-        for (int ds = 0; ds < P::DS; ++ds) {
-            const uint4 ka = *reinterpret_cast<const uint4*>(&ks_[P::koff(col32, ds * 16 + hl * 8)]);
+        for (int ds = 0; ds < P::DS; ++ds)
+            ka[ds] = *reinterpret_cast<const uint4*>(&ks_[P::koff(col32, ds * 16 + hl * 8)]);
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) sacc[nt] = mfma32<ST>(ka, qb[nt][ds], sacc[nt]);
-        }
+        for (int ds = 0; ds < P::DS; ++ds)
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) sacc[nt] = mfma32<ST>(ka[ds], qb[nt][ds], sacc[nt]);
 
         // scores -> probabilities, in the C layout: value jj is key
         // j0 + (jj / 4) * 8 + hl * 4 + jj % 4 of this lane's column
@@ -290,19 +315,21 @@ void prefill_attn(PrefillArgs a) {
                 }
             }
             const float nmc = m[nt] == -INFINITY ? 0.f : -m[nt] * c;
-            uint32_t h16[16];
-            float ls = 0.f;
+            uint32_t w[8];
+            float ls[2];
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const float p = fexp2(fmaf(sv_[jj], c, nmc));
-                h16[jj] = to_st<ST>(p);
-                ls += from_st<ST>(h16[jj]);
+            for (int e = 0; e < 8; ++e) {
+                w[e] = pack_p<ST>(fexp2(fmaf(sv_[2 * e], c, nmc)), fexp2(fmaf(sv_[2 * e + 1], c, nmc)));
+                // keep the packed word opaque, so the sum below unpacks it rather
+                // than converting each half a second time
+                asm volatile("" : "+v"(w[e]));
+                const float ps = sum_pair<ST>(w[e]);
+                ls[e & 1] = e < 2 ? ps : ls[e & 1] + ps;
             }
-            lsum[nt] += ls;
+            lsum[nt] += ls[0] + ls[1];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                pb[nt][kk] = make_uint4(h16[kk * 8 + 0] | (h16[kk * 8 + 1] << 16), h16[kk * 8 + 2] | (h16[kk * 8 + 3] << 16),
-                                        h16[kk * 8 + 4] | (h16[kk * 8 + 5] << 16), h16[kk * 8 + 6] | (h16[kk * 8 + 7] << 16));
+                pb[nt][kk] = make_uint4(w[kk * 4 + 0], w[kk * 4 + 1], w[kk * 4 + 2], w[kk * 4 + 3]);
         }
 
         // O^T += V^T P^T: A = V^T rows (head elements) with the keys in the order
@@ -312,15 +339,16 @@ void prefill_attn(PrefillArgs a) {
             const int d = dt * 32 + col32;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                uint32_t w[4];
+                u16x2_t w[4];
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     const int e = 2 * e2;
                     const int key0 = kk * 16 + (e >> 2) * 8 + hl * 4 + (e & 3);
-                    w[e2] = static_cast<uint32_t>(vs_[key0 * D + d]) |
-                            (static_cast<uint32_t>(vs_[(key0 + 1) * D + d]) << 16);
+                    w[e2][0] = vs_[key0 * D + d];
+                    w[e2][1] = vs_[(key0 + 1) * D + d];
                 }
-                const uint4 va = make_uint4(w[0], w[1], w[2], w[3]);
+                const uint4 va = make_uint4(__builtin_bit_cast(uint32_t, w[0]), __builtin_bit_cast(uint32_t, w[1]),
+                                            __builtin_bit_cast(uint32_t, w[2]), __builtin_bit_cast(uint32_t, w[3]));
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) o[nt][dt] = mfma32<ST>(va, pb[nt][kk], o[nt][dt]);
             }
