@@ -38,7 +38,8 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #ifndef KVC_PF_NT
 #define KVC_PF_NT 1           // 32-column tiles per wave
@@ -58,7 +59,7 @@ constexpr int kBN = 32;                // keys per tile
 constexpr float kPRescaleLog2 = 8.f;
 
 template <int ST>
-__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+__device__ __forceinline__ f32x16_t mfma32(const u32x4& a, const u32x4& b, const f32x16_t& c) {
     if constexpr (ST == BF16)
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -111,26 +112,123 @@ struct PCfg {
     static constexpr int DS = D / 16;           // MFMA k-steps over the head dimension
     static constexpr int DT = D / 32;           // 32-wide tiles of the head dimension
     static constexpr int TILE = kBN * D;        // elements per K (or V) tile
+    static constexpr int TILE_BYTES = TILE * 2;
     static constexpr int NLD = TILE * 2 / 1024; // 1 KB LDS-DMA instructions per tile and tensor
     static constexpr int LPW = 2 * ((NLD + kPWaves - 1) / kPWaves);   // DMA loads per wave per stage
-    // element offset of (key r, head element d) in a K tile: rows of D elements,
-    // 16-byte chunks XOR-swizzled by the row so the 32 lanes reading one chunk of
-    // 32 different rows hit distinct banks. V tiles are plain rows: their reads
-    // take one element of one row per lane, consecutive lanes consecutive elements.
-    __device__ static constexpr int koff(int r, int d) {
-        return r * D + (((d >> 3) ^ (r & (CPR - 1))) << 3) + (d & 7);
+    static constexpr int K_OFF = 0;                      // byte offset of the K stages
+    static constexpr int V_OFF = kNB * TILE_BYTES;       // byte offset of the V stages
+    static constexpr int LDS_BYTES = 2 * kNB * TILE_BYTES;
+    // The stage and row offsets travel as the 16-bit immediate of the LDS reads.
+    static_assert(V_OFF + (kNB - 1) * TILE_BYTES + 24 * D * 2 < 65536, "LDS read offsets fit 16 bits");
+
+    // K tile: rows of D elements with the 16-byte chunks XOR-swizzled by the row,
+    // so the 32 lanes that read one chunk of 32 different rows hit distinct banks.
+    __device__ static constexpr int kslot(int r, int c) { return c ^ (r & (CPR - 1)); }
+
+    // V tile: rows of D elements, 16-byte chunk c of row r at slot vslot(r, c).
+    // The transposed reads take 8 bytes per lane from 4 rows r (r % 4 = 0..3)
+    // at the same 32-byte pair of chunks, in two pairs per 16-lane group; the
+    // permutation puts those 4 x 2 pieces on distinct 32-byte bank groups of a
+    // 256-byte bank period, and the 4 pieces of one group on distinct ones of
+    // a 128-byte period.
+    __device__ static constexpr int vslot(int r, int c) {
+        const int u = c >> 1, h = c & 1;
+        int up = 0;
+        if constexpr (D == 128) up = 4 * (u & 1) + (((u >> 1) + r) & 3);
+        else if constexpr (D == 64) up = (u + r) & 3;
+        else up = u ^ ((r >> 1) & 1);
+        return 2 * up + h;
+    }
+    // inverse of vslot for a fixed row: which chunk lands in slot sl
+    __device__ static constexpr int vchunk(int r, int sl) {
+        const int up = sl >> 1, h = sl & 1;
+        int u = 0;
+        if constexpr (D == 128) u = 2 * ((up - r) & 3) + (up >> 2);
+        else if constexpr (D == 64) u = (up - r) & 3;
+        else u = up ^ ((r >> 1) & 1);
+        return 2 * u + h;
     }
 };
+
+// ---- LDS reads (explicit, each group waits for its own data) -------------
+// The transposed read ds_read_b64_tr_b16 works on groups of 16 lanes: lane
+// 16g + 4a + b receives element b of the 8 bytes read by lanes 16g + 4i + a,
+// i = 0..3, as its elements i. Each lane here reads 4 head elements of one key,
+// so every lane gets 4 consecutive keys of one head element.
+#define KVC_RD128(o, a) "ds_read_b128 %" #o ", %" #a " offset:%[off]\n\t"
+#define KVC_RDTR(o, a, imm) "ds_read_b64_tr_b16 %" #o ", %" #a " offset:%[" #imm "]\n\t"
+
+// K operands of one tile: DS reads of 16 bytes at addr[ds] + OFF.
+template <int DS, int OFF>
+__device__ __forceinline__ void read_k(u32x4 (&k)[DS], const uint32_t (&addr)[DS]) {
+    if constexpr (DS == 8) {
+        asm volatile(KVC_RD128(0, 8) KVC_RD128(1, 9) KVC_RD128(2, 10) KVC_RD128(3, 11)
+                     KVC_RD128(4, 12) KVC_RD128(5, 13) KVC_RD128(6, 14) KVC_RD128(7, 15) "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7])
+                     : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]),
+                       "v"(addr[6]), "v"(addr[7]), [off] "i"(OFF)
+                     : "memory");
+    } else if constexpr (DS == 4) {
+        asm volatile(KVC_RD128(0, 4) KVC_RD128(1, 5) KVC_RD128(2, 6) KVC_RD128(3, 7) "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+                     : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), [off] "i"(OFF)
+                     : "memory");
+    } else {
+        static_assert(DS == 2, "head dimension 32, 64 or 128");
+        asm volatile(KVC_RD128(0, 2) KVC_RD128(1, 3) "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(k[0]), "=&v"(k[1])
+                     : "v"(addr[0]), "v"(addr[1]), [off] "i"(OFF)
+                     : "memory");
+    }
+}
+
+// V^T operands of one tile: for head tile dt and key step kk, two transposed
+// reads (keys +0..3 and +8..11 of the lane's 4-key group) at addr[dt] + OFF +
+// (16 kk + 8 h) rows.
+template <int DT, int OFF, int ROWB>
+__device__ __forceinline__ void read_vt(u32x2 (&v)[DT][2][2], const uint32_t (&addr)[DT]) {
+    constexpr int o00 = OFF, o01 = OFF + 8 * ROWB, o10 = OFF + 16 * ROWB, o11 = OFF + 24 * ROWB;
+    if constexpr (DT == 4) {
+        asm volatile(KVC_RDTR(0, 16, o00) KVC_RDTR(1, 16, o01) KVC_RDTR(2, 16, o10) KVC_RDTR(3, 16, o11)
+                     KVC_RDTR(4, 17, o00) KVC_RDTR(5, 17, o01) KVC_RDTR(6, 17, o10) KVC_RDTR(7, 17, o11)
+                     KVC_RDTR(8, 18, o00) KVC_RDTR(9, 18, o01) KVC_RDTR(10, 18, o10) KVC_RDTR(11, 18, o11)
+                     KVC_RDTR(12, 19, o00) KVC_RDTR(13, 19, o01) KVC_RDTR(14, 19, o10) KVC_RDTR(15, 19, o11)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
+                       "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1]),
+                       "=&v"(v[2][0][0]), "=&v"(v[2][0][1]), "=&v"(v[2][1][0]), "=&v"(v[2][1][1]),
+                       "=&v"(v[3][0][0]), "=&v"(v[3][0][1]), "=&v"(v[3][1][0]), "=&v"(v[3][1][1])
+                     : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]),
+                       [o00] "i"(o00), [o01] "i"(o01), [o10] "i"(o10), [o11] "i"(o11)
+                     : "memory");
+    } else if constexpr (DT == 2) {
+        asm volatile(KVC_RDTR(0, 8, o00) KVC_RDTR(1, 8, o01) KVC_RDTR(2, 8, o10) KVC_RDTR(3, 8, o11)
+                     KVC_RDTR(4, 9, o00) KVC_RDTR(5, 9, o01) KVC_RDTR(6, 9, o10) KVC_RDTR(7, 9, o11)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
+                       "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1])
+                     : "v"(addr[0]), "v"(addr[1]),
+                       [o00] "i"(o00), [o01] "i"(o01), [o10] "i"(o10), [o11] "i"(o11)
+                     : "memory");
+    } else {
+        static_assert(DT == 1, "head dimension 32, 64 or 128");
+        asm volatile(KVC_RDTR(0, 4, o00) KVC_RDTR(1, 4, o01) KVC_RDTR(2, 4, o10) KVC_RDTR(3, 4, o11)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1])
+                     : "v"(addr[0]), [o00] "i"(o00), [o01] "i"(o01), [o10] "i"(o10), [o11] "i"(o11)
+                     : "memory");
+    }
+}
+#undef KVC_RD128
+#undef KVC_RDTR
 
 template <int D, int ST>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(KVC_PF_WAVES_PER_EU)))
 void prefill_attn(PrefillArgs a) {
     using P = PCfg<D>;
-    // One LDS object per ring stage: with compile-time stage indices the compiler
-    // can tell that a DMA into one stage does not touch the stage being read, and
-    // does not wait for it.
-    __shared__ __attribute__((aligned(16))) uint16_t sk0[P::TILE], sk1[P::TILE], sk2[P::TILE], sk3[P::TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t sv0[P::TILE], sv1[P::TILE], sv2[P::TILE], sv3[P::TILE];
+    // K stages then V stages. The loop reads them only through the explicit
+    // LDS reads above, after its own wait and barrier.
+    __shared__ __attribute__((aligned(16))) uint16_t smem[P::LDS_BYTES / 2];
     static_assert(kNB >= 2 && kNB <= 4, "the ring has two to four stages");
 
     const int tid = threadIdx.x;
@@ -179,45 +277,51 @@ void prefill_attn(PrefillArgs a) {
     //    (16 bytes per lane, lane i at byte 16 * i of the instruction's 1 KB).
     //    Tiles past the range are issued too, clamped to the last key, so every
     //    wave issues the same number of loads per stage.
-    auto kstage = [&](auto slot_c) -> uint16_t* {
-        constexpr int S = decltype(slot_c)::value;
-        if constexpr (S == 0) return sk0;
-        else if constexpr (S == 1) return sk1;
-        else if constexpr (S == 2) return sk2;
-        else return sk3;
-    };
-    auto vstage = [&](auto slot_c) -> uint16_t* {
-        constexpr int S = decltype(slot_c)::value;
-        if constexpr (S == 0) return sv0;
-        else if constexpr (S == 1) return sv1;
-        else if constexpr (S == 2) return sv2;
-        else return sv3;
-    };
     auto issue = [&](auto slot_c, int t) {
-        uint16_t* kd = kstage(slot_c);
-        uint16_t* vd = vstage(slot_c);
+        constexpr int S = decltype(slot_c)::value;
+        uint16_t* kd = smem + (P::K_OFF + S * P::TILE_BYTES) / 2;
+        uint16_t* vd = smem + (P::V_OFF + S * P::TILE_BYTES) / 2;
 #pragma unroll
         for (int n = wave; n < P::NLD; n += kPWaves) {
             const int e = n * 512 + lane * 8;       // element offset inside the tile
             const int r = e / D;
-            const int phys = (e % D) >> 3;
-            const int chunk = phys ^ (r & (P::CPR - 1));
+            const int sl = (e % D) >> 3;
             int j = t * kBN + r;
             j = j < n_keys ? j : n_keys - 1;
             const int64_t row = static_cast<int64_t>(j) * D;
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kg + row + chunk * 8),
-                                             (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vg + row + phys * 8),
-                                             (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(kg + row + P::kslot(r, sl) * 8),
+                (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(vg + row + P::vchunk(r, sl) * 8),
+                (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0, 0);
         }
     };
     issue(std::integral_constant<int, 0>{}, 0);
     if constexpr (kNB > 2) issue(std::integral_constant<int, 1>{}, 1);
     if constexpr (kNB > 3) issue(std::integral_constant<int, 2>{}, 2);
 
+    // -- LDS read addresses of this lane (stage and row steps are immediates)
+    const uint32_t lds0 = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t*)smem));
+    uint32_t kaddr[P::DS];
+#pragma unroll
+    for (int ds = 0; ds < P::DS; ++ds)
+        kaddr[ds] = lds0 + (col32 * D + P::kslot(col32, 2 * ds + hl) * 8) * 2;
+    uint32_t vaddr[P::DT];
+    {
+        const int grp = lane >> 4, ii = (lane >> 2) & 3, aa = lane & 3;
+        const int rv = (grp >> 1) * 4 + ii;     // key row read by this lane (+ 8 and + 16 steps)
+#pragma unroll
+        for (int dt = 0; dt < P::DT; ++dt) {
+            const int cv = dt * 4 + 2 * (grp & 1) + (aa >> 1);
+            vaddr[dt] = lds0 + (rv * D + P::vslot(rv, cv) * 8) * 2 + (aa & 1) * 8;
+        }
+    }
+
     // -- Q^T as the B operand, rounded as the storage type: 8 consecutive head
     //    elements of this lane's column per k-step
-    uint4 qb[kNT][P::DS];
+    u32x4 qb[kNT][P::DS];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
         const int h = g * a.G + a.r0 + col_r[nt];
@@ -241,7 +345,7 @@ void prefill_attn(PrefillArgs a) {
                 }
                 w[e] = to_st<ST>(x0) | (to_st<ST>(x1) << 16);
             }
-            qb[nt][ds] = make_uint4(w[0], w[1], w[2], w[3]);
+            qb[nt][ds] = u32x4{w[0], w[1], w[2], w[3]};
         }
     }
 
@@ -268,25 +372,25 @@ void prefill_attn(PrefillArgs a) {
 
         const int j0 = t * kBN;
         const bool plain = j0 + kBN - 1 <= vis_all && j0 + kBN <= n_keys;
-        const uint16_t* ks_ = kstage(slot_c);
-        const uint16_t* vs_ = vstage(slot_c);
 
         // S^T tile per column tile: 32 keys x 32 columns
+        u32x4 ka[P::DS];
+        read_k<P::DS, P::K_OFF + S * P::TILE_BYTES>(ka, kaddr);
         f32x16_t sacc[kNT];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) sacc[nt] = f32x16_t{};
-        uint4 ka[P::DS];
-#pragma unroll
-        for (int ds = 0; ds < P::DS; ++ds)
-            ka[ds] = *reinterpret_cast<const uint4*>(&ks_[P::koff(col32, ds * 16 + hl * 8)]);
 #pragma unroll
         for (int ds = 0; ds < P::DS; ++ds)
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) sacc[nt] = mfma32<ST>(ka[ds], qb[nt][ds], sacc[nt]);
 
+        // V^T operands, read while the score MFMAs run
+        u32x2 vt[P::DT][2][2];
+        read_vt<P::DT, P::V_OFF + S * P::TILE_BYTES, D * 2>(vt, vaddr);
+
         // scores -> probabilities, in the C layout: value jj is key
         // j0 + (jj / 4) * 8 + hl * 4 + jj % 4 of this lane's column
-        uint4 pb[kNT][2];
+        u32x4 pb[kNT][2];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
             float sv_[16];
@@ -328,31 +432,19 @@ void prefill_attn(PrefillArgs a) {
             }
             lsum[nt] += ls[0] + ls[1];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                pb[nt][kk] = make_uint4(w[kk * 4 + 0], w[kk * 4 + 1], w[kk * 4 + 2], w[kk * 4 + 3]);
+            for (int kk = 0; kk < 2; ++kk) pb[nt][kk] = u32x4{w[kk * 4 + 0], w[kk * 4 + 1], w[kk * 4 + 2], w[kk * 4 + 3]};
         }
 
-        // O^T += V^T P^T: A = V^T rows (head elements) with the keys in the order
-        // of P^T's registers: for k-step kk, element e is key kk * 16 + (e / 4) * 8 + hl * 4 + e % 4
+        // O^T += V^T P^T: for key step kk, A element e of the lane is key
+        // kk * 16 + (e / 4) * 8 + hl * 4 + e % 4 at head element dt * 32 + lane % 32
 #pragma unroll
-        for (int dt = 0; dt < P::DT; ++dt) {
-            const int d = dt * 32 + col32;
+        for (int dt = 0; dt < P::DT; ++dt)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                u16x2_t w[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const int e = 2 * e2;
-                    const int key0 = kk * 16 + (e >> 2) * 8 + hl * 4 + (e & 3);
-                    w[e2][0] = vs_[key0 * D + d];
-                    w[e2][1] = vs_[(key0 + 1) * D + d];
-                }
-                const uint4 va = make_uint4(__builtin_bit_cast(uint32_t, w[0]), __builtin_bit_cast(uint32_t, w[1]),
-                                            __builtin_bit_cast(uint32_t, w[2]), __builtin_bit_cast(uint32_t, w[3]));
+                const u32x4 va = {vt[dt][kk][0][0], vt[dt][kk][0][1], vt[dt][kk][1][0], vt[dt][kk][1][1]};
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) o[nt][dt] = mfma32<ST>(va, pb[nt][kk], o[nt][dt]);
             }
-        }
     };
     for (int t0 = 0; t0 < n_tiles; t0 += kNB) {
         step(std::integral_constant<int, 0>{}, t0);
