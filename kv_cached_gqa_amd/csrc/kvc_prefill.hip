@@ -10,8 +10,9 @@
 //    chunk's queries. Its columns are (query i, query head r) pairs, query-major
 //    (c = i * G + r), so all G heads that share K/V sit in the same tiles and
 //    every K/V tile staged in LDS serves all of them ("Heads, GQA and K/V
-//    cache": a group of queries shares the same keys and values). Each wave
-//    owns NT tiles of 32 columns.
+//    cache": a group of queries shares the same keys and values). Each of the
+//    8 waves owns NT tiles of 32 columns; two waves share a SIMD, so one's
+//    softmax runs while the other's MFMAs do.
 //  * S^T = K Q^T. A = K tile rows from LDS (16 bytes per lane), B = Q^T held in
 //    registers for the whole launch. The C layout gives each lane one column
 //    (lane % 32) and 16 of the 32 keys; the other 16 are in lane ^ 32, so the
@@ -45,13 +46,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define KVC_PF_NT 1           // 32-column tiles per wave
 #endif
 #ifndef KVC_PF_WAVES_PER_EU
-#define KVC_PF_WAVES_PER_EU 2   // two work-groups per CU: one softmax overlaps the other's MFMAs
+#define KVC_PF_WAVES_PER_EU 2   // two waves per SIMD: one's softmax overlaps the other's MFMAs
 #endif
 #ifndef KVC_PF_STAGES
 #define KVC_PF_STAGES 3       // key/value tiles in the LDS ring
 #endif
 
-constexpr int kPWaves = 4;
+#ifndef KVC_PF_WAVES
+#define KVC_PF_WAVES 8        // waves per work-group: every staged K/V tile serves 8 x 32 columns
+#endif
+constexpr int kPWaves = KVC_PF_WAVES;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kNT = KVC_PF_NT;
 constexpr int kNB = KVC_PF_STAGES;
@@ -87,14 +91,16 @@ __device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
     }
 }
 
-// Sum of the two values of a packed pair, exactly as stored.
+// acc + the two values of a packed pair, as stored: a dot product with (1, 1)
+// (exact products, float32 sum) in one instruction.
 template <int ST>
-__device__ __forceinline__ float sum_pair(uint32_t w) {
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
     if constexpr (ST == BF16) {
-        return __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
+        const bf16x2_t one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
     } else {
-        const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
-        return static_cast<float>(v[0]) + static_cast<float>(v[1]);
+        const f16x2_t one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), one, acc, false);
     }
 }
 
@@ -233,7 +239,7 @@ void prefill_attn(PrefillArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches on it
     const int col32 = lane & 31;
     const int hl = lane >> 5;                   // which half of the k-dimension this lane feeds
 
@@ -404,13 +410,15 @@ void prefill_attn(PrefillArgs a) {
                     if (j > lim || j >= n_keys) sv_[jj] = -INFINITY;
                 }
             }
+            // The reference max moves only when a score passes it by the
+            // threshold; each half-column checks its own 16 keys, and only then
+            // is the column's max formed across the two halves (lane ^ 32).
             float mt = sv_[0];
 #pragma unroll
             for (int jj = 1; jj < 16; ++jj) mt = fmaxf(mt, sv_[jj]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const bool need = mt - m[nt] > thresh;
-            if (__any(need)) {
-                if (need) {
+            if (__any(mt - m[nt] > thresh)) {
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                if (mt - m[nt] > thresh) {
                     const float alpha = m[nt] == -INFINITY ? 0.f : fexp2((m[nt] - mt) * c);
                     m[nt] = mt;
                     lsum[nt] *= alpha;
@@ -420,15 +428,11 @@ void prefill_attn(PrefillArgs a) {
             }
             const float nmc = m[nt] == -INFINITY ? 0.f : -m[nt] * c;
             uint32_t w[8];
-            float ls[2];
+            float ls[2] = {0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 w[e] = pack_p<ST>(fexp2(fmaf(sv_[2 * e], c, nmc)), fexp2(fmaf(sv_[2 * e + 1], c, nmc)));
-                // keep the packed word opaque, so the sum below unpacks it rather
-                // than converting each half a second time
-                asm volatile("" : "+v"(w[e]));
-                const float ps = sum_pair<ST>(w[e]);
-                ls[e & 1] = e < 2 ? ps : ls[e & 1] + ps;
+                ls[e & 1] = add_pair<ST>(w[e], ls[e & 1]);
             }
             lsum[nt] += ls[0] + ls[1];
 #pragma unroll
