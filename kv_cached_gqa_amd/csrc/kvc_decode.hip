@@ -4,37 +4,41 @@
 // "kv-cache-decoding", "Prefill and decode": one row of t + 1 scores per head).
 //
 // Decode reads every cached key and value once and does ~4 flops per byte,
-// so it is bound by HBM bandwidth. The design keeps the loads wide, coalesced
-// and always in flight, and keeps the vector ALU work per key small:
+// so it is bound by HBM bandwidth. The design keeps many bytes in flight on
+// every CU, for the whole launch, and keeps the vector ALU work per key small:
 //
 //  * Work split ("stream-K"). Unit u = (batch row b, KV head g) owns n_b keys.
 //    The units are laid end to end along one axis of sum(n_b) * H_kv keys and
 //    every work-group takes an equal slice of it, so ragged row lengths cost
-//    no load imbalance. The grid is exactly the number of work-groups the GPU
-//    keeps resident, so there is one round and no tail. A slice that crosses
-//    unit boundaries is cut into segments; segment (work-group k, unit u) is
-//    stored at index k + u, which is unique because each new segment starts at
-//    a slice boundary, a unit boundary or both.
-//  * Lane layout. One key row of D elements is LPK lanes x 16 bytes; a wave
-//    covers KPW = 64 / LPK consecutive keys per load, i.e. one contiguous
-//    stretch of memory. All query rows of the slab (the G query heads that
-//    share the KV head, times the chunk's query positions) are held in every
-//    lane group, so each key and value is read from HBM exactly once for the
-//    whole group ("Heads, GQA and K/V cache": heads sharing one K/V).
-//    Loads are double-buffered: the next batch is in flight while the current
-//    one is being used.
+//    no load imbalance. One work-group per CU: all of them start together, so
+//    none is starved by older waves at the memory arbiters. A slice that
+//    crosses unit boundaries is cut into segments; segment (work-group k,
+//    unit u) is stored at index k + u, which is unique because each new
+//    segment starts at a slice boundary, a unit boundary or both.
+//  * Loads. Each wave streams its own keys through a private ring of NS LDS
+//    stages filled by LDS-DMA (global_load_lds, 16 bytes per lane): NS - 1
+//    stages are in flight while one is used, with no registers held for them.
+//    The ring runs straight across segment boundaries, so the next unit's keys
+//    are already on their way while a segment is merged. Each wave waits for
+//    its own loads only (an explicit vmcnt), so the loop has no barrier.
+//  * Lane layout. One key row of D elements is LPK lanes x 16 bytes; a load of
+//    64 lanes covers KPW = 64 / LPK consecutive keys, one contiguous 1 KB. All
+//    query rows of the slab (the G query heads that share the KV head, times
+//    the chunk's query positions) are held in every lane group, so each key
+//    and value is read from HBM exactly once for the whole group ("Heads, GQA
+//    and K/V cache": heads sharing one K/V). The queries of the work-group's
+//    segments are converted once into an LDS table at the start.
 //  * q.k: 16-bit dot2 instructions (exact products, fp32 accumulation) or fp32
 //    FMA, then a DPP sum over the LPK lanes of the key. Scores stay in raw
 //    q.k units; the softmax scale and log2(e) are folded into one FMA before
 //    exp2. The running max only triggers a rescale when it grows somewhere in
 //    the wave. p stays fp32 and p*v is an fp32 FMA.
-//  * Merge. At the end of a segment the lane groups and the four waves merge
-//    their (max, sum, output). A unit held by one segment is normalised and
-//    written at once; otherwise the segment's partial record goes to the
-//    workspace and a second, small kernel merges each split unit's records.
-//    (Merging inside the first kernel would need agent-scope fences per
-//    segment, which write back and invalidate an XCD's L2 and cost far more
-//    than the second launch.)
+//  * Merge. At the end of a segment the lane groups and the waves merge their
+//    (max, sum, output). A unit held by one segment is normalised and written
+//    at once; otherwise the segment's partial record goes to the workspace and
+//    a second, small kernel merges each split unit's records.
+#include <type_traits>
+
 #include "kvc_device.h"
 
 namespace kvc {
@@ -42,97 +46,127 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef KVC_DECODE_WAVES4
-#define KVC_DECODE_WAVES4 4   // waves per work-group for 4 query rows or fewer
+#ifndef KVC_DECODE_WAVES
+#define KVC_DECODE_WAVES 4        // waves per work-group
 #endif
-#ifndef KVC_DECODE_WAVES8
-#define KVC_DECODE_WAVES8 4   // waves per work-group for 5 to 8 query rows
+#ifndef KVC_DECODE_STAGES
+#define KVC_DECODE_STAGES 3       // LDS ring stages per wave
 #endif
-
-template <int ST>
-struct Layout {
-    static constexpr int esz = ST == F32 ? 4 : 2;
-    static constexpr int epl = 16 / esz;   // elements per lane per 16-byte load
-};
-
-template <int ST>
-__device__ __forceinline__ float dot16(const uint32_t (&q)[4], const uint4& k, float acc) {
-    const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        if constexpr (ST == BF16)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[e]),
-                                                  __builtin_bit_cast(bf16x2_t, kw[e]), acc, false);
-        else
-            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q[e]),
-                                         __builtin_bit_cast(f16x2_t, kw[e]), acc, false);
-    }
-    return acc;
-}
-
-template <int ST, int EPL>
-__device__ __forceinline__ void unpack_v(const uint4& v, float (&o)[EPL]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        if constexpr (ST == F32) {
-            o[e] = __uint_as_float(w[e]);
-        } else if constexpr (ST == BF16) {
-            o[2 * e] = __uint_as_float(w[e] << 16);
-            o[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-        } else {
-            o[2 * e] = f16_to_f32(w[e] & 0xFFFFu);
-            o[2 * e + 1] = f16_to_f32(w[e] >> 16);
-        }
-    }
-}
-
 #ifndef KVC_DECODE_U
-#define KVC_DECODE_U 1        // keys per lane group in one batch
-#endif
-#ifndef KVC_DECODE_NBUF
-#define KVC_DECODE_NBUF 3     // batches held in registers: NBUF - 1 in flight while one is used
-#endif
-
-#ifndef KVC_DECODE_CH
-#define KVC_DECODE_CH 1       // 16-byte chunks per lane per key row (4 query rows or fewer)
+#define KVC_DECODE_U 2            // 1 KB loads per tensor per stage (4 query rows or fewer)
 #endif
 #ifndef KVC_DECODE_RESCALE_LOG2
 #define KVC_DECODE_RESCALE_LOG2 8.0f
 #endif
 #ifndef KVC_DECODE_BLOCKS_PER_CU
-#define KVC_DECODE_BLOCKS_PER_CU 0   // 0: as many as stay resident
+#define KVC_DECODE_BLOCKS_PER_CU 2
+#endif
+#ifndef KVC_DECODE_LATE_PCT
+#define KVC_DECODE_LATE_PCT 70       // slice of a later-dispatched work-group, % of a first-round one
 #endif
 
 // Rescale threshold (log2 units): the running reference max moves only when a
 // score exceeds it by more than this, so p = exp2(s - m) stays below 2^8.
 constexpr float kRescaleLog2 = KVC_DECODE_RESCALE_LOG2;
+constexpr int kQTableSegs = 8;    // segments whose queries the LDS table holds at once
+constexpr int kLdsLimit = 160 * 1024;
+
+template <int ST>
+__device__ __forceinline__ float dot16(const uint32_t (&q)[4], const u32x4& k, float acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // copy the element out first: a bit cast applied to a vector element
+        // directly has been seen to read element 0 for every e
+        const uint32_t kw = k[e];
+        if constexpr (ST == BF16)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[e]), __builtin_bit_cast(bf16x2_t, kw),
+                                                  acc, false);
+        else
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q[e]), __builtin_bit_cast(f16x2_t, kw), acc, false);
+    }
+    return acc;
+}
+
+template <int ST, int EPC>
+__device__ __forceinline__ void unpack_v(const u32x4& v, float (&o)[EPC]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (ST == F32) {
+            o[e] = __uint_as_float(v[e]);
+        } else if constexpr (ST == BF16) {
+            o[2 * e] = __uint_as_float(v[e] << 16);
+            o[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+        } else {
+            o[2 * e] = f16_to_f32(v[e] & 0xFFFFu);
+            o[2 * e + 1] = f16_to_f32(v[e] >> 16);
+        }
+    }
+}
 
 template <int D, int ST, int R>
 struct Cfg {
-    static constexpr int ESZ = Layout<ST>::esz;
-    static constexpr int CH = R <= 4 ? KVC_DECODE_CH : 1;   // 16-byte chunks per lane per key row
-    static constexpr int EPC = 16 / ESZ;           // elements per chunk
-    static constexpr int EPL = CH * EPC;           // elements per lane
-    static constexpr int LPK = D / EPL;            // lanes per key row
-    static constexpr int KPW = 64 / LPK;           // keys per wave per load
-    static constexpr int U = KVC_DECODE_U;
-    static constexpr int WAVES = R <= 4 ? KVC_DECODE_WAVES4 : KVC_DECODE_WAVES8;
+    static constexpr int ESZ = ST == F32 ? 4 : 2;
+    static constexpr int EPC = 16 / ESZ;               // elements per lane (16 bytes)
+    static constexpr int LPK = D / EPC;                // lanes per key row
+    static constexpr int KPW = 64 / LPK;               // keys per 1 KB load
+    static constexpr int WAVES = KVC_DECODE_WAVES;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int NBUF = KVC_DECODE_NBUF;
-    static constexpr int KEYS_PER_WAVE = KPW * U;  // keys per wave per batch
-    static constexpr int KEYS_PER_BATCH = KEYS_PER_WAVE * WAVES;    // keys per work-group round
-    static constexpr int NQ = ST == F32 ? EPL : EPL / 2;   // q registers per row
-    // element index of chunk c, element e of lane `sub`
-    __device__ static constexpr int elem(int sub, int c, int e) { return c * (D / CH) + sub * EPC + e; }
+    static constexpr int U = (R <= 4 && ST != F32) ? KVC_DECODE_U : 1;   // loads per tensor per stage
+    static constexpr int KPS = U * KPW;                // keys per wave per stage
+    static constexpr int KPB = WAVES * KPS;            // keys per work-group batch
+    static constexpr int STAGE_BYTES = U * 2048;       // K and V of one stage of one wave
+    static constexpr int FIXED_BYTES = kQTableSegs * R * D * ESZ + WAVES * R * (D + 2) * 4;
+    // ring stages: as many as asked for, fewer if the LDS budget (at the work-groups
+    // per CU asked for) does not hold them
+    static constexpr int fit_stages() {
+        int ns = KVC_DECODE_STAGES;
+        const int per_cu = KVC_DECODE_BLOCKS_PER_CU > 0 ? KVC_DECODE_BLOCKS_PER_CU : 1;
+        while (ns > 2 && (WAVES * ns * STAGE_BYTES + FIXED_BYTES) * per_cu > kLdsLimit) --ns;
+        return ns;
+    }
+    static constexpr int NS = fit_stages();
+    static constexpr int RING_BYTES = WAVES * NS * STAGE_BYTES;
+    static constexpr int QROW_WORDS = D * ESZ / 4;     // one query row in the storage format
+    static constexpr int LDS_BYTES = RING_BYTES + FIXED_BYTES;
+    static_assert(LDS_BYTES <= kLdsLimit, "decode LDS budget");
+    static_assert((NS - 1) * 2 * U < 64, "vmcnt field");
+    static_assert((NS - 1) * STAGE_BYTES + STAGE_BYTES < 65536, "ring offsets fit the LDS immediate");
 };
 
-template <int D, int ST, int R>
-struct Batch {
-    uint4 k[Cfg<D, ST, R>::U][Cfg<D, ST, R>::CH];
-    uint4 v[Cfg<D, ST, R>::U][Cfg<D, ST, R>::CH];
-};
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding; LDS and export counters not waited).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Work-group barrier for LDS data only: this wave's LDS operations are done,
+// then every wave has arrived. (__syncthreads would also wait for every load
+// in flight, draining the DMA ring.) The clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// K and V words of this lane for one 1 KB load of a stage: ring bytes at
+// addr + OFF and addr + OFF + 1024, read after their own wait.
+template <int OFF>
+__device__ __forceinline__ void read_kv(u32x4& k, u32x4& v, uint32_t addr) {
+    asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(k), "=&v"(v)
+                 : "v"(addr), "i"(OFF), "i"(OFF + 1024)
+                 : "memory");
+}
+
+// f(integral_constant<0>), ..., f(integral_constant<N - 1>), unrolled.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
 
 template <int LPK, int M>
 __device__ __forceinline__ void lane_group_sum(float (&x)[M]) {
@@ -144,247 +178,230 @@ __device__ __forceinline__ void lane_group_sum(float (&x)[M]) {
     }
 }
 
-#ifndef KVC_DECODE_WAVES_PER_EU
-#define KVC_DECODE_WAVES_PER_EU 1
-#endif
+// One segment of the work-group's slice: keys [j0, j1) of unit (b, g), whose
+// last slab query sits at position n_b - Tc.
+struct Seg {
+    int b, g;
+    int j0, j1, n_b;
+    int nbat;                // work-group batches of KPB keys
+    int64_t head;            // element offset of the unit's key 0
+    int64_t x_end;           // key-axis position where the segment ends
+    int64_t rec;             // workspace record, or -1: the whole unit, written directly
+};
 
 template <int D, int ST, int R>
-__global__ __launch_bounds__((Cfg<D, ST, R>::THREADS)) __attribute__((amdgpu_waves_per_eu(KVC_DECODE_WAVES_PER_EU)))
+__global__ __launch_bounds__((Cfg<D, ST, R>::THREADS)) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_attn(DecodeArgs a) {
     using C = Cfg<D, ST, R>;
     constexpr int kWaves = C::WAVES, kThreads = C::THREADS;
-    constexpr int EPL = C::EPL, EPC = C::EPC, CH = C::CH, LPK = C::LPK, KPW = C::KPW, U = C::U, NQ = C::NQ;
-    constexpr int ESZ = C::ESZ;
+    constexpr int EPC = C::EPC, LPK = C::LPK, KPW = C::KPW, U = C::U, NS = C::NS;
+    constexpr int KPS = C::KPS, KPB = C::KPB, ESZ = C::ESZ;
 
+    // Separate LDS objects: the ring (written by LDS-DMA, read only through the
+    // explicit reads above), the query table and the merge area.
+    __shared__ __attribute__((aligned(16))) uint8_t ring[C::RING_BYTES];
+    __shared__ __attribute__((aligned(16))) uint32_t qtab[kQTableSegs][R][C::QROW_WORDS];
     __shared__ float sm_o[kWaves][R][D];
     __shared__ float sm_m[kWaves][R];
     __shared__ float sm_l[kWaves][R];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = lane / LPK;
     const int sub = lane % LPK;
     const int rows_act = a.Gc * a.Tc;
     const float c = a.scale_log2;
-    const float thresh = kRescaleLog2 / c;     // the threshold in raw q.k units (0: any growth)
+    const float thresh = kRescaleLog2 / c;     // the threshold in raw q.k units
 
-    const int64_t x_begin = static_cast<int64_t>(blockIdx.x) * a.keys_per_block;
-    int64_t x_end = x_begin + a.keys_per_block;
+    const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
+    int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
     if (x_end > a.total_keys) x_end = a.total_keys;
+    if (x_begin >= x_end) return;
 
     const char* kc = static_cast<const char*>(a.k_cache);
     const char* vc = static_cast<const char*>(a.v_cache);
 
-    for (int64_t x = x_begin; x < x_end;) {
-        // -- locate the unit holding key x (wave-uniform) --
+    // -- the segment that starts at key-axis position x (wave-uniform) --
+    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
         int lo = 0, hi = a.rows;   // prefix[lo] <= x < prefix[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (a.prefix[mid] <= x) lo = mid; else hi = mid;
         }
-        const int b = lo;
-        const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
-        const int g = static_cast<int>((x - a.prefix[b]) / n_b);
-        const int u_idx = b * a.Hkv + g;
-        const int64_t unit_start = a.prefix[b] + static_cast<int64_t>(g) * n_b;
+        Seg sg;
+        sg.b = lo;
+        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
+        sg.g = static_cast<int>((x - a.prefix[lo]) / n_b);
+        const int64_t unit_start = a.prefix[lo] + static_cast<int64_t>(sg.g) * n_b;
         int64_t seg_end = unit_start + n_b;
         if (seg_end > x_end) seg_end = x_end;
-        const int j0 = static_cast<int>(x - unit_start);
-        const int j1 = static_cast<int>(seg_end - unit_start);
-        const bool whole_unit = j0 == 0 && j1 == n_b;
+        sg.j0 = static_cast<int>(x - unit_start);
+        sg.j1 = static_cast<int>(seg_end - unit_start);
+        sg.n_b = static_cast<int>(n_b);
+        sg.nbat = (sg.j1 - sg.j0 + KPB - 1) / KPB;
+        sg.head = a.layer_off + sg.b * a.row_stride + sg.g * a.head_stride;
+        sg.x_end = seg_end;
+        sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
+        return sg;
+    };
 
-        const int64_t head_base = a.layer_off + b * a.row_stride + g * a.head_stride;
-        const int qpos0 = static_cast<int>(n_b) - a.Tc;   // absolute position of slab query 0
+    // -- the query table: the slab's rows of up to kQTableSegs segments from x,
+    //    rounded to the storage type (rows past the slab are zero) --
+    auto load_qtab = [&](int64_t x) __attribute__((always_inline)) {
+        for (int sgi = 0; sgi < kQTableSegs && x < x_end; ++sgi) {
+            const Seg sg = locate(x);
+            for (int idx = tid; idx < R * D; idx += kThreads) {
+                const int r = idx / D, e = idx - (idx / D) * D;
+                float val = 0.f;
+                if (r < rows_act) {
+                    const int h = sg.g * a.G + a.r0 + r / a.Tc;
+                    const int i = a.i0 + r % a.Tc;
+                    const int64_t qe = ((static_cast<int64_t>(a.row0 + sg.b) * a.Hq + h) * a.T + i) * D + e;
+                    if (a.q_dtype == F32) val = static_cast<const float*>(a.q)[qe];
+                    else if (a.q_dtype == BF16) val = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
+                    else val = f16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
+                }
+                if constexpr (ST == F32) {
+                    reinterpret_cast<float*>(qtab[sgi][r])[e] = val;
+                } else {
+                    const uint32_t h16 = ST == BF16 ? f32_to_bf16_rne(val) : f32_to_f16_rne(val);
+                    reinterpret_cast<uint16_t*>(qtab[sgi][r])[e] = static_cast<uint16_t>(h16);
+                }
+            }
+            x = sg.x_end;
+        }
+        __syncthreads();
+    };
 
-        float qf[ST == F32 ? R : 1][ST == F32 ? EPL : 1];   // fp32 caches: q as float
-        uint32_t qp[R][NQ];                                 // 16-bit caches: q as packed pairs
-        int qpos[R];
-        float m[R], l[R], o[R][EPL];
+    // -- issue side: the next stage of this wave's keys, possibly in a later
+    //    segment; past the slice's end it reloads the last key (never used) --
+    Seg is = locate(x_begin);
+    int is_t = 0;
+    bool is_live = true;
+    uint8_t* const ring_w = ring + wave * (NS * C::STAGE_BYTES);
+    auto issue = [&](auto slot_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot_c)::value;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int j = is.j0 + is_t * KPB + wave * KPS + u * KPW + grp;
+            j = j < is.j1 ? j : is.j1 - 1;
+            const int64_t off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
+            uint8_t* dst = ring_w + S * C::STAGE_BYTES + u * 2048;
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kc + off),
+                                             (void __attribute__((address_space(3)))*)(dst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vc + off),
+                                             (void __attribute__((address_space(3)))*)(dst + 1024), 16, 0, 0);
+        }
+        if (is_live && ++is_t == is.nbat) {
+            if (is.x_end >= x_end) {
+                is_live = false;
+            } else {
+                is = locate(is.x_end);
+                is_t = 0;
+            }
+        }
+    };
+
+    // -- consume side --
+    const uint32_t rd_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                                 (__attribute__((address_space(3))) uint8_t*)ring_w)) + lane * 16;
+    Seg cs = locate(x_begin);
+    int cs_t = 0, cs_q = 0;
+    uint32_t qp[R][4];                 // the lane's 16 bytes of each query row
+    int qpos[R];
+    float m[R], l[R], o[R][EPC];
+    auto start_segment = [&]() __attribute__((always_inline)) {
+        const int qpos0 = cs.n_b - a.Tc;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(&qtab[cs_q][r][sub * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qp[r][e] = w[e];
+            qpos[r] = r < rows_act ? qpos0 + r % a.Tc : -1;
             m[r] = -INFINITY;
             l[r] = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) o[r][e] = 0.f;
+            for (int e = 0; e < EPC; ++e) o[r][e] = 0.f;
         }
+    };
 
-        // -- stream the segment's keys through a ring of register batches --
-        // Batch t of wave w = keys [j0 + t * KEYS_PER_BATCH + w * KEYS_PER_WAVE, + KEYS_PER_WAVE).
-        // The assignment is static, so the summation order (and the result) is the same
-        // on every run.
-        const int key_w0 = j0 + wave * C::KEYS_PER_WAVE + grp;   // this lane's first key
-        const int n_batches = (j1 - j0 + C::KEYS_PER_BATCH - 1) / C::KEYS_PER_BATCH;
-
-        auto issue = [&](Batch<D, ST, R>& bt, int t) {
+    auto consume = [&](auto slot_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot_c)::value;
+        const int kb = cs.j0 + cs_t * KPB + wave * KPS;          // this wave's first key of the stage
+        const bool plain = kb + KPS - 1 < cs.j1 && kb + KPS - 1 <= cs.n_b - a.Tc;
+        u32x4 kx[U], vx[U];
+        static_for<U>([&](auto u_c) {
+            constexpr int u = decltype(u_c)::value;
+            read_kv<S * C::STAGE_BYTES + u * 2048>(kx[u], vx[u], rd_addr);
+        });
+        float s[U * R];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                int j = key_w0 + t * C::KEYS_PER_BATCH + u * KPW;
-                j = j < j1 ? j : j1 - 1;
-                const int64_t row = (head_base + static_cast<int64_t>(j) * D) * ESZ;
-#pragma unroll
-                for (int ch = 0; ch < CH; ++ch) {
-                    const int64_t off = row + C::elem(sub, ch, 0) * ESZ;
-                    bt.k[u][ch] = *reinterpret_cast<const uint4*>(kc + off);
-                    bt.v[u][ch] = *reinterpret_cast<const uint4*>(vc + off);
-                }
-            }
-        };
-
-        auto consume = [&](const Batch<D, ST, R>& bt, int t) {
-            const int jb = key_w0 + t * C::KEYS_PER_BATCH;           // key of u = 0 for this lane
-            const int jw_last = j0 + wave * C::KEYS_PER_WAVE + t * C::KEYS_PER_BATCH + C::KEYS_PER_WAVE - 1;
-            const bool plain = jw_last < j1 && jw_last <= qpos0;     // no key of this wave is masked
-            float s[U * R];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int ch = 0; ch < CH; ++ch) {
-                        if constexpr (ST == F32) {
-                            const uint32_t kw[4] = {bt.k[u][ch].x, bt.k[u][ch].y, bt.k[u][ch].z, bt.k[u][ch].w};
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) acc = fmaf(qf[r][ch * 4 + e], __uint_as_float(kw[e]), acc);
-                        } else {
-                            acc = dot16<ST>(reinterpret_cast<const uint32_t(&)[4]>(qp[r][ch * 4]), bt.k[u][ch], acc);
-                        }
-                    }
-                    s[u * R + r] = acc;
-                }
-            }
-            lane_group_sum<LPK, U * R>(s);
-            if (!plain) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int j = jb + u * KPW;
-#pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        if (!(j < j1 && j <= qpos[r])) s[u * R + r] = -INFINITY;
-                }
-            }
-            // the reference max moves only when a score passes it by the threshold
-            float mt[R];
-            bool need = false;
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                mt[r] = s[r];
-#pragma unroll
-                for (int u = 1; u < U; ++u) mt[r] = fmaxf(mt[r], s[u * R + r]);
-                need |= (mt[r] - m[r] > thresh) || (mt[r] > m[r] && thresh == 0.f);
-            }
-            if (__any(need)) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    if ((mt[r] - m[r] > thresh) || (mt[r] > m[r] && thresh == 0.f)) {
-                        const float alpha = m[r] == -INFINITY ? 0.f : fexp2((m[r] - mt[r]) * c);
-                        m[r] = mt[r];
-                        l[r] *= alpha;
-#pragma unroll
-                        for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
-                    }
-                }
-            }
-            float nmc[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) nmc[r] = m[r] == -INFINITY ? 0.f : -m[r] * c;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float vf[EPL];
-#pragma unroll
-                for (int ch = 0; ch < CH; ++ch)
-                    unpack_v<ST, EPC>(bt.v[u][ch], reinterpret_cast<float(&)[EPC]>(vf[ch * EPC]));
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const float p = fexp2(fmaf(s[u * R + r], c, nmc[r]));
-                    l[r] += p;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
-                }
-            }
-        };
-
-        // -- the slab's queries, as raw 16-byte words. Every load below is issued
-        //    unconditionally (rows past the slab reread row 0 and are zeroed, a
-        //    16-bit q rereads its first word): a load under a branch would make
-        //    the compiler wait for all outstanding loads where the paths meet,
-        //    which serialises the key/value pipeline.
-        // A lane needs EPC * qsz bytes per chunk: 32 (two words of 16), 16, or 8
-        // (fp32 cache, 16-bit q), read from the enclosing aligned 16 bytes, which
-        // lie inside the row because rows are multiples of 16 bytes.
-        const int qsz = a.q_dtype == F32 ? 4 : 2;
-        const int qnb = EPC * qsz;
-        uint4 qraw[R][CH][2];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int rr = r < rows_act ? r : 0;
-            const int hr = rr / a.Tc, ir = rr - (rr / a.Tc) * a.Tc;
-            const int h = g * a.G + a.r0 + hr;
-            const int i = a.i0 + ir;
-            const int64_t qrow = ((static_cast<int64_t>(a.row0 + b) * a.Hq + h) * a.T + i) * D;
-#pragma unroll
-            for (int ch = 0; ch < CH; ++ch) {
-                const char* qb = static_cast<const char*>(a.q) + (qrow + C::elem(sub, ch, 0)) * qsz;
-                const char* p0 = qnb == 8 ? qb - (reinterpret_cast<uintptr_t>(qb) & 15) : qb;
-                qraw[r][ch][0] = *reinterpret_cast<const uint4*>(p0);
-                qraw[r][ch][1] = *reinterpret_cast<const uint4*>(qnb == 32 ? qb + 16 : p0);
-            }
-        }
-        // word offset of the lane's first element inside the 16 bytes read (8-byte case)
-        const int qwsh = qnb == 8 ? static_cast<int>((C::elem(sub, 0, 0) * qsz / 8) & 1) * 2 : 0;
-
-        // ring of NBUF batches: batch t lives in slot t % NBUF, NBUF - 1 batches ahead.
-        // Batches past the segment's end are issued too (clamped to its last key).
-        Batch<D, ST, R> ring[C::NBUF];
-#pragma unroll
-        for (int k = 0; k < C::NBUF - 1; ++k) issue(ring[k], k);
-
-        // -- convert the queries (waits only for the q words), rounded as the storage type --
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            qpos[r] = r < rows_act ? qpos0 + r % a.Tc : -1;
-#pragma unroll
-            for (int ch = 0; ch < CH; ++ch) {
-                float tmp[EPC];
-                const uint32_t w0[8] = {qraw[r][ch][0].x, qraw[r][ch][0].y, qraw[r][ch][0].z, qraw[r][ch][0].w,
-                                        qraw[r][ch][1].x, qraw[r][ch][1].y, qraw[r][ch][1].z, qraw[r][ch][1].w};
-                uint32_t w[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w[e] = qwsh ? w0[(e + 2) & 7] : w0[e];
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) {
-                    float x;
-                    if (a.q_dtype == F32) x = __uint_as_float(w[e]);
-                    else if (a.q_dtype == BF16) x = bf16_to_f32((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-                    else x = f16_to_f32((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-                    tmp[e] = r < rows_act ? round_as<ST>(x) : 0.f;
-                }
+                float acc = 0.f;
                 if constexpr (ST == F32) {
 #pragma unroll
-                    for (int e = 0; e < EPC; ++e) qf[r][ch * EPC + e] = tmp[e];
+                    for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(qp[r][e]), __uint_as_float(kx[u][e]), acc);
                 } else {
+                    acc = dot16<ST>(qp[r], kx[u], acc);
+                }
+                s[u * R + r] = acc;
+            }
+        }
+        lane_group_sum<LPK, U * R>(s);
+        if (!plain) {
 #pragma unroll
-                    for (int e = 0; e < EPC / 2; ++e) {
-                        const uint32_t lo16 = ST == BF16 ? f32_to_bf16_rne(tmp[2 * e]) : f32_to_f16_rne(tmp[2 * e]);
-                        const uint32_t hi16 = ST == BF16 ? f32_to_bf16_rne(tmp[2 * e + 1]) : f32_to_f16_rne(tmp[2 * e + 1]);
-                        qp[r][ch * (EPC / 2) + e] = lo16 | (hi16 << 16);
-                    }
+            for (int u = 0; u < U; ++u) {
+                const int j = kb + u * KPW + grp;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (!(j < cs.j1 && j <= qpos[r])) s[u * R + r] = -INFINITY;
+            }
+        }
+        // the reference max moves only when a score passes it by the threshold
+        float mt[R];
+        bool need = false;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            mt[r] = s[r];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mt[r] = fmaxf(mt[r], s[u * R + r]);
+            need |= mt[r] - m[r] > thresh;
+        }
+        if (__any(need)) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (mt[r] - m[r] > thresh) {
+                    const float alpha = m[r] == -INFINITY ? 0.f : fexp2((m[r] - mt[r]) * c);
+                    m[r] = mt[r];
+                    l[r] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) o[r][e] *= alpha;
                 }
             }
         }
-
-        for (int t0 = 0; t0 < n_batches; t0 += C::NBUF) {
+        float nmc[R];
 #pragma unroll
-            for (int k = 0; k < C::NBUF; ++k) {
-                const int t = t0 + k;
-                if (t >= n_batches) break;
-                issue(ring[(k + C::NBUF - 1) % C::NBUF], t + C::NBUF - 1);
-                consume(ring[k], t);
+        for (int r = 0; r < R; ++r) nmc[r] = m[r] == -INFINITY ? 0.f : -m[r] * c;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[EPC];
+            unpack_v<ST, EPC>(vx[u], vf);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float p = fexp2(fmaf(s[u * R + r], c, nmc[r]));
+                l[r] += p;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
             }
         }
+    };
 
-        // -- merge the lane groups of this wave --
+    // -- end of a segment: merge the lane groups, then the waves; write the
+    //    output itself or the segment's partial record --
+    auto finish_segment = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             float mw = m[r];
@@ -395,7 +412,7 @@ void decode_attn(DecodeArgs a) {
 #pragma unroll
             for (int d = LPK; d < 64; d <<= 1) lw += __shfl_xor(lw, d);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
+            for (int e = 0; e < EPC; ++e) {
                 float ow = o[r][e] * w;
 #pragma unroll
                 for (int d = LPK; d < 64; d <<= 1) ow += __shfl_xor(ow, d);
@@ -408,9 +425,7 @@ void decode_attn(DecodeArgs a) {
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int ch = 0; ch < CH; ++ch)
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) sm_o[wave][r][C::elem(sub, ch, e)] = o[r][ch * EPC + e];
+                for (int e = 0; e < EPC; ++e) sm_o[wave][r][sub * EPC + e] = o[r][e];
         }
         if (lane == 0) {
 #pragma unroll
@@ -419,9 +434,7 @@ void decode_attn(DecodeArgs a) {
                 sm_l[wave][r] = l[r];
             }
         }
-        __syncthreads();
-
-        // -- merge the waves: the output itself, or this segment's partial record --
+        lds_barrier();
         for (int idx = tid; idx < rows_act * D; idx += kThreads) {
             const int r = idx / D, d = idx - (idx / D) * D;
             float M = sm_m[0][r];
@@ -434,22 +447,54 @@ void decode_attn(DecodeArgs a) {
                 ov = fmaf(sm_o[w][r][d], f, ov);
                 lv = fmaf(sm_l[w][r], f, lv);
             }
-            if (whole_unit) {
-                const int h = g * a.G + a.r0 + r / a.Tc;
+            if (cs.rec < 0) {
+                const int h = cs.g * a.G + a.r0 + r / a.Tc;
                 const int i = a.i0 + r % a.Tc;
-                a.out[((static_cast<int64_t>(a.row0 + b) * a.Hq + h) * a.T + i) * D + d] = ov / lv;
+                a.out[((static_cast<int64_t>(a.row0 + cs.b) * a.Hq + h) * a.T + i) * D + d] = ov / lv;
             } else {
-                const int64_t rec = static_cast<int64_t>(blockIdx.x + u_idx) * kMaxDecodeRows + r;
-                a.ws_o[rec * D + d] = ov;
+                const int64_t rr = cs.rec * kMaxDecodeRows + r;
+                a.ws_o[rr * D + d] = ov;
                 if (d == 0) {
-                    a.ws_ml[rec * 2] = M;
-                    a.ws_ml[rec * 2 + 1] = lv;
+                    a.ws_ml[rr * 2] = M;
+                    a.ws_ml[rr * 2 + 1] = lv;
                 }
             }
         }
-        __syncthreads();
-        x = seg_end;
+        lds_barrier();
+    };
+
+    // -- the loop: stage t sits in slot t % NS; NS - 1 stages are issued ahead,
+    //    before the query table is built, so the two latencies overlap --
+    static_for<NS - 1>([&](auto k) { issue(k); });
+    load_qtab(x_begin);
+    start_segment();
+    bool done = false;
+    auto step = [&](auto slot_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot_c)::value;
+        issue(std::integral_constant<int, (S + NS - 1) % NS>{});
+        wait_vm<(NS - 1) * 2 * U>();      // this stage's loads have landed
+        consume(slot_c);
+        if (++cs_t == cs.nbat) {
+            finish_segment();
+            if (cs.x_end >= x_end) {
+                done = true;
+            } else {
+                cs = locate(cs.x_end);
+                cs_t = 0;
+                if (++cs_q == kQTableSegs) {   // more segments than the table holds: reload it
+                    load_qtab(cs.x_end - (cs.j1 - cs.j0));
+                    cs_q = 0;
+                }
+                start_segment();
+            }
+        }
+    };
+    while (!done) {
+        static_for<NS>([&](auto k) {
+            if (!done) step(k);
+        });
     }
+    wait_vm<0>();   // the ring's trailing reloads land before the work-group ends
 }
 
 // One work-group per unit: merge the partial records of a unit whose keys
@@ -463,8 +508,8 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     const int g = u - b * a.Hkv;
     const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
     const int64_t ustart = a.prefix[b] + g * n_b;
-    const int k_first = static_cast<int>(ustart / a.keys_per_block);
-    const int k_last = static_cast<int>((ustart + n_b - 1) / a.keys_per_block);
+    const int k_first = static_cast<int>(decode_slice_of(a, ustart));
+    const int k_last = static_cast<int>(decode_slice_of(a, ustart + n_b - 1));
     if (k_first == k_last) return;
     const int rows_act = a.Gc * a.Tc;
     const float c = a.scale_log2;
@@ -523,12 +568,34 @@ hipError_t run(DecodeArgs& a, hipStream_t s) {
                  (KVC_DECODE_BLOCKS_PER_CU > 0 ? KVC_DECODE_BLOCKS_PER_CU : resident[slot]);
     if (nb > kMaxDecodeBlocks) nb = kMaxDecodeBlocks;
     // at least a couple of load batches per work-group
-    constexpr int64_t kMinKeys = 2 * Cfg<D, ST, R>::KEYS_PER_BATCH;
+    constexpr int64_t kMinKeys = 2 * Cfg<D, ST, R>::KPB;
     const int64_t by_size = (a.total_keys + kMinKeys - 1) / kMinKeys;
     if (nb > by_size) nb = by_size;
     if (nb < 1) nb = 1;
-    a.keys_per_block = (a.total_keys + nb - 1) / nb;
-    a.n_blocks = static_cast<int32_t>((a.total_keys + a.keys_per_block - 1) / a.keys_per_block);
+    // Work-groups beyond the first dispatch round (one per CU) share a CU with an
+    // older one, which the memory system serves first; they get a smaller slice,
+    // KVC_DECODE_LATE_PCT percent of a first-round one.
+    int64_t n1 = nb < cus[slot] ? nb : cus[slot];
+    int64_t n2 = nb - n1;
+    const int64_t denom = n1 * 100 + n2 * KVC_DECODE_LATE_PCT;
+    int64_t kpb = (a.total_keys * 100 + denom - 1) / denom;
+    int64_t kpb2 = kpb * KVC_DECODE_LATE_PCT / 100;
+    if (kpb2 < 1) kpb2 = 1;
+    if (a.total_keys <= n1 * kpb) {
+        n1 = (a.total_keys + kpb - 1) / kpb;
+        n2 = 0;
+    } else {
+        n2 = (a.total_keys - n1 * kpb + kpb2 - 1) / kpb2;
+    }
+    if (n1 + n2 > kMaxDecodeBlocks) {   // rounding pushed past the cap: equal slices
+        kpb = kpb2 = (a.total_keys + nb - 1) / nb;
+        n1 = (a.total_keys + kpb - 1) / kpb;
+        n2 = 0;
+    }
+    a.keys_per_block = kpb;
+    a.keys_per_block2 = kpb2;
+    a.n_first = static_cast<int32_t>(n1);
+    a.n_blocks = static_cast<int32_t>(n1 + n2);
     kernel<<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -538,7 +605,7 @@ hipError_t run(DecodeArgs& a, hipStream_t s) {
         const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
         for (int g = 0; g < a.Hkv && !split; ++g) {
             const int64_t us = a.prefix[b] + g * n_b;
-            split = us / a.keys_per_block != (us + n_b - 1) / a.keys_per_block;
+            split = decode_slice_of(a, us) != decode_slice_of(a, us + n_b - 1);
         }
     }
     if (!split) return hipSuccess;

@@ -3,7 +3,7 @@
 // launch functions each kernel file defines.
 #pragma once
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace kvc {
@@ -55,7 +55,9 @@ struct DecodeArgs {
     int64_t row_stride;
     int64_t head_stride;
     int64_t total_keys;      // sum over rows of n_b * H_kv
-    int64_t keys_per_block;  // slice of the key axis per work-group
+    int64_t keys_per_block;  // slice of the key axis per work-group of the first n_first
+    int64_t keys_per_block2; // slice per later work-group
+    int32_t n_first;         // work-groups with the first slice size
     int32_t row0, rows;      // batch rows of this launch
     int32_t Hq, Hkv, G, T;   // T = query positions in the chunk
     int32_t D;
@@ -90,7 +92,18 @@ struct PrefillArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
-// Fills in n_blocks and keys_per_block from the device's resident capacity.
+// Decode work-group k's slice of the key axis starts at decode_slice_begin(a, k);
+// key x lies in work-group decode_slice_of(a, x)'s slice.
+__host__ __device__ inline int64_t decode_slice_begin(const DecodeArgs& a, int64_t k) {
+    return k <= a.n_first ? k * a.keys_per_block
+                          : a.n_first * a.keys_per_block + (k - a.n_first) * a.keys_per_block2;
+}
+__host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t x) {
+    const int64_t x1 = static_cast<int64_t>(a.n_first) * a.keys_per_block;
+    return x < x1 ? x / a.keys_per_block : a.n_first + (x - x1) / a.keys_per_block2;
+}
+
+// Fills in the work split (n_blocks, slice sizes) from the device's resident capacity.
 hipError_t launch_decode(DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
