@@ -16,7 +16,13 @@ every visible position, q, the float32 output, and the append's read+write)
 divided by the step time. The roofline object times the decode attention
 (partial + combine kernels) alone with HIP events on the stream it runs on.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+Besides the headline line it reports, under "extra", the chunked-prefill
+workload (B=4, 32 chunks of T=512 up to 16384 keys, bf16, MFMA path: TFLOP/s and
+% of the bf16 matrix peak) and the long-context decode workload (B=8, H_q=64,
+H_kv=8, 32768 cached keys: GB/s for T=1 and T=4 attention calls).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+    python bench.py --pmc-workload      # calibration copy + attention calls, for rocprofv3 --pmc
 """
 from __future__ import annotations
 
@@ -34,6 +40,8 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn HBM GB/s (% peak) + tokens/s, GQA 32q/8kv d128 ctx4k B=32"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak, published
+PMC_COPY_BYTES = 256 << 20     # calibration copy size for the traffic counters
 B, HQ, HKV, D, MAX_LEN = 32, 32, 8, 128, 4096
 WORKLOAD = ("batched decode, one Llama-3-8B-shaped layer: B=32, H_q=32, H_kv=8, d_h=128, "
             "bf16 cache max_len 4096, lengths U{1024..4095} seed 0, T=1")
@@ -47,6 +55,9 @@ def parse():
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time budget of the oracle sample")
+    ap.add_argument("--no-extra", action="store_true", help="skip the prefill and long-context figures")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="run the counter workload (calibration copy, then attention calls) and exit")
     return ap.parse_args()
 
 
@@ -62,7 +73,7 @@ def step_bytes(lengths) -> tuple[int, int]:
     return att, app
 
 
-def gpu_bench(args, lengths):
+def make_caches(n_instances, lengths):
     import torch
     from kv_cached_gqa_amd.kvc import KVCache
 
@@ -70,7 +81,7 @@ def gpu_bench(args, lengths):
     torch.cuda.set_device(dev)
     gen = torch.Generator(device=dev)
     caches = []
-    for c in range(args.instances):
+    for c in range(n_instances):
         gen.manual_seed(1000 + c)
         cache = KVCache(1, HKV, D, MAX_LEN, batch=B, n_q_heads=HQ, dtype="bf16", device=dev)
         k = torch.randn((B, HKV, MAX_LEN - 1, D), generator=gen, device=dev, dtype=torch.bfloat16)
@@ -79,6 +90,13 @@ def gpu_bench(args, lengths):
         del k, v
         cache.truncate(lengths)
         caches.append(cache)
+    return caches, gen, dev
+
+
+def gpu_bench(args, lengths):
+    import torch
+
+    caches, gen, dev = make_caches(args.instances, lengths)
     n_in = 8
     gen.manual_seed(7)
     qs = [torch.randn((B, HQ, 1, D), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(n_in)]
@@ -127,6 +145,104 @@ def gpu_bench(args, lengths):
     return ms_step, us_attend, wall
 
 
+def pmc_workload(lengths):
+    """What the traffic counters are collected on: a calibration copy of known
+    size (PMC_COPY_BYTES read and written), then 40 attention calls on the
+    batched-decode workload over 4 cache instances."""
+    import torch
+    src = torch.ones(PMC_COPY_BYTES // 4, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    caches, gen, dev = make_caches(4, lengths)
+    for c in caches:
+        c.append(0, torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.bfloat16),
+                 torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.bfloat16))
+    q = torch.randn((B, HQ, 1, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    out = torch.empty((B, HQ, 1, D), device=dev, dtype=torch.float32)
+    for i in range(40):
+        caches[i % 4].attend(0, q, out=out)
+    torch.cuda.synchronize()
+
+
+def event_time(fn, reps, stream):
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def prefill_bench():
+    """Chunked prefill: B=4, H_q=32, H_kv=8, d_h=128, bf16, 32 chunks of T=512
+    appended and attended in turn (queries at s = 0, 512, ..., 15872)."""
+    import torch
+    from kv_cached_gqa_amd.kvc import KVCache
+    from kv_cached_gqa_amd import work
+    b, hq, hkv, d, t, nch = 4, 32, 8, 128, 512, 32
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    cache = KVCache(1, hkv, d, t * nch, batch=b, n_q_heads=hq, dtype="bf16", device=dev)
+    ks = [torch.randn((b, hkv, t, d), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(4)]
+    vs = [torch.randn((b, hkv, t, d), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(4)]
+    qs = [torch.randn((b, hq, t, d), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(4)]
+    out = torch.empty((b, hq, t, d), device=dev, dtype=torch.float32)
+
+    def run(_):
+        cache.truncate(0)
+        for c in range(nch):
+            cache.append(0, ks[c % 4], vs[c % 4])
+            cache.attend(0, qs[c % 4], out=out)
+    run(0)
+    torch.cuda.synchronize()
+    ms = event_time(run, 3, torch.cuda.current_stream())
+    flops = sum(work.attend_flops([c * t] * b, t, hq, d) for c in range(nch))
+    tf = flops / (ms * 1e-3) / 1e12
+    cache.close()
+    return {"workload": "chunked prefill: B=4, H_q=32, H_kv=8, d_h=128, bf16, 32 chunks of T=512 (append + attend "
+                        "each), keys up to 16384",
+            "ms_per_run": round(ms, 4), "tflops": round(tf, 1), "pct_peak_bf16_mfma": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "flops_per_run": flops}
+
+
+def long_ctx_bench():
+    """Long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys;
+    attention calls with T=1 and T=4 (a draft block) after one append."""
+    import torch
+    from kv_cached_gqa_amd.kvc import KVCache
+    from kv_cached_gqa_amd import work
+    b, hq, hkv, d, s0, ml = 8, 64, 8, 128, 32768, 32776
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(13)
+    cache = KVCache(1, hkv, d, ml, batch=b, n_q_heads=hq, dtype="bf16", device=dev)
+    for _ in range(4):
+        k = torch.randn((b, hkv, s0 // 4, d), generator=gen, device=dev, dtype=torch.bfloat16)
+        cache.append(0, k, k)
+        del k
+    res = {"workload": "long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys"}
+    for t in (1, 4):
+        cache.truncate(s0)
+        kv = torch.randn((b, hkv, t, d), generator=gen, device=dev, dtype=torch.bfloat16)
+        cache.append(0, kv, kv)
+        q = torch.randn((b, hq, t, d), generator=gen, device=dev, dtype=torch.bfloat16)
+        out = torch.empty((b, hq, t, d), device=dev, dtype=torch.float32)
+        for _ in range(3):
+            cache.attend(0, q, out=out)
+        ms = event_time(lambda i: cache.attend(0, q, out=out), 20, torch.cuda.current_stream())
+        byt = work.attend_bytes([s0] * b, t, hq, hkv, d, "bf16", "bf16")
+        res[f"T{t}"] = {"us_per_attend": round(ms * 1e3, 2), "gbs": round(byt / (ms * 1e-3) / 1e9, 1),
+                        "pct_peak_hbm": round(100 * byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    cache.close()
+    return res
+
+
 def cpu_baseline(lengths, seconds: float) -> dict:
     """The oracle, as it stands, on the same workload: whole steps (truncate,
     append, attend of all 32 rows) until `seconds` of CPU time are spent, with
@@ -173,8 +289,13 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     lengths = lengths_seed0()
+    if args.pmc_workload:
+        pmc_workload(lengths)
+        return
     att, app = step_bytes(lengths)
     ms_step, us_attend, wall = gpu_bench(args, lengths)
+    from kv_cached_gqa_amd.measure import stored_traffic
+    traffic = stored_traffic()
     gbs = (att + app) / (ms_step * 1e-3) / 1e9
     att_gbs = att / (us_attend * 1e-6) / 1e9
     rec = {
@@ -198,9 +319,11 @@ def main():
         "bytes_per_step": att + app,
         "roofline": {"bound": "hbm", "kernel": "decode attention: decode_attn + decode_combine",
                      "achieved": round(att_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(att_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(att_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": att, "launch_us": round(us_attend, 3)},
     }
+    if not args.no_extra:
+        rec["extra"] = {"chunked_prefill": prefill_bench(), "long_context_decode": long_ctx_bench()}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(lengths, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -1,0 +1,142 @@
+"""Measurement helpers: HBM traffic from rocprofv3 counters, calibrated.
+
+The TCC counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch) do not read the
+bytes a kernel moves one to one on this GPU. Each is therefore scaled by what
+it reads for a plain elementwise copy of known size (N bytes read, N written)
+in the same run: factor = N / counter(copy). The calibrated traffic of a
+kernel is counter(kernel) * factor.
+
+    python -m kv_cached_gqa_amd.measure summarize --fetch DIR --write DIR \\
+        --copy-bytes N --out profiles/<name>.md --cmd-fetch "..." --cmd-write "..."
+
+reads the *_counter_collection.csv files of two rocprofv3 --pmc runs (one
+counter each) and writes a short markdown summary whose last lines hold the
+calibrated bytes per attention call and a digest of the decode sources, which
+bench.py reads back (and ignores once the sources have changed).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+# Sources whose change invalidates a stored decode traffic figure.
+DECODE_SOURCES = ("csrc/kvc_decode.hip", "csrc/kvc_kernels.h", "csrc/kvc_device.h", "csrc/kvc_api.cpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attend_c3_bf16_traffic.md")
+COPY_KERNEL_TAG = "MulFunctor"          # the calibration copy: torch.mul(src, 1, out=dst)
+
+
+def source_digest(files=DECODE_SOURCES) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(PKG, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def read_counters(run_dir: str) -> dict[str, dict[str, list[float]]]:
+    """{kernel name: {counter: [value per dispatch]}} from one rocprofv3 --pmc run."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    per: dict[str, dict[str, dict[str, float]]] = defaultdict(lambda: defaultdict(dict))
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                did = r.get("Dispatch_Id") or r.get("Correlation_Id") or str(len(per))
+                per[r["Kernel_Name"]][r["Counter_Name"]][did] = (
+                    per[r["Kernel_Name"]][r["Counter_Name"]].get(did, 0.0) + float(r["Counter_Value"]))
+    return {k: {c: list(d.values()) for c, d in v.items()} for k, v in per.items()}
+
+
+def _mean_for(counters, tag: str, counter: str) -> tuple[float, int]:
+    vals = [x for name, cs in counters.items() if tag in name for x in cs.get(counter, [])]
+    if not vals:
+        raise KeyError(f"no dispatch of a kernel matching {tag!r} with {counter}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize(fetch_dir: str, write_dir: str, copy_bytes: int, out: str, cmd_fetch: str, cmd_write: str,
+              kernels=("decode_attn", "decode_combine")) -> int:
+    fc, wc = read_counters(fetch_dir), read_counters(write_dir)
+    cf, ncf = _mean_for(fc, COPY_KERNEL_TAG, "FETCH_SIZE")
+    cw, ncw = _mean_for(wc, COPY_KERNEL_TAG, "WRITE_SIZE")
+    f_fac, w_fac = copy_bytes / cf, copy_bytes / cw
+    rows, total = [], 0.0
+    for k in kernels:
+        f, nf = _mean_for(fc, k, "FETCH_SIZE")
+        w, nw = _mean_for(wc, k, "WRITE_SIZE")
+        rb, wb = f * f_fac, w * w_fac
+        total += rb + wb
+        rows.append(f"| {k} | {nf} | {f:,.1f} | {rb / 1e6:,.2f} | {w:,.1f} | {wb / 1e6:,.2f} |")
+    text = [
+        "# HBM traffic of one decode attention call, batched decode (B=32, H_q=32, H_kv=8, d_h=128, bf16, "
+        "lengths U{1024..4095} seed 0, T=1)",
+        "",
+        "Two rocprofv3 counter runs of `bench.py --pmc-workload` (a calibration copy, then attention calls on "
+        "the batched-decode workload over 4 cache instances), one counter each:",
+        "",
+        f"    {cmd_fetch}",
+        f"    {cmd_write}",
+        "",
+        f"Calibration copy (torch.mul(src, 1, out=dst), {copy_bytes:,} bytes read and written): "
+        f"FETCH_SIZE {cf:,.1f} KiB per dispatch over {ncf} dispatches -> factor {f_fac:.2f} B per counter unit; "
+        f"WRITE_SIZE {cw:,.1f} KiB over {ncw} -> factor {w_fac:.2f}.",
+        "",
+        "| Kernel | Dispatches | FETCH_SIZE (KiB) | Read (MB, calibrated) | WRITE_SIZE (KiB) | Written (MB, calibrated) |",
+        "|---|---|---|---|---|---|",
+        *rows,
+        "",
+        f"traffic_bytes_per_attend: {int(round(total))}",
+        f"decode_sources_sha256: {source_digest()}",
+        "",
+    ]
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    with open(out, "w") as fh:
+        fh.write("\n".join(text))
+    return int(round(total))
+
+
+def stored_traffic(path: str = TRAFFIC_FILE) -> int | None:
+    """Calibrated bytes per attention call from the stored summary, or None when
+    there is none or the decode sources changed since it was taken."""
+    try:
+        with open(path) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    vals = {}
+    for ln in lines:
+        if ":" in ln and not ln.startswith(("|", "#", " ")):
+            k, _, v = ln.partition(":")
+            vals[k.strip()] = v.strip()
+    if vals.get("decode_sources_sha256") != source_digest():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_attend"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("summarize")
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--copy-bytes", type=int, required=True)
+    s.add_argument("--out", default=TRAFFIC_FILE)
+    s.add_argument("--cmd-fetch", default="")
+    s.add_argument("--cmd-write", default="")
+    a = ap.parse_args()
+    total = summarize(a.fetch, a.write, a.copy_bytes, a.out, a.cmd_fetch, a.cmd_write)
+    print(f"wrote {a.out}: {total:,} bytes per attention call")
+
+
+if __name__ == "__main__":
+    main()
