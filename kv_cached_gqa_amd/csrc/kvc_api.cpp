@@ -24,6 +24,7 @@
 
 using kvc::kMaxDecodeBlocks;
 using kvc::kMaxDecodeRows;
+using kvc::kWsRecordRows;
 using kvc::kMaxRowsPerLaunch;
 
 struct kvc_cache {
@@ -55,11 +56,12 @@ int64_t committed(const kvc_cache* c, int b) {
     return s;
 }
 
-// Segments the decode workspace must hold: one per work-group plus one per unit
-// boundary inside a launch.
+// Records of kWsRecordRows rows the decode workspace holds: one per work-group
+// plus one per unit boundary inside a launch, with room for slabs of up to
+// kMaxDecodeRows rows (whose records are kMaxDecodeRows rows wide).
 int64_t workspace_segments(const kvc_config& c) {
     const int64_t units = static_cast<int64_t>(std::min(c.batch, kMaxRowsPerLaunch)) * c.n_kv_heads;
-    return kMaxDecodeBlocks + units;
+    return kMaxDecodeBlocks + (kMaxDecodeRows / kWsRecordRows) * units;
 }
 
 int ensure_workspace(kvc_cache* c) {
@@ -71,8 +73,8 @@ int ensure_workspace(kvc_cache* c) {
     const int dev = attr.device;
     if (dev != prev && hipSetDevice(dev) != hipSuccess) return KVC_ERR_HIP;
     const int64_t segs = workspace_segments(c->cfg);
-    const size_t o_bytes = static_cast<size_t>(segs) * kMaxDecodeRows * c->cfg.d_head * sizeof(float);
-    const size_t ml_bytes = static_cast<size_t>(segs) * kMaxDecodeRows * 2 * sizeof(float);
+    const size_t o_bytes = static_cast<size_t>(segs) * kWsRecordRows * c->cfg.d_head * sizeof(float);
+    const size_t ml_bytes = static_cast<size_t>(segs) * kWsRecordRows * 2 * sizeof(float);
     void* o = nullptr;
     void* ml = nullptr;
     int rc = KVC_OK;
@@ -265,6 +267,7 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
                 a.out = out;
                 a.ws_o = c->ws_o;
                 a.ws_ml = c->ws_ml;
+                a.ws_rows_cap = c->ws_segments * kWsRecordRows;
                 a.layer_off = (static_cast<int64_t>(layer) * cf.batch + row0) * row_stride;
                 a.row_stride = row_stride;
                 a.head_stride = head_stride;

@@ -39,7 +39,7 @@
 //    a second, small kernel merges each split unit's records.
 #include <type_traits>
 
-#include "kvc_device.h"
+#include "kvc_mfma.h"
 
 namespace kvc {
 namespace {
@@ -452,7 +452,7 @@ void decode_attn(DecodeArgs a) {
                 const int i = a.i0 + r % a.Tc;
                 a.out[((static_cast<int64_t>(a.row0 + cs.b) * a.Hq + h) * a.T + i) * D + d] = ov / lv;
             } else {
-                const int64_t rr = cs.rec * kMaxDecodeRows + r;
+                const int64_t rr = cs.rec * a.rec_rows + r;
                 a.ws_o[rr * D + d] = ov;
                 if (d == 0) {
                     a.ws_ml[rr * 2] = M;
@@ -497,6 +497,601 @@ void decode_attn(DecodeArgs a) {
     wait_vm<0>();   // the ring's trailing reloads land before the work-group ends
 }
 
+// ---- slabs of 9 to 32 query rows: row-split work-groups --------------------
+// A KV head with more query rows than one lane group holds (for example 8 heads
+// x a 4-token draft block) is served by RS waves of 8 rows each over the same
+// keys, so the cache is streamed once for all of them. The work-group shares
+// one LDS ring: each wave loads its share of a stage (UB 1 KB blocks of K and
+// of V), waits for its own loads, and one barrier per stage makes the stage
+// visible to all waves and frees the one read before. Each wave merges only its
+// lane groups and writes its own rows; there is no cross-wave merge.
+
+#ifndef KVC_DECODE_ROWS_UB
+#define KVC_DECODE_ROWS_UB 2          // 1 KB blocks per tensor each wave loads per stage
+#endif
+#ifndef KVC_DECODE_ROWS_STAGES
+#define KVC_DECODE_ROWS_STAGES 3
+#endif
+
+template <int D, int ST, int RS>
+struct RCfg {
+    static constexpr int ESZ = ST == F32 ? 4 : 2;
+    static constexpr int EPC = 16 / ESZ;
+    static constexpr int LPK = D / EPC;
+    static constexpr int KPW = 64 / LPK;               // keys per 1 KB block
+    static constexpr int R = 8;                        // query rows per wave
+    static constexpr int ROWS = RS * R;
+    static constexpr int THREADS = 64 * RS;
+    static constexpr int UB = KVC_DECODE_ROWS_UB;
+    static constexpr int BLOCKS = RS * UB;             // blocks per tensor per stage
+    static constexpr int KPS = BLOCKS * KPW;           // keys per stage
+    static constexpr int STAGE_BYTES = BLOCKS * 2048;
+    static constexpr int QSEGS = 2;                    // segments the query table holds
+    static constexpr int QROW_WORDS = D * ESZ / 4;
+    static constexpr int FIXED_BYTES = QSEGS * ROWS * D * ESZ;
+    static constexpr int fit_stages() {
+        int ns = KVC_DECODE_ROWS_STAGES;
+        while (ns > 2 && (ns * STAGE_BYTES + FIXED_BYTES) * 2 > kLdsLimit) --ns;
+        return ns;
+    }
+    static constexpr int NS = fit_stages();
+    static constexpr int LDS_BYTES = NS * STAGE_BYTES + FIXED_BYTES;
+    static_assert(LDS_BYTES <= kLdsLimit, "decode LDS budget");
+    static_assert(NS * STAGE_BYTES < 65536, "ring offsets fit the LDS immediate");
+};
+
+template <int D, int ST, int RS>
+__global__ __launch_bounds__((RCfg<D, ST, RS>::THREADS)) __attribute__((amdgpu_waves_per_eu(1)))
+void decode_rows(DecodeArgs a) {
+    using C = RCfg<D, ST, RS>;
+    constexpr int EPC = C::EPC, LPK = C::LPK, KPW = C::KPW, UB = C::UB, NS = C::NS, R = C::R;
+    constexpr int KPS = C::KPS, ESZ = C::ESZ, ROWS = C::ROWS;
+
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * C::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint32_t qtab[C::QSEGS][ROWS][C::QROW_WORDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane / LPK;
+    const int sub = lane % LPK;
+    const int rows_act = a.Gc * a.Tc;
+    const float c = a.scale_log2;
+    const float thresh = kRescaleLog2 / c;
+
+    const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
+    int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
+    if (x_end > a.total_keys) x_end = a.total_keys;
+    if (x_begin >= x_end) return;
+
+    const char* kc = static_cast<const char*>(a.k_cache);
+    const char* vc = static_cast<const char*>(a.v_cache);
+
+    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
+        int lo = 0, hi = a.rows;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.prefix[mid] <= x) lo = mid; else hi = mid;
+        }
+        Seg sg;
+        sg.b = lo;
+        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
+        sg.g = static_cast<int>((x - a.prefix[lo]) / n_b);
+        const int64_t unit_start = a.prefix[lo] + static_cast<int64_t>(sg.g) * n_b;
+        int64_t seg_end = unit_start + n_b;
+        if (seg_end > x_end) seg_end = x_end;
+        sg.j0 = static_cast<int>(x - unit_start);
+        sg.j1 = static_cast<int>(seg_end - unit_start);
+        sg.n_b = static_cast<int>(n_b);
+        sg.nbat = (sg.j1 - sg.j0 + KPS - 1) / KPS;
+        sg.head = a.layer_off + sg.b * a.row_stride + sg.g * a.head_stride;
+        sg.x_end = seg_end;
+        sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
+        return sg;
+    };
+
+    auto load_qtab = [&](int64_t x) __attribute__((always_inline)) {
+        for (int sgi = 0; sgi < C::QSEGS && x < x_end; ++sgi) {
+            const Seg sg = locate(x);
+            for (int idx = tid; idx < ROWS * D; idx += C::THREADS) {
+                const int r = idx / D, e = idx - (idx / D) * D;
+                float val = 0.f;
+                if (r < rows_act) {
+                    const int h = sg.g * a.G + a.r0 + r / a.Tc;
+                    const int i = a.i0 + r % a.Tc;
+                    const int64_t qe = ((static_cast<int64_t>(a.row0 + sg.b) * a.Hq + h) * a.T + i) * D + e;
+                    if (a.q_dtype == F32) val = static_cast<const float*>(a.q)[qe];
+                    else if (a.q_dtype == BF16) val = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
+                    else val = f16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
+                }
+                if constexpr (ST == F32) {
+                    reinterpret_cast<float*>(qtab[sgi][r])[e] = val;
+                } else {
+                    const uint32_t h16 = ST == BF16 ? f32_to_bf16_rne(val) : f32_to_f16_rne(val);
+                    reinterpret_cast<uint16_t*>(qtab[sgi][r])[e] = static_cast<uint16_t>(h16);
+                }
+            }
+            x = sg.x_end;
+        }
+        __syncthreads();
+    };
+
+    // -- issue side: this wave's UB blocks of the next stage --
+    Seg is = locate(x_begin);
+    int is_t = 0;
+    bool is_live = true;
+    auto issue = [&](auto slot_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot_c)::value;
+#pragma unroll
+        for (int ub = 0; ub < UB; ++ub) {
+            const int bi = wave * UB + ub;
+            int j = is.j0 + is_t * KPS + bi * KPW + grp;
+            j = j < is.j1 ? j : is.j1 - 1;
+            const int64_t off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
+            uint8_t* dst = ring + S * C::STAGE_BYTES + bi * 2048;
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kc + off),
+                                             (void __attribute__((address_space(3)))*)(dst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vc + off),
+                                             (void __attribute__((address_space(3)))*)(dst + 1024), 16, 0, 0);
+        }
+        if (is_live && ++is_t == is.nbat) {
+            if (is.x_end >= x_end) {
+                is_live = false;
+            } else {
+                is = locate(is.x_end);
+                is_t = 0;
+            }
+        }
+    };
+
+    // -- consume side: this wave's rows wave * R .. wave * R + R - 1 of the slab --
+    const uint32_t rd_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                                 (__attribute__((address_space(3))) uint8_t*)ring)) + lane * 16;
+    Seg cs = locate(x_begin);
+    int cs_t = 0, cs_q = 0;
+    uint32_t qp[R][4];
+    int qpos[R];
+    float m[R], l[R], o[R][EPC];
+    auto start_segment = [&]() __attribute__((always_inline)) {
+        const int qpos0 = cs.n_b - a.Tc;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int rr = wave * R + r;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(&qtab[cs_q][rr][sub * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qp[r][e] = w[e];
+            qpos[r] = rr < rows_act ? qpos0 + rr % a.Tc : -1;
+            m[r] = -INFINITY;
+            l[r] = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) o[r][e] = 0.f;
+        }
+    };
+
+    auto consume = [&](auto slot_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot_c)::value;
+        const int kb = cs.j0 + cs_t * KPS;               // first key of the stage
+        const bool plain = kb + KPS - 1 < cs.j1 && kb + KPS - 1 <= cs.n_b - a.Tc;
+        static_for<C::BLOCKS>([&](auto bi_c) {
+            constexpr int bi = decltype(bi_c)::value;
+            u32x4 kx, vx;
+            read_kv<S * C::STAGE_BYTES + bi * 2048>(kx, vx, rd_addr);
+            float s[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float acc = 0.f;
+                if constexpr (ST == F32) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(qp[r][e]), __uint_as_float(kx[e]), acc);
+                } else {
+                    acc = dot16<ST>(qp[r], kx, acc);
+                }
+                s[r] = acc;
+            }
+            lane_group_sum<LPK, R>(s);
+            if (!plain) {
+                const int j = kb + bi * KPW + grp;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (!(j < cs.j1 && j <= qpos[r])) s[r] = -INFINITY;
+            }
+            bool need = false;
+#pragma unroll
+            for (int r = 0; r < R; ++r) need |= s[r] - m[r] > thresh;
+            if (__any(need)) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (s[r] - m[r] > thresh) {
+                        const float alpha = m[r] == -INFINITY ? 0.f : fexp2((m[r] - s[r]) * c);
+                        m[r] = s[r];
+                        l[r] *= alpha;
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) o[r][e] *= alpha;
+                    }
+                }
+            }
+            float vf[EPC];
+            unpack_v<ST, EPC>(vx, vf);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float p = fexp2(fmaf(s[r], c, m[r] == -INFINITY ? 0.f : -m[r] * c));
+                l[r] += p;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
+            }
+        });
+    };
+
+    // -- end of a segment: merge this wave's lane groups, write its rows --
+    auto finish_segment = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float mw = m[r];
+#pragma unroll
+            for (int d = LPK; d < 64; d <<= 1) mw = fmaxf(mw, __shfl_xor(mw, d));
+            const float w = mw == -INFINITY ? 0.f : fexp2((m[r] - mw) * c);
+            float lw = l[r] * w;
+#pragma unroll
+            for (int d = LPK; d < 64; d <<= 1) lw += __shfl_xor(lw, d);
+            float ow[EPC];
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                ow[e] = o[r][e] * w;
+#pragma unroll
+                for (int d = LPK; d < 64; d <<= 1) ow[e] += __shfl_xor(ow[e], d);
+            }
+            const int rr = wave * R + r;
+            if (grp == 0 && rr < rows_act) {
+                if (cs.rec < 0) {
+                    const int h = cs.g * a.G + a.r0 + rr / a.Tc;
+                    const int i = a.i0 + rr % a.Tc;
+                    float* dst = a.out + ((static_cast<int64_t>(a.row0 + cs.b) * a.Hq + h) * a.T + i) * D + sub * EPC;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) dst[e] = ow[e] / lw;
+                } else {
+                    const int64_t rec = cs.rec * a.rec_rows + rr;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) a.ws_o[rec * D + sub * EPC + e] = ow[e];
+                    if (sub == 0) {
+                        a.ws_ml[rec * 2] = mw;
+                        a.ws_ml[rec * 2 + 1] = lw;
+                    }
+                }
+            }
+        }
+    };
+
+    // -- the loop: stage t in slot t % NS, NS - 1 stages issued ahead --
+    static_for<NS - 1>([&](auto k) { issue(k); });
+    load_qtab(x_begin);
+    start_segment();
+    bool done = false;
+    auto step = [&](auto slot_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot_c)::value;
+        wait_vm<(NS - 2) * 2 * UB>();   // this wave's part of stage t has landed
+        lds_barrier();                   // every wave's part has; every wave is done with stage t - 1
+        issue(std::integral_constant<int, (S + NS - 1) % NS>{});
+        consume(slot_c);
+        if (++cs_t == cs.nbat) {
+            finish_segment();
+            if (cs.x_end >= x_end) {
+                done = true;
+            } else {
+                cs = locate(cs.x_end);
+                cs_t = 0;
+                if (++cs_q == C::QSEGS) {    // more segments than the table holds: reload it
+                    load_qtab(cs.x_end - (cs.j1 - cs.j0));
+                    cs_q = 0;
+                }
+                start_segment();
+            }
+        }
+    };
+    while (!done) {
+        static_for<NS>([&](auto k) {
+            if (!done) step(k);
+        });
+    }
+    wait_vm<0>();
+}
+
+// ---- slabs of 9 to 32 query rows, 16-bit caches: matrix cores --------------
+// With 8 heads x a 4-token draft (or any G*T in 9..32) one KV head serves up to
+// 32 query rows, 32 flops per byte: the vector ALUs cannot keep up with HBM, so
+// the two products run as MFMA tiles, the same S^T = K Q^T and O^T = V^T P^T
+// tiles as the prefill kernel, with the slab's rows as the 32 columns. One wave
+// per work-group streams 32-key K and V tiles of its slice through a private
+// LDS ring (LDS-DMA, explicit vmcnt waits, no barrier); the slab queries of its
+// first segments sit in an LDS table; each segment ends in a partial record
+// (or the output) per column, merged by decode_combine.
+
+#ifndef KVC_DECODE_MFMA_STAGES
+#define KVC_DECODE_MFMA_STAGES 4
+#endif
+#ifndef KVC_DECODE_MFMA_BLOCKS_PER_CU
+#define KVC_DECODE_MFMA_BLOCKS_PER_CU 2
+#endif
+
+template <int D>
+struct MCfg : TileLayout<D> {
+    using L = TileLayout<D>;
+    static constexpr int QSEGS = 2;                          // segments the query table holds
+    static constexpr int QT_BYTES = QSEGS * 32 * D * 2;      // 32 columns of D 16-bit elements each
+    static constexpr int fit_stages() {
+        int ns = KVC_DECODE_MFMA_STAGES;
+        while (ns > 2 && ((ns * 2 * L::TILE_BYTES + QT_BYTES) * KVC_DECODE_MFMA_BLOCKS_PER_CU > kLdsLimit ||
+                          ns * 2 * L::TILE_BYTES + 24 * D * 2 > 65535))
+            --ns;
+        return ns;
+    }
+    static constexpr int NS = fit_stages();
+    static constexpr int STAGE_BYTES = 2 * L::TILE_BYTES;    // K tile, then V tile
+    static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+    static_assert((NS - 1) * 2 * L::NLD < 64, "vmcnt field");
+    static_assert((NS - 1) * STAGE_BYTES + L::TILE_BYTES + 24 * D * 2 < 65536, "LDS read offsets fit 16 bits");
+};
+
+template <int D, int ST>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
+void decode_mfma(DecodeArgs a) {
+    using P = MCfg<D>;
+    constexpr int NS = P::NS, DS = P::DS, DT = P::DT, NLD = P::NLD;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[P::LDS_BYTES / 2];
+    __shared__ __attribute__((aligned(16))) uint16_t qtab[P::QSEGS][32][D];
+
+    const int lane = threadIdx.x;
+    const int col32 = lane & 31;                 // this lane's column: slab row col32
+    const int hl = lane >> 5;
+    const int rows_act = a.Gc * a.Tc;
+    const float c = a.scale_log2;
+    const float thresh = kRescaleLog2 / c;
+
+    const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
+    int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
+    if (x_end > a.total_keys) x_end = a.total_keys;
+    if (x_begin >= x_end) return;
+
+    const uint16_t* kg = static_cast<const uint16_t*>(a.k_cache);
+    const uint16_t* vg = static_cast<const uint16_t*>(a.v_cache);
+
+    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
+        int lo = 0, hi = a.rows;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.prefix[mid] <= x) lo = mid; else hi = mid;
+        }
+        Seg sg;
+        sg.b = lo;
+        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
+        sg.g = static_cast<int>((x - a.prefix[lo]) / n_b);
+        const int64_t unit_start = a.prefix[lo] + static_cast<int64_t>(sg.g) * n_b;
+        int64_t seg_end = unit_start + n_b;
+        if (seg_end > x_end) seg_end = x_end;
+        sg.j0 = static_cast<int>(x - unit_start);
+        sg.j1 = static_cast<int>(seg_end - unit_start);
+        sg.n_b = static_cast<int>(n_b);
+        sg.nbat = (sg.j1 - sg.j0 + kBN - 1) / kBN;
+        sg.head = a.layer_off + sg.b * a.row_stride + sg.g * a.head_stride;
+        sg.x_end = seg_end;
+        sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
+        return sg;
+    };
+
+    // -- the query table: 32 columns (slab rows; past the slab zero) per segment,
+    //    rounded to the storage type --
+    auto load_qtab = [&](int64_t x) __attribute__((always_inline)) {
+        for (int sgi = 0; sgi < P::QSEGS && x < x_end; ++sgi) {
+            const Seg sg = locate(x);
+            for (int idx = lane; idx < 32 * D; idx += 64) {
+                const int r = idx / D, e = idx - (idx / D) * D;
+                float val = 0.f;
+                if (r < rows_act) {
+                    const int h = sg.g * a.G + a.r0 + r / a.Tc;
+                    const int i = a.i0 + r % a.Tc;
+                    const int64_t qe = ((static_cast<int64_t>(a.row0 + sg.b) * a.Hq + h) * a.T + i) * D + e;
+                    if (a.q_dtype == F32) val = static_cast<const float*>(a.q)[qe];
+                    else if (a.q_dtype == BF16) val = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
+                    else val = f16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
+                }
+                qtab[sgi][r][e] = static_cast<uint16_t>(ST == BF16 ? f32_to_bf16_rne(val) : f32_to_f16_rne(val));
+            }
+            x = sg.x_end;
+        }
+        __syncthreads();
+    };
+
+    // -- issue side: the next 32-key tile, K chunks XOR-swizzled, V chunks
+    //    permuted for the transposed reads; past the slice's end the last key
+    //    is reloaded (never used) --
+    Seg is = locate(x_begin);
+    int is_t = 0;
+    bool is_live = true;
+    auto issue = [&](auto slot_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot_c)::value;
+        uint16_t* kd = smem + S * P::STAGE_BYTES / 2;
+        uint16_t* vd = kd + P::TILE;
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+            const int e = n * 512 + lane * 8;    // element offset inside the tile
+            const int r = e / D;
+            const int sl = (e % D) >> 3;
+            int j = is.j0 + is_t * kBN + r;
+            j = j < is.j1 ? j : is.j1 - 1;
+            const int64_t row = is.head + static_cast<int64_t>(j) * D;
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(kg + row + P::kslot(r, sl) * 8),
+                (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(vg + row + P::vchunk(r, sl) * 8),
+                (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0, 0);
+        }
+        if (is_live && ++is_t == is.nbat) {
+            if (is.x_end >= x_end) {
+                is_live = false;
+            } else {
+                is = locate(is.x_end);
+                is_t = 0;
+            }
+        }
+    };
+
+    // -- LDS read addresses of this lane (stage offsets are immediates) --
+    const uint32_t lds0 = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t*)smem));
+    uint32_t kaddr[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) kaddr[ds] = lds0 + (col32 * D + P::kslot(col32, 2 * ds + hl) * 8) * 2;
+    uint32_t vaddr[DT];
+    {
+        const int grp = lane >> 4, ii = (lane >> 2) & 3, aa = lane & 3;
+        const int rv = (grp >> 1) * 4 + ii;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int cv = dt * 4 + 2 * (grp & 1) + (aa >> 1);
+            vaddr[dt] = lds0 + P::TILE_BYTES + (rv * D + P::vslot(rv, cv) * 8) * 2 + (aa & 1) * 8;
+        }
+    }
+
+    // -- consume side --
+    Seg cs = locate(x_begin);
+    int cs_t = 0, cs_q = 0;
+    u32x4 qb[DS];
+    int qpos;
+    float m, lsum;
+    f32x16_t o[DT];
+    auto start_segment = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+            qb[ds] = *reinterpret_cast<const u32x4*>(&qtab[cs_q][col32][ds * 16 + hl * 8]);
+        qpos = col32 < rows_act ? cs.n_b - a.Tc + col32 % a.Tc : -1;
+        m = -INFINITY;
+        lsum = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
+    };
+
+    auto consume = [&](auto slot_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot_c)::value;
+        const int j0 = cs.j0 + cs_t * kBN;
+        const bool plain = j0 + kBN <= cs.j1 && j0 + kBN - 1 <= cs.n_b - a.Tc;
+        u32x4 ka[DS];
+        read_k<DS, S * P::STAGE_BYTES>(ka, kaddr);
+        f32x16_t sacc = f32x16_t{};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) sacc = mfma32<ST>(ka[ds], qb[ds], sacc);
+        u32x2 vt[DT][2][2];
+        read_vt<DT, S * P::STAGE_BYTES, D * 2>(vt, vaddr);
+
+        // scores -> probabilities; value jj is key j0 + (jj / 4) * 8 + hl * 4 + jj % 4
+        float sv_[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) sv_[jj] = sacc[jj];
+        if (!plain) {
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                const int j = j0 + (jj >> 2) * 8 + hl * 4 + (jj & 3);
+                if (!(j < cs.j1 && j <= qpos)) sv_[jj] = -INFINITY;
+            }
+        }
+        float mt = sv_[0];
+#pragma unroll
+        for (int jj = 1; jj < 16; ++jj) mt = fmaxf(mt, sv_[jj]);
+        if (__any(mt - m > thresh)) {
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            if (mt - m > thresh) {
+                const float alpha = m == -INFINITY ? 0.f : fexp2((m - mt) * c);
+                m = mt;
+                lsum *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+            }
+        }
+        const float nmc = m == -INFINITY ? 0.f : -m * c;
+        uint32_t w[8];
+        float ls[2] = {0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            w[e] = pack_p<ST>(fexp2(fmaf(sv_[2 * e], c, nmc)), fexp2(fmaf(sv_[2 * e + 1], c, nmc)));
+            ls[e & 1] = add_pair<ST>(w[e], ls[e & 1]);
+        }
+        lsum += ls[0] + ls[1];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x4 va = {vt[dt][kk][0][0], vt[dt][kk][0][1], vt[dt][kk][1][0], vt[dt][kk][1][1]};
+                const u32x4 pb = {w[kk * 4 + 0], w[kk * 4 + 1], w[kk * 4 + 2], w[kk * 4 + 3]};
+                o[dt] = mfma32<ST>(va, pb, o[dt]);
+            }
+    };
+
+    // -- end of a segment: column col32's (max, sum, output); the lane holds
+    //    head elements dt * 32 + (jj / 4) * 8 + hl * 4 + jj % 4 --
+    auto finish_segment = [&]() __attribute__((always_inline)) {
+        const float l_all = lsum + __shfl_xor(lsum, 32);
+        if (col32 < rows_act) {
+            if (cs.rec < 0) {
+                const float inv = 1.f / l_all;
+                const int h = cs.g * a.G + a.r0 + col32 / a.Tc;
+                const int i = a.i0 + col32 % a.Tc;
+                float* dst = a.out + ((static_cast<int64_t>(a.row0 + cs.b) * a.Hq + h) * a.T + i) * D;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        *reinterpret_cast<float4*>(dst + dt * 32 + q4 * 8 + hl * 4) =
+                            make_float4(o[dt][q4 * 4 + 0] * inv, o[dt][q4 * 4 + 1] * inv,
+                                        o[dt][q4 * 4 + 2] * inv, o[dt][q4 * 4 + 3] * inv);
+            } else {
+                const int64_t rr = cs.rec * a.rec_rows + col32;
+                float* dst = a.ws_o + rr * D;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        *reinterpret_cast<float4*>(dst + dt * 32 + q4 * 8 + hl * 4) =
+                            make_float4(o[dt][q4 * 4 + 0], o[dt][q4 * 4 + 1], o[dt][q4 * 4 + 2], o[dt][q4 * 4 + 3]);
+                if (hl == 0) {
+                    a.ws_ml[rr * 2] = m;
+                    a.ws_ml[rr * 2 + 1] = l_all;
+                }
+            }
+        }
+    };
+
+    // -- the loop: tile t in slot t % NS, NS - 1 tiles issued ahead --
+    static_for<NS - 1>([&](auto k) { issue(k); });
+    load_qtab(x_begin);
+    start_segment();
+    bool done = false;
+    auto step = [&](auto slot_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot_c)::value;
+        issue(std::integral_constant<int, (S + NS - 1) % NS>{});
+        wait_vm<(NS - 1) * 2 * NLD>();   // this tile's loads have landed
+        consume(slot_c);
+        if (++cs_t == cs.nbat) {
+            finish_segment();
+            if (cs.x_end >= x_end) {
+                done = true;
+            } else {
+                cs = locate(cs.x_end);
+                cs_t = 0;
+                if (++cs_q == P::QSEGS) {    // more segments than the table holds: reload it
+                    load_qtab(cs.x_end - (cs.j1 - cs.j0));
+                    cs_q = 0;
+                }
+                start_segment();
+            }
+        }
+    };
+    while (!done) {
+        static_for<NS>([&](auto k) {
+            if (!done) step(k);
+        });
+    }
+    wait_vm<0>();
+}
+
 // One work-group per unit: merge the partial records of a unit whose keys
 // span several work-groups (units held by one work-group were written by
 // decode_attn and are skipped).
@@ -521,7 +1116,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
 #pragma unroll
             for (int t = 0; t < kMaxSeg; ++t) {
                 const int k = k0 + t;
-                const int64_t rec = static_cast<int64_t>((k <= k_last ? k : k_last) + u) * kMaxDecodeRows + r;
+                const int64_t rec = static_cast<int64_t>((k <= k_last ? k : k_last) + u) * a.rec_rows + r;
                 mk[t] = k <= k_last ? a.ws_ml[rec * 2] : -INFINITY;
                 lk[t] = a.ws_ml[rec * 2 + 1];
                 okv[t] = a.ws_o[rec * D + d];
@@ -546,36 +1141,35 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     }
 }
 
-template <int D, int ST, int R>
-hipError_t run(DecodeArgs& a, hipStream_t s) {
-    auto kernel = decode_attn<D, ST, R>;
-    // Resident work-groups per CU for this instantiation, per device (cached).
-    static int resident[64] = {};
+// CUs of the current device (cached per device).
+hipError_t device_cus(int& n_cu) {
     static int cus[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    const int slot = dev & 63;
-    if (resident[slot] == 0) {
-        int per_cu = 0, n_cu = 0;
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, Cfg<D, ST, R>::THREADS, 0);
+    if (cus[dev & 63] == 0) {
+        int n = 0;
+        const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        cus[slot] = n_cu > 0 ? n_cu : 1;
-        resident[slot] = per_cu > 0 ? per_cu : 1;
+        cus[dev & 63] = n > 0 ? n : 1;
     }
-    int64_t nb = static_cast<int64_t>(cus[slot]) *
-                 (KVC_DECODE_BLOCKS_PER_CU > 0 ? KVC_DECODE_BLOCKS_PER_CU : resident[slot]);
+    n_cu = cus[dev & 63];
+    return hipSuccess;
+}
+
+// Cut the key axis into work-group slices: up to per_cu work-groups per CU, at
+// least min_keys keys each, and no more records than the workspace holds.
+// Work-groups beyond the first dispatch round (one per CU) share a CU with an
+// older one, which the memory system serves first; they get a smaller slice,
+// KVC_DECODE_LATE_PCT percent of a first-round one.
+void split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min_keys) {
+    int64_t nb = static_cast<int64_t>(n_cu) * per_cu;
     if (nb > kMaxDecodeBlocks) nb = kMaxDecodeBlocks;
-    // at least a couple of load batches per work-group
-    constexpr int64_t kMinKeys = 2 * Cfg<D, ST, R>::KPB;
-    const int64_t by_size = (a.total_keys + kMinKeys - 1) / kMinKeys;
+    const int64_t by_ws = a.ws_rows_cap / a.rec_rows - static_cast<int64_t>(a.rows) * a.Hkv;
+    if (nb > by_ws) nb = by_ws;
+    const int64_t by_size = (a.total_keys + min_keys - 1) / min_keys;
     if (nb > by_size) nb = by_size;
     if (nb < 1) nb = 1;
-    // Work-groups beyond the first dispatch round (one per CU) share a CU with an
-    // older one, which the memory system serves first; they get a smaller slice,
-    // KVC_DECODE_LATE_PCT percent of a first-round one.
-    int64_t n1 = nb < cus[slot] ? nb : cus[slot];
+    int64_t n1 = nb < n_cu ? nb : n_cu;
     int64_t n2 = nb - n1;
     const int64_t denom = n1 * 100 + n2 * KVC_DECODE_LATE_PCT;
     int64_t kpb = (a.total_keys * 100 + denom - 1) / denom;
@@ -587,7 +1181,7 @@ hipError_t run(DecodeArgs& a, hipStream_t s) {
     } else {
         n2 = (a.total_keys - n1 * kpb + kpb2 - 1) / kpb2;
     }
-    if (n1 + n2 > kMaxDecodeBlocks) {   // rounding pushed past the cap: equal slices
+    if (n1 + n2 > nb) {   // rounding pushed past the cap: equal slices
         kpb = kpb2 = (a.total_keys + nb - 1) / nb;
         n1 = (a.total_keys + kpb - 1) / kpb;
         n2 = 0;
@@ -596,10 +1190,11 @@ hipError_t run(DecodeArgs& a, hipStream_t s) {
     a.keys_per_block2 = kpb2;
     a.n_first = static_cast<int32_t>(n1);
     a.n_blocks = static_cast<int32_t>(n1 + n2);
-    kernel<<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // the merge pass is needed only if some unit spans several work-groups
+}
+
+// The merge pass, if some unit spans several work-groups.
+template <int D>
+hipError_t combine_if_split(DecodeArgs& a, hipStream_t s) {
     bool split = false;
     for (int b = 0; b < a.rows && !split; ++b) {
         const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
@@ -613,10 +1208,53 @@ hipError_t run(DecodeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int D, int ST, int R>
+hipError_t run(DecodeArgs& a, hipStream_t s) {
+    int n_cu = 0;
+    hipError_t e = device_cus(n_cu);
+    if (e != hipSuccess) return e;
+    a.rec_rows = R;
+    split_slices(a, n_cu, KVC_DECODE_BLOCKS_PER_CU, 2 * Cfg<D, ST, R>::KPB);
+    decode_attn<D, ST, R><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return combine_if_split<D>(a, s);
+}
+
+template <int D, int ST, int RS>
+hipError_t run_rows(DecodeArgs& a, hipStream_t s) {
+    int n_cu = 0;
+    hipError_t e = device_cus(n_cu);
+    if (e != hipSuccess) return e;
+    a.rec_rows = RCfg<D, ST, RS>::ROWS;
+    split_slices(a, n_cu, 2, 2 * RCfg<D, ST, RS>::KPS);
+    decode_rows<D, ST, RS><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return combine_if_split<D>(a, s);
+}
+
+template <int D, int ST>
+hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
+    int n_cu = 0;
+    hipError_t e = device_cus(n_cu);
+    if (e != hipSuccess) return e;
+    a.rec_rows = 32;
+    split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN);
+    decode_mfma<D, ST><<<a.n_blocks, 64, 0, s>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return combine_if_split<D>(a, s);
+}
+
 template <int D, int ST>
 hipError_t run_r(DecodeArgs& a, hipStream_t s) {
-    if (a.Gc * a.Tc <= 4) return run<D, ST, 4>(a, s);
-    return run<D, ST, 8>(a, s);
+    const int rows = a.Gc * a.Tc;
+    if (rows <= 4) return run<D, ST, 4>(a, s);
+    if (rows <= 8) return run<D, ST, 8>(a, s);
+    if constexpr (ST != F32) return run_mfma<D, ST>(a, s);
+    if (rows <= 16) return run_rows<D, ST, 2>(a, s);
+    return run_rows<D, ST, 4>(a, s);
 }
 
 template <int D>
@@ -637,6 +1275,7 @@ bool decode_supported(int D, int st_dtype) {
 
 hipError_t launch_decode(DecodeArgs& a, hipStream_t s) {
     if (a.Gc * a.Tc < 1 || a.Gc * a.Tc > kMaxDecodeRows) return hipErrorInvalidValue;
+    if (a.ws_rows_cap < static_cast<int64_t>(kMaxDecodeRows) * (a.rows * a.Hkv + 1)) return hipErrorInvalidValue;
     if (a.total_keys < 1) return hipErrorInvalidValue;
     switch (a.D) {
         case 32: return run_d<32>(a, s);

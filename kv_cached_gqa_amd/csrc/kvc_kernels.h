@@ -11,9 +11,11 @@ namespace kvc {
 // Rows of the batch one launch covers; larger batches are split into several
 // launches so that per-row tables fit in the kernel argument block.
 constexpr int kMaxRowsPerLaunch = 256;
-// Query rows (query heads of one group x query positions) one decode work item
-// carries in registers.
-constexpr int kMaxDecodeRows = 8;
+// Query rows (query heads of one group x query positions) of one decode slab.
+constexpr int kMaxDecodeRows = 32;
+// Rows per workspace record of the split-K workspace as allocated (a launch
+// with slabs of more rows uses fewer, wider records).
+constexpr int kWsRecordRows = 8;
 // Upper bound on decode work-groups per launch (sizes the split-K workspace).
 constexpr int kMaxDecodeBlocks = 8192;
 
@@ -49,8 +51,10 @@ struct DecodeArgs {
     const void* v_cache;
     const void* q;           // [B][Hq][T][D], q_dtype, whole-batch base
     float* out;              // [B][Hq][T][D] float32, whole-batch base
-    float* ws_o;             // [segments][kMaxDecodeRows][D] unnormalised partial outputs
-    float* ws_ml;            // [segments][kMaxDecodeRows][2] running max (raw q.k units) and sum
+    float* ws_o;             // [records][rec_rows][D] unnormalised partial outputs
+    float* ws_ml;            // [records][rec_rows][2] running max (raw q.k units) and sum
+    int64_t ws_rows_cap;     // rows the workspace holds (records x rec_rows <= this)
+    int32_t rec_rows;        // rows per record in this launch (set by launch_decode)
     int64_t layer_off;       // element offset of (layer, row0, 0, 0, 0)
     int64_t row_stride;
     int64_t head_stride;
