@@ -795,9 +795,10 @@ void decode_rows(DecodeArgs a) {
     wait_vm<0>();
 }
 
-// ---- slabs of 9 to 32 query rows, 16-bit caches: matrix cores --------------
-// With 8 heads x a 4-token draft (or any G*T in 9..32) one KV head serves up to
-// 32 query rows, 32 flops per byte: the vector ALUs cannot keep up with HBM, so
+// ---- slabs of 5 to 32 query rows, 16-bit caches: matrix cores --------------
+// With 8 heads x a 4-token draft (or any G*T in 5..32) one KV head serves up to
+// 32 query rows, up to 32 flops per byte: the vector ALUs do not keep up with
+// HBM (at 8 rows they already trail the matrix-core kernel by a third), so
 // the two products run as MFMA tiles, the same S^T = K Q^T and O^T = V^T P^T
 // tiles as the prefill kernel, with the slab's rows as the 32 columns. One wave
 // per work-group streams 32-key K and V tiles of its slice through a private
@@ -806,16 +807,22 @@ void decode_rows(DecodeArgs a) {
 // (or the output) per column, merged by decode_combine.
 
 #ifndef KVC_DECODE_MFMA_STAGES
-#define KVC_DECODE_MFMA_STAGES 4
+#define KVC_DECODE_MFMA_STAGES 2       // one tile in flight per wave ...
 #endif
 #ifndef KVC_DECODE_MFMA_BLOCKS_PER_CU
-#define KVC_DECODE_MFMA_BLOCKS_PER_CU 2
+#define KVC_DECODE_MFMA_BLOCKS_PER_CU 3   // ... and three waves per CU (measured best)
+#endif
+#ifndef KVC_DECODE_MFMA_QSEGS
+#define KVC_DECODE_MFMA_QSEGS 2
+#endif
+#ifndef KVC_DECODE_MFMA_MIN_ROWS
+#define KVC_DECODE_MFMA_MIN_ROWS 5    // 16-bit slabs with at least this many rows use the matrix cores
 #endif
 
 template <int D>
 struct MCfg : TileLayout<D> {
     using L = TileLayout<D>;
-    static constexpr int QSEGS = 2;                          // segments the query table holds
+    static constexpr int QSEGS = KVC_DECODE_MFMA_QSEGS;      // segments the query table holds
     static constexpr int QT_BYTES = QSEGS * 32 * D * 2;      // 32 columns of D 16-bit elements each
     static constexpr int fit_stages() {
         int ns = KVC_DECODE_MFMA_STAGES;
@@ -1250,6 +1257,9 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
 template <int D, int ST>
 hipError_t run_r(DecodeArgs& a, hipStream_t s) {
     const int rows = a.Gc * a.Tc;
+    if constexpr (ST != F32) {
+        if (rows >= KVC_DECODE_MFMA_MIN_ROWS) return run_mfma<D, ST>(a, s);
+    }
     if (rows <= 4) return run<D, ST, 4>(a, s);
     if (rows <= 8) return run<D, ST, 8>(a, s);
     if constexpr (ST != F32) return run_mfma<D, ST>(a, s);
