@@ -26,8 +26,11 @@
 //    query rows of the slab (the G query heads that share the KV head, times
 //    the chunk's query positions) are held in every lane group, so each key
 //    and value is read from HBM exactly once for the whole group ("Heads, GQA
-//    and K/V cache": heads sharing one K/V). The queries of the work-group's
-//    segments are converted once into an LDS table at the start.
+//    and K/V cache": heads sharing one K/V). A segment's query rows travel the
+//    same way: wave 0 loads them by LDS-DMA into one of NS query slots just
+//    before the segment's first stage, so its own wait for the stage before
+//    covers them, and the barriers of the previous segment's merge publish them
+//    to every wave; each wave converts them to the storage type itself.
 //  * q.k: 16-bit dot2 instructions (exact products, fp32 accumulation) or fp32
 //    FMA, then a DPP sum over the LPK lanes of the key. Scores stay in raw
 //    q.k units; the softmax scale and log2(e) are folded into one FMA before
@@ -70,7 +73,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Rescale threshold (log2 units): the running reference max moves only when a
 // score exceeds it by more than this, so p = exp2(s - m) stays below 2^8.
 constexpr float kRescaleLog2 = KVC_DECODE_RESCALE_LOG2;
-constexpr int kQTableSegs = 8;    // segments whose queries the LDS table holds at once
 constexpr int kLdsLimit = 160 * 1024;
 
 template <int ST>
@@ -117,19 +119,25 @@ struct Cfg {
     static constexpr int KPS = U * KPW;                // keys per wave per stage
     static constexpr int KPB = WAVES * KPS;            // keys per work-group batch
     static constexpr int STAGE_BYTES = U * 2048;       // K and V of one stage of one wave
-    static constexpr int FIXED_BYTES = kQTableSegs * R * D * ESZ + WAVES * R * (D + 2) * 4;
+    // one query slot: the slab's R rows as the caller passed them (up to 4 bytes
+    // an element), in whole 1 KB DMA blocks
+    static constexpr int QSLOT_BYTES = (R * D * 4 + 1023) / 1024 * 1024;
+    static constexpr int MERGE_BYTES = WAVES * R * (D + 2) * 4;
+    static constexpr int lds_for(int ns) {
+        return WAVES * ns * STAGE_BYTES + ns * QSLOT_BYTES + MERGE_BYTES;
+    }
     // ring stages: as many as asked for, fewer if the LDS budget (at the work-groups
     // per CU asked for) does not hold them
     static constexpr int fit_stages() {
         int ns = KVC_DECODE_STAGES;
         const int per_cu = KVC_DECODE_BLOCKS_PER_CU > 0 ? KVC_DECODE_BLOCKS_PER_CU : 1;
-        while (ns > 2 && (WAVES * ns * STAGE_BYTES + FIXED_BYTES) * per_cu > kLdsLimit) --ns;
+        while (ns > 2 && lds_for(ns) * per_cu > kLdsLimit) --ns;
         return ns;
     }
     static constexpr int NS = fit_stages();
     static constexpr int RING_BYTES = WAVES * NS * STAGE_BYTES;
-    static constexpr int QROW_WORDS = D * ESZ / 4;     // one query row in the storage format
-    static constexpr int LDS_BYTES = RING_BYTES + FIXED_BYTES;
+    static constexpr int LDS_BYTES = lds_for(NS);
+    static_assert(NS >= 2, "ring stages");
     static_assert(LDS_BYTES <= kLdsLimit, "decode LDS budget");
     static_assert((NS - 1) * 2 * U < 64, "vmcnt field");
     static_assert((NS - 1) * STAGE_BYTES + STAGE_BYTES < 65536, "ring offsets fit the LDS immediate");
@@ -159,6 +167,17 @@ __device__ __forceinline__ void read_kv(u32x4& k, u32x4& v, uint32_t addr) {
                  : "memory");
 }
 
+// An LDS read the compiler does not see. Before an LDS access of its own that
+// might alias a pending LDS-DMA write it waits for every load in flight; this
+// read carries its own wait instead.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
 // f(integral_constant<0>), ..., f(integral_constant<N - 1>), unrolled.
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -178,7 +197,7 @@ __device__ __forceinline__ void lane_group_sum(float (&x)[M]) {
     }
 }
 
-// One segment of the work-group's slice: keys [j0, j1) of unit (b, g), whose
+// One segment of a work-group's slice: keys [j0, j1) of unit (b, g), whose
 // last slab query sits at position n_b - Tc.
 struct Seg {
     int b, g;
@@ -189,6 +208,62 @@ struct Seg {
     int64_t rec;             // workspace record, or -1: the whole unit, written directly
 };
 
+// The slab's query rows, lane's share (EPC elements from element sub * EPC of
+// each row), converted to the storage format, from an LDS slot at byte address
+// `slot` that holds the rows as the caller passed them (row r at r * D * qsize).
+template <int D, int ST, int R>
+__device__ __forceinline__ void load_q_rows(uint32_t (&qp)[R][4], uint32_t slot, int q_dtype, int sub) {
+    constexpr int EPC = ST == F32 ? 4 : 8;
+    if (q_dtype == ST) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32x4 w = lds_read_b128(slot + r * D * (ST == F32 ? 4 : 2) + sub * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qp[r][e] = w[e];
+        }
+        return;
+    }
+    // a different query type: widen to float, then round to the storage type
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float f[EPC];
+        if (q_dtype == F32) {
+            // EPC floats: 16 or 32 bytes
+#pragma unroll
+            for (int h = 0; h < EPC / 4; ++h) {
+                const u32x4 w = lds_read_b128(slot + r * D * 4 + sub * EPC * 4 + h * 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f[h * 4 + e] = __uint_as_float(w[e]);
+            }
+        } else {
+            // EPC 16-bit values: 8 or 16 bytes (an aligned 16-byte read covers them)
+            const uint32_t at = slot + r * D * 2 + sub * EPC * 2;
+            const u32x4 w = lds_read_b128(at & ~15u);
+            const int w0 = (at & 15u) >> 2;
+#pragma unroll
+            for (int e = 0; e < EPC / 2; ++e) {
+                uint32_t x = w[0];
+                if constexpr (EPC == 4) x = w0 + e == 1 ? w[1] : (w0 + e == 2 ? w[2] : (w0 + e == 3 ? w[3] : w[0]));
+                else x = e == 1 ? w[1] : (e == 2 ? w[2] : (e == 3 ? w[3] : w[0]));
+                const uint32_t lo = x & 0xFFFFu, hi = x >> 16;
+                f[2 * e] = q_dtype == BF16 ? bf16_to_f32(lo) : f16_to_f32(lo);
+                f[2 * e + 1] = q_dtype == BF16 ? bf16_to_f32(hi) : f16_to_f32(hi);
+            }
+        }
+        if constexpr (ST == F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qp[r][e] = __float_as_uint(f[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = ST == BF16 ? f32_to_bf16_rne(f[2 * e]) : f32_to_f16_rne(f[2 * e]);
+                const uint32_t hi = ST == BF16 ? f32_to_bf16_rne(f[2 * e + 1]) : f32_to_f16_rne(f[2 * e + 1]);
+                qp[r][e] = (lo & 0xFFFFu) | (hi << 16);
+            }
+        }
+    }
+}
+
 template <int D, int ST, int R>
 __global__ __launch_bounds__((Cfg<D, ST, R>::THREADS)) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_attn(DecodeArgs a) {
@@ -197,10 +272,10 @@ void decode_attn(DecodeArgs a) {
     constexpr int EPC = C::EPC, LPK = C::LPK, KPW = C::KPW, U = C::U, NS = C::NS;
     constexpr int KPS = C::KPS, KPB = C::KPB, ESZ = C::ESZ;
 
-    // Separate LDS objects: the ring (written by LDS-DMA, read only through the
-    // explicit reads above), the query table and the merge area.
+    // Separate LDS objects: the ring and the query slots (written by LDS-DMA
+    // and read only through the explicit reads above) and the merge area.
     __shared__ __attribute__((aligned(16))) uint8_t ring[C::RING_BYTES];
-    __shared__ __attribute__((aligned(16))) uint32_t qtab[kQTableSegs][R][C::QROW_WORDS];
+    __shared__ __attribute__((aligned(16))) uint8_t qslot[NS][C::QSLOT_BYTES];
     __shared__ float sm_o[kWaves][R][D];
     __shared__ float sm_m[kWaves][R];
     __shared__ float sm_l[kWaves][R];
@@ -213,6 +288,7 @@ void decode_attn(DecodeArgs a) {
     const int rows_act = a.Gc * a.Tc;
     const float c = a.scale_log2;
     const float thresh = kRescaleLog2 / c;     // the threshold in raw q.k units
+    const int qrow_bytes = D * (a.q_dtype == F32 ? 4 : 2);
 
     const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
     int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
@@ -221,67 +297,84 @@ void decode_attn(DecodeArgs a) {
 
     const char* kc = static_cast<const char*>(a.k_cache);
     const char* vc = static_cast<const char*>(a.v_cache);
+    const char* qg = static_cast<const char*>(a.q);
 
-    // -- the segment that starts at key-axis position x (wave-uniform) --
-    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
-        int lo = 0, hi = a.rows;   // prefix[lo] <= x < prefix[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (a.prefix[mid] <= x) lo = mid; else hi = mid;
-        }
+    // -- segments: the one of unit (b, g) that starts at key-axis position x --
+    auto make_seg = [&](int b, int g, int64_t x) __attribute__((always_inline)) -> Seg {
         Seg sg;
-        sg.b = lo;
-        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
-        sg.g = static_cast<int>((x - a.prefix[lo]) / n_b);
-        const int64_t unit_start = a.prefix[lo] + static_cast<int64_t>(sg.g) * n_b;
+        sg.b = b;
+        sg.g = g;
+        const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
+        const int64_t unit_start = a.prefix[b] + static_cast<int64_t>(g) * n_b;
         int64_t seg_end = unit_start + n_b;
         if (seg_end > x_end) seg_end = x_end;
         sg.j0 = static_cast<int>(x - unit_start);
         sg.j1 = static_cast<int>(seg_end - unit_start);
         sg.n_b = static_cast<int>(n_b);
         sg.nbat = (sg.j1 - sg.j0 + KPB - 1) / KPB;
-        sg.head = a.layer_off + sg.b * a.row_stride + sg.g * a.head_stride;
+        sg.head = a.layer_off + b * a.row_stride + g * a.head_stride;
         sg.x_end = seg_end;
-        sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
+        sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + b * a.Hkv + g;
         return sg;
     };
-
-    // -- the query table: the slab's rows of up to kQTableSegs segments from x,
-    //    rounded to the storage type (rows past the slab are zero) --
-    auto load_qtab = [&](int64_t x) __attribute__((always_inline)) {
-        for (int sgi = 0; sgi < kQTableSegs && x < x_end; ++sgi) {
-            const Seg sg = locate(x);
-            for (int idx = tid; idx < R * D; idx += kThreads) {
-                const int r = idx / D, e = idx - (idx / D) * D;
-                float val = 0.f;
-                if (r < rows_act) {
-                    const int h = sg.g * a.G + a.r0 + r / a.Tc;
-                    const int i = a.i0 + r % a.Tc;
-                    const int64_t qe = ((static_cast<int64_t>(a.row0 + sg.b) * a.Hq + h) * a.T + i) * D + e;
-                    if (a.q_dtype == F32) val = static_cast<const float*>(a.q)[qe];
-                    else if (a.q_dtype == BF16) val = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
-                    else val = f16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
-                }
-                if constexpr (ST == F32) {
-                    reinterpret_cast<float*>(qtab[sgi][r])[e] = val;
-                } else {
-                    const uint32_t h16 = ST == BF16 ? f32_to_bf16_rne(val) : f32_to_f16_rne(val);
-                    reinterpret_cast<uint16_t*>(qtab[sgi][r])[e] = static_cast<uint16_t>(h16);
-                }
-            }
-            x = sg.x_end;
+    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
+        int lo = 0, hi = a.rows;   // prefix[lo] <= x < prefix[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.prefix[mid] <= x) lo = mid; else hi = mid;
         }
-        __syncthreads();
+        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
+        return make_seg(lo, static_cast<int>((x - a.prefix[lo]) / n_b), x);
+    };
+    // the segment after sg (which ended at its unit's end): the next unit
+    auto next_seg = [&](const Seg& sg) __attribute__((always_inline)) -> Seg {
+        int b = sg.b, g = sg.g + 1;
+        if (g == a.Hkv) {
+            g = 0;
+            ++b;
+        }
+        return make_seg(b, g, sg.x_end);
+    };
+    // -- the slab's query rows of a segment into a query slot (wave 0; one
+    //    LDS-DMA load per 1 KB; rows past the slab repeat its last row) --
+    auto issue_q = [&](const Seg& sg, int slot) __attribute__((always_inline)) {
+        const int cpr = qrow_bytes / 16;                 // 16-byte chunks per row
+        const int n16 = R * cpr;
+        for (int n = 0; n * 64 < n16; ++n) {
+            int ch = n * 64 + lane;
+            if (ch >= n16) ch = n16 - 1;
+            int r = ch / cpr;
+            const int part = ch - r * cpr;
+            if (r >= rows_act) r = rows_act - 1;
+            const int h = sg.g * a.G + a.r0 + r / a.Tc;
+            const int i = a.i0 + r % a.Tc;
+            const int64_t off = ((static_cast<int64_t>(a.row0 + sg.b) * a.Hq + h) * a.T + i) * qrow_bytes + part * 16;
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(qg + off),
+                                             (void __attribute__((address_space(3)))*)(&qslot[slot][n * 1024]), 16, 0,
+                                             0);
+        }
     };
 
-    // -- issue side: the next stage of this wave's keys, possibly in a later
-    //    segment; past the slice's end it reloads the last key (never used) --
+    // -- issue side: the next stage of this wave's keys. A finished segment is
+    //    left at the start of the next call, for the next unit (wave 0 first
+    //    loads that unit's queries); past the slice's end it reloads the last
+    //    key (never used) --
     Seg is = locate(x_begin);
-    int is_t = 0;
+    int is_t = 0, is_sn = 0;
     bool is_live = true;
     uint8_t* const ring_w = ring + wave * (NS * C::STAGE_BYTES);
     auto issue = [&](auto slot_c) __attribute__((always_inline)) {
         constexpr int S = decltype(slot_c)::value;
+        if (is_live && is_t == is.nbat) {
+            if (is.x_end < x_end) {
+                is = next_seg(is);
+                is_t = 0;
+                ++is_sn;
+                if (wave == 0) issue_q(is, is_sn % NS);
+            } else {
+                is_live = false;
+            }
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int j = is.j0 + is_t * KPB + wave * KPS + u * KPW + grp;
@@ -293,31 +386,21 @@ void decode_attn(DecodeArgs a) {
             __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vc + off),
                                              (void __attribute__((address_space(3)))*)(dst + 1024), 16, 0, 0);
         }
-        if (is_live && ++is_t == is.nbat) {
-            if (is.x_end >= x_end) {
-                is_live = false;
-            } else {
-                is = locate(is.x_end);
-                is_t = 0;
-            }
-        }
+        if (is_live) ++is_t;
     };
-
     // -- consume side --
     const uint32_t rd_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
                                  (__attribute__((address_space(3))) uint8_t*)ring_w)) + lane * 16;
     Seg cs = locate(x_begin);
-    int cs_t = 0, cs_q = 0;
+    int cs_t = 0, cs_sn = 0;
     uint32_t qp[R][4];                 // the lane's 16 bytes of each query row
     int qpos[R];
     float m[R], l[R], o[R][EPC];
     auto start_segment = [&]() __attribute__((always_inline)) {
+        load_q_rows<D, ST, R>(qp, lds_addr(qslot[cs_sn % NS]), a.q_dtype, sub);
         const int qpos0 = cs.n_b - a.Tc;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(&qtab[cs_q][r][sub * 4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) qp[r][e] = w[e];
             qpos[r] = r < rows_act ? qpos0 + r % a.Tc : -1;
             m[r] = -INFINITY;
             l[r] = 0.f;
@@ -398,7 +481,6 @@ void decode_attn(DecodeArgs a) {
             }
         }
     };
-
     // -- end of a segment: merge the lane groups, then the waves; write the
     //    output itself or the segment's partial record --
     auto finish_segment = [&]() __attribute__((always_inline)) {
@@ -463,10 +545,13 @@ void decode_attn(DecodeArgs a) {
         lds_barrier();
     };
 
-    // -- the loop: stage t sits in slot t % NS; NS - 1 stages are issued ahead,
-    //    before the query table is built, so the two latencies overlap --
+    // -- the loop: stage t sits in slot t % NS; NS - 1 stages are issued ahead.
+    //    Wave 0 loads the first segment's queries before them; every wave
+    //    reads them once they have landed --
+    if (wave == 0) issue_q(is, 0);
     static_for<NS - 1>([&](auto k) { issue(k); });
-    load_qtab(x_begin);
+    if (wave == 0) wait_vm<(NS - 1) * 2 * U>();    // the query loads precede every stage load
+    lds_barrier();
     start_segment();
     bool done = false;
     auto step = [&](auto slot_c) __attribute__((always_inline)) {
@@ -475,16 +560,16 @@ void decode_attn(DecodeArgs a) {
         wait_vm<(NS - 1) * 2 * U>();      // this stage's loads have landed
         consume(slot_c);
         if (++cs_t == cs.nbat) {
+            // the next segment's queries were loaded before its first stage,
+            // which the wait above covers for wave 0; the barriers in
+            // finish_segment make them visible to every wave
             finish_segment();
             if (cs.x_end >= x_end) {
                 done = true;
             } else {
-                cs = locate(cs.x_end);
+                cs = next_seg(cs);
                 cs_t = 0;
-                if (++cs_q == kQTableSegs) {   // more segments than the table holds: reload it
-                    load_qtab(cs.x_end - (cs.j1 - cs.j0));
-                    cs_q = 0;
-                }
+                ++cs_sn;
                 start_segment();
             }
         }
@@ -1099,9 +1184,10 @@ void decode_mfma(DecodeArgs a) {
     wait_vm<0>();
 }
 
-// One work-group per unit: merge the partial records of a unit whose keys
-// span several work-groups (units held by one work-group were written by
-// decode_attn and are skipped).
+// Merge the partial records of units whose keys span several work-groups
+// (units held by one work-group were written by the attention kernel and are
+// skipped). Work-group (u, y) covers outputs y*256 .. y*256+255 of unit u's
+// slab, one (row, element) per thread.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     constexpr int kMaxSeg = 16;
@@ -1113,39 +1199,38 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     const int k_first = static_cast<int>(decode_slice_of(a, ustart));
     const int k_last = static_cast<int>(decode_slice_of(a, ustart + n_b - 1));
     if (k_first == k_last) return;
-    const int rows_act = a.Gc * a.Tc;
+    const int idx = static_cast<int>(blockIdx.y) * 256 + static_cast<int>(threadIdx.x);
+    if (idx >= a.Gc * a.Tc * D) return;
     const float c = a.scale_log2;
-    for (int idx = threadIdx.x; idx < rows_act * D; idx += 256) {
-        const int r = idx / D, d = idx - (idx / D) * D;
-        float M = -INFINITY, ov = 0.f, lv = 0.f;
-        for (int k0 = k_first; k0 <= k_last; k0 += kMaxSeg) {
-            float mk[kMaxSeg], lk[kMaxSeg], okv[kMaxSeg];
+    const int r = idx / D, d = idx - (idx / D) * D;
+    float M = -INFINITY, ov = 0.f, lv = 0.f;
+    for (int k0 = k_first; k0 <= k_last; k0 += kMaxSeg) {
+        float mk[kMaxSeg], lk[kMaxSeg], okv[kMaxSeg];
 #pragma unroll
-            for (int t = 0; t < kMaxSeg; ++t) {
-                const int k = k0 + t;
-                const int64_t rec = static_cast<int64_t>((k <= k_last ? k : k_last) + u) * a.rec_rows + r;
-                mk[t] = k <= k_last ? a.ws_ml[rec * 2] : -INFINITY;
-                lk[t] = a.ws_ml[rec * 2 + 1];
-                okv[t] = a.ws_o[rec * D + d];
-            }
-            float Mn = M;
-#pragma unroll
-            for (int t = 0; t < kMaxSeg; ++t) Mn = fmaxf(Mn, mk[t]);
-            const float sc = M == -INFINITY ? 0.f : fexp2((M - Mn) * c);
-            ov *= sc;
-            lv *= sc;
-#pragma unroll
-            for (int t = 0; t < kMaxSeg; ++t) {
-                const float f = mk[t] == -INFINITY ? 0.f : fexp2((mk[t] - Mn) * c);
-                ov = fmaf(okv[t], f, ov);
-                lv = fmaf(lk[t], f, lv);
-            }
-            M = Mn;
+        for (int t = 0; t < kMaxSeg; ++t) {
+            const int k = k0 + t;
+            const int64_t rec = static_cast<int64_t>((k <= k_last ? k : k_last) + u) * a.rec_rows + r;
+            mk[t] = k <= k_last ? a.ws_ml[rec * 2] : -INFINITY;
+            lk[t] = a.ws_ml[rec * 2 + 1];
+            okv[t] = a.ws_o[rec * D + d];
         }
-        const int h = g * a.G + a.r0 + r / a.Tc;
-        const int i = a.i0 + r % a.Tc;
-        a.out[((static_cast<int64_t>(a.row0 + b) * a.Hq + h) * a.T + i) * D + d] = ov / lv;
+        float Mn = M;
+#pragma unroll
+        for (int t = 0; t < kMaxSeg; ++t) Mn = fmaxf(Mn, mk[t]);
+        const float sc = M == -INFINITY ? 0.f : fexp2((M - Mn) * c);
+        ov *= sc;
+        lv *= sc;
+#pragma unroll
+        for (int t = 0; t < kMaxSeg; ++t) {
+            const float f = mk[t] == -INFINITY ? 0.f : fexp2((mk[t] - Mn) * c);
+            ov = fmaf(okv[t], f, ov);
+            lv = fmaf(lk[t], f, lv);
+        }
+        M = Mn;
     }
+    const int h = g * a.G + a.r0 + r / a.Tc;
+    const int i = a.i0 + r % a.Tc;
+    a.out[((static_cast<int64_t>(a.row0 + b) * a.Hq + h) * a.T + i) * D + d] = ov / lv;
 }
 
 // CUs of the current device (cached per device).
@@ -1211,7 +1296,8 @@ hipError_t combine_if_split(DecodeArgs& a, hipStream_t s) {
         }
     }
     if (!split) return hipSuccess;
-    decode_combine<D><<<a.rows * a.Hkv, 256, 0, s>>>(a);
+    const dim3 grid(a.rows * a.Hkv, (a.Gc * a.Tc * D + 255) / 256);
+    decode_combine<D><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ struct AppendArgs {
 // ---------------------------------------------------------------------------
 // Split-K decode attention over a flattened key axis ("stream-K"):
 // work unit u = (row b, KV head g) owns n_b keys; the units are laid end to
-// end (b-major) and each work-group takes an equal slice of that axis.
+// end (b-major) and each work-group takes a slice of that axis.
 // A slab is a set of query rows of one unit: query heads g*G + r0 .. + Gc and
 // query positions i0 .. i0 + Tc of the chunk (Gc * Tc <= kMaxDecodeRows).
 // ---------------------------------------------------------------------------

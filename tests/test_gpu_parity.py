@@ -209,11 +209,55 @@ def test_ragged_rows_groups_and_chunks(dtype, D):
         assert cache_bits_equal(cache, orc)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_decode_slabs_split_over_many_work_groups(dtype, D):
+    """Decode slabs of 4..32 query rows per KV head over contexts of thousands of
+    keys, so that one (row, KV head) spans many work-groups and one work-group's
+    slice crosses unit boundaries: 16-bit caches take the matrix-core decode
+    kernel from 5 rows on, fp32 caches the row-split kernel above 8 rows. A row
+    that starts empty gets only the chunk's own keys."""
+    log(f"decode split slabs dtype={dtype} D={D}")
+    rng = np.random.default_rng(700 + D)
+    #          B  Hq  Hkv T   context lengths before the chunk
+    cases = ((2, 8, 1, 4, (9001, 2999)),        # 32 rows
+             (3, 10, 2, 1, (4096, 1, 6143)),    # 5 rows
+             (4, 12, 4, 2, (0, 2050, 3333, 777)),  # 6 rows
+             (1, 32, 2, 1, (12000,)),           # 16 rows, two long units
+             (3, 4, 4, 9, (1500, 31, 2600)),     # 9 rows = 1 head x 9 positions
+             (2, 4, 2, 2, (5000, 64)))          # 4 rows (vector kernel)
+    for (B, Hq, Hkv, T, lens) in cases:
+        lens = np.array(lens)
+        max_len = int(lens.max()) + T
+        cache, orc = _new((1, B, Hq, Hkv, D, max_len), dtype)
+        n0 = int(lens.max())
+        k, v = (rng.standard_normal((B, Hkv, n0, D), dtype=np.float32) for _ in range(2))
+        cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
+        orc.append(0, k, v)
+        cache.truncate(lens)
+        orc.truncate(lens)
+        q, k, v = (rng.standard_normal(s, dtype=np.float32) for s in ((B, Hq, T, D), (B, Hkv, T, D), (B, Hkv, T, D)))
+        # a slightly peaked softmax: scores spread over several units of log-weight
+        q *= 2.0
+        cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
+        orc.append(0, k, v)
+        got = cache.attend(0, to_device(q, "fp32", DEV)).cpu().numpy()
+        want = orc.attend(0, q)
+        mabs, rel = compare_out(got, want, dtype)
+        log(f"  B={B} Hq={Hq} Hkv={Hkv} T={T}: rel {rel:.2e} max abs {mabs:.2e}")
+        assert np.isfinite(got).all()
+        if dtype == "fp32":
+            assert mabs <= FP32_MAX_ABS, (Hq, Hkv, T, mabs)
+        else:
+            assert rel <= HALF_REL_FROB, (Hq, Hkv, T, rel)
+
+
 def test_batch_wider_than_one_launch():
-    """B=300 rows (two launches of at most 256 rows each)."""
+    """B=300 rows (two launches of at most 256 rows each), on the vector (2 and 8
+    query rows per KV head) and matrix-core (6 rows) decode kernels."""
     log("B=300 rows")
     rng = np.random.default_rng(300)
-    B, Hq, Hkv, D, max_len = 300, 4, 2, 64, 48
+    B, Hq, Hkv, D, max_len = 300, 4, 2, 64, 52
     cache, orc = _new((1, B, Hq, Hkv, D, max_len), "bf16")
     lens = rng.integers(0, 40, size=B)
     k, v = (rng.standard_normal((B, Hkv, 40, D), dtype=np.float32) for _ in range(2))
@@ -221,7 +265,7 @@ def test_batch_wider_than_one_launch():
     orc.append(0, k, v)
     cache.truncate(lens)
     orc.truncate(lens)
-    for T in (1, 4):
+    for T in (1, 4, 3):
         q, k, v = (rng.standard_normal(s, dtype=np.float32) for s in ((B, Hq, T, D), (B, Hkv, T, D), (B, Hkv, T, D)))
         cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
         orc.append(0, k, v)
