@@ -487,17 +487,14 @@ void decode_attn(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             float mw = m[r];
-#pragma unroll
-            for (int d = LPK; d < 64; d <<= 1) mw = fmaxf(mw, __shfl_xor(mw, d));
+            mw = across_groups<LPK, true>(mw);
             const float w = mw == -INFINITY ? 0.f : fexp2((m[r] - mw) * c);
             float lw = l[r] * w;
-#pragma unroll
-            for (int d = LPK; d < 64; d <<= 1) lw += __shfl_xor(lw, d);
+            lw = across_groups<LPK, false>(lw);
 #pragma unroll
             for (int e = 0; e < EPC; ++e) {
                 float ow = o[r][e] * w;
-#pragma unroll
-                for (int d = LPK; d < 64; d <<= 1) ow += __shfl_xor(ow, d);
+                ow = across_groups<LPK, false>(ow);
                 o[r][e] = ow;
             }
             m[r] = mw;
@@ -812,18 +809,15 @@ void decode_rows(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             float mw = m[r];
-#pragma unroll
-            for (int d = LPK; d < 64; d <<= 1) mw = fmaxf(mw, __shfl_xor(mw, d));
+            mw = across_groups<LPK, true>(mw);
             const float w = mw == -INFINITY ? 0.f : fexp2((m[r] - mw) * c);
             float lw = l[r] * w;
-#pragma unroll
-            for (int d = LPK; d < 64; d <<= 1) lw += __shfl_xor(lw, d);
+            lw = across_groups<LPK, false>(lw);
             float ow[EPC];
 #pragma unroll
             for (int e = 0; e < EPC; ++e) {
                 ow[e] = o[r][e] * w;
-#pragma unroll
-                for (int d = LPK; d < 64; d <<= 1) ow[e] += __shfl_xor(ow[e], d);
+                ow[e] = across_groups<LPK, false>(ow[e]);
             }
             const int rr = wave * R + r;
             if (grp == 0 && rr < rows_act) {
@@ -1089,7 +1083,7 @@ void decode_mfma(DecodeArgs a) {
 #pragma unroll
         for (int jj = 1; jj < 16; ++jj) mt = fmaxf(mt, sv_[jj]);
         if (__any(mt - m > thresh)) {
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = xor_op<32, true>(mt);
             if (mt - m > thresh) {
                 const float alpha = m == -INFINITY ? 0.f : fexp2((m - mt) * c);
                 m = mt;
@@ -1120,7 +1114,7 @@ void decode_mfma(DecodeArgs a) {
     // -- end of a segment: column col32's (max, sum, output); the lane holds
     //    head elements dt * 32 + (jj / 4) * 8 + hl * 4 + jj % 4 --
     auto finish_segment = [&]() __attribute__((always_inline)) {
-        const float l_all = lsum + __shfl_xor(lsum, 32);
+        const float l_all = xor_op<32, false>(lsum);
         if (col32 < rows_act) {
             if (cs.rec < 0) {
                 const float inv = 1.f / l_all;

@@ -100,8 +100,11 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 // DPP row operations act within rows of 16 lanes. quad_perm [1,0,3,2] and
 // [2,3,0,1] exchange with lanes 1 and 2 away; after those a whole quad holds
 // one value, so row_half_mirror (lane i <-> 7 - i) pairs quad 0 with quad 1,
-// and row_mirror (i <-> 15 - i) pairs the two 8-lane halves. Distances 16 and
-// 32 go through ds_swizzle-style shuffles.
+// and row_mirror (i <-> 15 - i) pairs the two 8-lane halves; row_ror:n rotates
+// a row (lane i gets lane i - n, mod 16). Distances 16 and 32 use gfx950's
+// v_permlane16_swap / v_permlane32_swap (VALU, no LDS traffic): applied to
+// (x, x) they return, in each lane, x of that lane and of the lane 16 (32)
+// away, in an order that depends on the lane.
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
@@ -112,6 +115,38 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm(1,0,3,2)
 constexpr int kDppXor2 = 0x4E;        // quad_perm(2,3,0,1)
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
+constexpr int kDppRor4 = 0x124;
+constexpr int kDppRor8 = 0x128;
+
+// op(x, x of the lane D away), D = 16 or 32; op is commutative.
+template <int D, bool MAX>
+__device__ __forceinline__ float xor_op(float x) {
+    static_assert(D == 16 || D == 32, "lane swap distance");
+    const uint32_t u = __float_as_uint(x);
+    float a, b;
+    if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    }
+    return MAX ? fmaxf(a, b) : a + b;
+}
+
+// Sum (or max) over the lanes that share lane % N (N = 4..64, power of two):
+// across the 64 / N aligned groups of N lanes. Every lane gets the result.
+template <int N, bool MAX>
+__device__ __forceinline__ float across_groups(float x) {
+    static_assert(N >= 4 && N <= 64, "group width");
+    if constexpr (N == 4) x = MAX ? fmaxf(x, dpp_f<kDppRor4>(x)) : x + dpp_f<kDppRor4>(x);
+    if constexpr (N <= 8) x = MAX ? fmaxf(x, dpp_f<kDppRor8>(x)) : x + dpp_f<kDppRor8>(x);
+    if constexpr (N <= 16) x = xor_op<16, MAX>(x);
+    if constexpr (N <= 32) x = xor_op<32, MAX>(x);
+    return x;
+}
 
 // In-place sums of M independent values over aligned groups of N lanes
 // (N in 1..16). The steps go across all M values before the next step, so a
@@ -145,8 +180,8 @@ __device__ __forceinline__ float group_sum(float x) {
     if constexpr (N >= 4) x += dpp_f<kDppXor2>(x);
     if constexpr (N >= 8) x += dpp_f<kDppHalfMirror>(x);
     if constexpr (N >= 16) x += dpp_f<kDppMirror>(x);
-    if constexpr (N >= 32) x += __shfl_xor(x, 16);
-    if constexpr (N >= 64) x += __shfl_xor(x, 32);
+    if constexpr (N >= 32) x = xor_op<16, false>(x);
+    if constexpr (N >= 64) x = xor_op<32, false>(x);
     return x;
 }
 

@@ -253,7 +253,7 @@ void prefill_attn(PrefillArgs a) {
 #pragma unroll
             for (int jj = 1; jj < 16; ++jj) mt = fmaxf(mt, sv_[jj]);
             if (__any(mt - m[nt] > thresh)) {
-                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                mt = xor_op<32, true>(mt);
                 if (mt - m[nt] > thresh) {
                     const float alpha = m[nt] == -INFINITY ? 0.f : fexp2((m[nt] - mt) * c);
                     m[nt] = mt;
@@ -305,7 +305,7 @@ void prefill_attn(PrefillArgs a) {
     //    dt * 32 + (jj / 4) * 8 + hl * 4 + jj % 4
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-        const float l_all = lsum[nt] + __shfl_xor(lsum[nt], 32);
+        const float l_all = xor_op<32, false>(lsum[nt]);
         if (!col_ok[nt]) continue;
         const float inv = 1.f / l_all;
         const int h = g * a.G + a.r0 + col_r[nt];
