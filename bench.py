@@ -19,7 +19,9 @@ divided by the step time. The roofline object times the decode attention
 Besides the headline line it reports, under "extra", the chunked-prefill
 workload (B=4, 32 chunks of T=512 up to 16384 keys, bf16, MFMA path: TFLOP/s and
 % of the bf16 matrix peak) and the long-context decode workload (B=8, H_q=64,
-H_kv=8, 32768 cached keys: GB/s for T=1 and T=4 attention calls).
+H_kv=8, 32768 cached keys: GB/s for T=1 and T=4 attention calls), and the
+tiny decoder (48-token prompt, 160 greedy steps, attention through the C ABI):
+wall time of the cached and the uncached generation and their work counters.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
     python bench.py --pmc-workload      # calibration copy + attention calls, for rocprofv3 --pmc
@@ -55,7 +57,8 @@ def parse():
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time budget of the oracle sample")
-    ap.add_argument("--no-extra", action="store_true", help="skip the prefill and long-context figures")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the prefill, long-context and tiny-decoder figures")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run the counter workload (calibration copy, then attention calls) and exit")
     return ap.parse_args()
@@ -211,6 +214,40 @@ def prefill_bench():
             "flops_per_run": flops}
 
 
+def tiny_decoder_bench():
+    """The tiny decoder of "kv-cache-decoding" (vocab 96, d_model 128, 4 heads,
+    4 layers; 48-token prompt, 160 greedy steps) on the GPU, attention through
+    the C ABI with an fp32 cache: wall time of the cached and of the uncached
+    generation (one warm-up run of each first) and their work counters."""
+    import torch
+    from kv_cached_gqa_amd.tiny_decoder import TinyDecoder, generate_no_cache, generate_with_cache
+    from kv_cached_gqa_amd.workloads import TinyDecoderSpec, tiny_decoder_prompt, tiny_decoder_weights
+    spec = TinyDecoderSpec()
+    model = TinyDecoder(tiny_decoder_weights(0, spec), spec)
+    prompt, n_new = tiny_decoder_prompt(1, 48, spec), 160
+    res = {"workload": "tiny decoder: vocab 96, d_model 128, 4 heads, 4 layers, fp32 cache; "
+                       "48-token prompt, 160 greedy steps"}
+    for name, run in (("cached", lambda: generate_with_cache(model, prompt, n_new)),
+                      ("uncached", lambda: generate_no_cache(model, prompt, n_new))):
+        out = run()
+        if name == "cached":
+            out[2].close()
+        torch.cuda.synchronize()
+        model.scores = model.positions = 0
+        t0 = time.perf_counter()
+        out = run()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        if name == "cached":
+            out[2].close()
+        res[name] = {"ms": round(dt * 1e3, 2), "tokens_per_s": round(n_new / dt, 1),
+                     "attention_scores": model.scores, "positions": model.positions, "ids": out[0]}
+    res["same_ids"] = res["cached"].pop("ids") == res["uncached"].pop("ids")
+    res["speedup"] = round(res["uncached"]["ms"] / res["cached"]["ms"], 2)
+    model.close()
+    return res
+
+
 def long_ctx_bench():
     """Long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys;
     attention calls with T=1 and T=4 (a draft block) after one append."""
@@ -323,7 +360,8 @@ def main():
                      "bytes_per_launch": att, "launch_us": round(us_attend, 3)},
     }
     if not args.no_extra:
-        rec["extra"] = {"chunked_prefill": prefill_bench(), "long_context_decode": long_ctx_bench()}
+        rec["extra"] = {"chunked_prefill": prefill_bench(), "long_context_decode": long_ctx_bench(),
+                        "tiny_decoder": tiny_decoder_bench()}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(lengths, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -197,3 +197,54 @@ def script_long_ctx_spec(seed: int = 0, n_cycles: int = 64, s0: int = 32768, dra
                 yield Call("pass", 0, 1, q, k, v, tag=f"decode{c}.{a}")
             yield Call("truncate", n=np.full(B, s0, dtype=np.int64), tag=f"reset{c}")
     return shape, calls()
+
+
+# ---- tiny decoder-only model ("kv-cache-decoding": the benchmark spec and
+#      "Correctness tests": vocab 96, d_model 128, 4 heads, 4 layers, max_len
+#      256, a 48-token prompt and 160 greedy steps) ------------------------------
+
+@dataclass(frozen=True)
+class TinyDecoderSpec:
+    vocab: int = 96
+    d_model: int = 128
+    n_heads: int = 4
+    n_layers: int = 4
+    max_len: int = 256
+
+    @property
+    def d_head(self) -> int:
+        return self.d_model // self.n_heads
+
+
+def tiny_decoder_weights(seed: int = 0, spec: TinyDecoderSpec = TinyDecoderSpec()) -> dict:
+    """Random float32 weights of the tiny decoder: token and position tables
+    N(0, 1); every projection [rows, cols] N(0, 1/rows) (so activations keep
+    unit scale); layer-norm gains 1 and biases 0. Draw order: tok_emb, pos_emb,
+    then per layer w_q, w_k, w_v, w_o, w_1 [d, 4d], w_2 [4d, d], then w_out."""
+    rng = np.random.default_rng(seed)
+    d = spec.d_model
+
+    def proj(rows, cols):
+        return _normal(rng, (rows, cols), float(1.0 / np.sqrt(rows)))
+
+    w = {"tok_emb": _normal(rng, (spec.vocab, d), 1.0), "pos_emb": _normal(rng, (spec.max_len, d), 1.0),
+         "layers": []}
+    for _ in range(spec.n_layers):
+        lw = {}
+        for name, shape in (("w_q", (d, d)), ("w_k", (d, d)), ("w_v", (d, d)), ("w_o", (d, d)),
+                            ("w_1", (d, 4 * d)), ("w_2", (4 * d, d))):
+            lw[name] = proj(*shape)
+        for name in ("g1", "g2"):
+            lw[name] = np.ones(d, np.float32)
+        for name in ("b1", "b2"):
+            lw[name] = np.zeros(d, np.float32)
+        w["layers"].append(lw)
+    w["g_out"] = np.ones(d, np.float32)
+    w["b_out"] = np.zeros(d, np.float32)
+    w["w_out"] = proj(d, spec.vocab)
+    return w
+
+
+def tiny_decoder_prompt(seed: int = 1, length: int = 48, spec: TinyDecoderSpec = TinyDecoderSpec()) -> list:
+    """A prompt of `length` token ids drawn uniformly from the vocabulary."""
+    return [int(x) for x in np.random.default_rng(seed).integers(0, spec.vocab, size=length)]
