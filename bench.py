@@ -248,6 +248,41 @@ def tiny_decoder_bench():
     return res
 
 
+def rope_bench():
+    """The batched-decode step's append (B=32, H_kv=8, d_h=128, bf16, T=1, rows
+    at 2000 positions) with the keys rotated (kvc_append_rope) against the
+    plain append, and the rotation of the step's queries (kvc_rope_q, H_q=32):
+    microseconds per call, HIP events over 200 calls."""
+    import torch
+    from kv_cached_gqa_amd.kvc import KVCache
+    b, hq, hkv, d = 32, 32, 8, 128
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(17)
+    cache = KVCache(1, hkv, d, 2048, batch=b, n_q_heads=hq, dtype="bf16", device=dev)
+    k = torch.randn((b, hkv, 2000, d), generator=gen, device=dev, dtype=torch.bfloat16)
+    cache.append(0, k, k)
+    del k
+    kv = torch.randn((b, hkv, 1, d), generator=gen, device=dev, dtype=torch.bfloat16)
+    q = torch.randn((b, hq, 1, d), generator=gen, device=dev, dtype=torch.bfloat16)
+    st = torch.cuda.current_stream()
+    res = {"workload": "append of one decode step, B=32, H_kv=8, d_h=128, bf16, positions 2000"}
+
+    def step(rope):
+        cache.append(0, kv, kv, rope_base=500000.0 if rope else None)
+        cache.truncate(2000)
+
+    for name, fn in (("append_us", lambda i: step(False)), ("append_rope_us", lambda i: step(True)),
+                     ("rope_q_us", lambda i: cache.rope_q(0, q, 500000.0))):
+        if name == "rope_q_us":
+            cache.append(0, kv, kv)              # the chunk the queries belong to
+        for i in range(10):
+            fn(i)
+        res[name] = round(event_time(fn, 200, st) * 1e3, 2)
+    cache.close()
+    return res
+
+
 def long_ctx_bench():
     """Long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys;
     attention calls with T=1 and T=4 (a draft block) after one append."""
@@ -361,7 +396,7 @@ def main():
     }
     if not args.no_extra:
         rec["extra"] = {"chunked_prefill": prefill_bench(), "long_context_decode": long_ctx_bench(),
-                        "tiny_decoder": tiny_decoder_bench()}
+                        "tiny_decoder": tiny_decoder_bench(), "rope": rope_bench()}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(lengths, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

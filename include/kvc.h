@@ -100,6 +100,32 @@ void kvc_destroy(kvc_cache* cache);
 int kvc_append(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
                int32_t in_dtype, int32_t T, void* stream);
 
+/* Append with the rotary position embedding of the keys ("KV cache,
+ * incremental decode, ...": keys are stored after RoPE, so a cached key never
+ * changes; "kv-cache-decoding", "Position information with a cache"; the
+ * rotary variant and base are left open there, this is the stated reading).
+ *  As kvc_append, except that each key vector of row b at slot p = fill + t is
+ *  rotated before it is stored: for each pair (i, i + d_head/2), i < d_head/2,
+ *  with f_i = rope_base^(-2i / d_head) and angle a = p * f_i,
+ *    k'[i]            = k[i] cos a - k[i + d_head/2] sin a
+ *    k'[i + d_head/2] = k[i + d_head/2] cos a + k[i] sin a,
+ *  computed in float64 (angles, sines and cosines; each product and the sum
+ *  rounded, no fused multiply-add), rounded to float32, then to the storage
+ *  dtype (round-to-nearest-even). Values are stored unrotated.
+ * Errors: as kvc_append; KVC_ERR_ARG also for rope_base not finite or <= 0. */
+int kvc_append_rope(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+                    int32_t in_dtype, int32_t T, double rope_base, void* stream);
+
+/* Rotate a chunk's queries in place with the same embedding, at the positions
+ * the next kvc_attend of this layer gives them: row b's query t sits at
+ * s_b + t, s_b = fill[layer][b] - T (so call it after the chunk's append).
+ *  q: device [batch][n_q_heads][T][d_head] of q_dtype, 16-byte aligned; the
+ *     result is rounded to q_dtype (float64 -> float32 -> q_dtype, nearest even).
+ * Errors: KVC_ERR_ARG (null pointer, layer out of range, T < 1, bad rope_base),
+ * KVC_ERR_DTYPE, KVC_ERR_STATE (fill[layer][b] < T for some row), KVC_ERR_HIP. */
+int kvc_rope_q(const kvc_cache* cache, int32_t layer, void* q, int32_t q_dtype, int32_t T,
+               double rope_base, void* stream);
+
 /* Attention of a chunk's queries over everything a layer holds
  * ("KV cache, ...", section 2.3; "kv-cache-decoding", shapes table).
  *  q: device [batch][n_q_heads][T][d_head] of q_dtype. For an fp16/bf16 cache

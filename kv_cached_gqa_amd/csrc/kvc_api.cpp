@@ -156,8 +156,20 @@ void kvc_destroy(kvc_cache* c) {
     delete c;
 }
 
-int kvc_append(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new, int32_t in_dtype, int32_t T,
-               void* stream) {
+}  // extern "C"
+
+namespace {
+
+bool rope_base_ok(double base) { return std::isfinite(base) && base > 0.0; }
+
+// Frequencies of the rotary pairs (i, i + D/2): base^(-2i / D), i < D/2.
+void rope_freqs(double base, int D, double* out) {
+    for (int i = 0; i < D / 2; ++i) out[i] = std::pow(base, -2.0 * i / D);
+}
+
+// Append with or without the rotary embedding of K (rope_base > 0).
+int append_impl(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new, int32_t in_dtype, int32_t T,
+                double rope_base, void* stream) {
     if (!c || !k_new || !v_new) return KVC_ERR_ARG;
     const kvc_config& cf = c->cfg;
     if (layer < 0 || layer >= cf.n_layers || T < 1) return KVC_ERR_ARG;
@@ -187,10 +199,54 @@ int kvc_append(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new
         a.D = cf.d_head;
         a.in_dtype = in_dtype;
         a.st_dtype = cf.dtype;
+        a.rope = rope_base > 0.0 ? 1 : 0;
+        if (a.rope) rope_freqs(rope_base, cf.d_head, a.inv_freq);
         for (int b = 0; b < a.rows; ++b) a.fill[b] = static_cast<int32_t>(f[row0 + b]);
         if (kvc::launch_append(a, s) != hipSuccess) return KVC_ERR_HIP;
     }
     for (int b = 0; b < cf.batch; ++b) f[b] += T;
+    return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_append(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new, int32_t in_dtype, int32_t T,
+               void* stream) {
+    return append_impl(c, layer, k_new, v_new, in_dtype, T, 0.0, stream);
+}
+
+int kvc_append_rope(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new, int32_t in_dtype,
+                    int32_t T, double rope_base, void* stream) {
+    if (!rope_base_ok(rope_base)) return KVC_ERR_ARG;
+    return append_impl(c, layer, k_new, v_new, in_dtype, T, rope_base, stream);
+}
+
+int kvc_rope_q(const kvc_cache* c, int32_t layer, void* q, int32_t q_dtype, int32_t T, double rope_base,
+               void* stream) {
+    if (!c || !q) return KVC_ERR_ARG;
+    const kvc_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || T < 1 || !rope_base_ok(rope_base)) return KVC_ERR_ARG;
+    if (!dtype_ok(q_dtype)) return KVC_ERR_DTYPE;
+    if (!aligned16(q)) return KVC_ERR_ARG;
+    const int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
+    for (int b = 0; b < cf.batch; ++b)
+        if (f[b] < T) return KVC_ERR_STATE;
+    const int64_t row_bytes = static_cast<int64_t>(cf.n_q_heads) * T * cf.d_head * kvc::itemsize(q_dtype);
+    for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
+        kvc::RopeArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.x = static_cast<char*>(q) + row0 * row_bytes;
+        a.rows = std::min(kMaxRowsPerLaunch, cf.batch - row0);
+        a.H = cf.n_q_heads;
+        a.T = T;
+        a.D = cf.d_head;
+        a.dtype = q_dtype;
+        rope_freqs(rope_base, cf.d_head, a.inv_freq);
+        for (int b = 0; b < a.rows; ++b) a.pos0[b] = static_cast<int32_t>(f[row0 + b] - T);
+        if (kvc::launch_rope(a, static_cast<hipStream_t>(stream)) != hipSuccess) return KVC_ERR_HIP;
+    }
     return KVC_OK;
 }
 

@@ -8,6 +8,12 @@
 // rows*H_kv contiguous runs. Each thread moves 8 elements (16 or 32 bytes),
 // consecutive threads move consecutive vectors: every wave reads and writes
 // one contiguous stretch per run, fully coalesced. blockIdx.y selects K or V.
+//
+// With rope set, K is stored rotated at its absolute positions fill_b + t
+// ("KV cache, incremental decode, ...": keys are kept after RoPE, so a cached
+// key never changes; "kv-cache-decoding", "Position information with a
+// cache"): each thread then takes 8 pairs (elements i and i + D/2) of one
+// position. rope_kernel rotates a chunk's queries in place the same way.
 #include "kvc_device.h"
 
 namespace kvc {
@@ -15,10 +21,33 @@ namespace {
 
 template <int IN, int ST>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-    const int vec_per_run = (a.T * a.D) >> 3;
-    const int64_t n_vec = static_cast<int64_t>(a.rows) * a.H * vec_per_run;
     const void* src = blockIdx.y == 0 ? a.k_in : a.v_in;
     void* dst = blockIdx.y == 0 ? a.k_cache : a.v_cache;
+    if (blockIdx.y == 0 && a.rope) {
+        const int half = a.D >> 1;
+        const int blk_per_pos = half >> 3;                      // 8-pair blocks per position
+        const int64_t n_blk = static_cast<int64_t>(a.rows) * a.H * a.T * blk_per_pos;
+        for (int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; v < n_blk;
+             v += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+            const int64_t run_t = v / blk_per_pos;              // (row, head, t)
+            const int i0 = static_cast<int>(v - run_t * blk_per_pos) * 8;
+            const int64_t run = run_t / a.T;
+            const int t = static_cast<int>(run_t - run * a.T);
+            const int b = static_cast<int>(run / a.H);
+            const int g = static_cast<int>(run - static_cast<int64_t>(b) * a.H);
+            float x1[8], x2[8], y1[8], y2[8];
+            load8<IN>(src, run_t * a.D + i0, x1);
+            load8<IN>(src, run_t * a.D + i0 + half, x2);
+            rope8(x1, x2, static_cast<int64_t>(a.fill[b]) + t, a.inv_freq + i0, y1, y2);
+            const int64_t d = a.layer_off + b * a.row_stride + g * a.head_stride +
+                              (static_cast<int64_t>(a.fill[b]) + t) * a.D + i0;
+            store8<ST>(dst, d, y1);
+            store8<ST>(dst, d + half, y2);
+        }
+        return;
+    }
+    const int vec_per_run = (a.T * a.D) >> 3;
+    const int64_t n_vec = static_cast<int64_t>(a.rows) * a.H * vec_per_run;
     for (int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; v < n_vec;
          v += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const int64_t run = v / vec_per_run;
@@ -44,7 +73,42 @@ hipError_t dispatch_st(const AppendArgs& a, dim3 grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DT>
+__global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
+    const int half = a.D >> 1;
+    const int blk_per_pos = half >> 3;
+    const int64_t n_blk = static_cast<int64_t>(a.rows) * a.H * a.T * blk_per_pos;
+    for (int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; v < n_blk;
+         v += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t run_t = v / blk_per_pos;
+        const int i0 = static_cast<int>(v - run_t * blk_per_pos) * 8;
+        const int64_t run = run_t / a.T;
+        const int t = static_cast<int>(run_t - run * a.T);
+        const int b = static_cast<int>(run / a.H);
+        float x1[8], x2[8], y1[8], y2[8];
+        load8<DT>(a.x, run_t * a.D + i0, x1);
+        load8<DT>(a.x, run_t * a.D + i0 + half, x2);
+        rope8(x1, x2, static_cast<int64_t>(a.pos0[b]) + t, a.inv_freq + i0, y1, y2);
+        store8<DT>(a.x, run_t * a.D + i0, y1);
+        store8<DT>(a.x, run_t * a.D + i0 + half, y2);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
+    const int64_t n_blk = static_cast<int64_t>(a.rows) * a.H * a.T * (a.D >> 4);
+    int64_t blocks = (n_blk + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    switch (a.dtype) {
+        case F32: rope_kernel<F32><<<static_cast<unsigned>(blocks), 256, 0, s>>>(a); break;
+        case F16: rope_kernel<F16><<<static_cast<unsigned>(blocks), 256, 0, s>>>(a); break;
+        case BF16: rope_kernel<BF16><<<static_cast<unsigned>(blocks), 256, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
     const int64_t n_vec = static_cast<int64_t>(a.rows) * a.H * ((a.T * a.D) >> 3);

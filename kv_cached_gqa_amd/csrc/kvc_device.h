@@ -93,6 +93,28 @@ __device__ __forceinline__ void store8(void* base, int64_t elem, const float (&v
     }
 }
 
+// Rotary position embedding of 8 pairs, elements i0 + e (x1[e]) and
+// i0 + e + D/2 (x2[e]) of one head vector at position pos, with the pairs'
+// frequencies f[e] (the "rotate half" pairing): angle = pos * f[e] in float64,
+// y1 = x1 cos - x2 sin, y2 = x2 cos + x1 sin, each product and the sum rounded
+// in float64 (no fused multiply-add), then rounded to float32.
+__device__ __forceinline__ void rope8(const float (&x1)[8], const float (&x2)[8], int64_t pos, const double* f,
+                                      float (&y1)[8], float (&y2)[8]) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const double ang = static_cast<double>(pos) * f[e];
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        const double a = static_cast<double>(x1[e]) * cs;
+        const double b = static_cast<double>(x2[e]) * sn;
+        const double c = static_cast<double>(x2[e]) * cs;
+        const double d = static_cast<double>(x1[e]) * sn;
+        y1[e] = static_cast<float>(a - b);
+        y2[e] = static_cast<float>(c + d);
+    }
+}
+
 // Hardware base-2 exponential (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -11,6 +11,8 @@ namespace kvc {
 // Rows of the batch one launch covers; larger batches are split into several
 // launches so that per-row tables fit in the kernel argument block.
 constexpr int kMaxRowsPerLaunch = 256;
+// Rotary pairs per head vector (d_head / 2 for d_head <= 128).
+constexpr int kMaxRopePairs = 64;
 // Query rows (query heads of one group x query positions) of one decode slab.
 constexpr int kMaxDecodeRows = 32;
 // Rows per workspace record of the split-K workspace as allocated (a launch
@@ -36,7 +38,21 @@ struct AppendArgs {
     int64_t head_stride;     // elements between heads: max_len * D
     int32_t rows, H, T, D;
     int32_t in_dtype, st_dtype;
+    int32_t rope;                      // 1: rotate K at its positions (rotary embedding)
     int32_t fill[kMaxRowsPerLaunch];   // first slot written, per row
+    double inv_freq[kMaxRopePairs];    // rotary frequencies of pairs (i, i + D/2), i < D/2
+};
+
+// ---------------------------------------------------------------------------
+// Rotary embedding of a [rows][H][T][D] tensor in place, row b's position t at
+// pos0[b] + t (the queries of a chunk).
+// ---------------------------------------------------------------------------
+struct RopeArgs {
+    void* x;                 // chunk base for row `row0` (element type = dtype)
+    int32_t rows, H, T, D;
+    int32_t dtype;
+    int32_t pos0[kMaxRowsPerLaunch];
+    double inv_freq[kMaxRopePairs];
 };
 
 // ---------------------------------------------------------------------------
@@ -96,6 +112,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 // Decode work-group k's slice of the key axis starts at decode_slice_begin(a, k);
 // key x lies in work-group decode_slice_of(a, x)'s slice.
 __host__ __device__ inline int64_t decode_slice_begin(const DecodeArgs& a, int64_t k) {

@@ -36,8 +36,8 @@ OK = 0
 ERR_ARG, ERR_CAPACITY, ERR_STATE, ERR_DTYPE = -1, -2, -3, -4
 ERR_STORAGE, ERR_HIP, ERR_NOMEM, ERR_UNSUPPORTED = -5, -6, -7, -8
 
-EXPORTED = ("kvc_create", "kvc_destroy", "kvc_append", "kvc_attend", "kvc_seq_len",
-            "kvc_truncate", "kvc_nbytes", "kvc_strerror")
+EXPORTED = ("kvc_create", "kvc_destroy", "kvc_append", "kvc_append_rope", "kvc_rope_q", "kvc_attend",
+            "kvc_seq_len", "kvc_truncate", "kvc_nbytes", "kvc_strerror")
 
 
 class KVCConfig(ctypes.Structure):
@@ -53,6 +53,10 @@ _lib.kvc_destroy.argtypes = [_vp]
 _lib.kvc_destroy.restype = None
 _lib.kvc_append.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _vp]
 _lib.kvc_append.restype = ctypes.c_int
+_lib.kvc_append_rope.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, ctypes.c_double, _vp]
+_lib.kvc_append_rope.restype = ctypes.c_int
+_lib.kvc_rope_q.argtypes = [_vp, _i32, _vp, _i32, _i32, ctypes.c_double, _vp]
+_lib.kvc_rope_q.restype = ctypes.c_int
 _lib.kvc_attend.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp, _vp]
 _lib.kvc_attend.restype = ctypes.c_int
 _lib.kvc_seq_len.argtypes = [_vp, _i32, ctypes.POINTER(_i64)]
@@ -178,16 +182,30 @@ class KVCache:
         return self._h
 
     # -- the contract --
-    def append(self, layer: int, k_new, v_new, stream=None) -> None:
+    def append(self, layer: int, k_new, v_new, stream=None, rope_base: Optional[float] = None) -> None:
         """Store k_new, v_new [B, H_kv, T, d_h] (device, contiguous) at slots
-        [fill, fill + T) of `layer`, rounded to the storage dtype."""
+        [fill, fill + T) of `layer`, rounded to the storage dtype. With
+        rope_base, K is stored rotated at its positions (kvc_append_rope)."""
         self._check_chunk(k_new, self.n_kv_heads, "k_new")
         self._check_chunk(v_new, self.n_kv_heads, "v_new")
         if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
             raise KVCArgumentError(ERR_ARG, "k_new and v_new differ in shape or dtype")
-        _check(_lib.kvc_append(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
-                               DTYPE_CODES[dtype_name(k_new)], int(k_new.shape[2]), _stream_ptr(stream)),
-               "kvc_append")
+        if rope_base is None:
+            _check(_lib.kvc_append(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
+                                   DTYPE_CODES[dtype_name(k_new)], int(k_new.shape[2]), _stream_ptr(stream)),
+                   "kvc_append")
+        else:
+            _check(_lib.kvc_append_rope(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
+                                        DTYPE_CODES[dtype_name(k_new)], int(k_new.shape[2]), float(rope_base),
+                                        _stream_ptr(stream)), "kvc_append_rope")
+
+    def rope_q(self, layer: int, q, rope_base: float, stream=None):
+        """Rotate q [B, H_q, T, d_h] (device, contiguous) in place at the
+        positions the next attend of `layer` gives the chunk; returns q."""
+        self._check_chunk(q, self.n_q_heads, "q")
+        _check(_lib.kvc_rope_q(self._h, int(layer), q.data_ptr(), DTYPE_CODES[dtype_name(q)], int(q.shape[2]),
+                               float(rope_base), _stream_ptr(stream)), "kvc_rope_q")
+        return q
 
     def attend(self, layer: int, q, out=None, stream=None):
         """softmax(q K^T / sqrt(d_h)) V over everything `layer` holds, with the

@@ -15,5 +15,8 @@ from .kvc_oracle import (  # noqa: F401
     round_bf16_bits,
     round_f16_bits,
     round_to_storage,
+    rope_freqs,
+    rope_rotate,
+    rope_rotate64,
     storage_bits,
 )

@@ -31,6 +31,14 @@ What it computes, and where the pages define it:
   ("KV cache, ...", section 2.4).
 * nbytes = 2 L B H_kv max_len d_h itemsize ("KV cache, ...", section 2.5;
   "Heads, GQA and K/V cache", "Memory and the window limit").
+* append_rope / rope_rotate: keys stored after the rotary embedding at their
+  absolute positions ("Generation and the KV Cache", "What the cache
+  stores": K is stored after RoPE; "kv-cache-decoding", "Position
+  information with a cache": a query and a key are rotated by angles of
+  their absolute positions, so scores depend only on the distance). The
+  pages leave the variant open; the reading here pairs element i with
+  i + d_h/2, frequency base^(-2i/d_h), computed in float64 and rounded to
+  float32 before the storage rounding.
 
 Readings where the pages are silent (each one is listed with its reason in the
 design notes of the repository):
@@ -135,6 +143,27 @@ def storage_bits(values_f32: np.ndarray, dtype: str) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Mask and byte count, as closed forms.
 # ---------------------------------------------------------------------------
+
+def rope_freqs(d_head: int, base: float) -> np.ndarray:
+    """Frequencies of the rotary pairs (i, i + d_head/2): base^(-2i / d_head)."""
+    return np.float64(base) ** (-2.0 * np.arange(d_head // 2) / d_head)
+
+
+def rope_rotate64(x: np.ndarray, positions: np.ndarray, base: float) -> np.ndarray:
+    """Rotate head vectors x [..., T, d_head] at positions [..., T] (broadcast):
+    each pair (x_i, x_{i + d/2}) turns by the angle position * f_i. float64."""
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
+    ang = np.asarray(positions, dtype=np.int64).astype(np.float64)[..., None] * rope_freqs(x.shape[-1], base)
+    c, sn = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * sn, x2 * c + x1 * sn], axis=-1)
+
+
+def rope_rotate(x: np.ndarray, positions: np.ndarray, base: float) -> np.ndarray:
+    """rope_rotate64 rounded to float32 (round to nearest even)."""
+    return rope_rotate64(x, positions, base).astype(np.float32)
+
 
 def causal_mask(T: int, n_keys: int, q_offset: int) -> np.ndarray:
     """Boolean [T, n_keys]: query i (absolute position q_offset + i) may see key j
@@ -246,6 +275,28 @@ class OracleCache:
             self.K[layer, b, :, fb:fb + T] = kr[b]
             self.V[layer, b, :, fb:fb + T] = vr[b]
         self.fill[layer] += T
+
+    def append_rope(self, layer: int, k_new: np.ndarray, v_new: np.ndarray, base: float) -> None:
+        """append with the keys rotated at their slots fill + t first."""
+        k_new = np.asarray(k_new)
+        if k_new.ndim != 4 or k_new.shape[:2] != (self.B, self.Hkv):
+            raise OracleError(f"k/v must be [B={self.B}, H_kv={self.Hkv}, T, d_h={self.D}]")
+        if not (np.isfinite(base) and base > 0):
+            raise OracleError("rope base must be finite and positive")
+        T = k_new.shape[2]
+        pos = self.fill[layer][:, None, None] + np.arange(T)[None, None, :]        # [B, 1, T]
+        self.append(layer, rope_rotate(k_new.astype(np.float32), pos, base), v_new)
+
+    def rope_query(self, layer: int, q: np.ndarray, base: float, q_dtype: str = "fp32") -> np.ndarray:
+        """q [B, H_q, T, d_h] rotated at the positions the next attend of
+        `layer` gives it (s_b + t, s_b = fill - T), rounded to float32 and then
+        to q_dtype. Returns float32 values."""
+        q = np.asarray(q, dtype=np.float32)
+        T = q.shape[2]
+        if (self.fill[layer] < T).any():
+            raise OracleError("rope_query needs the chunk appended first (fill >= T)")
+        pos = (self.fill[layer] - T)[:, None, None] + np.arange(T)[None, None, :]
+        return round_to_storage(rope_rotate(q, pos, base), q_dtype)
 
     # -- attend (the plain definition) --------------------------------------
 

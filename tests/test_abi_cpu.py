@@ -123,6 +123,29 @@ def test_append_and_attend_reject_before_any_launch(kvc):
         lib.kvc_destroy(h)
 
 
+def test_rope_calls_reject_before_any_launch(kvc):
+    rc, h = _create(kvc, L=2, B=3, Hq=4, Hkv=2, D=32, max_len=8, dtype=2)
+    assert rc == kvc.OK
+    lib = kvc.lib()
+    p = _BASE
+    try:
+        for base in (0.0, -10.0, float("inf"), float("nan")):
+            assert lib.kvc_append_rope(h, 0, p, p, 0, 1, base, None) == kvc.ERR_ARG
+            assert lib.kvc_rope_q(h, 0, p, 0, 1, base, None) == kvc.ERR_ARG
+        assert lib.kvc_append_rope(h, 2, p, p, 0, 1, 1e4, None) == kvc.ERR_ARG       # layer out of range
+        assert lib.kvc_append_rope(h, 0, p, p, 0, 9, 1e4, None) == kvc.ERR_CAPACITY
+        assert lib.kvc_append_rope(h, 0, p, p, 7, 1, 1e4, None) == kvc.ERR_DTYPE
+        assert lib.kvc_rope_q(h, 0, p, 2, 1, 1e4, None) == kvc.ERR_STATE             # nothing appended yet
+        assert lib.kvc_rope_q(h, 0, None, 2, 1, 1e4, None) == kvc.ERR_ARG
+        assert lib.kvc_rope_q(h, 0, p + 2, 2, 1, 1e4, None) == kvc.ERR_ARG           # misaligned
+        assert lib.kvc_rope_q(h, 0, p, 2, 0, 1e4, None) == kvc.ERR_ARG               # T < 1
+        assert lib.kvc_rope_q(None, 0, p, 2, 1, 1e4, None) == kvc.ERR_ARG
+        lens = (ctypes.c_int64 * 3)()
+        assert lib.kvc_seq_len(h, 0, lens) == kvc.OK and list(lens) == [0, 0, 0]
+    finally:
+        lib.kvc_destroy(h)
+
+
 def test_null_handles(kvc):
     lib = kvc.lib()
     lens = (ctypes.c_int64 * 1)()

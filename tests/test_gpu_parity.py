@@ -367,3 +367,80 @@ def test_chunked_prefill_bf16_full_size():
         assert rel <= HALF_REL_FROB, (n, rel)
         assert np.isfinite(got).all()
     log(f"  worst rel {worst:.3e}")
+
+
+def _ulp_gap(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in representable steps between equal-signed stored values."""
+    return np.abs(a_bits.astype(np.int64) - b_bits.astype(np.int64))
+
+
+@pytest.mark.parametrize("st", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_append_rope_and_rope_q(st, D):
+    """Keys stored rotated at per-row positions (fills 2000, 1 and 777, then
+    chunks of 1, 5 and 16), values unrotated, queries rotated in place; against
+    the oracle's append_rope / rope_query. Both sides compute the rotation in
+    float64 with the same operation order and round to float32 and then to
+    the storage type, so the stored bits agree except where the two sine and
+    cosine implementations round an angle differently and the float32 result
+    lands on the other side of a rounding boundary: at most one storage step,
+    and rare (asserted below 1 in 10^4 elements). Attention of rotated queries
+    over the rotated keys is then held to the usual bound."""
+    from oracle import storage_bits
+    import torch
+    log(f"rope append/q st={st} D={D}")
+    rng = np.random.default_rng(800 + D)
+    B, Hq, Hkv, max_len, base = 3, 4, 2, 2100, 10000.0
+    cache, orc = _new((1, B, Hq, Hkv, D, max_len), st)
+    k0, v0 = (rng.standard_normal((B, Hkv, 2000, D), dtype=np.float32) for _ in range(2))
+    cache.append(0, to_device(k0, "fp32", DEV), to_device(v0, "fp32", DEV))
+    orc.append(0, k0, v0)
+    lens = np.array([2000, 1, 777])
+    cache.truncate(lens)
+    orc.truncate(lens)
+    q_in = "fp32" if st == "fp32" else st
+    for T in (1, 5, 16):
+        k, v, q = (rng.standard_normal(s, dtype=np.float32) for s in ((B, Hkv, T, D), (B, Hkv, T, D), (B, Hq, T, D)))
+        f0 = orc.seq_len(0).copy()
+        cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV), rope_base=base)
+        orc.append_rope(0, k, v, base)
+        qd = to_device(q, q_in, DEV)
+        cache.rope_q(0, qd, base)
+        qr_ref = orc.rope_query(0, input_values(q, q_in), base, q_in)
+        torch.cuda.synchronize()
+        kb, vb = gpu_bits(cache.k_storage), gpu_bits(cache.v_storage)
+        ko, vo = storage_bits(orc.K, st), storage_bits(orc.V, st)
+        for b in range(B):
+            sl = (0, b, slice(None), slice(int(f0[b]), int(f0[b]) + T))
+            gap = _ulp_gap(kb[sl], ko[sl])
+            assert gap.max() <= 1 and (gap > 0).mean() <= 1e-4, (b, T, gap.max(), (gap > 0).mean())
+            assert np.array_equal(vb[sl], vo[sl])
+        qgap = _ulp_gap(gpu_bits(qd), storage_bits(qr_ref, q_in))
+        assert qgap.max() <= 1 and (qgap > 0).mean() <= 1e-4
+        got = cache.attend(0, qd).cpu().numpy()
+        want = orc.attend(0, np.asarray(qr_ref, dtype=np.float32))
+        mabs, rel = compare_out(got, want, st)
+        log(f"  T={T}: key steps off {int((gap > 0).sum())}, attention rel {rel:.2e} abs {mabs:.2e}")
+        if st == "fp32":
+            assert mabs <= FP32_MAX_ABS
+        else:
+            assert rel <= HALF_REL_FROB
+
+
+def test_append_rope_at_large_positions():
+    """Positions 32760..32775 (angles up to 3.3e4 rad at the first frequency):
+    the float64 angle keeps the rotation exact to float32 rounding."""
+    from oracle import storage_bits
+    import torch
+    log("rope at positions near 32768")
+    rng = np.random.default_rng(900)
+    cache, orc = _new((1, 1, 2, 1, 128, 32776), "fp32")
+    k0 = rng.standard_normal((1, 1, 32760, 128), dtype=np.float32)
+    cache.append(0, to_device(k0, "fp32", DEV), to_device(k0, "fp32", DEV))
+    orc.append(0, k0, k0)
+    k = rng.standard_normal((1, 1, 16, 128), dtype=np.float32)
+    cache.append(0, to_device(k, "fp32", DEV), to_device(k, "fp32", DEV), rope_base=500000.0)
+    orc.append_rope(0, k, k, 500000.0)
+    torch.cuda.synchronize()
+    gap = _ulp_gap(gpu_bits(cache.k_storage)[0, 0, 0, 32760:], storage_bits(orc.K, "fp32")[0, 0, 0, 32760:])
+    assert gap.max() <= 1 and (gap > 0).mean() <= 1e-3

@@ -569,3 +569,76 @@ def test_planted_raw_chunk_fails_rounding_pin():
     oc.append(0, k, k)
     want = torch.from_numpy(k).to(torch.float16).float().numpy()
     assert not np.array_equal(oc.K[0, :, :, :3], want)
+
+
+# ---------------------------------------------------------------------------
+# Rotary embedding of stored keys ("Generation and the KV Cache", "What the
+# cache stores"; "kv-cache-decoding", "Position information with a cache")
+# ---------------------------------------------------------------------------
+
+def test_rope_matches_the_complex_rotation():
+    """Pair (x_i, x_{i+d/2}) as the complex number x_i + i x_{i+d/2}, turned by
+    exp(i * position * base^(-2i/d)): a different computation of the same
+    rotation (pins the pairing, the sign and the frequencies)."""
+    from oracle import rope_rotate64
+    rng = np.random.default_rng(21)
+    for d in (4, 32, 128):
+        x = rng.standard_normal((3, 7, d))
+        pos = rng.integers(0, 40000, size=(3, 7))
+        half = d // 2
+        z = x[..., :half] + 1j * x[..., half:]
+        f = np.array([10000.0 ** (-2.0 * i / d) for i in range(half)])
+        w = z * np.exp(1j * pos[..., None] * f)
+        want = np.concatenate([w.real, w.imag], axis=-1)
+        assert np.abs(rope_rotate64(x, pos, 10000.0) - want).max() < 1e-11
+
+
+def test_rope_special_cases_and_invariants():
+    from oracle import rope_freqs, rope_rotate, rope_rotate64
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((2, 5, 64)).astype(np.float32)
+    # position 0 is the identity, exactly (cos 0 = 1, sin 0 = 0)
+    assert np.array_equal(rope_rotate(x, np.zeros((2, 5), np.int64), 500000.0), x)
+    # frequencies: f_0 = 1, f_{d/2-1} = base^(-(d-2)/d); base 10000, d = 4: (1, 1/100)
+    assert rope_freqs(4, 10000.0)[0] == 1.0 and abs(rope_freqs(4, 10000.0)[1] - 0.01) < 1e-17
+    # each pair keeps its length
+    y = rope_rotate64(x, rng.integers(0, 10 ** 6, size=(2, 5)), 10000.0)
+    n_x = x[..., :32].astype(np.float64) ** 2 + x[..., 32:].astype(np.float64) ** 2
+    n_y = y[..., :32] ** 2 + y[..., 32:] ** 2
+    assert np.abs(n_x - n_y).max() < 1e-12
+
+
+def test_rope_scores_depend_only_on_distance():
+    """q at position m and k at position n: q.k is unchanged when both move by
+    the same shift (the pages' reason cached keys never need updating)."""
+    from oracle import rope_rotate64
+    rng = np.random.default_rng(23)
+    q, k = rng.standard_normal((2, 128))
+    for m, n, shift in ((5, 3, 1000), (0, 0, 77), (30000, 12, 999)):
+        a = float(rope_rotate64(q[None], np.array([m]), 10000.0)[0] @ rope_rotate64(k[None], np.array([n]), 10000.0)[0])
+        b = float(rope_rotate64(q[None], np.array([m + shift]), 10000.0)[0] @
+                  rope_rotate64(k[None], np.array([n + shift]), 10000.0)[0])
+        assert abs(a - b) < 1e-9 * max(1.0, abs(a))
+
+
+def test_append_rope_stores_rotated_keys_and_plain_values():
+    """Keys land rotated at their own slots (per-row fills), values unrotated;
+    attention of rotated queries over them equals attention over keys rotated
+    by hand at the same positions."""
+    from oracle import rope_rotate
+    rng = np.random.default_rng(24)
+    oc = OracleCache(1, 2, 4, 2, 32, 40, "fp32")
+    k0, v0 = _rand(rng, 2, 2, 6, 32), _rand(rng, 2, 2, 6, 32)
+    oc.append(0, k0, v0)
+    oc.truncate(np.array([6, 2]))
+    k, v, q = _rand(rng, 2, 2, 3, 32), _rand(rng, 2, 2, 3, 32), _rand(rng, 2, 4, 3, 32)
+    oc.append_rope(0, k, v, 10000.0)
+    for b, s in enumerate((6, 2)):
+        want = rope_rotate(k[b], np.arange(s, s + 3)[None], 10000.0)
+        assert np.array_equal(oc.K[0, b, :, s:s + 3], want)
+        assert np.array_equal(oc.V[0, b, :, s:s + 3], v[b])
+    qr = oc.rope_query(0, q, 10000.0)
+    for b, s in enumerate((6, 2)):
+        assert np.array_equal(qr[b], rope_rotate(q[b], np.arange(s, s + 3)[None], 10000.0))
+    with pytest.raises(OracleError):
+        oc.append_rope(0, k, v, 0.0)
