@@ -21,7 +21,8 @@ workload (B=4, 32 chunks of T=512 up to 16384 keys, bf16, MFMA path: TFLOP/s and
 % of the bf16 matrix peak) and the long-context decode workload (B=8, H_q=64,
 H_kv=8, 32768 cached keys: GB/s for T=1 and T=4 attention calls), and the
 tiny decoder (48-token prompt, 160 greedy steps, attention through the C ABI):
-wall time of the cached and the uncached generation and their work counters.
+wall time of the cached and the uncached generation and their work counters;
+the rotary append and query rotation; and latent-cache appends.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
     python bench.py --pmc-workload      # calibration copy + attention calls, for rocprofv3 --pmc
@@ -283,6 +284,33 @@ def rope_bench():
     return res
 
 
+def latent_bench():
+    """Latent-cache appends (B=32, r=512, d_R=64, bf16): one decode step (T=1)
+    and one prefill chunk (T=512), microseconds per call (HIP events)."""
+    import torch
+    from kv_cached_gqa_amd.kvc import LatentCache
+    b, r, dr = 32, 512, 64
+    dev = torch.device("cuda:0")
+    lc = LatentCache(1, r, dr, 1024, batch=b, dtype="bf16", device=dev)
+    st = torch.cuda.current_stream()
+    res = {"workload": "latent cache append, B=32, r=512, d_R=64, bf16"}
+    for t in (1, 512):
+        c = torch.randn((b, t, r), device=dev, dtype=torch.bfloat16)
+        kr = torch.randn((b, t, dr), device=dev, dtype=torch.bfloat16)
+
+        def step(i):
+            lc.append(0, c, kr)
+            lc.truncate(0)
+
+        for i in range(10):
+            step(i)
+        us = event_time(step, 200, st) * 1e3
+        moved = 2 * b * t * (r + dr) * 2           # read + write, bf16 in and out
+        res[f"T{t}"] = {"us": round(us, 2), "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
+    lc.close()
+    return res
+
+
 def long_ctx_bench():
     """Long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys;
     attention calls with T=1 and T=4 (a draft block) after one append."""
@@ -396,7 +424,8 @@ def main():
     }
     if not args.no_extra:
         rec["extra"] = {"chunked_prefill": prefill_bench(), "long_context_decode": long_ctx_bench(),
-                        "tiny_decoder": tiny_decoder_bench(), "rope": rope_bench()}
+                        "tiny_decoder": tiny_decoder_bench(), "rope": rope_bench(),
+                        "latent_cache": latent_bench()}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(lengths, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -162,6 +162,58 @@ int kvc_truncate(kvc_cache* cache, const int64_t* n, int32_t count);
  * out: host uint64. Errors: KVC_ERR_ARG. */
 int kvc_nbytes(const kvc_cache* cache, uint64_t* out);
 
+/* ---- Latent cache (multi-head latent attention) ---------------------------
+ * One compressed latent c (rank r) and one shared rotary key k_R (d_R) per
+ * position instead of per-head K and V, under the same rules as the K/V cache:
+ * per-layer fill, committed length = min over layers, metadata-only rollback
+ * ("KV cache, incremental decode, ...", section 2.6, LatentCache). */
+typedef struct kvc_latent_config {
+    int32_t n_layers;   /* L */
+    int32_t batch;      /* B */
+    int32_t rank;       /* r: latent width, a multiple of 8 */
+    int32_t rope_dim;   /* d_R: shared rotary key width, a multiple of 8 */
+    int32_t dtype;      /* kvc_dtype of the stored values */
+    int64_t max_len;    /* preallocated positions per row, N_max */
+} kvc_latent_config;
+
+typedef struct kvc_latent kvc_latent;
+
+/* Create a latent-cache handle over caller-owned storage.
+ *  c_store: device [n_layers][batch][max_len][rank] of cfg->dtype, at least
+ *    c_bytes >= that size; kr_store: [n_layers][batch][max_len][rope_dim],
+ *    kr_bytes likewise. Both 16-byte aligned and zero-filled by the caller, who
+ *    keeps ownership for the life of the handle. Every fill starts at 0.
+ * Errors: KVC_ERR_ARG (null cfg/out, nonpositive dims, rank or rope_dim not a
+ * multiple of 8 or below 8, max_len * width >= 2^31), KVC_ERR_DTYPE,
+ * KVC_ERR_STORAGE, KVC_ERR_NOMEM. No device work. */
+int kvc_latent_create(const kvc_latent_config* cfg, void* c_store, void* kr_store, uint64_t c_bytes,
+                      uint64_t kr_bytes, kvc_latent** out);
+
+/* Free the handle (never the caller's storage). NULL is a no-op. */
+void kvc_latent_destroy(kvc_latent* cache);
+
+/* Append T positions to one layer: c_new device [batch][T][rank], kr_new
+ * [batch][T][rope_dim], both of in_dtype and 16-byte aligned; row b's chunk
+ * goes to slots [fill[layer][b], + T), rounded to the storage dtype (nearest
+ * even, as kvc_append), then fill[layer][b] += T. Inputs are copied.
+ * Errors: KVC_ERR_ARG (null, layer out of range, T < 1, misaligned),
+ * KVC_ERR_DTYPE, KVC_ERR_CAPACITY (fill + T > max_len), KVC_ERR_HIP. */
+int kvc_latent_append(kvc_latent* cache, int32_t layer, const void* c_new, const void* kr_new,
+                      int32_t in_dtype, int32_t T, void* stream);
+
+/* Per-row lengths: layer -1 = committed (min over layers), else that layer's
+ * fill. out_lens: host int64 [batch]. Errors: KVC_ERR_ARG. */
+int kvc_latent_seq_len(const kvc_latent* cache, int32_t layer, int64_t* out_lens);
+
+/* Set every layer's fill of each row to n (count 1: all rows; count = batch:
+ * per row), 0 <= n_b <= committed length. Metadata only.
+ * Errors: KVC_ERR_ARG (null, count), KVC_ERR_STATE (n out of range). */
+int kvc_latent_truncate(kvc_latent* cache, const int64_t* n, int32_t count);
+
+/* Storage bytes, L * B * N_max * (r + d_R) * itemsize ("KV cache, ...",
+ * section 2.6). out: host uint64. Errors: KVC_ERR_ARG. */
+int kvc_latent_nbytes(const kvc_latent* cache, uint64_t* out);
+
 /* A static, human-readable text for a kvc_status code. */
 const char* kvc_strerror(int status);
 

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libkvc.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 ARCH = "gfx950"
-SOURCES = ["kvc_api.cpp", "kvc_append.hip", "kvc_decode.hip", "kvc_prefill.hip"]
+SOURCES = ["kvc_api.cpp", "kvc_latent.cpp", "kvc_append.hip", "kvc_decode.hip", "kvc_prefill.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

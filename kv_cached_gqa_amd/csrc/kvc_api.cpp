@@ -200,6 +200,7 @@ int append_impl(kvc_cache* c, int32_t layer, const void* k_new, const void* v_ne
         a.in_dtype = in_dtype;
         a.st_dtype = cf.dtype;
         a.rope = rope_base > 0.0 ? 1 : 0;
+        a.n_tensors = 2;
         if (a.rope) rope_freqs(rope_base, cf.d_head, a.inv_freq);
         for (int b = 0; b < a.rows; ++b) a.fill[b] = static_cast<int32_t>(f[row0 + b]);
         if (kvc::launch_append(a, s) != hipSuccess) return KVC_ERR_HIP;

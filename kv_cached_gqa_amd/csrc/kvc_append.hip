@@ -115,7 +115,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
     int64_t blocks = (n_vec + 255) / 256;
     if (blocks > 8192) blocks = 8192;   // grid-stride beyond this
     if (blocks < 1) blocks = 1;
-    dim3 grid(static_cast<unsigned>(blocks), 2);
+    dim3 grid(static_cast<unsigned>(blocks), a.n_tensors == 1 ? 1 : 2);
     switch (a.in_dtype) {
         case F32: return dispatch_st<F32>(a, grid, s);
         case F16: return dispatch_st<F16>(a, grid, s);

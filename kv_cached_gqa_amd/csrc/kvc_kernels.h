@@ -39,6 +39,7 @@ struct AppendArgs {
     int32_t rows, H, T, D;
     int32_t in_dtype, st_dtype;
     int32_t rope;                      // 1: rotate K at its positions (rotary embedding)
+    int32_t n_tensors;                 // 2: K and V; 1: the first tensor only (k_in -> k_cache)
     int32_t fill[kMaxRowsPerLaunch];   // first slot written, per row
     double inv_freq[kMaxRopePairs];    // rotary frequencies of pairs (i, i + D/2), i < D/2
 };

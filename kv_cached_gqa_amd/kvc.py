@@ -37,7 +37,9 @@ ERR_ARG, ERR_CAPACITY, ERR_STATE, ERR_DTYPE = -1, -2, -3, -4
 ERR_STORAGE, ERR_HIP, ERR_NOMEM, ERR_UNSUPPORTED = -5, -6, -7, -8
 
 EXPORTED = ("kvc_create", "kvc_destroy", "kvc_append", "kvc_append_rope", "kvc_rope_q", "kvc_attend",
-            "kvc_seq_len", "kvc_truncate", "kvc_nbytes", "kvc_strerror")
+            "kvc_seq_len", "kvc_truncate", "kvc_nbytes", "kvc_strerror",
+            "kvc_latent_create", "kvc_latent_destroy", "kvc_latent_append", "kvc_latent_seq_len",
+            "kvc_latent_truncate", "kvc_latent_nbytes")
 
 
 class KVCConfig(ctypes.Structure):
@@ -65,6 +67,18 @@ _lib.kvc_truncate.argtypes = [_vp, ctypes.POINTER(_i64), _i32]
 _lib.kvc_truncate.restype = ctypes.c_int
 _lib.kvc_nbytes.argtypes = [_vp, ctypes.POINTER(_u64)]
 _lib.kvc_nbytes.restype = ctypes.c_int
+_lib.kvc_latent_create.argtypes = [_vp, _vp, _vp, _u64, _u64, ctypes.POINTER(_vp)]
+_lib.kvc_latent_create.restype = ctypes.c_int
+_lib.kvc_latent_destroy.argtypes = [_vp]
+_lib.kvc_latent_destroy.restype = None
+_lib.kvc_latent_append.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _vp]
+_lib.kvc_latent_append.restype = ctypes.c_int
+_lib.kvc_latent_seq_len.argtypes = [_vp, _i32, ctypes.POINTER(_i64)]
+_lib.kvc_latent_seq_len.restype = ctypes.c_int
+_lib.kvc_latent_truncate.argtypes = [_vp, ctypes.POINTER(_i64), _i32]
+_lib.kvc_latent_truncate.restype = ctypes.c_int
+_lib.kvc_latent_nbytes.argtypes = [_vp, ctypes.POINTER(_u64)]
+_lib.kvc_latent_nbytes.restype = ctypes.c_int
 _lib.kvc_strerror.argtypes = [ctypes.c_int]
 _lib.kvc_strerror.restype = ctypes.c_char_p
 
@@ -262,6 +276,78 @@ class KVCache:
                                             f"got {tuple(t.shape)}")
         if not t.is_contiguous() or t.device != self.k_storage.device:
             raise KVCArgumentError(ERR_ARG, f"{name} must be contiguous and on {self.k_storage.device}")
+
+
+class KVCLatentConfig(ctypes.Structure):
+    _fields_ = [("n_layers", _i32), ("batch", _i32), ("rank", _i32), ("rope_dim", _i32), ("dtype", _i32),
+                ("max_len", _i64)]
+
+
+class LatentCache:
+    """Latent cache of multi-head latent attention ("KV cache, incremental
+    decode, ...", section 2.6): zero-filled device storage c (L, B, max_len, r)
+    and k_rope (L, B, max_len, d_R) and a libkvc handle over it, with the K/V
+    cache's rules (per-layer fill, committed length, truncate)."""
+
+    def __init__(self, n_layers: int, rank: int, rope_dim: int, max_len: int, batch: int = 1,
+                 dtype: str = "fp32", device=None):
+        torch = _torch()
+        if dtype not in DTYPE_CODES:
+            raise KVCArgumentError(ERR_DTYPE, f"dtype {dtype!r}")
+        self.n_layers, self.batch, self.max_len = int(n_layers), int(batch), int(max_len)
+        self.rank, self.rope_dim, self.dtype = int(rank), int(rope_dim), dtype
+        self.device = torch.device(device if device is not None else "cuda")
+        tdt = torch_dtype(dtype)
+        self.c_storage = torch.zeros((self.n_layers, self.batch, self.max_len, self.rank), dtype=tdt,
+                                     device=self.device)
+        self.kr_storage = torch.zeros((self.n_layers, self.batch, self.max_len, self.rope_dim), dtype=tdt,
+                                      device=self.device)
+        cfg = KVCLatentConfig(self.n_layers, self.batch, self.rank, self.rope_dim, DTYPE_CODES[dtype], self.max_len)
+        h = _vp()
+        nb = lambda t: t.numel() * t.element_size()  # noqa: E731
+        _check(_lib.kvc_latent_create(ctypes.byref(cfg), self.c_storage.data_ptr(), self.kr_storage.data_ptr(),
+                                      nb(self.c_storage), nb(self.kr_storage), ctypes.byref(h)), "kvc_latent_create")
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _lib.kvc_latent_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def append(self, layer: int, c_new, kr_new, stream=None) -> None:
+        """Store c_new [B, T, r] and kr_new [B, T, d_R] (device, contiguous, one
+        dtype) at slots [fill, fill + T) of `layer`, rounded to the storage dtype."""
+        for t, w, name in ((c_new, self.rank, "c_new"), (kr_new, self.rope_dim, "kr_new")):
+            if t.dim() != 3 or t.shape[0] != self.batch or t.shape[2] != w:
+                raise KVCArgumentError(ERR_ARG, f"{name} must be [B={self.batch}, T, {w}], got {tuple(t.shape)}")
+            if not t.is_contiguous() or t.device != self.c_storage.device:
+                raise KVCArgumentError(ERR_ARG, f"{name} must be contiguous and on {self.c_storage.device}")
+        if c_new.shape[1] != kr_new.shape[1] or c_new.dtype != kr_new.dtype:
+            raise KVCArgumentError(ERR_ARG, "c_new and kr_new differ in T or dtype")
+        _check(_lib.kvc_latent_append(self._h, int(layer), c_new.data_ptr(), kr_new.data_ptr(),
+                                      DTYPE_CODES[dtype_name(c_new)], int(c_new.shape[1]), _stream_ptr(stream)),
+               "kvc_latent_append")
+
+    def seq_len(self, layer: Optional[int] = None) -> np.ndarray:
+        out = (_i64 * self.batch)()
+        _check(_lib.kvc_latent_seq_len(self._h, -1 if layer is None else int(layer), out), "kvc_latent_seq_len")
+        return np.frombuffer(out, dtype=np.int64).copy()
+
+    def truncate(self, n) -> None:
+        arr = np.ascontiguousarray(np.atleast_1d(np.asarray(n, dtype=np.int64)))
+        _check(_lib.kvc_latent_truncate(self._h, arr.ctypes.data_as(ctypes.POINTER(_i64)), int(arr.size)),
+               "kvc_latent_truncate")
+
+    def nbytes(self) -> int:
+        out = _u64()
+        _check(_lib.kvc_latent_nbytes(self._h, ctypes.byref(out)), "kvc_latent_nbytes")
+        return int(out.value)
 
 
 def exported_symbols(names: Sequence[str] = EXPORTED) -> dict:

@@ -7,6 +7,7 @@ from .kvc_oracle import (  # noqa: F401
     DTYPES,
     OracleCache,
     OracleError,
+    OracleLatentCache,
     OracleCapacityError,
     bf16_bits_to_f32,
     causal_mask,

@@ -364,3 +364,56 @@ class OracleCache:
     def stored_bits(self, which: str = "K") -> np.ndarray:
         arr = self.K if which == "K" else self.V
         return storage_bits(arr, self.dtype)
+
+
+class OracleLatentCache:
+    """The latent cache of multi-head latent attention ("KV cache, incremental
+    decode, ...", section 2.6): one latent c (rank r) and one shared rotary key
+    k_R (d_R) per position, under the K/V cache's rules (per-layer fill,
+    committed length = min over layers, metadata-only truncate). Storage
+    C (L, B, max_len, r) and KR (L, B, max_len, d_R) holds the values rounded
+    to the storage dtype (as float32), zero before anything is written."""
+
+    def __init__(self, n_layers: int, batch: int, rank: int, rope_dim: int, max_len: int, dtype: str):
+        if dtype not in DTYPES:
+            raise OracleError(f"dtype {dtype!r}")
+        if min(n_layers, batch, rank, rope_dim, max_len) < 1:
+            raise OracleError("dimensions must be positive")
+        self.L, self.B, self.r, self.dR, self.max_len, self.dtype = n_layers, batch, rank, rope_dim, max_len, dtype
+        self.C = np.zeros((n_layers, batch, max_len, rank), np.float32)
+        self.KR = np.zeros((n_layers, batch, max_len, rope_dim), np.float32)
+        self.fill = np.zeros((n_layers, batch), np.int64)
+
+    def seq_len(self, layer: int = -1) -> np.ndarray:
+        return self.fill.min(axis=0).copy() if layer < 0 else self.fill[layer].copy()
+
+    def append(self, layer: int, c_new: np.ndarray, kr_new: np.ndarray) -> None:
+        """c_new [B, T, r], kr_new [B, T, d_R] (float32 values) at slots
+        [fill, fill + T) of `layer`, rounded; nothing changes on an error."""
+        if not 0 <= layer < self.L:
+            raise OracleError(f"layer {layer} out of range")
+        c_new, kr_new = np.asarray(c_new), np.asarray(kr_new)
+        if c_new.shape[:1] != (self.B,) or c_new.ndim != 3 or c_new.shape[2] != self.r \
+                or kr_new.shape != (self.B, c_new.shape[1], self.dR):
+            raise OracleError(f"c_new [B={self.B}, T, {self.r}] and kr_new [B, T, {self.dR}] expected")
+        T = c_new.shape[1]
+        if T < 1:
+            raise OracleError("T must be at least 1")
+        if (self.fill[layer] + T > self.max_len).any():
+            raise OracleCapacityError("append would run past max_len")
+        cr = round_to_storage(c_new.astype(np.float32), self.dtype)
+        kr = round_to_storage(kr_new.astype(np.float32), self.dtype)
+        for b in range(self.B):
+            f = int(self.fill[layer, b])
+            self.C[layer, b, f:f + T] = cr[b]
+            self.KR[layer, b, f:f + T] = kr[b]
+        self.fill[layer] += T
+
+    def truncate(self, n) -> None:
+        n = np.broadcast_to(np.asarray(n, dtype=np.int64), (self.B,))
+        if (n < 0).any() or (n > self.seq_len()).any():
+            raise OracleError("truncate needs 0 <= n <= committed length")
+        self.fill[:] = n[None, :]
+
+    def nbytes(self) -> int:
+        return self.L * self.B * self.max_len * (self.r + self.dR) * _ITEMSIZE[self.dtype]

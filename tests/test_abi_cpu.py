@@ -168,3 +168,53 @@ def test_nbytes_matches_page_figures(kvc):
     assert kvc.lib().kvc_nbytes(h, ctypes.byref(nb)) == kvc.OK
     assert nb.value == 262144
     kvc.lib().kvc_destroy(h)
+
+
+def _latent_create(kvc, L=2, B=3, r=64, dR=16, max_len=8, dtype=2, c_bytes=None, kr_bytes=None, base=None):
+    lib = kvc.lib()
+    cfg = kvc.KVCLatentConfig(L, B, r, dR, dtype, max_len)
+    item = 4 if dtype == 0 else 2
+    cb = c_bytes if c_bytes is not None else L * B * max_len * r * item
+    kb = kr_bytes if kr_bytes is not None else L * B * max_len * dR * item
+    h = ctypes.c_void_p()
+    p = _BASE if base is None else base
+    rc = lib.kvc_latent_create(ctypes.byref(cfg), p, p, cb, kb, ctypes.byref(h))
+    return rc, h
+
+
+def test_latent_cache_abi(kvc):
+    """Creation checks, nbytes = L B N_max (r + d_R) itemsize ("KV cache, ...",
+    section 2.6), per-layer lengths, truncate bounds, append errors before any
+    launch."""
+    lib = kvc.lib()
+    assert _latent_create(kvc, r=60)[0] == kvc.ERR_ARG            # not a multiple of 8
+    assert _latent_create(kvc, dR=0)[0] == kvc.ERR_ARG
+    assert _latent_create(kvc, dtype=9)[0] == kvc.ERR_DTYPE
+    assert _latent_create(kvc, c_bytes=10)[0] == kvc.ERR_STORAGE
+    assert _latent_create(kvc, base=_BASE + 4)[0] == kvc.ERR_STORAGE
+    rc, h = _latent_create(kvc, L=60, B=1, r=512, dR=64, max_len=4096, dtype=1)
+    assert rc == kvc.OK
+    nb = ctypes.c_uint64()
+    assert lib.kvc_latent_nbytes(h, ctypes.byref(nb)) == kvc.OK and nb.value == 283115520
+    lib.kvc_latent_destroy(h)
+    rc, h = _latent_create(kvc)
+    assert rc == kvc.OK
+    p = _BASE
+    try:
+        assert lib.kvc_latent_append(h, 2, p, p, 0, 1, None) == kvc.ERR_ARG       # layer out of range
+        assert lib.kvc_latent_append(h, 0, p, p, 0, 0, None) == kvc.ERR_ARG       # T < 1
+        assert lib.kvc_latent_append(h, 0, p + 4, p, 0, 1, None) == kvc.ERR_ARG   # misaligned
+        assert lib.kvc_latent_append(h, 0, p, p, 6, 1, None) == kvc.ERR_DTYPE
+        assert lib.kvc_latent_append(h, 0, p, p, 0, 9, None) == kvc.ERR_CAPACITY
+        lens = (ctypes.c_int64 * 3)()
+        assert lib.kvc_latent_seq_len(h, -1, lens) == kvc.OK and list(lens) == [0, 0, 0]
+        assert lib.kvc_latent_seq_len(h, 2, lens) == kvc.ERR_ARG
+        one = (ctypes.c_int64 * 1)(1)
+        assert lib.kvc_latent_truncate(h, one, 1) == kvc.ERR_STATE                # beyond the committed length
+        zero = (ctypes.c_int64 * 1)(0)
+        assert lib.kvc_latent_truncate(h, zero, 1) == kvc.OK
+        assert lib.kvc_latent_truncate(h, zero, 2) == kvc.ERR_ARG                 # count neither 1 nor B
+        assert lib.kvc_latent_nbytes(None, ctypes.byref(nb)) == kvc.ERR_ARG
+    finally:
+        lib.kvc_latent_destroy(h)
+    lib.kvc_latent_destroy(None)

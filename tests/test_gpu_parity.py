@@ -444,3 +444,41 @@ def test_append_rope_at_large_positions():
     torch.cuda.synchronize()
     gap = _ulp_gap(gpu_bits(cache.k_storage)[0, 0, 0, 32760:], storage_bits(orc.K, "fp32")[0, 0, 0, 32760:])
     assert gap.max() <= 1 and (gap > 0).mean() <= 1e-3
+
+
+@pytest.mark.parametrize("st", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("inp", ["fp32", "bf16"])
+def test_latent_cache_append_bit_exact(st, inp):
+    """The latent cache ("KV cache, incremental decode, ...", section 2.6):
+    latents (r = 512) and rotary keys (d_R = 64) with edge values, chunks of
+    1, 7 and 33 positions over 3 layers, a per-row rollback and fresh chunks;
+    storage bits, fills and nbytes equal the oracle's. Also B = 300 (two
+    launches of rows)."""
+    from oracle import OracleLatentCache, storage_bits
+    from kv_cached_gqa_amd.kvc import LatentCache
+    import torch
+    log(f"latent cache st={st} in={inp}")
+    rng = np.random.default_rng(1000)
+    for (L, B, r, dR, max_len) in ((3, 3, 512, 64, 64), (1, 300, 32, 8, 12)):
+        lc = LatentCache(L, r, dR, max_len, batch=B, dtype=st, device=DEV)
+        orc = OracleLatentCache(L, B, r, dR, max_len, st)
+        steps = (1, 7, 33) if max_len == 64 else (1, 3)
+        for T in steps:
+            for layer in range(L):
+                c = _edge_values(rng, B * T * r)[:B * T * r].reshape(B, T, r).astype(np.float32)
+                kr = _edge_values(rng, B * T * dR)[:B * T * dR].reshape(B, T, dR).astype(np.float32)
+                lc.append(layer, to_device(c, inp, DEV), to_device(kr, inp, DEV))
+                orc.append(layer, input_values(c, inp), input_values(kr, inp))
+        n = rng.integers(0, int(orc.seq_len()[0]) + 1, size=B)
+        lc.truncate(n)
+        orc.truncate(n)
+        for layer in range(L):
+            c, kr = (rng.standard_normal((B, 2, w), dtype=np.float32) for w in (r, dR))
+            lc.append(layer, to_device(c, inp, DEV), to_device(kr, inp, DEV))
+            orc.append(layer, input_values(c, inp), input_values(kr, inp))
+        torch.cuda.synchronize()
+        assert np.array_equal(gpu_bits(lc.c_storage), storage_bits(orc.C, st))
+        assert np.array_equal(gpu_bits(lc.kr_storage), storage_bits(orc.KR, st))
+        assert np.array_equal(lc.seq_len(), orc.seq_len())
+        assert lc.nbytes() == orc.nbytes()
+        lc.close()

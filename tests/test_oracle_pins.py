@@ -642,3 +642,56 @@ def test_append_rope_stores_rotated_keys_and_plain_values():
         assert np.array_equal(qr[b], rope_rotate(q[b], np.arange(s, s + 3)[None], 10000.0))
     with pytest.raises(OracleError):
         oc.append_rope(0, k, v, 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Latent cache ("KV cache, incremental decode, ...", section 2.6: LatentCache
+# follows the same rules on [B, T, r] and [B, T, d_R] chunks; nbytes
+# L B N_max (r + d_R) itemsize)
+# ---------------------------------------------------------------------------
+
+def test_latent_cache_nbytes_closed_form():
+    from oracle import OracleLatentCache
+    # 60 layers, one row, 4096 positions, r = 512, d_R = 64, fp16:
+    # 60 * 4096 * 576 * 2 = 283,115,520 bytes, worked by hand from the formula
+    assert OracleLatentCache(60, 1, 512, 64, 4096, "fp16").nbytes() == 283115520
+    # against the K/V cache of the same positions: (r + d_R) in place of 2 H_kv d_h
+    oc = OracleCache(60, 1, 128, 128, 128, 4096, "fp16")
+    assert oc.nbytes() / OracleLatentCache(60, 1, 512, 64, 4096, "fp16").nbytes() == (2 * 128 * 128) / 576
+
+
+def test_latent_cache_follows_the_cache_rules():
+    """Per-layer fill with the committed length moving after the last layer;
+    stored values are the rounded inputs (nearest even, as torch's casts);
+    truncate then append equals never having appended; errors change nothing."""
+    import torch
+    from oracle import OracleLatentCache
+    rng = np.random.default_rng(31)
+    for dt, tdt in (("fp32", None), ("fp16", torch.float16), ("bf16", torch.bfloat16)):
+        lc = OracleLatentCache(3, 2, 16, 8, 20, dt)
+        c, kr = _rand(rng, 2, 5, 16), _rand(rng, 2, 5, 8)
+        for layer in range(3):
+            assert lc.seq_len().tolist() == [0, 0]
+            lc.append(layer, c, kr)
+        assert lc.seq_len().tolist() == [5, 5]
+        want_c = c if tdt is None else torch.from_numpy(c).to(tdt).float().numpy()
+        assert np.array_equal(lc.C[1, :, :5], want_c)
+        # rollback then a fresh chunk == a cache that never saw the rolled-back positions
+        c2, kr2 = _rand(rng, 2, 3, 16), _rand(rng, 2, 3, 8)
+        lc.truncate(np.array([4, 2]))
+        for layer in range(3):
+            lc.append(layer, c2, kr2)
+        rnd = (lambda x: x) if tdt is None else (lambda x: torch.from_numpy(x).to(tdt).float().numpy())
+        for b, n in enumerate((4, 2)):
+            want = np.concatenate([rnd(c[b, :n]), rnd(c2[b])])
+            want_kr = np.concatenate([rnd(kr[b, :n]), rnd(kr2[b])])
+            for layer in range(3):
+                assert np.array_equal(lc.C[layer, b, :n + 3], want)
+                assert np.array_equal(lc.KR[layer, b, :n + 3], want_kr)
+        assert lc.seq_len().tolist() == [7, 5]
+        before = (lc.C.copy(), lc.fill.copy())
+        with pytest.raises(OracleCapacityError):
+            lc.append(0, _rand(rng, 2, 14, 16), _rand(rng, 2, 14, 8))
+        with pytest.raises(OracleError):
+            lc.truncate(np.array([9, 9]))
+        assert np.array_equal(lc.C, before[0]) and np.array_equal(lc.fill, before[1])
