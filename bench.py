@@ -182,6 +182,25 @@ def event_time(fn, reps, stream):
     return e0.elapsed_time(e1) / reps
 
 
+def call_time_us(fn, reps, stream) -> float:
+    """Median over `reps` calls of fn's time on the GPU, each call bracketed by
+    its own events and synchronised (the launch latency included), for calls
+    too small to time back to back: a queued loop of them is bound by the
+    host and its timing depends on what the process ran before."""
+    import torch
+    times = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    times.sort()
+    return times[len(times) // 2]
+
+
 def prefill_bench():
     """Chunked prefill: B=4, H_q=32, H_kv=8, d_h=128, bf16, 32 chunks of T=512
     appended and attended in turn (queries at s = 0, 512, ..., 15872)."""
@@ -253,7 +272,7 @@ def rope_bench():
     """The batched-decode step's append (B=32, H_kv=8, d_h=128, bf16, T=1, rows
     at 2000 positions) with the keys rotated (kvc_append_rope) against the
     plain append, and the rotation of the step's queries (kvc_rope_q, H_q=32):
-    microseconds per call, HIP events over 200 calls."""
+    microseconds per call (median of 50 synchronised calls, launch included)."""
     import torch
     from kv_cached_gqa_amd.kvc import KVCache
     b, hq, hkv, d = 32, 32, 8, 128
@@ -279,14 +298,15 @@ def rope_bench():
             cache.append(0, kv, kv)              # the chunk the queries belong to
         for i in range(10):
             fn(i)
-        res[name] = round(event_time(fn, 200, st) * 1e3, 2)
+        res[name] = round(call_time_us(fn, 50, st), 2)
     cache.close()
     return res
 
 
 def latent_bench():
     """Latent-cache appends (B=32, r=512, d_R=64, bf16): one decode step (T=1)
-    and one prefill chunk (T=512), microseconds per call (HIP events)."""
+    and one prefill chunk (T=512), microseconds per call (median of 50
+    synchronised calls, launch included)."""
     import torch
     from kv_cached_gqa_amd.kvc import LatentCache
     b, r, dr = 32, 512, 64
@@ -304,7 +324,7 @@ def latent_bench():
 
         for i in range(10):
             step(i)
-        us = event_time(step, 200, st) * 1e3
+        us = call_time_us(step, 50, st)
         moved = 2 * b * t * (r + dr) * 2           # read + write, bf16 in and out
         res[f"T{t}"] = {"us": round(us, 2), "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
     lc.close()
