@@ -158,9 +158,57 @@ int kvc_seq_len(const kvc_cache* cache, int32_t layer, int64_t* out_lens);
 int kvc_truncate(kvc_cache* cache, const int64_t* n, int32_t count);
 
 /* Storage bytes, 2 * L * B * H_kv * max_len * d_head * itemsize
- * ("KV cache, ...", section 2.5). Workspace and metadata are not counted.
+ * ("KV cache, ...", section 2.5); for a paged handle the pools,
+ * 2 * L * n_blocks * H_kv * block_size * d_head * itemsize. Workspace, block
+ * table and metadata are not counted.
  * out: host uint64. Errors: KVC_ERR_ARG. */
 int kvc_nbytes(const kvc_cache* cache, uint64_t* out);
+
+/* ---- Paged cache ------------------------------------------------------------
+ * The same cache in fixed-size blocks ("kv-cache-decoding", "Batching caches
+ * of different lengths": a table maps each request to its blocks; a sequence
+ * takes a block when it grows into it and frees its blocks when it ends;
+ * "KV cache, incremental decode, ...", Key takeaways: a float16 paged cache
+ * compares exactly with the contiguous one). A paged handle takes every call
+ * above (append, append_rope, rope_q, attend, seq_len, truncate, nbytes) with
+ * the same semantics and results; only the storage differs. */
+
+/* Create a paged handle over caller-owned block pools.
+ *  block_size: positions per block, a power of two from 64 to 4096 (at least
+ *    the decode kernel's key batch for this d_head and dtype, else
+ *    KVC_ERR_UNSUPPORTED; 128 and above always qualifies).
+ *  n_blocks: blocks in the pool, shared by all rows.
+ *  k_pool, v_pool: device buffers, each at least pool_bytes_each bytes, holding
+ *    [n_layers][n_blocks][n_kv_heads][block_size][d_head] elements of
+ *    cfg->dtype, 16-byte aligned (zero-filling is not required: a position is
+ *    read only after it was written). Caller-owned, alive for the handle's life.
+ *  cfg->max_len bounds each row's length; the block table has
+ *  ceil(max_len / block_size) entries per row, one table for all layers, so
+ *  position p of row b, KV head g, layer l sits at element
+ *    ((l * n_blocks + table[b][p / block_size]) * n_kv_heads + g) * block_size
+ *    + p % block_size) * d_head
+ *  of each pool. The library owns the device copy of the table (allocated and
+ *  zeroed here, on the pools' device) and a free list of blocks.
+ *  Blocks: an append (any layer) that takes row b past its held blocks takes
+ *  the next ones from the free list, and enqueues the table update on its
+ *  stream ahead of its own kernel; truncate to n gives back the row's blocks
+ *  past ceil(n / block_size). If the free list cannot cover an append, the
+ *  append fails with KVC_ERR_CAPACITY and nothing changes.
+ *  Attention over a paged cache runs every chunk on the split-K decode kernel
+ *  in slabs of at most 8 query rows per KV head (no matrix-core prefill path).
+ * Errors: as kvc_create; KVC_ERR_ARG also for a bad block_size or n_blocks;
+ * KVC_ERR_NOMEM if the device table cannot be allocated. */
+int kvc_create_paged(const kvc_config* cfg, int32_t block_size, int32_t n_blocks, void* k_pool,
+                     void* v_pool, uint64_t pool_bytes_each, kvc_cache** out);
+
+/* Blocks in use and in the pool. Host metadata only.
+ * Errors: KVC_ERR_ARG (null), KVC_ERR_STATE (not a paged handle). */
+int kvc_paged_blocks(const kvc_cache* cache, int32_t* in_use, int32_t* total);
+
+/* Copy the host block table, int32 [batch][ceil(max_len / block_size)], -1 for
+ * an entry with no block, into out (n entries, which must equal that size).
+ * Errors: KVC_ERR_ARG (null, n), KVC_ERR_STATE (not a paged handle). */
+int kvc_block_table(const kvc_cache* cache, int32_t* out, int64_t n);
 
 /* ---- Latent cache (multi-head latent attention) ---------------------------
  * One compressed latent c (rank r) and one shared rotary key k_R (d_R) per

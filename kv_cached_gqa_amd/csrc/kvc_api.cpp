@@ -10,6 +10,13 @@
 // Device work is enqueued on the caller's stream; metadata advances when the
 // enqueue succeeded, which keeps host state and stream order consistent
 // without any synchronisation.
+//
+// A paged cache ("kv-cache-decoding", "Batching caches of different lengths")
+// keeps the same bookkeeping and adds a pool of fixed-size blocks: a row takes
+// a block from the free list when an append first grows into it and gives its
+// blocks back when truncate cuts them off. The host holds the block table and
+// the free list; each change to the table is enqueued on the caller's stream
+// (a small kernel writes the device copy) ahead of the append that needs it.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -37,6 +44,16 @@ struct kvc_cache {
     float* ws_o;
     float* ws_ml;
     int64_t ws_segments;
+    // paged storage (block_size > 0): pools of [n_layers][n_blocks][n_kv_heads]
+    // [block_size][d_head], one block table [batch][width] shared by all layers
+    int32_t block_size;
+    int32_t bshift;
+    int32_t n_blocks;
+    int32_t width;                 // table entries per row: ceil(max_len / block_size)
+    int32_t* d_table;              // device copy of the table (library-owned)
+    std::vector<int32_t> table;    // host table, -1 = no block
+    std::vector<int32_t> held;     // blocks held per row (a prefix of its table row)
+    std::vector<int32_t> free_ids; // free blocks, taken from the back
 };
 
 namespace {
@@ -48,6 +65,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 uint64_t storage_bytes(const kvc_config& c) {
     return 2ull * static_cast<uint64_t>(c.n_layers) * c.batch * c.n_kv_heads * static_cast<uint64_t>(c.max_len) *
            c.d_head * kvc::itemsize(c.dtype);
+}
+
+// Elements of one layer's block pool.
+int64_t pool_layer_elems(const kvc_cache* c) {
+    return static_cast<int64_t>(c->n_blocks) * c->cfg.n_kv_heads * c->block_size * c->cfg.d_head;
+}
+
+uint64_t pool_bytes(const kvc_config& c, int32_t block_size, int32_t n_blocks) {
+    return 2ull * static_cast<uint64_t>(c.n_layers) * static_cast<uint64_t>(n_blocks) * c.n_kv_heads *
+           static_cast<uint64_t>(block_size) * c.d_head * kvc::itemsize(c.dtype);
 }
 
 int64_t committed(const kvc_cache* c, int b) {
@@ -138,19 +165,100 @@ int kvc_create(const kvc_config* cfg, void* k_store, void* v_store, uint64_t sto
     h->ws_o = nullptr;
     h->ws_ml = nullptr;
     h->ws_segments = 0;
+    h->block_size = 0;
+    h->d_table = nullptr;
+    *out = h;
+    return KVC_OK;
+}
+
+int kvc_create_paged(const kvc_config* cfg, int32_t block_size, int32_t n_blocks, void* k_pool, void* v_pool,
+                     uint64_t pool_bytes_each, kvc_cache** out) {
+    if (!cfg || !out) return KVC_ERR_ARG;
+    const kvc_config c = *cfg;
+    if (c.n_layers < 1 || c.batch < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.d_head < 1 || c.max_len < 1)
+        return KVC_ERR_ARG;
+    if (c.n_q_heads % c.n_kv_heads) return KVC_ERR_ARG;
+    if (block_size < 64 || (block_size & (block_size - 1)) || block_size > 4096 || n_blocks < 1) return KVC_ERR_ARG;
+    const int64_t width = (c.max_len + block_size - 1) / block_size;
+    if (width * c.batch >= (int64_t(1) << 31) || c.max_len >= (int64_t(1) << 31)) return KVC_ERR_ARG;
+    if (!dtype_ok(c.dtype)) return KVC_ERR_DTYPE;
+    if (!kvc::decode_supported(c.d_head, c.dtype)) return KVC_ERR_UNSUPPORTED;
+    // a decode batch of keys spans at most two blocks
+    if (block_size < std::max(kvc::decode_vector_batch_keys(c.d_head, c.dtype, 4),
+                              kvc::decode_vector_batch_keys(c.d_head, c.dtype, 8)))
+        return KVC_ERR_UNSUPPORTED;
+    if (!k_pool || !v_pool || !aligned16(k_pool) || !aligned16(v_pool)) return KVC_ERR_STORAGE;
+    if (pool_bytes_each < pool_bytes(c, block_size, n_blocks) / 2) return KVC_ERR_STORAGE;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, k_pool) != hipSuccess) {
+        (void)hipGetLastError();
+        return KVC_ERR_STORAGE;
+    }
+    kvc_cache* h = new (std::nothrow) kvc_cache();
+    if (!h) return KVC_ERR_NOMEM;
+    try {
+        h->fill.assign(static_cast<size_t>(c.n_layers) * c.batch, 0);
+        h->table.assign(static_cast<size_t>(width) * c.batch, -1);
+        h->held.assign(c.batch, 0);
+        h->free_ids.resize(n_blocks);
+        for (int32_t i = 0; i < n_blocks; ++i) h->free_ids[i] = n_blocks - 1 - i;   // block 0 is taken first
+    } catch (...) {
+        delete h;
+        return KVC_ERR_NOMEM;
+    }
+    h->cfg = c;
+    h->k_store = k_pool;
+    h->v_store = v_pool;
+    h->device = -1;
+    h->ws_o = nullptr;
+    h->ws_ml = nullptr;
+    h->ws_segments = 0;
+    h->block_size = block_size;
+    h->bshift = 0;
+    while ((1 << h->bshift) < block_size) ++h->bshift;
+    h->n_blocks = n_blocks;
+    h->width = static_cast<int32_t>(width);
+    h->d_table = nullptr;
+    // the device table, on the pool's device; entries are written before use
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) {
+        delete h;
+        return KVC_ERR_HIP;
+    }
+    if (attr.device != prev && hipSetDevice(attr.device) != hipSuccess) {
+        delete h;
+        return KVC_ERR_HIP;
+    }
+    void* t = nullptr;
+    const size_t tb = static_cast<size_t>(width) * c.batch * sizeof(int32_t);
+    const bool ok = hipMalloc(&t, tb) == hipSuccess && hipMemset(t, 0, tb) == hipSuccess;
+    if (attr.device != prev) (void)hipSetDevice(prev);
+    if (!ok) {
+        if (t) (void)hipFree(t);
+        (void)hipGetLastError();
+        delete h;
+        return KVC_ERR_NOMEM;
+    }
+    h->d_table = static_cast<int32_t*>(t);
     *out = h;
     return KVC_OK;
 }
 
 void kvc_destroy(kvc_cache* c) {
     if (!c) return;
-    if (c->ws_o) {
+    if (c->ws_o || c->d_table) {
         int prev = 0;
         (void)hipGetDevice(&prev);
-        (void)hipSetDevice(c->device);
+        hipPointerAttribute_t attr;
+        const int dev = c->ws_o ? c->device
+                                : (hipPointerGetAttributes(&attr, c->d_table) == hipSuccess ? attr.device : prev);
+        (void)hipSetDevice(dev);
         (void)hipDeviceSynchronize();
-        (void)hipFree(c->ws_o);
-        (void)hipFree(c->ws_ml);
+        if (c->ws_o) {
+            (void)hipFree(c->ws_o);
+            (void)hipFree(c->ws_ml);
+        }
+        if (c->d_table) (void)hipFree(c->d_table);
         (void)hipSetDevice(prev);
     }
     delete c;
@@ -167,6 +275,53 @@ void rope_freqs(double base, int D, double* out) {
     for (int i = 0; i < D / 2; ++i) out[i] = std::pow(base, -2.0 * i / D);
 }
 
+// Blocks a row needs to hold n positions.
+int32_t blocks_for(const kvc_cache* c, int64_t n) {
+    return static_cast<int32_t>((n + c->block_size - 1) >> c->bshift);
+}
+
+// Paged cache: give every row the blocks that positions [0, f[b] + T) need,
+// and enqueue the table entries that change. All or nothing: KVC_ERR_CAPACITY
+// (pool exhausted) before anything changes.
+int grow_blocks(kvc_cache* c, const int64_t* f, int32_t T, hipStream_t s) {
+    const int B = c->cfg.batch;
+    int64_t need = 0;
+    for (int b = 0; b < B; ++b) need += std::max(0, blocks_for(c, f[b] + T) - c->held[b]);
+    if (need == 0) return KVC_OK;
+    if (need > static_cast<int64_t>(c->free_ids.size())) return KVC_ERR_CAPACITY;
+    kvc::TableSetArgs a;
+    a.table = c->d_table;
+    a.n = 0;
+    for (int b = 0; b < B; ++b) {
+        const int32_t want = blocks_for(c, f[b] + T);
+        for (int32_t k = c->held[b]; k < want; ++k) {
+            const int32_t id = c->free_ids.back();
+            c->free_ids.pop_back();
+            c->table[static_cast<size_t>(b) * c->width + k] = id;
+            a.index[a.n] = b * c->width + k;
+            a.value[a.n] = id;
+            if (++a.n == kvc::kMaxTableSets) {
+                if (kvc::launch_table_set(a, s) != hipSuccess) return KVC_ERR_HIP;
+                a.n = 0;
+            }
+        }
+        c->held[b] = std::max(c->held[b], want);
+    }
+    if (a.n > 0 && kvc::launch_table_set(a, s) != hipSuccess) return KVC_ERR_HIP;
+    return KVC_OK;
+}
+
+// Paged cache: give back the blocks past position n of row b.
+void shrink_blocks(kvc_cache* c, int b, int64_t n) {
+    const int32_t keep = blocks_for(c, n);
+    for (int32_t k = c->held[b] - 1; k >= keep; --k) {
+        int32_t& e = c->table[static_cast<size_t>(b) * c->width + k];
+        c->free_ids.push_back(e);
+        e = -1;
+    }
+    c->held[b] = std::min(c->held[b], keep);
+}
+
 // Append with or without the rotary embedding of K (rope_base > 0).
 int append_impl(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new, int32_t in_dtype, int32_t T,
                 double rope_base, void* stream) {
@@ -178,11 +333,15 @@ int append_impl(kvc_cache* c, int32_t layer, const void* k_new, const void* v_ne
     int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
     for (int b = 0; b < cf.batch; ++b)
         if (f[b] + T > cf.max_len) return KVC_ERR_CAPACITY;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (c->block_size) {
+        const int rc = grow_blocks(c, f, T, s);
+        if (rc != KVC_OK) return rc;
+    }
 
     const int64_t head_stride = cf.max_len * cf.d_head;
     const int64_t row_stride = head_stride * cf.n_kv_heads;
     const int64_t in_row = static_cast<int64_t>(cf.n_kv_heads) * T * cf.d_head * kvc::itemsize(in_dtype);
-    hipStream_t s = static_cast<hipStream_t>(stream);
     for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
         kvc::AppendArgs a;
         std::memset(&a, 0, sizeof(a));
@@ -201,6 +360,13 @@ int append_impl(kvc_cache* c, int32_t layer, const void* k_new, const void* v_ne
         a.st_dtype = cf.dtype;
         a.rope = rope_base > 0.0 ? 1 : 0;
         a.n_tensors = 2;
+        if (c->block_size) {
+            a.layer_off = layer * pool_layer_elems(c);
+            a.btab = c->d_table + static_cast<int64_t>(row0) * c->width;
+            a.btab_stride = c->width;
+            a.bshift = c->bshift;
+            a.pool_blocks = c->n_blocks;
+        }
         if (a.rope) rope_freqs(rope_base, cf.d_head, a.inv_freq);
         for (int b = 0; b < a.rows; ++b) a.fill[b] = static_cast<int32_t>(f[row0 + b]);
         if (kvc::launch_append(a, s) != hipSuccess) return KVC_ERR_HIP;
@@ -271,7 +437,10 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
 
     // Dispatch: a 16-bit cache with more than 32 query rows per KV head (a prefill
     // chunk) runs on the matrix cores; everything else on the split-K decode kernel.
-    if (cf.dtype != KVC_F32 && static_cast<int64_t>(T) * G > 32 && kvc::prefill_supported(cf.d_head, cf.dtype)) {
+    // A paged cache runs every chunk on the split-K vector kernel.
+    const bool paged = c->block_size > 0;
+    if (!paged && cf.dtype != KVC_F32 && static_cast<int64_t>(T) * G > 32 &&
+        kvc::prefill_supported(cf.d_head, cf.dtype)) {
         const int Gc = std::min(G, 32);
         for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
             const int rows = std::min(kMaxRowsPerLaunch, cf.batch - row0);
@@ -308,10 +477,11 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
         return KVC_OK;
     }
 
-    // Slabs of at most kMaxDecodeRows query rows per KV head: Gc query heads
-    // of the group times Tc query positions.
-    const int Gc = std::min(G, kMaxDecodeRows);
-    const int Tc = std::max(1, kMaxDecodeRows / Gc);
+    // Slabs of at most kMaxDecodeRows (paged: kMaxPagedDecodeRows) query rows
+    // per KV head: Gc query heads of the group times Tc query positions.
+    const int slab = paged ? kvc::kMaxPagedDecodeRows : kMaxDecodeRows;
+    const int Gc = std::min(G, slab);
+    const int Tc = std::max(1, slab / Gc);
     for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
         const int rows = std::min(kMaxRowsPerLaunch, cf.batch - row0);
         for (int r0 = 0; r0 < G; r0 += Gc) {
@@ -342,6 +512,15 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
                 a.q_dtype = q_dtype;
                 a.st_dtype = cf.dtype;
                 a.scale_log2 = scale_log2;
+                if (paged) {
+                    a.layer_off = layer * pool_layer_elems(c);
+                    a.row_stride = 0;
+                    a.head_stride = 0;
+                    a.btab = c->d_table + static_cast<int64_t>(row0) * c->width;
+                    a.btab_stride = c->width;
+                    a.bshift = c->bshift;
+                    a.pool_blocks = c->n_blocks;
+                }
                 int64_t acc = 0;
                 for (int b = 0; b < rows; ++b) {
                     a.prefix[b] = acc;
@@ -376,13 +555,30 @@ int kvc_truncate(kvc_cache* c, const int64_t* n, int32_t count) {
     for (int b = 0; b < B; ++b) {
         const int64_t nb = n[count == 1 ? 0 : b];
         for (int l = 0; l < c->cfg.n_layers; ++l) c->fill[static_cast<size_t>(l) * B + b] = nb;
+        if (c->block_size) shrink_blocks(c, b, nb);
     }
     return KVC_OK;
 }
 
 int kvc_nbytes(const kvc_cache* c, uint64_t* out) {
     if (!c || !out) return KVC_ERR_ARG;
-    *out = storage_bytes(c->cfg);
+    *out = c->block_size ? pool_bytes(c->cfg, c->block_size, c->n_blocks) : storage_bytes(c->cfg);
+    return KVC_OK;
+}
+
+int kvc_paged_blocks(const kvc_cache* c, int32_t* in_use, int32_t* total) {
+    if (!c || !in_use || !total) return KVC_ERR_ARG;
+    if (!c->block_size) return KVC_ERR_STATE;
+    *total = c->n_blocks;
+    *in_use = c->n_blocks - static_cast<int32_t>(c->free_ids.size());
+    return KVC_OK;
+}
+
+int kvc_block_table(const kvc_cache* c, int32_t* out, int64_t n) {
+    if (!c || !out) return KVC_ERR_ARG;
+    if (!c->block_size) return KVC_ERR_STATE;
+    if (n != static_cast<int64_t>(c->table.size())) return KVC_ERR_ARG;
+    std::copy(c->table.begin(), c->table.end(), out);
     return KVC_OK;
 }
 

@@ -19,6 +19,18 @@
 namespace kvc {
 namespace {
 
+// Element offset of position p of row b, head g: contiguous (L, B, H, max_len,
+// D) storage, or a paged pool (the block's id clamped into the pool, so a
+// stale table entry can never address outside it).
+__device__ __forceinline__ int64_t slot_offset(const AppendArgs& a, int b, int g, int64_t p) {
+    if (a.btab == nullptr)
+        return a.layer_off + b * a.row_stride + g * a.head_stride + p * a.D;
+    int blk = a.btab[static_cast<int64_t>(b) * a.btab_stride + (p >> a.bshift)];
+    blk = blk < 0 ? 0 : (blk >= a.pool_blocks ? a.pool_blocks - 1 : blk);
+    const int64_t mask = (int64_t(1) << a.bshift) - 1;
+    return a.layer_off + (((static_cast<int64_t>(blk) * a.H + g) << a.bshift) + (p & mask)) * a.D;
+}
+
 template <int IN, int ST>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const void* src = blockIdx.y == 0 ? a.k_in : a.v_in;
@@ -39,8 +51,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
             load8<IN>(src, run_t * a.D + i0, x1);
             load8<IN>(src, run_t * a.D + i0 + half, x2);
             rope8(x1, x2, static_cast<int64_t>(a.fill[b]) + t, a.inv_freq + i0, y1, y2);
-            const int64_t d = a.layer_off + b * a.row_stride + g * a.head_stride +
-                              (static_cast<int64_t>(a.fill[b]) + t) * a.D + i0;
+            const int64_t d = slot_offset(a, b, g, static_cast<int64_t>(a.fill[b]) + t) + i0;
             store8<ST>(dst, d, y1);
             store8<ST>(dst, d + half, y2);
         }
@@ -56,8 +67,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         const int g = static_cast<int>(run - static_cast<int64_t>(b) * a.H);
         float x[8];
         load8<IN>(src, v * 8, x);
-        const int64_t d = a.layer_off + b * a.row_stride + g * a.head_stride +
-                          static_cast<int64_t>(a.fill[b]) * a.D + static_cast<int64_t>(within) * 8;
+        const int e = within * 8;
+        const int64_t d = slot_offset(a, b, g, static_cast<int64_t>(a.fill[b]) + e / a.D) + e % a.D;
         store8<ST>(dst, d, x);
     }
 }
@@ -94,7 +105,17 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
     }
 }
 
+__global__ __launch_bounds__(256) void table_set_kernel(TableSetArgs a) {
+    for (int i = threadIdx.x; i < a.n; i += 256) a.table[a.index[i]] = a.value[i];
+}
+
 }  // namespace
+
+hipError_t launch_table_set(const TableSetArgs& a, hipStream_t s) {
+    if (a.n < 1 || a.n > kMaxTableSets) return hipErrorInvalidValue;
+    table_set_kernel<<<1, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
 
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
     const int64_t n_blk = static_cast<int64_t>(a.rows) * a.H * a.T * (a.D >> 4);

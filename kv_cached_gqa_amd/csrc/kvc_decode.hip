@@ -264,7 +264,7 @@ __device__ __forceinline__ void load_q_rows(uint32_t (&qp)[R][4], uint32_t slot,
     }
 }
 
-template <int D, int ST, int R>
+template <int D, int ST, int R, bool PAGED>
 __global__ __launch_bounds__((Cfg<D, ST, R>::THREADS)) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_attn(DecodeArgs a) {
     using C = Cfg<D, ST, R>;
@@ -362,6 +362,26 @@ void decode_attn(DecodeArgs a) {
     Seg is = locate(x_begin);
     int is_t = 0, is_sn = 0;
     bool is_live = true;
+    // paged storage: element offsets of head is.g's rows in the physical
+    // blocks of logical blocks pg_blk and pg_blk + 1 of the issue cursor's
+    // unit. A work-group batch (KPB keys, at most one block) spans at most
+    // those two; the next block's entry is read when the cursor enters a
+    // block, with a scalar load, long before a batch needs it.
+    int pg_blk = 0;
+    int64_t pg_base = 0, pg_next = 0;
+    auto pg_phys = [&](int blk) __attribute__((always_inline)) -> int64_t {
+        const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
+        const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
+        int p = tab[static_cast<int64_t>(is.b) * a.btab_stride + bi];
+        p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
+        return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + is.g) << a.bshift) * D;
+    };
+    auto pg_enter = [&]() __attribute__((always_inline)) {
+        pg_blk = is.j0 >> a.bshift;
+        pg_base = pg_phys(pg_blk);
+        pg_next = pg_phys(pg_blk + 1);
+    };
+    if constexpr (PAGED) pg_enter();
     uint8_t* const ring_w = ring + wave * (NS * C::STAGE_BYTES);
     auto issue = [&](auto slot_c) __attribute__((always_inline)) {
         constexpr int S = decltype(slot_c)::value;
@@ -371,15 +391,31 @@ void decode_attn(DecodeArgs a) {
                 is_t = 0;
                 ++is_sn;
                 if (wave == 0) issue_q(is, is_sn % NS);
+                if constexpr (PAGED) pg_enter();
             } else {
                 is_live = false;
+            }
+        }
+        if constexpr (PAGED) {
+            const int blk = (is.j0 + is_t * KPB) >> a.bshift;
+            if (is_live && blk != pg_blk) {       // the batch starts in the next block
+                pg_blk = blk;
+                pg_base = pg_next;
+                pg_next = pg_phys(blk + 1);
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int j = is.j0 + is_t * KPB + wave * KPS + u * KPW + grp;
             j = j < is.j1 ? j : is.j1 - 1;
-            const int64_t off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
+            int64_t off;
+            if constexpr (PAGED) {
+                const int64_t row = ((j >> a.bshift) == pg_blk ? pg_base : pg_next) +
+                                    static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D;
+                off = (row + sub * EPC) * ESZ;
+            } else {
+                off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
+            }
             uint8_t* dst = ring_w + S * C::STAGE_BYTES + u * 2048;
             __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kc + off),
                                              (void __attribute__((address_space(3)))*)(dst), 16, 0, 0);
@@ -1302,7 +1338,12 @@ hipError_t run(DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     a.rec_rows = R;
     split_slices(a, n_cu, KVC_DECODE_BLOCKS_PER_CU, 2 * Cfg<D, ST, R>::KPB);
-    decode_attn<D, ST, R><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
+    if (a.btab) {
+        if ((1 << a.bshift) < Cfg<D, ST, R>::KPB) return hipErrorInvalidValue;   // a batch within two blocks
+        decode_attn<D, ST, R, true><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
+    } else {
+        decode_attn<D, ST, R, false><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return combine_if_split<D>(a, s);
@@ -1337,6 +1378,10 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
 template <int D, int ST>
 hipError_t run_r(DecodeArgs& a, hipStream_t s) {
     const int rows = a.Gc * a.Tc;
+    if (a.btab) {                 // paged storage: the vector kernel
+        if (rows > kMaxPagedDecodeRows) return hipErrorInvalidValue;
+        return rows <= 4 ? run<D, ST, 4>(a, s) : run<D, ST, 8>(a, s);
+    }
     if constexpr (ST != F32) {
         if (rows >= KVC_DECODE_MFMA_MIN_ROWS) return run_mfma<D, ST>(a, s);
     }
@@ -1358,6 +1403,22 @@ hipError_t run_d(DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int decode_vector_batch_keys(int D, int st_dtype, int rows) {
+    auto pick = [&](auto d_c) -> int {
+        constexpr int DD = decltype(d_c)::value;
+        switch (st_dtype) {
+            case F32: return rows <= 4 ? Cfg<DD, F32, 4>::KPB : Cfg<DD, F32, 8>::KPB;
+            case F16: return rows <= 4 ? Cfg<DD, F16, 4>::KPB : Cfg<DD, F16, 8>::KPB;
+            default: return rows <= 4 ? Cfg<DD, BF16, 4>::KPB : Cfg<DD, BF16, 8>::KPB;
+        }
+    };
+    switch (D) {
+        case 32: return pick(std::integral_constant<int, 32>{});
+        case 64: return pick(std::integral_constant<int, 64>{});
+        default: return pick(std::integral_constant<int, 128>{});
+    }
+}
 
 bool decode_supported(int D, int st_dtype) {
     return (D == 32 || D == 64 || D == 128) && (st_dtype == F32 || st_dtype == F16 || st_dtype == BF16);

@@ -15,6 +15,8 @@ constexpr int kMaxRowsPerLaunch = 256;
 constexpr int kMaxRopePairs = 64;
 // Query rows (query heads of one group x query positions) of one decode slab.
 constexpr int kMaxDecodeRows = 32;
+// The same for a paged cache (read by the vector kernel only).
+constexpr int kMaxPagedDecodeRows = 8;
 // Rows per workspace record of the split-K workspace as allocated (a launch
 // with slabs of more rows uses fewer, wider records).
 constexpr int kWsRecordRows = 8;
@@ -40,6 +42,11 @@ struct AppendArgs {
     int32_t in_dtype, st_dtype;
     int32_t rope;                      // 1: rotate K at its positions (rotary embedding)
     int32_t n_tensors;                 // 2: K and V; 1: the first tensor only (k_in -> k_cache)
+    // paged storage (btab non-null): position p of row b, head g sits in physical
+    // block btab[b * btab_stride + (p >> bshift)] of the layer's pool, at
+    // layer_off + ((block * H + g) << bshift + (p & mask)) * D
+    const int32_t* btab;               // block table from row `row0` on
+    int32_t btab_stride, bshift, pool_blocks;
     int32_t fill[kMaxRowsPerLaunch];   // first slot written, per row
     double inv_freq[kMaxRopePairs];    // rotary frequencies of pairs (i, i + D/2), i < D/2
 };
@@ -86,6 +93,12 @@ struct DecodeArgs {
     int32_t q_dtype, st_dtype;
     int32_t n_blocks;        // work-groups (set by launch_decode)
     float scale_log2;        // log2(e) / sqrt(D)
+    // paged storage (btab non-null): key j of unit (b, g) sits in physical block
+    // btab[b * btab_stride + (j >> bshift)] of the layer's pool, at element
+    // layer_off + ((block * Hkv + g) << bshift + (j & mask)) * D; only the
+    // vector kernel reads paged storage
+    const int32_t* btab;     // block table from row `row0` on
+    int32_t btab_stride, bshift, pool_blocks;
     int64_t prefix[kMaxRowsPerLaunch + 1];  // exclusive prefix of n_b * H_kv
 };
 
@@ -114,6 +127,16 @@ struct PrefillArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
+
+// Entries of a device block table set in stream order (n <= kMaxTableSets).
+constexpr int kMaxTableSets = 480;
+struct TableSetArgs {
+    int32_t* table;
+    int32_t n;
+    int32_t index[kMaxTableSets];
+    int32_t value[kMaxTableSets];
+};
+hipError_t launch_table_set(const TableSetArgs& a, hipStream_t stream);
 // Decode work-group k's slice of the key axis starts at decode_slice_begin(a, k);
 // key x lies in work-group decode_slice_of(a, x)'s slice.
 __host__ __device__ inline int64_t decode_slice_begin(const DecodeArgs& a, int64_t k) {
@@ -127,6 +150,9 @@ __host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t 
 
 // Fills in the work split (n_blocks, slice sizes) from the device's resident capacity.
 hipError_t launch_decode(DecodeArgs& a, hipStream_t stream);
+// Keys per work-group batch of the vector decode kernel for a slab of `rows`
+// query rows (a paged cache's block must hold a whole number of batches).
+int decode_vector_batch_keys(int D, int st_dtype, int rows);
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

@@ -38,6 +38,7 @@ ERR_STORAGE, ERR_HIP, ERR_NOMEM, ERR_UNSUPPORTED = -5, -6, -7, -8
 
 EXPORTED = ("kvc_create", "kvc_destroy", "kvc_append", "kvc_append_rope", "kvc_rope_q", "kvc_attend",
             "kvc_seq_len", "kvc_truncate", "kvc_nbytes", "kvc_strerror",
+            "kvc_create_paged", "kvc_paged_blocks", "kvc_block_table",
             "kvc_latent_create", "kvc_latent_destroy", "kvc_latent_append", "kvc_latent_seq_len",
             "kvc_latent_truncate", "kvc_latent_nbytes")
 
@@ -51,6 +52,12 @@ class KVCConfig(ctypes.Structure):
 _vp, _i32, _i64, _u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
 _lib.kvc_create.argtypes = [ctypes.POINTER(KVCConfig), _vp, _vp, _u64, ctypes.POINTER(_vp)]
 _lib.kvc_create.restype = ctypes.c_int
+_lib.kvc_create_paged.argtypes = [ctypes.POINTER(KVCConfig), _i32, _i32, _vp, _vp, _u64, ctypes.POINTER(_vp)]
+_lib.kvc_create_paged.restype = ctypes.c_int
+_lib.kvc_paged_blocks.argtypes = [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+_lib.kvc_paged_blocks.restype = ctypes.c_int
+_lib.kvc_block_table.argtypes = [_vp, ctypes.POINTER(_i32), _i64]
+_lib.kvc_block_table.restype = ctypes.c_int
 _lib.kvc_destroy.argtypes = [_vp]
 _lib.kvc_destroy.restype = None
 _lib.kvc_append.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _vp]
@@ -171,6 +178,7 @@ class KVCache:
         tdt = torch_dtype(dtype)
         self.k_storage = torch.zeros(shape, dtype=tdt, device=self.device)
         self.v_storage = torch.zeros(shape, dtype=tdt, device=self.device)
+        self._dev = self.k_storage.device
         cfg = KVCConfig(self.n_layers, self.batch, self.n_q_heads, self.n_kv_heads, self.d_head,
                         DTYPE_CODES[dtype], self.max_len)
         h = _vp()
@@ -274,8 +282,79 @@ class KVCache:
         if t.dim() != 4 or t.shape[0] != self.batch or t.shape[1] != heads or t.shape[3] != self.d_head:
             raise KVCArgumentError(ERR_ARG, f"{name} must be [B={self.batch}, H={heads}, T, d_h={self.d_head}], "
                                             f"got {tuple(t.shape)}")
-        if not t.is_contiguous() or t.device != self.k_storage.device:
-            raise KVCArgumentError(ERR_ARG, f"{name} must be contiguous and on {self.k_storage.device}")
+        if not t.is_contiguous() or t.device != self._dev:
+            raise KVCArgumentError(ERR_ARG, f"{name} must be contiguous and on {self._dev}")
+
+
+class PagedKVCache(KVCache):
+    """The same cache over block pools (kvc_create_paged): k_pool and v_pool
+    shaped (L, n_blocks, H_kv, block_size, d_h), one block table for all
+    layers, blocks taken on growth and given back on truncate ("kv-cache-
+    decoding", "Batching caches of different lengths"). Every call of KVCache
+    works unchanged; `update` returns gathered copies instead of views."""
+
+    def __init__(self, n_layers: int, n_kv_heads: int, d_head: int, max_len: int, batch: int = 1,
+                 n_q_heads: Optional[int] = None, dtype: str = "fp32", device=None, block_size: int = 128,
+                 n_blocks: Optional[int] = None):
+        torch = _torch()
+        if dtype not in DTYPE_CODES:
+            raise KVCArgumentError(ERR_DTYPE, f"dtype {dtype!r}")
+        self.n_layers, self.batch = int(n_layers), int(batch)
+        self.n_kv_heads, self.d_head, self.max_len = int(n_kv_heads), int(d_head), int(max_len)
+        self.n_q_heads = int(n_q_heads if n_q_heads is not None else n_kv_heads)
+        self.dtype = dtype
+        self.device = torch.device(device if device is not None else "cuda")
+        self.block_size = int(block_size)
+        self.width = -(-self.max_len // self.block_size)
+        self.n_blocks = int(n_blocks if n_blocks is not None else self.batch * self.width)
+        shape = (self.n_layers, self.n_blocks, self.n_kv_heads, self.block_size, self.d_head)
+        tdt = torch_dtype(dtype)
+        self.k_pool = torch.empty(shape, dtype=tdt, device=self.device)
+        self.v_pool = torch.empty(shape, dtype=tdt, device=self.device)
+        self._dev = self.k_pool.device
+        cfg = KVCConfig(self.n_layers, self.batch, self.n_q_heads, self.n_kv_heads, self.d_head,
+                        DTYPE_CODES[dtype], self.max_len)
+        h = _vp()
+        each = self.k_pool.numel() * self.k_pool.element_size()
+        _check(_lib.kvc_create_paged(ctypes.byref(cfg), self.block_size, self.n_blocks, self.k_pool.data_ptr(),
+                                     self.v_pool.data_ptr(), each, ctypes.byref(h)), "kvc_create_paged")
+        self._h = h
+
+    def block_table(self) -> np.ndarray:
+        """The host block table, int32 [B, ceil(max_len / block_size)], -1 = none."""
+        out = np.empty((self.batch, self.width), dtype=np.int32)
+        _check(_lib.kvc_block_table(self._h, out.ctypes.data_as(ctypes.POINTER(_i32)), int(out.size)),
+               "kvc_block_table")
+        return out
+
+    def blocks(self) -> tuple:
+        """(blocks in use, blocks in the pool)."""
+        used, total = _i32(), _i32()
+        _check(_lib.kvc_paged_blocks(self._h, ctypes.byref(used), ctypes.byref(total)), "kvc_paged_blocks")
+        return int(used.value), int(total.value)
+
+    def gather(self, layer: int, n: Optional[int] = None):
+        """Copies [B, H_kv, n, d_h] of K and V of `layer` in position order
+        (n defaults to the longest row's fill; positions a row has no block
+        for read as zero)."""
+        torch = _torch()
+        n = int(self.seq_len(layer).max()) if n is None else int(n)
+        tab = torch.from_numpy(self.block_table().astype(np.int64)).to(self._dev)
+        p = torch.arange(n, device=self._dev)
+        blk = tab[:, p // self.block_size]                            # [B, n]
+        have = (blk >= 0)[:, None, :, None]
+        blk = blk.clamp(min=0)
+        out = []
+        for pool in (self.k_pool[layer], self.v_pool[layer]):      # [n_blocks, H, bs, D]
+            x = pool[blk, :, (p % self.block_size)[None, :].expand_as(blk)]   # [B, n, H, D]
+            x = x.permute(0, 2, 1, 3)
+            out.append(torch.where(have, x, torch.zeros((), dtype=x.dtype, device=x.device)).contiguous())
+        return out[0], out[1]
+
+    def update(self, layer: int, k_new, v_new, stream=None):
+        """Append, then return copies of everything the layer stores."""
+        self.append(layer, k_new, v_new, stream)
+        return self.gather(layer)
 
 
 class KVCLatentConfig(ctypes.Structure):

@@ -218,3 +218,35 @@ def test_latent_cache_abi(kvc):
     finally:
         lib.kvc_latent_destroy(h)
     lib.kvc_latent_destroy(None)
+
+
+def test_paged_create_validation(kvc):
+    """kvc_create_paged rejects bad shapes, block sizes and pools before it
+    touches the device; the paged queries reject a contiguous-less call."""
+    lib = kvc.lib()
+    h = ctypes.c_void_p()
+    buf = ctypes.create_string_buffer(64)
+    p = (ctypes.addressof(buf) + 15) & ~15          # aligned, never dereferenced
+
+    def create(block_size, n_blocks, D=128, dtype=kvc.BF16, nbytes=1 << 40, pool=p, cfg=True):
+        c = kvc.KVCConfig(2, 4, 8, 2, D, dtype, 1000)
+        return lib.kvc_create_paged(ctypes.byref(c) if cfg else None, block_size, n_blocks, pool, pool,
+                                    nbytes, ctypes.byref(h))
+
+    assert create(128, 8, cfg=False) == kvc.ERR_ARG
+    for bs in (0, 32, 96, 100, 8192):                 # below 64, not a power of two, above 4096
+        assert create(bs, 8) == kvc.ERR_ARG, bs
+    assert create(128, 0) == kvc.ERR_ARG
+    assert create(128, 8, dtype=7) == kvc.ERR_DTYPE
+    assert create(128, 8, D=48) == kvc.ERR_UNSUPPORTED
+    # d_head 32 in 16 bits reads 128 keys per work-group batch: a 64-position
+    # block would let one batch span three blocks
+    assert create(64, 8, D=32) == kvc.ERR_UNSUPPORTED
+    assert create(128, 8, pool=None) == kvc.ERR_STORAGE
+    assert create(128, 8, pool=p + 4) == kvc.ERR_STORAGE
+    need_each = 2 * 8 * 2 * 128 * 128 * 2               # L * n_blocks * H_kv * block * d_head * 2 bytes
+    assert create(128, 8, nbytes=need_each - 1) == kvc.ERR_STORAGE
+    used, total = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.kvc_paged_blocks(None, ctypes.byref(used), ctypes.byref(total)) == kvc.ERR_ARG
+    tab = (ctypes.c_int32 * 4)()
+    assert lib.kvc_block_table(None, tab, 4) == kvc.ERR_ARG
