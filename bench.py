@@ -331,6 +331,56 @@ def latent_bench():
     return res
 
 
+def paged_bench(lengths, us_contiguous: float):
+    """The batched-decode workload on paged caches (blocks of 128 and 256
+    positions): each cache grows one block per row per append, so a row's
+    blocks are interleaved with every other row's in the pool, as decode
+    growth leaves them; then the rows are cut to the drawn lengths, which
+    gives the blocks past each length back. One attention call (T=1) per
+    repetition over 4 rotating instances, HIP events on the stream; the held
+    pool bytes against the contiguous cache's 2 B H_kv max_len d_h itemsize."""
+    import torch
+    from kv_cached_gqa_amd.kvc import PagedKVCache
+    from kv_cached_gqa_amd import work
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(17)
+    att = work.attend_bytes(lengths, 1, HQ, HKV, D, "bf16", "bf16")
+    contiguous_bytes = 2 * B * HKV * MAX_LEN * D * 2
+    res = {"workload": WORKLOAD + ", paged", "contiguous_us_per_attend": round(us_contiguous, 2)}
+    st = torch.cuda.current_stream()
+    for bs in (128, 256):
+        caches = []
+        for c in range(4):
+            pc = PagedKVCache(1, HKV, D, MAX_LEN, batch=B, n_q_heads=HQ, dtype="bf16", device=dev, block_size=bs)
+            chunk = torch.randn((B, HKV, bs, D), generator=gen, device=dev, dtype=torch.bfloat16)
+            while int(pc.seq_len()[0]) < MAX_LEN - 1:
+                t = min(bs, MAX_LEN - 1 - int(pc.seq_len()[0]))
+                part = chunk if t == bs else chunk[:, :, :t].contiguous()
+                pc.append(0, part, part)
+            del chunk, part
+            pc.truncate(lengths)
+            kv = torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.bfloat16)
+            pc.append(0, kv, kv)
+            caches.append(pc)
+        q = torch.randn((B, HQ, 1, D), generator=gen, device=dev, dtype=torch.bfloat16)
+        out = torch.empty((B, HQ, 1, D), device=dev, dtype=torch.float32)
+        for i in range(8):
+            caches[i % 4].attend(0, q, out=out)
+        ms = event_time(lambda i: caches[i % 4].attend(0, q, out=out), 200, st)
+        used, _ = caches[0].blocks()
+        held = 2 * used * HKV * bs * D * 2
+        gbs = att / (ms * 1e-3) / 1e9
+        res[f"block{bs}"] = {"us_per_attend": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                             "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+                             "vs_contiguous": round(us_contiguous / (ms * 1e3), 3),
+                             "held_bytes": held, "held_vs_contiguous": round(held / contiguous_bytes, 3)}
+        for pc in caches:
+            pc.close()
+        torch.cuda.synchronize()
+    return res
+
+
 def long_ctx_bench():
     """Long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys;
     attention calls with T=1 and T=4 (a draft block) after one append."""
@@ -445,7 +495,7 @@ def main():
     if not args.no_extra:
         rec["extra"] = {"chunked_prefill": prefill_bench(), "long_context_decode": long_ctx_bench(),
                         "tiny_decoder": tiny_decoder_bench(), "rope": rope_bench(),
-                        "latent_cache": latent_bench()}
+                        "latent_cache": latent_bench(), "paged_decode": paged_bench(lengths, us_attend)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(lengths, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
