@@ -437,10 +437,8 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
 
     // Dispatch: a 16-bit cache with more than 32 query rows per KV head (a prefill
     // chunk) runs on the matrix cores; everything else on the split-K decode kernel.
-    // A paged cache runs every chunk on the split-K vector kernel.
     const bool paged = c->block_size > 0;
-    if (!paged && cf.dtype != KVC_F32 && static_cast<int64_t>(T) * G > 32 &&
-        kvc::prefill_supported(cf.d_head, cf.dtype)) {
+    if (cf.dtype != KVC_F32 && static_cast<int64_t>(T) * G > 32 && kvc::prefill_supported(cf.d_head, cf.dtype)) {
         const int Gc = std::min(G, 32);
         for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
             const int rows = std::min(kMaxRowsPerLaunch, cf.batch - row0);
@@ -470,6 +468,15 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
                 a.q_dtype = q_dtype;
                 a.st_dtype = cf.dtype;
                 a.scale_log2 = scale_log2;
+                if (paged) {
+                    a.layer_off = layer * pool_layer_elems(c);
+                    a.row_stride = 0;
+                    a.head_stride = 0;
+                    a.btab = c->d_table + static_cast<int64_t>(row0) * c->width;
+                    a.btab_stride = c->width;
+                    a.bshift = c->bshift;
+                    a.pool_blocks = c->n_blocks;
+                }
                 for (int b = 0; b < rows; ++b) a.offset[b] = static_cast<int32_t>(f[row0 + b] - T);
                 if (kvc::launch_prefill(a, s) != hipSuccess) return KVC_ERR_HIP;
             }
@@ -477,9 +484,9 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
         return KVC_OK;
     }
 
-    // Slabs of at most kMaxDecodeRows (paged: kMaxPagedDecodeRows) query rows
-    // per KV head: Gc query heads of the group times Tc query positions.
-    const int slab = paged ? kvc::kMaxPagedDecodeRows : kMaxDecodeRows;
+    // Slabs of at most kMaxDecodeRows (paged fp32: kMaxPagedDecodeRows) query
+    // rows per KV head: Gc query heads of the group times Tc query positions.
+    const int slab = paged && cf.dtype == KVC_F32 ? kvc::kMaxPagedDecodeRows : kMaxDecodeRows;
     const int Gc = std::min(G, slab);
     const int Tc = std::max(1, slab / Gc);
     for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {

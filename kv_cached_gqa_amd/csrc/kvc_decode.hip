@@ -953,7 +953,7 @@ struct MCfg : TileLayout<D> {
     static_assert((NS - 1) * STAGE_BYTES + L::TILE_BYTES + 24 * D * 2 < 65536, "LDS read offsets fit 16 bits");
 };
 
-template <int D, int ST>
+template <int D, int ST, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_mfma(DecodeArgs a) {
     using P = MCfg<D>;
@@ -1028,10 +1028,37 @@ void decode_mfma(DecodeArgs a) {
     Seg is = locate(x_begin);
     int is_t = 0;
     bool is_live = true;
+    // paged storage: pool offsets of head is.g's rows in the blocks of logical
+    // blocks pg_blk and pg_blk + 1 of the issue cursor's unit (a 32-key tile
+    // spans at most these two); the next block's entry is read by a scalar load
+    // when the cursor enters a block
+    int pg_blk = 0;
+    int64_t pg_base = 0, pg_next = 0;
+    auto pg_phys = [&](int blk) __attribute__((always_inline)) -> int64_t {
+        const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
+        const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
+        int p = tab[static_cast<int64_t>(is.b) * a.btab_stride + bi];
+        p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
+        return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + is.g) << a.bshift) * D;
+    };
+    auto pg_enter = [&]() __attribute__((always_inline)) {
+        pg_blk = is.j0 >> a.bshift;
+        pg_base = pg_phys(pg_blk);
+        pg_next = pg_phys(pg_blk + 1);
+    };
+    if constexpr (PAGED) pg_enter();
     auto issue = [&](auto slot_c) __attribute__((always_inline)) {
         constexpr int S = decltype(slot_c)::value;
         uint16_t* kd = smem + S * P::STAGE_BYTES / 2;
         uint16_t* vd = kd + P::TILE;
+        if constexpr (PAGED) {
+            const int blk = (is.j0 + is_t * kBN) >> a.bshift;
+            if (is_live && blk != pg_blk) {       // the tile starts in the next block
+                pg_blk = blk;
+                pg_base = pg_next;
+                pg_next = pg_phys(blk + 1);
+            }
+        }
 #pragma unroll
         for (int n = 0; n < NLD; ++n) {
             const int e = n * 512 + lane * 8;    // element offset inside the tile
@@ -1039,7 +1066,12 @@ void decode_mfma(DecodeArgs a) {
             const int sl = (e % D) >> 3;
             int j = is.j0 + is_t * kBN + r;
             j = j < is.j1 ? j : is.j1 - 1;
-            const int64_t row = is.head + static_cast<int64_t>(j) * D;
+            int64_t row;
+            if constexpr (PAGED)
+                row = ((j >> a.bshift) == pg_blk ? pg_base : pg_next) +
+                      static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D;
+            else
+                row = is.head + static_cast<int64_t>(j) * D;
             __builtin_amdgcn_global_load_lds(
                 (const void __attribute__((address_space(1)))*)(kg + row + P::kslot(r, sl) * 8),
                 (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, 0);
@@ -1053,6 +1085,7 @@ void decode_mfma(DecodeArgs a) {
             } else {
                 is = locate(is.x_end);
                 is_t = 0;
+                if constexpr (PAGED) pg_enter();
             }
         }
     };
@@ -1369,7 +1402,12 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     a.rec_rows = 32;
     split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN);
-    decode_mfma<D, ST><<<a.n_blocks, 64, 0, s>>>(a);
+    if (a.btab) {
+        if ((1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks
+        decode_mfma<D, ST, true><<<a.n_blocks, 64, 0, s>>>(a);
+    } else {
+        decode_mfma<D, ST, false><<<a.n_blocks, 64, 0, s>>>(a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return combine_if_split<D>(a, s);
@@ -1378,7 +1416,10 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
 template <int D, int ST>
 hipError_t run_r(DecodeArgs& a, hipStream_t s) {
     const int rows = a.Gc * a.Tc;
-    if (a.btab) {                 // paged storage: the vector kernel
+    if (a.btab) {                 // paged storage: the vector kernel, the matrix-core kernel for 16 bits
+        if constexpr (ST != F32) {
+            if (rows >= KVC_DECODE_MFMA_MIN_ROWS) return run_mfma<D, ST>(a, s);
+        }
         if (rows > kMaxPagedDecodeRows) return hipErrorInvalidValue;
         return rows <= 4 ? run<D, ST, 4>(a, s) : run<D, ST, 8>(a, s);
     }

@@ -15,7 +15,7 @@ constexpr int kMaxRowsPerLaunch = 256;
 constexpr int kMaxRopePairs = 64;
 // Query rows (query heads of one group x query positions) of one decode slab.
 constexpr int kMaxDecodeRows = 32;
-// The same for a paged cache (read by the vector kernel only).
+// The same for a paged fp32 cache (16-bit paged caches take kMaxDecodeRows).
 constexpr int kMaxPagedDecodeRows = 8;
 // Rows per workspace record of the split-K workspace as allocated (a launch
 // with slabs of more rows uses fewer, wider records).
@@ -95,8 +95,8 @@ struct DecodeArgs {
     float scale_log2;        // log2(e) / sqrt(D)
     // paged storage (btab non-null): key j of unit (b, g) sits in physical block
     // btab[b * btab_stride + (j >> bshift)] of the layer's pool, at element
-    // layer_off + ((block * Hkv + g) << bshift + (j & mask)) * D; only the
-    // vector kernel reads paged storage
+    // layer_off + ((block * Hkv + g) << bshift + (j & mask)) * D; the vector and
+    // matrix-core kernels read paged storage, the fp32 row-split kernel does not
     const int32_t* btab;     // block table from row `row0` on
     int32_t btab_stride, bshift, pool_blocks;
     int64_t prefix[kMaxRowsPerLaunch + 1];  // exclusive prefix of n_b * H_kv
@@ -122,6 +122,9 @@ struct PrefillArgs {
     int32_t q_per_block;     // queries per work-group
     int32_t q_dtype, st_dtype;
     float scale_log2;
+    // paged storage (btab non-null), as in DecodeArgs
+    const int32_t* btab;
+    int32_t btab_stride, bshift, pool_blocks;
     int32_t offset[kMaxRowsPerLaunch];   // per row: s_b, the chunk's query offset
 };
 

@@ -64,7 +64,7 @@ struct PCfg : TileLayout<D> {
     static_assert(V_OFF + (kNB - 1) * L::TILE_BYTES + 24 * D * 2 < 65536, "LDS read offsets fit 16 bits");
 };
 
-template <int D, int ST>
+template <int D, int ST, bool PAGED>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(KVC_PF_WAVES_PER_EU)))
 void prefill_attn(PrefillArgs a) {
     using P = PCfg<D>;
@@ -93,7 +93,8 @@ void prefill_attn(PrefillArgs a) {
     int q_hi = q_lo + a.q_per_block - 1;
     if (q_hi > a.i0 + a.Ti - 1) q_hi = a.i0 + a.Ti - 1;
 
-    const int64_t head_base = a.layer_off + b * a.row_stride + g * a.head_stride;
+    // contiguous storage: this head's rows; paged storage: the layer's pool
+    const int64_t head_base = PAGED ? a.layer_off : a.layer_off + b * a.row_stride + g * a.head_stride;
     const uint16_t* kg = static_cast<const uint16_t*>(a.k_cache) + head_base;
     const uint16_t* vg = static_cast<const uint16_t*>(a.v_cache) + head_base;
 
@@ -119,10 +120,23 @@ void prefill_attn(PrefillArgs a) {
     //    (16 bytes per lane, lane i at byte 16 * i of the instruction's 1 KB).
     //    Tiles past the range are issued too, clamped to the last key, so every
     //    wave issues the same number of loads per stage.
+    //    Paged storage: a 32-key tile lies in one block (blocks hold a power of
+    //    two >= 64 keys); a tile past the range is clamped to the last tile, and
+    //    the block's pool offset comes from a scalar load of the table.
     auto issue = [&](auto slot_c, int t) {
         constexpr int S = decltype(slot_c)::value;
         uint16_t* kd = smem + (P::K_OFF + S * P::TILE_BYTES) / 2;
         uint16_t* vd = smem + (P::V_OFF + S * P::TILE_BYTES) / 2;
+        int64_t blk_base = 0;
+        if constexpr (PAGED) {
+            t = t < n_tiles ? t : n_tiles - 1;
+            const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
+            int bi = (t * kBN) >> a.bshift;
+            bi = bi < a.btab_stride ? bi : a.btab_stride - 1;
+            int p = tab[static_cast<int64_t>(b) * a.btab_stride + bi];
+            p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
+            blk_base = ((static_cast<int64_t>(p) * a.Hkv + g) << a.bshift) * D;
+        }
 #pragma unroll
         for (int n = wave; n < P::NLD; n += kPWaves) {
             const int e = n * 512 + lane * 8;       // element offset inside the tile
@@ -130,7 +144,11 @@ void prefill_attn(PrefillArgs a) {
             const int sl = (e % D) >> 3;
             int j = t * kBN + r;
             j = j < n_keys ? j : n_keys - 1;
-            const int64_t row = static_cast<int64_t>(j) * D;
+            int64_t row;
+            if constexpr (PAGED)
+                row = blk_base + static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D;
+            else
+                row = static_cast<int64_t>(j) * D;
             __builtin_amdgcn_global_load_lds(
                 (const void __attribute__((address_space(1)))*)(kg + row + P::kslot(r, sl) * 8),
                 (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, 0);
@@ -322,12 +340,21 @@ void prefill_attn(PrefillArgs a) {
     }
 }
 
-template <int D>
-hipError_t run_p(const PrefillArgs& a, hipStream_t s, unsigned grid) {
-    if (a.st_dtype == BF16) prefill_attn<D, BF16><<<grid, kPThreads, 0, s>>>(a);
-    else if (a.st_dtype == F16) prefill_attn<D, F16><<<grid, kPThreads, 0, s>>>(a);
+template <int D, bool PAGED>
+hipError_t run_pp(const PrefillArgs& a, hipStream_t s, unsigned grid) {
+    if (a.st_dtype == BF16) prefill_attn<D, BF16, PAGED><<<grid, kPThreads, 0, s>>>(a);
+    else if (a.st_dtype == F16) prefill_attn<D, F16, PAGED><<<grid, kPThreads, 0, s>>>(a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t run_p(const PrefillArgs& a, hipStream_t s, unsigned grid) {
+    if (a.btab) {
+        if ((1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within one block
+        return run_pp<D, true>(a, s, grid);
+    }
+    return run_pp<D, false>(a, s, grid);
 }
 
 }  // namespace
