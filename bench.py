@@ -201,17 +201,26 @@ def call_time_us(fn, reps, stream) -> float:
     return times[len(times) // 2]
 
 
-def prefill_bench():
+def new_cache(n_kv_heads, d_head, max_len, batch, n_q_heads, dev, block=None):
+    """A bf16 cache of one layer, contiguous or paged (blocks of `block`)."""
+    from kv_cached_gqa_amd.kvc import KVCache, PagedKVCache
+    if block is None:
+        return KVCache(1, n_kv_heads, d_head, max_len, batch=batch, n_q_heads=n_q_heads, dtype="bf16", device=dev)
+    return PagedKVCache(1, n_kv_heads, d_head, max_len, batch=batch, n_q_heads=n_q_heads, dtype="bf16", device=dev,
+                        block_size=block)
+
+
+def prefill_bench(block=None):
     """Chunked prefill: B=4, H_q=32, H_kv=8, d_h=128, bf16, 32 chunks of T=512
-    appended and attended in turn (queries at s = 0, 512, ..., 15872)."""
+    appended and attended in turn (queries at s = 0, 512, ..., 15872); on a
+    paged cache with blocks of `block` positions when given."""
     import torch
-    from kv_cached_gqa_amd.kvc import KVCache
     from kv_cached_gqa_amd import work
     b, hq, hkv, d, t, nch = 4, 32, 8, 128, 512, 32
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(11)
-    cache = KVCache(1, hkv, d, t * nch, batch=b, n_q_heads=hq, dtype="bf16", device=dev)
+    cache = new_cache(hkv, d, t * nch, b, hq, dev, block)
     ks = [torch.randn((b, hkv, t, d), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(4)]
     vs = [torch.randn((b, hkv, t, d), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(4)]
     qs = [torch.randn((b, hq, t, d), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(4)]
@@ -378,20 +387,25 @@ def paged_bench(lengths, us_contiguous: float):
         for pc in caches:
             pc.close()
         torch.cuda.synchronize()
+    # the matrix-core paths on paged storage: long-context decode (8 and 32
+    # query rows per KV head) and chunked prefill, blocks of 128
+    res["long_context_decode_block128"] = long_ctx_bench(128)
+    pf = prefill_bench(128)
+    res["chunked_prefill_block128"] = {k: pf[k] for k in ("ms_per_run", "tflops", "pct_peak_bf16_mfma")}
     return res
 
 
-def long_ctx_bench():
+def long_ctx_bench(block=None):
     """Long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys;
-    attention calls with T=1 and T=4 (a draft block) after one append."""
+    attention calls with T=1 and T=4 (a draft block) after one append; on a
+    paged cache with blocks of `block` positions when given."""
     import torch
-    from kv_cached_gqa_amd.kvc import KVCache
     from kv_cached_gqa_amd import work
     b, hq, hkv, d, s0, ml = 8, 64, 8, 128, 32768, 32776
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(13)
-    cache = KVCache(1, hkv, d, ml, batch=b, n_q_heads=hq, dtype="bf16", device=dev)
+    cache = new_cache(hkv, d, ml, b, hq, dev, block)
     for _ in range(4):
         k = torch.randn((b, hkv, s0 // 4, d), generator=gen, device=dev, dtype=torch.bfloat16)
         cache.append(0, k, k)
