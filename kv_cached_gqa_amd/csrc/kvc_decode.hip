@@ -66,6 +66,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #ifndef KVC_DECODE_BLOCKS_PER_CU
 #define KVC_DECODE_BLOCKS_PER_CU 2
 #endif
+#ifndef KVC_DECODE_KV_CPOL
+// Cache-policy bits of the vector kernels' K/V loads: non-temporal (each key
+// and value is read once per call; measured ~9% faster on the batched-decode
+// workload than the default policy).
+#define KVC_DECODE_KV_CPOL 2
+#endif
+#ifndef KVC_DECODE_MFMA_KV_CPOL
+#define KVC_DECODE_MFMA_KV_CPOL 2 // the same for the matrix-core decode kernel (~11% faster)
+#endif
 #ifndef KVC_DECODE_LATE_PCT
 #define KVC_DECODE_LATE_PCT 70       // slice of a later-dispatched work-group, % of a first-round one
 #endif
@@ -418,9 +427,11 @@ void decode_attn(DecodeArgs a) {
             }
             uint8_t* dst = ring_w + S * C::STAGE_BYTES + u * 2048;
             __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kc + off),
-                                             (void __attribute__((address_space(3)))*)(dst), 16, 0, 0);
+                                             (void __attribute__((address_space(3)))*)(dst), 16, 0,
+                                             KVC_DECODE_KV_CPOL);
             __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vc + off),
-                                             (void __attribute__((address_space(3)))*)(dst + 1024), 16, 0, 0);
+                                             (void __attribute__((address_space(3)))*)(dst + 1024), 16, 0,
+                                             KVC_DECODE_KV_CPOL);
         }
         if (is_live) ++is_t;
     };
@@ -748,9 +759,11 @@ void decode_rows(DecodeArgs a) {
             const int64_t off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
             uint8_t* dst = ring + S * C::STAGE_BYTES + bi * 2048;
             __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kc + off),
-                                             (void __attribute__((address_space(3)))*)(dst), 16, 0, 0);
+                                             (void __attribute__((address_space(3)))*)(dst), 16, 0,
+                                             KVC_DECODE_KV_CPOL);
             __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vc + off),
-                                             (void __attribute__((address_space(3)))*)(dst + 1024), 16, 0, 0);
+                                             (void __attribute__((address_space(3)))*)(dst + 1024), 16, 0,
+                                             KVC_DECODE_KV_CPOL);
         }
         if (is_live && ++is_t == is.nbat) {
             if (is.x_end >= x_end) {
@@ -1074,10 +1087,10 @@ void decode_mfma(DecodeArgs a) {
                 row = is.head + static_cast<int64_t>(j) * D;
             __builtin_amdgcn_global_load_lds(
                 (const void __attribute__((address_space(1)))*)(kg + row + P::kslot(r, sl) * 8),
-                (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, 0);
+                (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, KVC_DECODE_MFMA_KV_CPOL);
             __builtin_amdgcn_global_load_lds(
                 (const void __attribute__((address_space(1)))*)(vg + row + P::vchunk(r, sl) * 8),
-                (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0, 0);
+                (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0, KVC_DECODE_MFMA_KV_CPOL);
         }
         if (is_live && ++is_t == is.nbat) {
             if (is.x_end >= x_end) {

@@ -40,6 +40,10 @@ namespace {
 #ifndef KVC_PF_WAVES_PER_EU
 #define KVC_PF_WAVES_PER_EU 2   // two waves per SIMD: one's softmax overlaps the other's MFMAs
 #endif
+#ifndef KVC_PF_KV_CPOL
+#define KVC_PF_KV_CPOL 0      // cache-policy bits of the K/V tile loads (default: the query blocks
+                              // of a unit share its tiles in L2; non-temporal measured ~1% slower)
+#endif
 #ifndef KVC_PF_STAGES
 #define KVC_PF_STAGES 3       // key/value tiles in the LDS ring
 #endif
@@ -151,10 +155,10 @@ void prefill_attn(PrefillArgs a) {
                 row = static_cast<int64_t>(j) * D;
             __builtin_amdgcn_global_load_lds(
                 (const void __attribute__((address_space(1)))*)(kg + row + P::kslot(r, sl) * 8),
-                (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, 0);
+                (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, KVC_PF_KV_CPOL);
             __builtin_amdgcn_global_load_lds(
                 (const void __attribute__((address_space(1)))*)(vg + row + P::vchunk(r, sl) * 8),
-                (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0, 0);
+                (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0, KVC_PF_KV_CPOL);
         }
     };
     issue(std::integral_constant<int, 0>{}, 0);
