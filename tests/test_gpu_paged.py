@@ -282,3 +282,32 @@ def test_paged_batched_decode_full_size():
     _same_storage(cc, pc, range(shape.n_layers))
     cc.close()
     pc.close()
+
+
+def test_paged_batch_wider_than_one_launch():
+    """B=300 rows (two launches of at most 256 rows; the second launch's table
+    starts at row 256), ragged lengths: the vector kernel (2 rows per KV head),
+    the matrix-core decode kernel (8 rows) and the prefill kernel (a 24-position
+    chunk at 8 heads per group) give the contiguous cache's bits."""
+    import torch
+    log("paged B=300 rows")
+    rng = np.random.default_rng(995)
+    B, Hkv, D, max_len = 300, 2, 64, 330
+    for G in (2, 8):
+        cc, pc = _pair(1, B, G * Hkv, Hkv, D, max_len, "bf16", 64)
+        k, v = (rng.standard_normal((B, Hkv, 290, D), dtype=np.float32) for _ in range(2))
+        _both_append(cc, pc, 0, k, v)
+        lens = rng.integers(0, 291, size=B)
+        cc.truncate(lens)
+        pc.truncate(lens)
+        for T in (1, 24, 1):
+            k, v = (rng.standard_normal((B, Hkv, T, D), dtype=np.float32) for _ in range(2))
+            _both_append(cc, pc, 0, k, v)
+            q = to_device(rng.standard_normal((B, G * Hkv, T, D), dtype=np.float32), "bf16", DEV)
+            oc, op = cc.attend(0, q), pc.attend(0, q)
+            torch.cuda.synchronize()
+            assert torch.equal(oc.view(torch.int32), op.view(torch.int32)), (G, T)
+        _check_table(pc)
+        _same_storage(cc, pc, [0])
+        cc.close()
+        pc.close()
