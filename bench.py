@@ -110,16 +110,27 @@ def gpu_bench(args, lengths):
     torch.cuda.synchronize()
 
     def step(i):
+        # one decode step: roll back to the drawn lengths, append the new token's
+        # keys and values, attend (one call: the fused append and attention)
+        c = i % args.instances
+        cache = caches[c]
+        cache.truncate(lengths)
+        cache.append_attend(0, ks[i % n_in], vs[i % n_in], qs[i % n_in], out=outs[c])
+
+    def step_two_calls(i):
         c = i % args.instances
         cache = caches[c]
         cache.truncate(lengths)
         cache.append(0, ks[i % n_in], vs[i % n_in])
         cache.attend(0, qs[i % n_in], out=outs[c])
 
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step_two_calls(i)
+    ms_step_two = event_time(lambda i: step_two_calls(args.warmup + i), args.steps, stream)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     e0.record(stream)
@@ -146,7 +157,7 @@ def gpu_bench(args, lengths):
     us_attend = a0.elapsed_time(a1) * 1e3 / reps
     for c in caches:
         c.close()
-    return ms_step, us_attend, wall
+    return ms_step, us_attend, wall, ms_step_two
 
 
 def pmc_workload(lengths):
@@ -477,7 +488,7 @@ def main():
         pmc_workload(lengths)
         return
     att, app = step_bytes(lengths)
-    ms_step, us_attend, wall = gpu_bench(args, lengths)
+    ms_step, us_attend, wall, ms_step_two = gpu_bench(args, lengths)
     from kv_cached_gqa_amd.measure import stored_traffic
     traffic = stored_traffic()
     gbs = (att + app) / (ms_step * 1e-3) / 1e9
@@ -499,6 +510,8 @@ def main():
                    "max_len": MAX_LEN, "T": 1, "cache_instances": args.instances,
                    "mean_context": float(np.mean(lengths) + 1)},
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "step": "truncate to the drawn lengths, then kvc_append_attend (append and attention in one call)",
+        "ms_per_step_append_then_attend": round(ms_step_two, 5),
         "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
         "bytes_per_step": att + app,
         "roofline": {"bound": "hbm", "kernel": "decode attention: decode_attn + decode_combine",

@@ -142,6 +142,25 @@ int kvc_rope_q(const kvc_cache* cache, int32_t layer, void* q, int32_t q_dtype, 
 int kvc_attend(kvc_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
                int32_t T, float* out, void* stream);
 
+/* Append a chunk, then attend to everything the layer holds, in one call: the
+ * same state change and bit-identical results as kvc_append(k_new, v_new,
+ * in_dtype, T) followed by kvc_attend(q, q_dtype, T, out) ("KV cache, ...",
+ * section 2.3: a pass appends its chunk, then attends over all stored
+ * positions; "kv-cache-decoding", steps 5-6).
+ *  When in_dtype is the storage dtype and T * (n_q_heads / n_kv_heads) is at
+ *  most 4 (8 for an fp32 cache), a decode step, the attention kernel reads the
+ *  chunk's keys and values from k_new and v_new and the merge pass that
+ *  follows it stores them in the cache, so no separate append launch runs.
+ *  Otherwise the call runs kvc_append, then kvc_attend. Either way k_new, v_new
+ *  and q must stay valid until the stream has passed the call. A NaN input is
+ *  stored as the canonical quiet NaN by kvc_append but copied bit for bit by
+ *  the fused path; every other value is stored the same way.
+ * Errors: those of kvc_append and kvc_attend; on an argument, dtype or
+ * capacity error nothing changes. */
+int kvc_append_attend(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+                      int32_t in_dtype, const void* q, int32_t q_dtype, int32_t T, float* out,
+                      void* stream);
+
 /* Per-row lengths ("KV cache, ...", section 2.3, seq_len).
  *  layer = -1: the committed length s_b = min over layers of fill[layer][b];
  *  0 <= layer < n_layers: that layer's fill count.

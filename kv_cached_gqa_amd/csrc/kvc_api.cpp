@@ -417,15 +417,17 @@ int kvc_rope_q(const kvc_cache* c, int32_t layer, void* q, int32_t q_dtype, int3
     return KVC_OK;
 }
 
-int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int32_t T, float* out, void* stream) {
-    if (!c || !q || !out) return KVC_ERR_ARG;
+}  // extern "C"
+
+namespace {
+
+// Attention of the last T positions of `layer` (arguments checked by the caller).
+// k_new, v_new non-null: a fused append whose chunk the decode kernel reads
+// from the input (one slab on the vector kernel; the fills already count it).
+int attend_impl(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int32_t T, float* out, void* stream,
+                const void* k_new, const void* v_new) {
     const kvc_config& cf = c->cfg;
-    if (layer < 0 || layer >= cf.n_layers || T < 1) return KVC_ERR_ARG;
-    if (!dtype_ok(q_dtype)) return KVC_ERR_DTYPE;
-    if (!aligned16(q) || !aligned16(out)) return KVC_ERR_ARG;
     const int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
-    for (int b = 0; b < cf.batch; ++b)
-        if (f[b] < T) return KVC_ERR_STATE;
     const int rc = ensure_workspace(c);
     if (rc != KVC_OK) return rc;
 
@@ -438,7 +440,8 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
     // Dispatch: a 16-bit cache with more than 32 query rows per KV head (a prefill
     // chunk) runs on the matrix cores; everything else on the split-K decode kernel.
     const bool paged = c->block_size > 0;
-    if (cf.dtype != KVC_F32 && static_cast<int64_t>(T) * G > 32 && kvc::prefill_supported(cf.d_head, cf.dtype)) {
+    if (!k_new && cf.dtype != KVC_F32 && static_cast<int64_t>(T) * G > 32 &&
+        kvc::prefill_supported(cf.d_head, cf.dtype)) {
         const int Gc = std::min(G, 32);
         for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
             const int rows = std::min(kMaxRowsPerLaunch, cf.batch - row0);
@@ -536,11 +539,63 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
                 }
                 a.prefix[rows] = acc;
                 a.total_keys = acc;
+                a.k_new = k_new;
+                a.v_new = v_new;
                 if (kvc::launch_decode(a, s) != hipSuccess) return KVC_ERR_HIP;
             }
         }
     }
     return KVC_OK;
+}
+
+// Whether append + attend of a chunk can run as one decode launch: the input
+// already has the storage type and the chunk is one slab of the vector kernel.
+bool fusable(const kvc_cache* c, int32_t in_dtype, int32_t T) {
+    const kvc_config& cf = c->cfg;
+    const int64_t rows = static_cast<int64_t>(T) * (cf.n_q_heads / cf.n_kv_heads);
+    return in_dtype == cf.dtype && rows <= (cf.dtype == KVC_F32 ? 8 : 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int32_t T, float* out, void* stream) {
+    if (!c || !q || !out) return KVC_ERR_ARG;
+    const kvc_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || T < 1) return KVC_ERR_ARG;
+    if (!dtype_ok(q_dtype)) return KVC_ERR_DTYPE;
+    if (!aligned16(q) || !aligned16(out)) return KVC_ERR_ARG;
+    const int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
+    for (int b = 0; b < cf.batch; ++b)
+        if (f[b] < T) return KVC_ERR_STATE;
+    return attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr);
+}
+
+int kvc_append_attend(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new, int32_t in_dtype,
+                      const void* q, int32_t q_dtype, int32_t T, float* out, void* stream) {
+    if (!c || !k_new || !v_new || !q || !out) return KVC_ERR_ARG;
+    const kvc_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || T < 1) return KVC_ERR_ARG;
+    if (!dtype_ok(in_dtype) || !dtype_ok(q_dtype)) return KVC_ERR_DTYPE;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out)) return KVC_ERR_ARG;
+    if (!fusable(c, in_dtype, T)) {
+        const int rc = append_impl(c, layer, k_new, v_new, in_dtype, T, 0.0, stream);
+        if (rc != KVC_OK) return rc;
+        return attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr);
+    }
+    int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
+    for (int b = 0; b < cf.batch; ++b)
+        if (f[b] + T > cf.max_len) return KVC_ERR_CAPACITY;
+    const int rc = ensure_workspace(c);
+    if (rc != KVC_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (c->block_size) {
+        const int rg = grow_blocks(c, f, T, s);
+        if (rg != KVC_OK) return rg;
+    }
+    for (int b = 0; b < cf.batch; ++b) f[b] += T;
+    return attend_impl(c, layer, q, q_dtype, T, out, stream, k_new, v_new);
 }
 
 int kvc_seq_len(const kvc_cache* c, int32_t layer, int64_t* out_lens) {

@@ -425,11 +425,22 @@ void decode_attn(DecodeArgs a) {
             } else {
                 off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
             }
+            const char* kp = kc;
+            const char* vp = vc;
+            if (a.k_new != nullptr) {
+                // fused append: the chunk's new keys come from the caller's input
+                const int jn = j - (is.n_b - a.T);
+                if (jn >= 0) {
+                    kp = static_cast<const char*>(a.k_new);
+                    vp = static_cast<const char*>(a.v_new);
+                    off = ((((static_cast<int64_t>(a.row0 + is.b) * a.Hkv + is.g) * a.T + jn) * D) + sub * EPC) * ESZ;
+                }
+            }
             uint8_t* dst = ring_w + S * C::STAGE_BYTES + u * 2048;
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kc + off),
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kp + off),
                                              (void __attribute__((address_space(3)))*)(dst), 16, 0,
                                              KVC_DECODE_KV_CPOL);
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vc + off),
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vp + off),
                                              (void __attribute__((address_space(3)))*)(dst + 1024), 16, 0,
                                              KVC_DECODE_KV_CPOL);
         }
@@ -1271,6 +1282,32 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     const int b = u / a.Hkv;
     const int g = u - b * a.Hkv;
     const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
+    if (a.k_new != nullptr && blockIdx.y == gridDim.y - 1) {
+        // fused append: store unit (b, g)'s T new keys and values at slots
+        // n_b - T .. n_b - 1 (bit copies, the input has the storage type)
+        const int esz = a.st_dtype == F32 ? 4 : 2;
+        const int64_t src0 = ((static_cast<int64_t>(a.row0 + b) * a.Hkv + g) * a.T) * D;
+        for (int e = threadIdx.x; e < a.T * D; e += 256) {
+            const int t = e / D, d = e - (e / D) * D;
+            const int64_t p = n_b - a.T + t;
+            int64_t dst;
+            if (a.btab != nullptr) {
+                int blk = a.btab[static_cast<int64_t>(b) * a.btab_stride + (p >> a.bshift)];
+                blk = blk < 0 ? 0 : (blk >= a.pool_blocks ? a.pool_blocks - 1 : blk);
+                dst = a.layer_off + (((static_cast<int64_t>(blk) * a.Hkv + g) << a.bshift) + (p & ((1 << a.bshift) - 1))) * D + d;
+            } else {
+                dst = a.layer_off + b * a.row_stride + g * a.head_stride + p * D + d;
+            }
+            if (esz == 4) {
+                static_cast<float*>(const_cast<void*>(a.k_cache))[dst] = static_cast<const float*>(a.k_new)[src0 + e];
+                static_cast<float*>(const_cast<void*>(a.v_cache))[dst] = static_cast<const float*>(a.v_new)[src0 + e];
+            } else {
+                static_cast<uint16_t*>(const_cast<void*>(a.k_cache))[dst] = static_cast<const uint16_t*>(a.k_new)[src0 + e];
+                static_cast<uint16_t*>(const_cast<void*>(a.v_cache))[dst] = static_cast<const uint16_t*>(a.v_new)[src0 + e];
+            }
+        }
+        return;
+    }
     const int64_t ustart = a.prefix[b] + g * n_b;
     const int k_first = static_cast<int>(decode_slice_of(a, ustart));
     const int k_last = static_cast<int>(decode_slice_of(a, ustart + n_b - 1));
@@ -1371,8 +1408,10 @@ hipError_t combine_if_split(DecodeArgs& a, hipStream_t s) {
             split = decode_slice_of(a, us) != decode_slice_of(a, us + n_b - 1);
         }
     }
-    if (!split) return hipSuccess;
-    const dim3 grid(a.rows * a.Hkv, (a.Gc * a.Tc * D + 255) / 256);
+    // a fused append adds one row of work-groups that store the new keys and values
+    if (!split && a.k_new == nullptr) return hipSuccess;
+    const unsigned merge_rows = split ? (a.Gc * a.Tc * D + 255) / 256 : 0;
+    const dim3 grid(a.rows * a.Hkv, merge_rows + (a.k_new != nullptr ? 1 : 0));
     decode_combine<D><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -1429,6 +1468,11 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
 template <int D, int ST>
 hipError_t run_r(DecodeArgs& a, hipStream_t s) {
     const int rows = a.Gc * a.Tc;
+    if (a.k_new != nullptr) {     // fused append: one slab on the vector kernel
+        if (rows > (ST == F32 ? 8 : KVC_DECODE_MFMA_MIN_ROWS - 1) || a.Gc != a.G || a.Tc != a.T || a.r0 || a.i0)
+            return hipErrorInvalidValue;
+        return rows <= 4 ? run<D, ST, 4>(a, s) : run<D, ST, 8>(a, s);
+    }
     if (a.btab) {                 // paged storage: the vector kernel, the matrix-core kernel for 16 bits
         if constexpr (ST != F32) {
             if (rows >= KVC_DECODE_MFMA_MIN_ROWS) return run_mfma<D, ST>(a, s);

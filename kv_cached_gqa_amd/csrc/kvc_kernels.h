@@ -99,6 +99,12 @@ struct DecodeArgs {
     // matrix-core kernels read paged storage, the fp32 row-split kernel does not
     const int32_t* btab;     // block table from row `row0` on
     int32_t btab_stride, bshift, pool_blocks;
+    // fused append (single slab on the vector kernel): the chunk's T new keys
+    // and values, [B][Hkv][T][D] of the storage type (whole-batch base), are
+    // read from here instead of the cache, and the merge pass stores them in the
+    // cache afterwards; null: the cache already holds them
+    const void* k_new;
+    const void* v_new;
     int64_t prefix[kMaxRowsPerLaunch + 1];  // exclusive prefix of n_b * H_kv
 };
 

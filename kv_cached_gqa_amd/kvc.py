@@ -37,6 +37,7 @@ ERR_ARG, ERR_CAPACITY, ERR_STATE, ERR_DTYPE = -1, -2, -3, -4
 ERR_STORAGE, ERR_HIP, ERR_NOMEM, ERR_UNSUPPORTED = -5, -6, -7, -8
 
 EXPORTED = ("kvc_create", "kvc_destroy", "kvc_append", "kvc_append_rope", "kvc_rope_q", "kvc_attend",
+            "kvc_append_attend",
             "kvc_seq_len", "kvc_truncate", "kvc_nbytes", "kvc_strerror",
             "kvc_create_paged", "kvc_paged_blocks", "kvc_block_table",
             "kvc_latent_create", "kvc_latent_destroy", "kvc_latent_append", "kvc_latent_seq_len",
@@ -68,6 +69,8 @@ _lib.kvc_rope_q.argtypes = [_vp, _i32, _vp, _i32, _i32, ctypes.c_double, _vp]
 _lib.kvc_rope_q.restype = ctypes.c_int
 _lib.kvc_attend.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp, _vp]
 _lib.kvc_attend.restype = ctypes.c_int
+_lib.kvc_append_attend.argtypes = [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp]
+_lib.kvc_append_attend.restype = ctypes.c_int
 _lib.kvc_seq_len.argtypes = [_vp, _i32, ctypes.POINTER(_i64)]
 _lib.kvc_seq_len.restype = ctypes.c_int
 _lib.kvc_truncate.argtypes = [_vp, ctypes.POINTER(_i64), _i32]
@@ -240,6 +243,25 @@ class KVCache:
             raise KVCArgumentError(ERR_ARG, "out must be contiguous float32 shaped like q")
         _check(_lib.kvc_attend(self._h, int(layer), q.data_ptr(), DTYPE_CODES[dtype_name(q)],
                                int(q.shape[2]), out.data_ptr(), _stream_ptr(stream)), "kvc_attend")
+        return out
+
+    def append_attend(self, layer: int, k_new, v_new, q, out=None, stream=None):
+        """append(layer, k_new, v_new) then attend(layer, q) in one call
+        (kvc_append_attend: one decode launch for a decode step whose input
+        already has the storage dtype). Returns float32 [B, H_q, T, d_h]."""
+        torch = _torch()
+        self._check_chunk(k_new, self.n_kv_heads, "k_new")
+        self._check_chunk(v_new, self.n_kv_heads, "v_new")
+        self._check_chunk(q, self.n_q_heads, "q")
+        if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype or q.shape[2] != k_new.shape[2]:
+            raise KVCArgumentError(ERR_ARG, "k_new, v_new and q differ in T or dtype")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
+            raise KVCArgumentError(ERR_ARG, "out must be contiguous float32 shaped like q")
+        _check(_lib.kvc_append_attend(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
+                                      DTYPE_CODES[dtype_name(k_new)], q.data_ptr(), DTYPE_CODES[dtype_name(q)],
+                                      int(q.shape[2]), out.data_ptr(), _stream_ptr(stream)), "kvc_append_attend")
         return out
 
     def update(self, layer: int, k_new, v_new, stream=None):

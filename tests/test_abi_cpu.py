@@ -250,3 +250,24 @@ def test_paged_create_validation(kvc):
     assert lib.kvc_paged_blocks(None, ctypes.byref(used), ctypes.byref(total)) == kvc.ERR_ARG
     tab = (ctypes.c_int32 * 4)()
     assert lib.kvc_block_table(None, tab, 4) == kvc.ERR_ARG
+
+
+def test_append_attend_rejects_before_any_launch(kvc):
+    """kvc_append_attend checks every argument of both halves first."""
+    rc, h = _create(kvc, dtype=2)
+    assert rc == kvc.OK
+    lib = kvc.lib()
+    p = _BASE
+    out = ctypes.c_void_p(_BASE)
+    assert lib.kvc_append_attend(None, 0, p, p, 2, p, 2, 1, out, None) == kvc.ERR_ARG
+    assert lib.kvc_append_attend(h, 0, None, p, 2, p, 2, 1, out, None) == kvc.ERR_ARG
+    assert lib.kvc_append_attend(h, 0, p, p, 2, None, 2, 1, out, None) == kvc.ERR_ARG
+    assert lib.kvc_append_attend(h, 2, p, p, 2, p, 2, 1, out, None) == kvc.ERR_ARG       # layer out of range
+    assert lib.kvc_append_attend(h, 0, p, p, 2, p, 2, 0, out, None) == kvc.ERR_ARG       # T < 1
+    assert lib.kvc_append_attend(h, 0, p, p, 9, p, 2, 1, out, None) == kvc.ERR_DTYPE
+    assert lib.kvc_append_attend(h, 0, p, p, 2, p, 9, 1, out, None) == kvc.ERR_DTYPE
+    assert lib.kvc_append_attend(h, 0, p + 8, p, 2, p, 2, 1, out, None) == kvc.ERR_ARG   # misaligned
+    assert lib.kvc_append_attend(h, 0, p, p, 2, p, 2, 9, out, None) == kvc.ERR_CAPACITY  # max_len 8
+    lens = (ctypes.c_int64 * 3)()
+    assert lib.kvc_seq_len(h, 0, lens) == kvc.OK and list(lens) == [0, 0, 0]
+    lib.kvc_destroy(h)

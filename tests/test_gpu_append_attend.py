@@ -1,0 +1,122 @@
+"""kvc_append_attend on the GPU: the same state and the same bits as
+kvc_append followed by kvc_attend ("KV cache, incremental decode, ...",
+section 2.3: a pass appends its chunk, then attends over all stored positions).
+
+A decode step whose input has the storage dtype runs as one decode launch that
+reads the chunk from the input; the merge pass stores it. Every other call runs
+append, then attend. Both are compared bit for bit with a second cache driven
+by the two separate calls: outputs, fills and stored bits. Inputs are finite
+(a NaN input is the one documented difference: canonicalised by append, copied
+by the fused path).
+"""
+import numpy as np
+import pytest
+
+from tests.harness import gpu_bits, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cached_gqa_amd import kvc  # noqa: F401  (fails loudly if libkvc.so is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+def _caches(paged, L, B, Hq, Hkv, D, max_len, dtype):
+    from kv_cached_gqa_amd.kvc import KVCache, PagedKVCache
+    if paged:
+        mk = lambda: PagedKVCache(L, Hkv, D, max_len, batch=B, n_q_heads=Hq, dtype=dtype,  # noqa: E731
+                                  device=DEV, block_size=128)
+    else:
+        mk = lambda: KVCache(L, Hkv, D, max_len, batch=B, n_q_heads=Hq, dtype=dtype, device=DEV)  # noqa: E731
+    return mk(), mk()
+
+
+def _storage(c, layer):
+    if hasattr(c, "gather"):
+        return c.gather(layer)
+    n = int(c.seq_len(layer).max())
+    return c.k_storage[layer, :, :, :n], c.v_storage[layer, :, :, :n]
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_append_attend_equals_append_then_attend(paged, dtype, D):
+    """Ragged rows (one empty), group sizes 1-8, decode steps and short chunks
+    (fused where the input has the storage dtype and the slab is one vector
+    slab), and chunks that fall back to the two calls."""
+    import torch
+    log(f"append_attend paged={paged} dtype={dtype} D={D}")
+    rng = np.random.default_rng(1100 + D)
+    L, B, Hkv, max_len = 2, 5, 2, 700
+    for G in (1, 2, 4, 8):
+        Hq = G * Hkv
+        fused_c, ref_c = _caches(paged, L, B, Hq, Hkv, D, max_len, dtype)
+        for layer in range(L):
+            k, v = (rng.standard_normal((B, Hkv, 600, D), dtype=np.float32) for _ in range(2))
+            for c in (fused_c, ref_c):
+                c.append(layer, to_device(k, dtype, DEV), to_device(v, dtype, DEV))
+        lens = np.array([0, 1, 127, 128, 555])
+        fused_c.truncate(lens)
+        ref_c.truncate(lens)
+        for step, T in enumerate((1, 1, 2, 1, 9, 1)):
+            inp = dtype if step != 3 else ("fp32" if dtype != "fp32" else "bf16")   # one call not fusable
+            for layer in range(L):
+                k, v = (rng.standard_normal((B, Hkv, T, D), dtype=np.float32) for _ in range(2))
+                q = rng.standard_normal((B, Hq, T, D), dtype=np.float32)
+                kd, vd, qd = to_device(k, inp, DEV), to_device(v, inp, DEV), to_device(q, "bf16", DEV)
+                of = fused_c.append_attend(layer, kd, vd, qd)
+                ref_c.append(layer, kd, vd)
+                orf = ref_c.attend(layer, qd)
+                torch.cuda.synchronize()
+                assert torch.equal(of.view(torch.int32), orf.view(torch.int32)), (G, step, layer, T)
+                assert np.array_equal(fused_c.seq_len(layer), ref_c.seq_len(layer))
+        for layer in range(L):
+            for a_, b_ in zip(_storage(fused_c, layer), _storage(ref_c, layer)):
+                assert np.array_equal(gpu_bits(a_), gpu_bits(b_)), (G, layer)
+        fused_c.close()
+        ref_c.close()
+
+
+def test_append_attend_batched_decode_full_size_and_wide_batch():
+    """The batched-decode workload (B=32, H_q=32, H_kv=8, d_h=128, bf16,
+    lengths U{1024..4095}) for three steps, and B=300 rows (two launches):
+    fused calls give the two-call path's bits."""
+    import torch
+    from kv_cached_gqa_amd import workloads as W
+    from kv_cached_gqa_amd.kvc import KVCache
+    log("append_attend batched decode full size, B=300")
+    rng = np.random.default_rng(1200)
+    shape = W.SHAPES["llama3_8b_layer_decode_bf16"]
+    lengths = W.batched_lengths(np.random.default_rng(0), shape.batch, 1024, shape.max_len - 1)
+    for (B, Hq, Hkv, D, max_len, lens) in ((shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.d_head,
+                                            shape.max_len, lengths),
+                                           (300, 4, 2, 64, 300, rng.integers(0, 290, size=300))):
+        caches = [KVCache(1, Hkv, D, max_len, batch=B, n_q_heads=Hq, dtype="bf16", device=DEV) for _ in range(2)]
+        k = torch.randn((B, Hkv, max_len - 1, D), device=DEV, dtype=torch.bfloat16)
+        lens = np.minimum(lens, max_len - 4)           # room for three steps
+        for c in caches:
+            c.append(0, k, k)
+            c.truncate(lens)
+        del k
+        for _ in range(3):
+            kn = torch.randn((B, Hkv, 1, D), device=DEV, dtype=torch.bfloat16)
+            vn = torch.randn((B, Hkv, 1, D), device=DEV, dtype=torch.bfloat16)
+            q = torch.randn((B, Hq, 1, D), device=DEV, dtype=torch.bfloat16)
+            of = caches[0].append_attend(0, kn, vn, q)
+            caches[1].append(0, kn, vn)
+            orf = caches[1].attend(0, q)
+            torch.cuda.synchronize()
+            assert torch.equal(of.view(torch.int32), orf.view(torch.int32)), B
+        assert np.array_equal(gpu_bits(caches[0].k_storage), gpu_bits(caches[1].k_storage))
+        assert np.array_equal(gpu_bits(caches[0].v_storage), gpu_bits(caches[1].v_storage))
+        for c in caches:
+            c.close()
