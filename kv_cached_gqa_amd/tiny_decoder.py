@@ -6,11 +6,12 @@ KV cache's C ABI ("kv-cache-decoding": the benchmark spec's steps 1-10 and
 The dense parts (embeddings, layer norms, projections, MLP, vocabulary
 projection) are plain float32 torch operations on the device: plumbing around
 the cache. Every key and value goes into a `KVCache` (fp32 storage) with
-`append` at the model's own positions, and every attention is a
-`KVCache.attend` call, so the cached path (one prefill call, then one token
-per call) and the uncached path (the whole sequence at t = 0 each step, in a
-cache emptied with `truncate(0)`) exercise append, the committed length, the
-bottom-right mask and truncate end to end.
+`append_attend` at the model's own positions (the append, then the attention
+over everything stored, in one call: one decode launch for a decode step), so
+the cached path (one prefill call, then one token per call) and the uncached
+path (the whole sequence at t = 0 each step, in a cache emptied with
+`truncate(0)`) exercise append, the committed length, the bottom-right mask
+and truncate end to end.
 
 Model: token embedding plus the position row of each token's absolute
 position (the cache's committed length t for the first new token); per layer a
@@ -72,8 +73,7 @@ class TinyDecoder:
         for layer, p in enumerate(self.layers):
             h = F.layer_norm(x, (s.d_model,), p["g1"], p["b1"], 1e-5)
             q, k, v = self._heads(h @ p["w_q"]), self._heads(h @ p["w_k"]), self._heads(h @ p["w_v"])
-            cache.append(layer, k, v)
-            att = cache.attend(layer, q)[0]                      # [heads, m, d_head] float32
+            att = cache.append_attend(layer, k, v, q)[0]         # [heads, m, d_head] float32
             x = x + att.permute(1, 0, 2).reshape(m, s.d_model) @ p["w_o"]
             h = F.layer_norm(x, (s.d_model,), p["g2"], p["b2"], 1e-5)
             x = x + torch.relu(h @ p["w_1"]) @ p["w_2"]
