@@ -406,6 +406,49 @@ def paged_bench(lengths, us_contiguous: float):
     return res
 
 
+def small_configs_bench():
+    """The latency-bound configs, decode tokens/s: the tiny GQA cache (L=4,
+    B=1, H_q=4, H_kv=2, d_h=32, fp32; a 16-token prefill, then 112 decode
+    steps) and the SmolLM2-shaped cache (L=30, B=1, H_q=9, H_kv=3, d_h=64,
+    fp16; a 512-token prefill, then 256 decode steps), inputs from their call
+    scripts moved to the device first. A decode step is every layer's
+    kvc_append_attend; the steps run once untimed, the cache is cut back to
+    the prefill, and the second run is timed with HIP events."""
+    import torch
+    from kv_cached_gqa_amd.kvc import KVCache, torch_dtype
+    from kv_cached_gqa_amd import workloads as W
+    dev = torch.device("cuda:0")
+    res = {}
+    for name, (shape, calls) in (("tiny_gqa_fp32", W.script_tiny_gqa()),
+                                 ("smollm2_135m_fp16", W.script_smollm2(rollback=0))):
+        tdt = torch_dtype(shape.dtype)
+        to = lambda x: torch.from_numpy(x).to(dev, tdt)  # noqa: E731
+        prefill, decode = [], []
+        for c in calls:
+            if c.op == "pass":
+                (prefill if c.tag == "prefill" else decode).append((c.layer, to(c.k), to(c.v), to(c.q)))
+        cache = KVCache(shape.n_layers, shape.n_kv_heads, shape.d_head, shape.max_len, batch=shape.batch,
+                        n_q_heads=shape.n_q_heads, dtype=shape.dtype, device=dev)
+        out = torch.empty_like(decode[0][3], dtype=torch.float32)
+        for layer, k, v, q in prefill:
+            cache.append_attend(layer, k, v, q)
+        p0 = int(cache.seq_len()[0])
+        n_steps = len(decode) // shape.n_layers
+
+        def run(_):
+            for layer, k, v, q in decode:
+                cache.append_attend(layer, k, v, q, out=out)
+        run(0)
+        cache.truncate(p0)
+        torch.cuda.synchronize()
+        ms = event_time(run, 1, torch.cuda.current_stream())
+        res[name] = {"layers": shape.n_layers, "decode_steps": n_steps, "ms": round(ms, 3),
+                     "tokens_per_s": round(n_steps * shape.batch / (ms * 1e-3), 1),
+                     "us_per_layer_call": round(ms * 1e3 / len(decode), 2)}
+        cache.close()
+    return res
+
+
 def long_ctx_bench(block=None):
     """Long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys;
     attention calls with T=1 and T=4 (a draft block) after one append; on a
@@ -438,10 +481,11 @@ def long_ctx_bench(block=None):
     return res
 
 
-def cpu_baseline(lengths, seconds: float) -> dict:
+def cpu_baseline(lengths, seconds: float, threads=1) -> dict:
     """The oracle, as it stands, on the same workload: whole steps (truncate,
     append, attend of all 32 rows) until `seconds` of CPU time are spent, with
-    BLAS limited to one thread. The preload is not timed."""
+    BLAS limited to `threads` threads (None: all cores). The preload is not
+    timed."""
     from threadpoolctl import threadpool_limits
     from oracle import OracleCache
     from kv_cached_gqa_amd.workloads import draw_kv, draw_qkv, SHAPES
@@ -457,7 +501,7 @@ def cpu_baseline(lengths, seconds: float) -> dict:
     inputs = [draw_qkv(rng, shape, 1) for _ in range(4)]
     att, app = step_bytes(lengths)
     steps = 0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         t0 = time.perf_counter()
         while True:
             q, k, v = inputs[steps % len(inputs)]
@@ -469,9 +513,10 @@ def cpu_baseline(lengths, seconds: float) -> dict:
             if el >= seconds:
                 break
     t_step = el / steps
-    return {"value": round((att + app) / t_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    cores = 1 if threads == 1 else (os.cpu_count() or 1)
+    return {"value": round((att + app) / t_step / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{steps} whole decode steps of the same workload (all 32 rows), float64 NumPy, "
-                      f"1 BLAS thread, {el:.1f} s",
+                      f"{cores} BLAS thread(s), {el:.1f} s",
             "tokens_per_s": round(B / t_step, 2), "s_per_step": round(t_step, 4)}
 
 
@@ -522,9 +567,11 @@ def main():
     if not args.no_extra:
         rec["extra"] = {"chunked_prefill": prefill_bench(), "long_context_decode": long_ctx_bench(),
                         "tiny_decoder": tiny_decoder_bench(), "rope": rope_bench(),
-                        "latent_cache": latent_bench(), "paged_decode": paged_bench(lengths, us_attend)}
+                        "latent_cache": latent_bench(), "paged_decode": paged_bench(lengths, us_attend),
+                        "small_configs": small_configs_bench()}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(lengths, args.cpu_seconds)
+        rec["cpu_baseline"]["all_cores"] = cpu_baseline(lengths, args.cpu_seconds / 2, threads=None)
     print(json.dumps(rec), flush=True)
 
 
