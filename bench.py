@@ -62,6 +62,8 @@ def parse():
                     help="skip the prefill, long-context and tiny-decoder figures")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run the counter workload (calibration copy, then attention calls) and exit")
+    ap.add_argument("--pmc-prefill", action="store_true",
+                    help="run the chunked-prefill workload once (32 chunks) for counter passes and exit")
     return ap.parse_args()
 
 
@@ -221,7 +223,7 @@ def new_cache(n_kv_heads, d_head, max_len, batch, n_q_heads, dev, block=None):
                         block_size=block)
 
 
-def prefill_bench(block=None):
+def prefill_bench(block=None, runs=3):
     """Chunked prefill: B=4, H_q=32, H_kv=8, d_h=128, bf16, 32 chunks of T=512
     appended and attended in turn (queries at s = 0, 512, ..., 15872); on a
     paged cache with blocks of `block` positions when given."""
@@ -244,7 +246,7 @@ def prefill_bench(block=None):
             cache.attend(0, qs[c % 4], out=out)
     run(0)
     torch.cuda.synchronize()
-    ms = event_time(run, 3, torch.cuda.current_stream())
+    ms = event_time(run, runs, torch.cuda.current_stream()) if runs > 1 else float("nan")
     flops = sum(work.attend_flops([c * t] * b, t, hq, d) for c in range(nch))
     tf = flops / (ms * 1e-3) / 1e12
     cache.close()
@@ -531,6 +533,9 @@ def main():
     lengths = lengths_seed0()
     if args.pmc_workload:
         pmc_workload(lengths)
+        return
+    if args.pmc_prefill:
+        prefill_bench(runs=1)
         return
     att, app = step_bytes(lengths)
     ms_step, us_attend, wall, ms_step_two = gpu_bench(args, lengths)
