@@ -44,6 +44,9 @@ namespace {
 #define KVC_PF_KV_CPOL 0      // cache-policy bits of the K/V tile loads (default: the query blocks
                               // of a unit share its tiles in L2; non-temporal measured ~1% slower)
 #endif
+#ifndef KVC_PF_QVEC
+#define KVC_PF_QVEC 1         // q already in the storage type: one 16-byte load per k-step (~2% faster)
+#endif
 #ifndef KVC_PF_STAGES
 #define KVC_PF_STAGES 4       // key/value tiles in the LDS ring (64 KB; 3 measured ~0.6% slower)
 #endif
@@ -193,6 +196,12 @@ void prefill_attn(PrefillArgs a) {
 #pragma unroll
         for (int ds = 0; ds < P::DS; ++ds) {
             const int64_t e0 = qrow + ds * 16 + hl * 8;
+            if (KVC_PF_QVEC && a.q_dtype == ST) {
+                // the caller's 16-bit q as stored: 8 elements, 16 bytes (rounding a
+                // 16-bit value to the same type leaves it as it is)
+                qb[nt][ds] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + e0);
+                continue;
+            }
             uint32_t w[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
