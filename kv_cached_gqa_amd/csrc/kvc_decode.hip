@@ -1028,6 +1028,22 @@ void decode_mfma(DecodeArgs a) {
     auto load_qtab = [&](int64_t x) __attribute__((always_inline)) {
         for (int sgi = 0; sgi < P::QSEGS && x < x_end; ++sgi) {
             const Seg sg = locate(x);
+            if (a.q_dtype == ST) {
+                // q already in the storage type: 8 elements (16 bytes) at a time
+                for (int c8 = lane; c8 < 4 * D; c8 += 64) {
+                    const int r = c8 / (D / 8), e = (c8 - r * (D / 8)) * 8;
+                    u32x4 w = {0u, 0u, 0u, 0u};
+                    if (r < rows_act) {
+                        const int h = sg.g * a.G + a.r0 + r / a.Tc;
+                        const int i = a.i0 + r % a.Tc;
+                        const int64_t qe = ((static_cast<int64_t>(a.row0 + sg.b) * a.Hq + h) * a.T + i) * D + e;
+                        w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + qe);
+                    }
+                    *reinterpret_cast<u32x4*>(&qtab[sgi][r][e]) = w;
+                }
+                x = sg.x_end;
+                continue;
+            }
             for (int idx = lane; idx < 32 * D; idx += 64) {
                 const int r = idx / D, e = idx - (idx / D) * D;
                 float val = 0.f;

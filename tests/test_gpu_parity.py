@@ -274,17 +274,22 @@ def test_batch_wider_than_one_launch():
     assert cache_bits_equal(cache, orc)
 
 
-def test_q_dtype_rule():
-    """An fp32 q for a bf16 cache is rounded to bf16 first: same output as a bf16 q."""
-    log("q dtype rule")
+@pytest.mark.parametrize("st", ["fp16", "bf16"])
+def test_q_dtype_rule(st):
+    """An fp32 q for a 16-bit cache is rounded to the storage type first: the
+    same output as a q passed in that type (read as stored), on the vector
+    decode kernel (T=1, 4 rows), the matrix-core decode kernel (T=3, 12 rows)
+    and the prefill kernel (T=16, 64 rows)."""
+    log(f"q dtype rule {st}")
     rng = np.random.default_rng(400)
-    cache, orc = _new((1, 2, 8, 2, 128, 64), "bf16")
+    cache, orc = _new((1, 2, 8, 2, 128, 64), st)
     k, v = (rng.standard_normal((2, 2, 50, 128), dtype=np.float32) for _ in range(2))
     cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
-    q = rng.standard_normal((2, 8, 3, 128), dtype=np.float32)
-    a = cache.attend(0, to_device(q, "fp32", DEV)).cpu().numpy()
-    b = cache.attend(0, to_device(q, "bf16", DEV)).cpu().numpy()
-    assert np.array_equal(a, b)
+    for T in (1, 3, 16):
+        q = rng.standard_normal((2, 8, T, 128), dtype=np.float32)
+        a = cache.attend(0, to_device(q, "fp32", DEV)).cpu().numpy()
+        b = cache.attend(0, to_device(q, st, DEV)).cpu().numpy()
+        assert np.array_equal(a, b), T
 
 
 def test_errors_leave_gpu_state_unchanged():
