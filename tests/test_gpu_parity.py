@@ -487,3 +487,40 @@ def test_latent_cache_append_bit_exact(st, inp):
         assert np.array_equal(lc.seq_len(), orc.seq_len())
         assert lc.nbytes() == orc.nbytes()
         lc.close()
+
+
+def test_longest_row_the_layout_allows():
+    """max_len * d_head just below 2^31 (16,777,215 positions at d_h=128, bf16,
+    one row and one KV head: 4 GiB per tensor). The far end of the row is
+    stored bit for bit by the fused call, and a T=1 query over all 16.7M keys
+    returns the value vector when every position holds the same one: the
+    softmax weights sum to 1 (a property that holds at any size, so no oracle
+    pass over the row is needed)."""
+    import torch
+    from kv_cached_gqa_amd.kvc import KVCache
+    ml = (1 << 24) - 1
+    log(f"longest row: max_len {ml}, d_h 128, bf16")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    cache = KVCache(1, 1, 128, ml, batch=1, n_q_heads=4, dtype="bf16", device=DEV)
+    vrow = torch.randn((128,), generator=gen, device=DEV).to(torch.bfloat16)
+    k = torch.randn((1, 1, ml - 1, 128), generator=gen, device=DEV, dtype=torch.bfloat16)
+    v = vrow.view(1, 1, 1, 128).expand(1, 1, ml - 1, 128).contiguous()
+    cache.append(0, k, v)
+    k_prev = k[0, 0, -1].clone()
+    del k, v
+    kn = torch.randn((1, 1, 1, 128), generator=gen, device=DEV, dtype=torch.bfloat16)
+    vn = vrow.view(1, 1, 1, 128).contiguous()
+    q = torch.randn((1, 4, 1, 128), generator=gen, device=DEV, dtype=torch.bfloat16)
+    out = cache.append_attend(0, kn, vn, q)
+    torch.cuda.synchronize()
+    assert cache.seq_len().tolist() == [ml]
+    assert np.array_equal(gpu_bits(cache.k_storage[0, 0, 0, ml - 1]), gpu_bits(kn[0, 0, 0]))
+    assert np.array_equal(gpu_bits(cache.k_storage[0, 0, 0, ml - 2]), gpu_bits(k_prev))
+    assert np.array_equal(gpu_bits(cache.v_storage[0, 0, 0, ml - 1]), gpu_bits(vrow))
+    want = vrow.float().cpu().numpy()
+    got = out[0, :, 0].cpu().numpy()
+    err = float(np.abs(got - want[None, :]).max() / np.abs(want).max())
+    log(f"  relative error against the value vector {err:.2e}")
+    assert np.isfinite(got).all() and err <= 1e-4
+    cache.close()
