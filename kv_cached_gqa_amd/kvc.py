@@ -73,7 +73,7 @@ _lib.kvc_append_attend.argtypes = [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _
 _lib.kvc_append_attend.restype = ctypes.c_int
 _lib.kvc_seq_len.argtypes = [_vp, _i32, ctypes.POINTER(_i64)]
 _lib.kvc_seq_len.restype = ctypes.c_int
-_lib.kvc_truncate.argtypes = [_vp, ctypes.POINTER(_i64), _i32]
+_lib.kvc_truncate.argtypes = [_vp, _vp, _i32]        # int64 lengths, by address
 _lib.kvc_truncate.restype = ctypes.c_int
 _lib.kvc_nbytes.argtypes = [_vp, ctypes.POINTER(_u64)]
 _lib.kvc_nbytes.restype = ctypes.c_int
@@ -85,7 +85,7 @@ _lib.kvc_latent_append.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _vp]
 _lib.kvc_latent_append.restype = ctypes.c_int
 _lib.kvc_latent_seq_len.argtypes = [_vp, _i32, ctypes.POINTER(_i64)]
 _lib.kvc_latent_seq_len.restype = ctypes.c_int
-_lib.kvc_latent_truncate.argtypes = [_vp, ctypes.POINTER(_i64), _i32]
+_lib.kvc_latent_truncate.argtypes = [_vp, _vp, _i32]
 _lib.kvc_latent_truncate.restype = ctypes.c_int
 _lib.kvc_latent_nbytes.argtypes = [_vp, ctypes.POINTER(_u64)]
 _lib.kvc_latent_nbytes.restype = ctypes.c_int
@@ -152,11 +152,24 @@ def dtype_name(t) -> str:
     return m[t.dtype]
 
 
-def _stream_ptr(stream) -> Optional[int]:
+def _stream_ptr(stream, device=None) -> Optional[int]:
+    """The HIP stream to enqueue on: `stream`, else the current stream of
+    `device` (read directly: building a torch Stream object per call costs
+    microseconds, which a launch-bound caller pays on every call)."""
+    if stream is not None:
+        return stream.cuda_stream
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+    idx = device.index if device is not None and device.index is not None else torch.cuda.current_device()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(idx)
+    return torch.cuda.current_stream(idx).cuda_stream
+
+
+def _lengths(n) -> tuple:
+    """(address, count, keep-alive) of n as contiguous int64."""
+    arr = np.ascontiguousarray(np.atleast_1d(np.asarray(n, dtype=np.int64)))
+    return arr.__array_interface__["data"][0], int(arr.size), arr
 
 
 class KVCache:
@@ -217,19 +230,19 @@ class KVCache:
             raise KVCArgumentError(ERR_ARG, "k_new and v_new differ in shape or dtype")
         if rope_base is None:
             _check(_lib.kvc_append(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
-                                   DTYPE_CODES[dtype_name(k_new)], int(k_new.shape[2]), _stream_ptr(stream)),
+                                   DTYPE_CODES[dtype_name(k_new)], int(k_new.shape[2]), _stream_ptr(stream, self._dev)),
                    "kvc_append")
         else:
             _check(_lib.kvc_append_rope(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
                                         DTYPE_CODES[dtype_name(k_new)], int(k_new.shape[2]), float(rope_base),
-                                        _stream_ptr(stream)), "kvc_append_rope")
+                                        _stream_ptr(stream, self._dev)), "kvc_append_rope")
 
     def rope_q(self, layer: int, q, rope_base: float, stream=None):
         """Rotate q [B, H_q, T, d_h] (device, contiguous) in place at the
         positions the next attend of `layer` gives the chunk; returns q."""
         self._check_chunk(q, self.n_q_heads, "q")
         _check(_lib.kvc_rope_q(self._h, int(layer), q.data_ptr(), DTYPE_CODES[dtype_name(q)], int(q.shape[2]),
-                               float(rope_base), _stream_ptr(stream)), "kvc_rope_q")
+                               float(rope_base), _stream_ptr(stream, self._dev)), "kvc_rope_q")
         return q
 
     def attend(self, layer: int, q, out=None, stream=None):
@@ -242,7 +255,7 @@ class KVCache:
         elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
             raise KVCArgumentError(ERR_ARG, "out must be contiguous float32 shaped like q")
         _check(_lib.kvc_attend(self._h, int(layer), q.data_ptr(), DTYPE_CODES[dtype_name(q)],
-                               int(q.shape[2]), out.data_ptr(), _stream_ptr(stream)), "kvc_attend")
+                               int(q.shape[2]), out.data_ptr(), _stream_ptr(stream, self._dev)), "kvc_attend")
         return out
 
     def append_attend(self, layer: int, k_new, v_new, q, out=None, stream=None):
@@ -261,7 +274,7 @@ class KVCache:
             raise KVCArgumentError(ERR_ARG, "out must be contiguous float32 shaped like q")
         _check(_lib.kvc_append_attend(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
                                       DTYPE_CODES[dtype_name(k_new)], q.data_ptr(), DTYPE_CODES[dtype_name(q)],
-                                      int(q.shape[2]), out.data_ptr(), _stream_ptr(stream)), "kvc_append_attend")
+                                      int(q.shape[2]), out.data_ptr(), _stream_ptr(stream, self._dev)), "kvc_append_attend")
         return out
 
     def update(self, layer: int, k_new, v_new, stream=None):
@@ -290,8 +303,8 @@ class KVCache:
         return j <= s + i
 
     def truncate(self, n) -> None:
-        arr = np.ascontiguousarray(np.atleast_1d(np.asarray(n, dtype=np.int64)))
-        _check(_lib.kvc_truncate(self._h, arr.ctypes.data_as(ctypes.POINTER(_i64)), int(arr.size)),
+        ptr, count, _keep = _lengths(n)
+        _check(_lib.kvc_truncate(self._h, ptr, count),
                "kvc_truncate")
 
     def nbytes(self) -> int:
@@ -403,6 +416,7 @@ class LatentCache:
                                      device=self.device)
         self.kr_storage = torch.zeros((self.n_layers, self.batch, self.max_len, self.rope_dim), dtype=tdt,
                                       device=self.device)
+        self._dev = self.c_storage.device
         cfg = KVCLatentConfig(self.n_layers, self.batch, self.rank, self.rope_dim, DTYPE_CODES[dtype], self.max_len)
         h = _vp()
         nb = lambda t: t.numel() * t.element_size()  # noqa: E731
@@ -432,7 +446,7 @@ class LatentCache:
         if c_new.shape[1] != kr_new.shape[1] or c_new.dtype != kr_new.dtype:
             raise KVCArgumentError(ERR_ARG, "c_new and kr_new differ in T or dtype")
         _check(_lib.kvc_latent_append(self._h, int(layer), c_new.data_ptr(), kr_new.data_ptr(),
-                                      DTYPE_CODES[dtype_name(c_new)], int(c_new.shape[1]), _stream_ptr(stream)),
+                                      DTYPE_CODES[dtype_name(c_new)], int(c_new.shape[1]), _stream_ptr(stream, self._dev)),
                "kvc_latent_append")
 
     def seq_len(self, layer: Optional[int] = None) -> np.ndarray:
@@ -441,8 +455,8 @@ class LatentCache:
         return np.frombuffer(out, dtype=np.int64).copy()
 
     def truncate(self, n) -> None:
-        arr = np.ascontiguousarray(np.atleast_1d(np.asarray(n, dtype=np.int64)))
-        _check(_lib.kvc_latent_truncate(self._h, arr.ctypes.data_as(ctypes.POINTER(_i64)), int(arr.size)),
+        ptr, count, _keep = _lengths(n)
+        _check(_lib.kvc_latent_truncate(self._h, ptr, count),
                "kvc_latent_truncate")
 
     def nbytes(self) -> int:
