@@ -1,0 +1,40 @@
+"""The traffic calibration (kv_cached_gqa_amd/measure.py) on the CPU, from
+synthetic rocprofv3 counter files: each counter is scaled by what it reads
+for a copy of known size, dispatches are averaged per kernel, and a stored
+figure is used only while the decode sources are the ones it was taken on."""
+import csv
+import os
+
+from kv_cached_gqa_amd import measure
+
+
+def _write_run(d, counter, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "p_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (kernel, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": kernel, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_calibrated_traffic_and_digest_gate(tmp_path):
+    copy = 1 << 20
+    copy_k = "void at::native::elementwise_kernel<MulFunctor<float>>"
+    # the copy reads 1 MiB but FETCH_SIZE shows half of it (512 KiB); WRITE_SIZE is exact (1024 KiB)
+    _write_run(tmp_path / "f", "FETCH_SIZE", [(copy_k, 512.0), (copy_k, 512.0),
+                                             ("decode_attn<128>", 1000.0), ("decode_attn<128>", 1200.0),
+                                             ("decode_combine<128>", 10.0)])
+    _write_run(tmp_path / "w", "WRITE_SIZE", [(copy_k, 1024.0), ("decode_attn<128>", 50.0),
+                                             ("decode_combine<128>", 4.0), ("decode_combine<128>", 6.0)])
+    out = tmp_path / "traffic.md"
+    total = measure.summarize(str(tmp_path / "f"), str(tmp_path / "w"), copy, str(out), "cmd f", "cmd w")
+    f_fac, w_fac = copy / 512.0, copy / 1024.0            # 2048 and 1024 bytes per counted KiB
+    want = (1100.0 * f_fac + 50.0 * w_fac) + (10.0 * f_fac + 5.0 * w_fac)
+    assert total == round(want)
+    text = out.read_text()
+    assert "cmd f" in text and "cmd w" in text
+    assert measure.stored_traffic(str(out)) == total           # sources unchanged: the figure is used
+    stale = text.replace(measure.source_digest(), "0" * 64)
+    out.write_text(stale)
+    assert measure.stored_traffic(str(out)) is None             # another digest: ignored
+    assert measure.stored_traffic(str(tmp_path / "missing.md")) is None
