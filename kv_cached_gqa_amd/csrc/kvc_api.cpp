@@ -298,6 +298,7 @@ int grow_blocks(kvc_cache* c, const int64_t* f, int32_t T, hipStream_t s) {
             const int32_t id = c->free_ids.back();
             c->free_ids.pop_back();
             c->table[static_cast<size_t>(b) * c->width + k] = id;
+            c->held[b] = k + 1;            // held at once: a failed launch below leaks no block
             a.index[a.n] = b * c->width + k;
             a.value[a.n] = id;
             if (++a.n == kvc::kMaxTableSets) {
@@ -305,7 +306,6 @@ int grow_blocks(kvc_cache* c, const int64_t* f, int32_t T, hipStream_t s) {
                 a.n = 0;
             }
         }
-        c->held[b] = std::max(c->held[b], want);
     }
     if (a.n > 0 && kvc::launch_table_set(a, s) != hipSuccess) return KVC_ERR_HIP;
     return KVC_OK;
@@ -579,14 +579,17 @@ int kvc_append_attend(kvc_cache* c, int32_t layer, const void* k_new, const void
     if (layer < 0 || layer >= cf.n_layers || T < 1) return KVC_ERR_ARG;
     if (!dtype_ok(in_dtype) || !dtype_ok(q_dtype)) return KVC_ERR_DTYPE;
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out)) return KVC_ERR_ARG;
+    int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
+    for (int b = 0; b < cf.batch; ++b)
+        if (f[b] + T > cf.max_len) return KVC_ERR_CAPACITY;
     if (!fusable(c, in_dtype, T)) {
+        // the workspace first, so that past the append only a launch can fail
+        const int rw = ensure_workspace(c);
+        if (rw != KVC_OK) return rw;
         const int rc = append_impl(c, layer, k_new, v_new, in_dtype, T, 0.0, stream);
         if (rc != KVC_OK) return rc;
         return attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr);
     }
-    int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
-    for (int b = 0; b < cf.batch; ++b)
-        if (f[b] + T > cf.max_len) return KVC_ERR_CAPACITY;
     const int rc = ensure_workspace(c);
     if (rc != KVC_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
