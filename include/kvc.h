@@ -213,9 +213,8 @@ int kvc_nbytes(const kvc_cache* cache, uint64_t* out);
  *  stream ahead of its own kernel; truncate to n gives back the row's blocks
  *  past ceil(n / block_size). If the free list cannot cover an append, the
  *  append fails with KVC_ERR_CAPACITY and nothing changes.
- *  Attention over a paged cache takes the same kernels as over a contiguous
- *  one, except that an fp32 cache's slabs hold at most 8 query rows per KV
- *  head (the vector kernel; a contiguous fp32 cache takes up to 32).
+ *  Attention over a paged cache takes the same kernels, with the same work
+ *  split, as over a contiguous one, so its results are bit-identical.
  * Errors: as kvc_create; KVC_ERR_ARG also for a bad block_size or n_blocks;
  * KVC_ERR_NOMEM if the device table cannot be allocated. */
 int kvc_create_paged(const kvc_config* cfg, int32_t block_size, int32_t n_blocks, void* k_pool,

@@ -487,11 +487,10 @@ int attend_impl(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
         return KVC_OK;
     }
 
-    // Slabs of at most kMaxDecodeRows (paged fp32: kMaxPagedDecodeRows) query
-    // rows per KV head: Gc query heads of the group times Tc query positions.
-    const int slab = paged && cf.dtype == KVC_F32 ? kvc::kMaxPagedDecodeRows : kMaxDecodeRows;
-    const int Gc = std::min(G, slab);
-    const int Tc = std::max(1, slab / Gc);
+    // Slabs of at most kMaxDecodeRows query rows per KV head: Gc query heads
+    // of the group times Tc query positions.
+    const int Gc = std::min(G, kMaxDecodeRows);
+    const int Tc = std::max(1, kMaxDecodeRows / Gc);
     for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
         const int rows = std::min(kMaxRowsPerLaunch, cf.batch - row0);
         for (int r0 = 0; r0 < G; r0 += Gc) {

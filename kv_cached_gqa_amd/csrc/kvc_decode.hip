@@ -680,7 +680,7 @@ struct RCfg {
     static_assert(NS * STAGE_BYTES < 65536, "ring offsets fit the LDS immediate");
 };
 
-template <int D, int ST, int RS>
+template <int D, int ST, int RS, bool PAGED>
 __global__ __launch_bounds__((RCfg<D, ST, RS>::THREADS)) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_rows(DecodeArgs a) {
     using C = RCfg<D, ST, RS>;
@@ -760,14 +760,46 @@ void decode_rows(DecodeArgs a) {
     Seg is = locate(x_begin);
     int is_t = 0;
     bool is_live = true;
+    // paged storage: pool offsets of head is.g's rows in the blocks of logical
+    // blocks pg_blk and pg_blk + 1 of the issue cursor's unit (a stage of KPS
+    // keys spans at most these two); the next block's entry is read by a
+    // scalar load when the cursor enters a block
+    int pg_blk = 0;
+    int64_t pg_base = 0, pg_next = 0;
+    auto pg_phys = [&](int blk) __attribute__((always_inline)) -> int64_t {
+        const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
+        const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
+        int p = tab[static_cast<int64_t>(is.b) * a.btab_stride + bi];
+        p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
+        return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + is.g) << a.bshift) * D;
+    };
+    auto pg_enter = [&]() __attribute__((always_inline)) {
+        pg_blk = is.j0 >> a.bshift;
+        pg_base = pg_phys(pg_blk);
+        pg_next = pg_phys(pg_blk + 1);
+    };
+    if constexpr (PAGED) pg_enter();
     auto issue = [&](auto slot_c) __attribute__((always_inline)) {
         constexpr int S = decltype(slot_c)::value;
+        if constexpr (PAGED) {
+            const int blk = (is.j0 + is_t * KPS) >> a.bshift;
+            if (is_live && blk != pg_blk) {       // the stage starts in the next block
+                pg_blk = blk;
+                pg_base = pg_next;
+                pg_next = pg_phys(blk + 1);
+            }
+        }
 #pragma unroll
         for (int ub = 0; ub < UB; ++ub) {
             const int bi = wave * UB + ub;
             int j = is.j0 + is_t * KPS + bi * KPW + grp;
             j = j < is.j1 ? j : is.j1 - 1;
-            const int64_t off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
+            int64_t off;
+            if constexpr (PAGED)
+                off = (((j >> a.bshift) == pg_blk ? pg_base : pg_next) +
+                       static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D + sub * EPC) * ESZ;
+            else
+                off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
             uint8_t* dst = ring + S * C::STAGE_BYTES + bi * 2048;
             __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kc + off),
                                              (void __attribute__((address_space(3)))*)(dst), 16, 0,
@@ -782,6 +814,7 @@ void decode_rows(DecodeArgs a) {
             } else {
                 is = locate(is.x_end);
                 is_t = 0;
+                if constexpr (PAGED) pg_enter();
             }
         }
     };
@@ -1457,7 +1490,12 @@ hipError_t run_rows(DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     a.rec_rows = RCfg<D, ST, RS>::ROWS;
     split_slices(a, n_cu, 2, 2 * RCfg<D, ST, RS>::KPS);
-    decode_rows<D, ST, RS><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
+    if (a.btab) {
+        if ((1 << a.bshift) < RCfg<D, ST, RS>::KPS) return hipErrorInvalidValue;   // a stage within two blocks
+        decode_rows<D, ST, RS, true><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
+    } else {
+        decode_rows<D, ST, RS, false><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return combine_if_split<D>(a, s);
@@ -1487,13 +1525,6 @@ hipError_t run_r(DecodeArgs& a, hipStream_t s) {
     if (a.k_new != nullptr) {     // fused append: one slab on the vector kernel
         if (rows > (ST == F32 ? 8 : KVC_DECODE_MFMA_MIN_ROWS - 1) || a.Gc != a.G || a.Tc != a.T || a.r0 || a.i0)
             return hipErrorInvalidValue;
-        return rows <= 4 ? run<D, ST, 4>(a, s) : run<D, ST, 8>(a, s);
-    }
-    if (a.btab) {                 // paged storage: the vector kernel, the matrix-core kernel for 16 bits
-        if constexpr (ST != F32) {
-            if (rows >= KVC_DECODE_MFMA_MIN_ROWS) return run_mfma<D, ST>(a, s);
-        }
-        if (rows > kMaxPagedDecodeRows) return hipErrorInvalidValue;
         return rows <= 4 ? run<D, ST, 4>(a, s) : run<D, ST, 8>(a, s);
     }
     if constexpr (ST != F32) {

@@ -15,8 +15,6 @@ constexpr int kMaxRowsPerLaunch = 256;
 constexpr int kMaxRopePairs = 64;
 // Query rows (query heads of one group x query positions) of one decode slab.
 constexpr int kMaxDecodeRows = 32;
-// The same for a paged fp32 cache (16-bit paged caches take kMaxDecodeRows).
-constexpr int kMaxPagedDecodeRows = 8;
 // Rows per workspace record of the split-K workspace as allocated (a launch
 // with slabs of more rows uses fewer, wider records).
 constexpr int kWsRecordRows = 8;
@@ -95,8 +93,7 @@ struct DecodeArgs {
     float scale_log2;        // log2(e) / sqrt(D)
     // paged storage (btab non-null): key j of unit (b, g) sits in physical block
     // btab[b * btab_stride + (j >> bshift)] of the layer's pool, at element
-    // layer_off + ((block * Hkv + g) << bshift + (j & mask)) * D; the vector and
-    // matrix-core kernels read paged storage, the fp32 row-split kernel does not
+    // layer_off + ((block * Hkv + g) << bshift + (j & mask)) * D
     const int32_t* btab;     // block table from row `row0` on
     int32_t btab_stride, bshift, pool_blocks;
     // fused append (single slab on the vector kernel): the chunk's T new keys

@@ -7,11 +7,9 @@ describes the paged layout: fixed-size blocks, a table per request, a block
 taken when a sequence grows into it and freed when it ends.
 
 Bars: with the same calls, a paged and a contiguous cache hold the same bits at
-every filled position, and, where both run the same kernel (every call on
-16-bit storage; slabs of at most 8 query rows per KV head on fp32), attention
-outputs are bit-identical, since the work split depends only on the lengths.
-The rest (fp32 slabs of more rows) and every shape against the oracle are
-held to the oracle's tolerances. Block accounting is exact: blocks in use = sum over rows of
+every filled position, and attention outputs are bit-identical, since both
+run the same kernel with a work split that depends only on the lengths.
+Every shape against the oracle is held to the oracle's tolerances. Block accounting is exact: blocks in use = sum over rows of
 ceil(held length / block_size), no block in two places.
 """
 import numpy as np
@@ -80,9 +78,8 @@ def _both_append(cc, pc, layer, k, v, inp="fp32"):
 def test_paged_equals_contiguous_bit_exact(dtype, D):
     """Ragged rows across block edges, decode steps, chunks, truncates that free
     and regrow blocks: the same stored bits and bit-identical attention outputs
-    (16-bit storage: every call, on the vector, matrix-core decode and prefill
-    kernels; fp32: slabs of up to 8 rows, and within 1e-5 beyond, where a
-    contiguous cache takes the row-split kernel)."""
+    on every kernel (16-bit storage: vector, matrix-core decode and prefill;
+    fp32: vector and row-split)."""
     import torch
     rng = np.random.default_rng(900 + D)
     for G in ((8,) if dtype == "fp32" else (4, 8)):
@@ -106,10 +103,7 @@ def test_paged_equals_contiguous_bit_exact(dtype, D):
                     q = to_device(rng.standard_normal((B, Hq, T, D), dtype=np.float32), "fp32", DEV)
                     oc, op = cc.attend(layer, q), pc.attend(layer, q)
                     torch.cuda.synchronize()
-                    if dtype != "fp32" or T * G <= 8:
-                        assert torch.equal(oc.view(torch.int32), op.view(torch.int32)), (bs, step, layer)
-                    else:
-                        assert float((oc - op).abs().max()) <= FP32_MAX_ABS, (bs, step, layer)
+                    assert torch.equal(oc.view(torch.int32), op.view(torch.int32)), (bs, step, layer)
                 _check_table(pc)
                 if step == 2:
                     cut = np.array([3, 0, bs + 5, 1, 2 * bs])
