@@ -516,7 +516,14 @@ def cpu_baseline(lengths, seconds: float, threads=1) -> dict:
                 break
     t_step = el / steps
     cores = 1 if threads == 1 else (os.cpu_count() or 1)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round((att + app) / t_step / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "host": {"cpu_model": model, "logical_cpus": os.cpu_count()},
             "sample": f"{steps} whole decode steps of the same workload (all 32 rows), float64 NumPy, "
                       f"{cores} BLAS thread(s), {el:.1f} s",
             "tokens_per_s": round(B / t_step, 2), "s_per_step": round(t_step, 4)}
