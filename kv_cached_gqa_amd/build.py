@@ -22,7 +22,9 @@ LIB = os.path.join(PKG, "libkvc.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 ARCH = "gfx950"
-SOURCES = ["kvc_api.cpp", "kvc_latent.cpp", "kvc_append.hip", "kvc_decode.hip", "kvc_prefill.hip"]
+# the decode kernels compile per (head dimension, storage type), in parallel
+DECODE_UNITS = [f"kvc_decode_d{d}_{t}.hip" for d in (128, 64, 32) for t in ("bf16", "f16", "f32")]
+SOURCES = [*DECODE_UNITS, "kvc_prefill.hip", "kvc_append.hip", "kvc_decode.hip", "kvc_api.cpp", "kvc_latent.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -52,7 +54,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(os.cpu_count() or 8, 16, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *DEVICE, "-shared", "-fPIC", *objs, "-o", tmp]

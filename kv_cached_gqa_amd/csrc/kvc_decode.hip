@@ -1,1561 +1,18 @@
-// Decode attention: softmax(q K^T / sqrt(D)) V for a few query rows per KV
-// head, over all keys the cache holds for each batch row
-// ("KV cache, incremental decode, ...", section 2.3, the bottom-right mask;
-// "kv-cache-decoding", "Prefill and decode": one row of t + 1 scores per head).
-//
-// Decode reads every cached key and value once and does ~4 flops per byte,
-// so it is bound by HBM bandwidth. The design keeps many bytes in flight on
-// every CU, for the whole launch, and keeps the vector ALU work per key small:
-//
-//  * Work split ("stream-K"). Unit u = (batch row b, KV head g) owns n_b keys.
-//    The units are laid end to end along one axis of sum(n_b) * H_kv keys and
-//    every work-group takes an equal slice of it, so ragged row lengths cost
-//    no load imbalance. One work-group per CU: all of them start together, so
-//    none is starved by older waves at the memory arbiters. A slice that
-//    crosses unit boundaries is cut into segments; segment (work-group k,
-//    unit u) is stored at index k + u, which is unique because each new
-//    segment starts at a slice boundary, a unit boundary or both.
-//  * Loads. Each wave streams its own keys through a private ring of NS LDS
-//    stages filled by LDS-DMA (global_load_lds, 16 bytes per lane): NS - 1
-//    stages are in flight while one is used, with no registers held for them.
-//    The ring runs straight across segment boundaries, so the next unit's keys
-//    are already on their way while a segment is merged. Each wave waits for
-//    its own loads only (an explicit vmcnt), so the loop has no barrier.
-//  * Lane layout. One key row of D elements is LPK lanes x 16 bytes; a load of
-//    64 lanes covers KPW = 64 / LPK consecutive keys, one contiguous 1 KB. All
-//    query rows of the slab (the G query heads that share the KV head, times
-//    the chunk's query positions) are held in every lane group, so each key
-//    and value is read from HBM exactly once for the whole group ("Heads, GQA
-//    and K/V cache": heads sharing one K/V). A segment's query rows travel the
-//    same way: wave 0 loads them by LDS-DMA into one of NS query slots just
-//    before the segment's first stage, so its own wait for the stage before
-//    covers them, and the barriers of the previous segment's merge publish them
-//    to every wave; each wave converts them to the storage type itself.
-//  * q.k: 16-bit dot2 instructions (exact products, fp32 accumulation) or fp32
-//    FMA, then a DPP sum over the LPK lanes of the key. Scores stay in raw
-//    q.k units; the softmax scale and log2(e) are folded into one FMA before
-//    exp2. The running max only triggers a rescale when it grows somewhere in
-//    the wave. p stays fp32 and p*v is an fp32 FMA.
-//  * Merge. At the end of a segment the lane groups and the waves merge their
-//    (max, sum, output). A unit held by one segment is normalised and written
-//    at once; otherwise the segment's partial record goes to the workspace and
-//    a second, small kernel merges each split unit's records.
-#include <type_traits>
-
-#include "kvc_mfma.h"
+// Decode attention dispatch: picks the instantiation of the split-K decode
+// kernels (kvc_decode_impl.h) for a cache's head dimension and storage type.
+// The instantiations live in kvc_decode_d<D>_<type>.hip, one translation unit
+// each, so that they compile in parallel.
+#include "kvc_kernels.h"
 
 namespace kvc {
-namespace {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-#ifndef KVC_DECODE_WAVES
-#define KVC_DECODE_WAVES 4        // waves per work-group
-#endif
-#ifndef KVC_DECODE_STAGES
-#define KVC_DECODE_STAGES 3       // LDS ring stages per wave
-#endif
-#ifndef KVC_DECODE_U
-#define KVC_DECODE_U 2            // 1 KB loads per tensor per stage (4 query rows or fewer)
-#endif
-#ifndef KVC_DECODE_RESCALE_LOG2
-#define KVC_DECODE_RESCALE_LOG2 8.0f
-#endif
-#ifndef KVC_DECODE_BLOCKS_PER_CU
-#define KVC_DECODE_BLOCKS_PER_CU 2
-#endif
-#ifndef KVC_DECODE_KV_CPOL
-// Cache-policy bits of the vector kernels' K/V loads: non-temporal (each key
-// and value is read once per call; measured ~9% faster on the batched-decode
-// workload than the default policy).
-#define KVC_DECODE_KV_CPOL 2
-#endif
-#ifndef KVC_DECODE_MFMA_KV_CPOL
-#define KVC_DECODE_MFMA_KV_CPOL 2 // the same for the matrix-core decode kernel (~11% faster)
-#endif
-#ifndef KVC_DECODE_LATE_PCT
-#define KVC_DECODE_LATE_PCT 70       // slice of a later-dispatched work-group, % of a first-round one
-#endif
-
-// Rescale threshold (log2 units): the running reference max moves only when a
-// score exceeds it by more than this, so p = exp2(s - m) stays below 2^8.
-constexpr float kRescaleLog2 = KVC_DECODE_RESCALE_LOG2;
-constexpr int kLdsLimit = 160 * 1024;
-
-template <int ST>
-__device__ __forceinline__ float dot16(const uint32_t (&q)[4], const u32x4& k, float acc) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        // copy the element out first: a bit cast applied to a vector element
-        // directly has been seen to read element 0 for every e
-        const uint32_t kw = k[e];
-        if constexpr (ST == BF16)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[e]), __builtin_bit_cast(bf16x2_t, kw),
-                                                  acc, false);
-        else
-            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q[e]), __builtin_bit_cast(f16x2_t, kw), acc, false);
-    }
-    return acc;
-}
-
-template <int ST, int EPC>
-__device__ __forceinline__ void unpack_v(const u32x4& v, float (&o)[EPC]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        if constexpr (ST == F32) {
-            o[e] = __uint_as_float(v[e]);
-        } else if constexpr (ST == BF16) {
-            o[2 * e] = __uint_as_float(v[e] << 16);
-            o[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
-        } else {
-            o[2 * e] = f16_to_f32(v[e] & 0xFFFFu);
-            o[2 * e + 1] = f16_to_f32(v[e] >> 16);
-        }
-    }
-}
-
-template <int D, int ST, int R>
-struct Cfg {
-    static constexpr int ESZ = ST == F32 ? 4 : 2;
-    static constexpr int EPC = 16 / ESZ;               // elements per lane (16 bytes)
-    static constexpr int LPK = D / EPC;                // lanes per key row
-    static constexpr int KPW = 64 / LPK;               // keys per 1 KB load
-    static constexpr int WAVES = KVC_DECODE_WAVES;
-    static constexpr int THREADS = 64 * WAVES;
-    static constexpr int U = (R <= 4 && ST != F32) ? KVC_DECODE_U : 1;   // loads per tensor per stage
-    static constexpr int KPS = U * KPW;                // keys per wave per stage
-    static constexpr int KPB = WAVES * KPS;            // keys per work-group batch
-    static constexpr int STAGE_BYTES = U * 2048;       // K and V of one stage of one wave
-    // one query slot: the slab's R rows as the caller passed them (up to 4 bytes
-    // an element), in whole 1 KB DMA blocks
-    static constexpr int QSLOT_BYTES = (R * D * 4 + 1023) / 1024 * 1024;
-    static constexpr int MERGE_BYTES = WAVES * R * (D + 2) * 4;
-    static constexpr int lds_for(int ns) {
-        return WAVES * ns * STAGE_BYTES + ns * QSLOT_BYTES + MERGE_BYTES;
-    }
-    // ring stages: as many as asked for, fewer if the LDS budget (at the work-groups
-    // per CU asked for) does not hold them
-    static constexpr int fit_stages() {
-        int ns = KVC_DECODE_STAGES;
-        const int per_cu = KVC_DECODE_BLOCKS_PER_CU > 0 ? KVC_DECODE_BLOCKS_PER_CU : 1;
-        while (ns > 2 && lds_for(ns) * per_cu > kLdsLimit) --ns;
-        return ns;
-    }
-    static constexpr int NS = fit_stages();
-    static constexpr int RING_BYTES = WAVES * NS * STAGE_BYTES;
-    static constexpr int LDS_BYTES = lds_for(NS);
-    static_assert(NS >= 2, "ring stages");
-    static_assert(LDS_BYTES <= kLdsLimit, "decode LDS budget");
-    static_assert((NS - 1) * 2 * U < 64, "vmcnt field");
-    static_assert((NS - 1) * STAGE_BYTES + STAGE_BYTES < 65536, "ring offsets fit the LDS immediate");
-};
-
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (gfx9 s_waitcnt encoding; LDS and export counters not waited).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// Work-group barrier for LDS data only: this wave's LDS operations are done,
-// then every wave has arrived. (__syncthreads would also wait for every load
-// in flight, draining the DMA ring.) The clobber keeps the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// K and V words of this lane for one 1 KB load of a stage: ring bytes at
-// addr + OFF and addr + OFF + 1024, read after their own wait.
-template <int OFF>
-__device__ __forceinline__ void read_kv(u32x4& k, u32x4& v, uint32_t addr) {
-    asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(k), "=&v"(v)
-                 : "v"(addr), "i"(OFF), "i"(OFF + 1024)
-                 : "memory");
-}
-
-// An LDS read the compiler does not see. Before an LDS access of its own that
-// might alias a pending LDS-DMA write it waits for every load in flight; this
-// read carries its own wait instead.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
-}
-__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-    return v;
-}
-// f(integral_constant<0>), ..., f(integral_constant<N - 1>), unrolled.
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (N > 0) {
-        static_for<N - 1>(f);
-        f(std::integral_constant<int, N - 1>{});
-    }
-}
-
-template <int LPK, int M>
-__device__ __forceinline__ void lane_group_sum(float (&x)[M]) {
-    if constexpr (LPK <= 16) {
-        group_sum_n<LPK, M>(x);
-    } else {
-#pragma unroll
-        for (int i = 0; i < M; ++i) x[i] = group_sum<LPK>(x[i]);
-    }
-}
-
-// One segment of a work-group's slice: keys [j0, j1) of unit (b, g), whose
-// last slab query sits at position n_b - Tc.
-struct Seg {
-    int b, g;
-    int j0, j1, n_b;
-    int nbat;                // work-group batches of KPB keys
-    int64_t head;            // element offset of the unit's key 0
-    int64_t x_end;           // key-axis position where the segment ends
-    int64_t rec;             // workspace record, or -1: the whole unit, written directly
-};
-
-// The slab's query rows, lane's share (EPC elements from element sub * EPC of
-// each row), converted to the storage format, from an LDS slot at byte address
-// `slot` that holds the rows as the caller passed them (row r at r * D * qsize).
-template <int D, int ST, int R>
-__device__ __forceinline__ void load_q_rows(uint32_t (&qp)[R][4], uint32_t slot, int q_dtype, int sub) {
-    constexpr int EPC = ST == F32 ? 4 : 8;
-    if (q_dtype == ST) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const u32x4 w = lds_read_b128(slot + r * D * (ST == F32 ? 4 : 2) + sub * 16);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) qp[r][e] = w[e];
-        }
-        return;
-    }
-    // a different query type: widen to float, then round to the storage type
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        float f[EPC];
-        if (q_dtype == F32) {
-            // EPC floats: 16 or 32 bytes
-#pragma unroll
-            for (int h = 0; h < EPC / 4; ++h) {
-                const u32x4 w = lds_read_b128(slot + r * D * 4 + sub * EPC * 4 + h * 16);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) f[h * 4 + e] = __uint_as_float(w[e]);
-            }
-        } else {
-            // EPC 16-bit values: 8 or 16 bytes (an aligned 16-byte read covers them)
-            const uint32_t at = slot + r * D * 2 + sub * EPC * 2;
-            const u32x4 w = lds_read_b128(at & ~15u);
-            const int w0 = (at & 15u) >> 2;
-#pragma unroll
-            for (int e = 0; e < EPC / 2; ++e) {
-                uint32_t x = w[0];
-                if constexpr (EPC == 4) x = w0 + e == 1 ? w[1] : (w0 + e == 2 ? w[2] : (w0 + e == 3 ? w[3] : w[0]));
-                else x = e == 1 ? w[1] : (e == 2 ? w[2] : (e == 3 ? w[3] : w[0]));
-                const uint32_t lo = x & 0xFFFFu, hi = x >> 16;
-                f[2 * e] = q_dtype == BF16 ? bf16_to_f32(lo) : f16_to_f32(lo);
-                f[2 * e + 1] = q_dtype == BF16 ? bf16_to_f32(hi) : f16_to_f32(hi);
-            }
-        }
-        if constexpr (ST == F32) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) qp[r][e] = __float_as_uint(f[e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = ST == BF16 ? f32_to_bf16_rne(f[2 * e]) : f32_to_f16_rne(f[2 * e]);
-                const uint32_t hi = ST == BF16 ? f32_to_bf16_rne(f[2 * e + 1]) : f32_to_f16_rne(f[2 * e + 1]);
-                qp[r][e] = (lo & 0xFFFFu) | (hi << 16);
-            }
-        }
-    }
-}
-
-template <int D, int ST, int R, bool PAGED>
-__global__ __launch_bounds__((Cfg<D, ST, R>::THREADS)) __attribute__((amdgpu_waves_per_eu(1)))
-void decode_attn(DecodeArgs a) {
-    using C = Cfg<D, ST, R>;
-    constexpr int kWaves = C::WAVES, kThreads = C::THREADS;
-    constexpr int EPC = C::EPC, LPK = C::LPK, KPW = C::KPW, U = C::U, NS = C::NS;
-    constexpr int KPS = C::KPS, KPB = C::KPB, ESZ = C::ESZ;
-
-    // Separate LDS objects: the ring and the query slots (written by LDS-DMA
-    // and read only through the explicit reads above) and the merge area.
-    __shared__ __attribute__((aligned(16))) uint8_t ring[C::RING_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t qslot[NS][C::QSLOT_BYTES];
-    __shared__ float sm_o[kWaves][R][D];
-    __shared__ float sm_m[kWaves][R];
-    __shared__ float sm_l[kWaves][R];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = lane / LPK;
-    const int sub = lane % LPK;
-    const int rows_act = a.Gc * a.Tc;
-    const float c = a.scale_log2;
-    const float thresh = kRescaleLog2 / c;     // the threshold in raw q.k units
-    const int qrow_bytes = D * (a.q_dtype == F32 ? 4 : 2);
-
-    const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
-    int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
-    if (x_end > a.total_keys) x_end = a.total_keys;
-    if (x_begin >= x_end) return;
-
-    const char* kc = static_cast<const char*>(a.k_cache);
-    const char* vc = static_cast<const char*>(a.v_cache);
-    const char* qg = static_cast<const char*>(a.q);
-
-    // -- segments: the one of unit (b, g) that starts at key-axis position x --
-    auto make_seg = [&](int b, int g, int64_t x) __attribute__((always_inline)) -> Seg {
-        Seg sg;
-        sg.b = b;
-        sg.g = g;
-        const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
-        const int64_t unit_start = a.prefix[b] + static_cast<int64_t>(g) * n_b;
-        int64_t seg_end = unit_start + n_b;
-        if (seg_end > x_end) seg_end = x_end;
-        sg.j0 = static_cast<int>(x - unit_start);
-        sg.j1 = static_cast<int>(seg_end - unit_start);
-        sg.n_b = static_cast<int>(n_b);
-        sg.nbat = (sg.j1 - sg.j0 + KPB - 1) / KPB;
-        sg.head = a.layer_off + b * a.row_stride + g * a.head_stride;
-        sg.x_end = seg_end;
-        sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + b * a.Hkv + g;
-        return sg;
-    };
-    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
-        int lo = 0, hi = a.rows;   // prefix[lo] <= x < prefix[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (a.prefix[mid] <= x) lo = mid; else hi = mid;
-        }
-        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
-        return make_seg(lo, static_cast<int>((x - a.prefix[lo]) / n_b), x);
-    };
-    // the segment after sg (which ended at its unit's end): the next unit
-    auto next_seg = [&](const Seg& sg) __attribute__((always_inline)) -> Seg {
-        int b = sg.b, g = sg.g + 1;
-        if (g == a.Hkv) {
-            g = 0;
-            ++b;
-        }
-        return make_seg(b, g, sg.x_end);
-    };
-    // -- the slab's query rows of a segment into a query slot (wave 0; one
-    //    LDS-DMA load per 1 KB; rows past the slab repeat its last row) --
-    auto issue_q = [&](const Seg& sg, int slot) __attribute__((always_inline)) {
-        const int cpr = qrow_bytes / 16;                 // 16-byte chunks per row
-        const int n16 = R * cpr;
-        for (int n = 0; n * 64 < n16; ++n) {
-            int ch = n * 64 + lane;
-            if (ch >= n16) ch = n16 - 1;
-            int r = ch / cpr;
-            const int part = ch - r * cpr;
-            if (r >= rows_act) r = rows_act - 1;
-            const int h = sg.g * a.G + a.r0 + r / a.Tc;
-            const int i = a.i0 + r % a.Tc;
-            const int64_t off = ((static_cast<int64_t>(a.row0 + sg.b) * a.Hq + h) * a.T + i) * qrow_bytes + part * 16;
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(qg + off),
-                                             (void __attribute__((address_space(3)))*)(&qslot[slot][n * 1024]), 16, 0,
-                                             0);
-        }
-    };
-
-    // -- issue side: the next stage of this wave's keys. A finished segment is
-    //    left at the start of the next call, for the next unit (wave 0 first
-    //    loads that unit's queries); past the slice's end it reloads the last
-    //    key (never used) --
-    Seg is = locate(x_begin);
-    int is_t = 0, is_sn = 0;
-    bool is_live = true;
-    // paged storage: element offsets of head is.g's rows in the physical
-    // blocks of logical blocks pg_blk and pg_blk + 1 of the issue cursor's
-    // unit. A work-group batch (KPB keys, at most one block) spans at most
-    // those two; the next block's entry is read when the cursor enters a
-    // block, with a scalar load, long before a batch needs it.
-    int pg_blk = 0;
-    int64_t pg_base = 0, pg_next = 0;
-    auto pg_phys = [&](int blk) __attribute__((always_inline)) -> int64_t {
-        const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
-        const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
-        int p = tab[static_cast<int64_t>(is.b) * a.btab_stride + bi];
-        p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
-        return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + is.g) << a.bshift) * D;
-    };
-    auto pg_enter = [&]() __attribute__((always_inline)) {
-        pg_blk = is.j0 >> a.bshift;
-        pg_base = pg_phys(pg_blk);
-        pg_next = pg_phys(pg_blk + 1);
-    };
-    if constexpr (PAGED) pg_enter();
-    uint8_t* const ring_w = ring + wave * (NS * C::STAGE_BYTES);
-    auto issue = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(slot_c)::value;
-        if (is_live && is_t == is.nbat) {
-            if (is.x_end < x_end) {
-                is = next_seg(is);
-                is_t = 0;
-                ++is_sn;
-                if (wave == 0) issue_q(is, is_sn % NS);
-                if constexpr (PAGED) pg_enter();
-            } else {
-                is_live = false;
-            }
-        }
-        if constexpr (PAGED) {
-            const int blk = (is.j0 + is_t * KPB) >> a.bshift;
-            if (is_live && blk != pg_blk) {       // the batch starts in the next block
-                pg_blk = blk;
-                pg_base = pg_next;
-                pg_next = pg_phys(blk + 1);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int j = is.j0 + is_t * KPB + wave * KPS + u * KPW + grp;
-            j = j < is.j1 ? j : is.j1 - 1;
-            int64_t off;
-            if constexpr (PAGED) {
-                const int64_t row = ((j >> a.bshift) == pg_blk ? pg_base : pg_next) +
-                                    static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D;
-                off = (row + sub * EPC) * ESZ;
-            } else {
-                off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
-            }
-            const char* kp = kc;
-            const char* vp = vc;
-            if (a.k_new != nullptr) {
-                // fused append: the chunk's new keys come from the caller's input
-                const int jn = j - (is.n_b - a.T);
-                if (jn >= 0) {
-                    kp = static_cast<const char*>(a.k_new);
-                    vp = static_cast<const char*>(a.v_new);
-                    off = ((((static_cast<int64_t>(a.row0 + is.b) * a.Hkv + is.g) * a.T + jn) * D) + sub * EPC) * ESZ;
-                }
-            }
-            uint8_t* dst = ring_w + S * C::STAGE_BYTES + u * 2048;
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kp + off),
-                                             (void __attribute__((address_space(3)))*)(dst), 16, 0,
-                                             KVC_DECODE_KV_CPOL);
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vp + off),
-                                             (void __attribute__((address_space(3)))*)(dst + 1024), 16, 0,
-                                             KVC_DECODE_KV_CPOL);
-        }
-        if (is_live) ++is_t;
-    };
-    // -- consume side --
-    const uint32_t rd_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-                                 (__attribute__((address_space(3))) uint8_t*)ring_w)) + lane * 16;
-    Seg cs = locate(x_begin);
-    int cs_t = 0, cs_sn = 0;
-    uint32_t qp[R][4];                 // the lane's 16 bytes of each query row
-    int qpos[R];
-    float m[R], l[R], o[R][EPC];
-    auto start_segment = [&]() __attribute__((always_inline)) {
-        load_q_rows<D, ST, R>(qp, lds_addr(qslot[cs_sn % NS]), a.q_dtype, sub);
-        const int qpos0 = cs.n_b - a.Tc;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            qpos[r] = r < rows_act ? qpos0 + r % a.Tc : -1;
-            m[r] = -INFINITY;
-            l[r] = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) o[r][e] = 0.f;
-        }
-    };
-
-    auto consume = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(slot_c)::value;
-        const int kb = cs.j0 + cs_t * KPB + wave * KPS;          // this wave's first key of the stage
-        const bool plain = kb + KPS - 1 < cs.j1 && kb + KPS - 1 <= cs.n_b - a.Tc;
-        u32x4 kx[U], vx[U];
-        static_for<U>([&](auto u_c) {
-            constexpr int u = decltype(u_c)::value;
-            read_kv<S * C::STAGE_BYTES + u * 2048>(kx[u], vx[u], rd_addr);
-        });
-        float s[U * R];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                float acc = 0.f;
-                if constexpr (ST == F32) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(qp[r][e]), __uint_as_float(kx[u][e]), acc);
-                } else {
-                    acc = dot16<ST>(qp[r], kx[u], acc);
-                }
-                s[u * R + r] = acc;
-            }
-        }
-        lane_group_sum<LPK, U * R>(s);
-        if (!plain) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int j = kb + u * KPW + grp;
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    if (!(j < cs.j1 && j <= qpos[r])) s[u * R + r] = -INFINITY;
-            }
-        }
-        // the reference max moves only when a score passes it by the threshold
-        float mt[R];
-        bool need = false;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            mt[r] = s[r];
-#pragma unroll
-            for (int u = 1; u < U; ++u) mt[r] = fmaxf(mt[r], s[u * R + r]);
-            need |= mt[r] - m[r] > thresh;
-        }
-        if (__any(need)) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (mt[r] - m[r] > thresh) {
-                    const float alpha = m[r] == -INFINITY ? 0.f : fexp2((m[r] - mt[r]) * c);
-                    m[r] = mt[r];
-                    l[r] *= alpha;
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) o[r][e] *= alpha;
-                }
-            }
-        }
-        float nmc[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) nmc[r] = m[r] == -INFINITY ? 0.f : -m[r] * c;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float vf[EPC];
-            unpack_v<ST, EPC>(vx[u], vf);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float p = fexp2(fmaf(s[u * R + r], c, nmc[r]));
-                l[r] += p;
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
-            }
-        }
-    };
-    // -- end of a segment: merge the lane groups, then the waves; write the
-    //    output itself or the segment's partial record --
-    auto finish_segment = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float mw = m[r];
-            mw = across_groups<LPK, true>(mw);
-            const float w = mw == -INFINITY ? 0.f : fexp2((m[r] - mw) * c);
-            float lw = l[r] * w;
-            lw = across_groups<LPK, false>(lw);
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                float ow = o[r][e] * w;
-                ow = across_groups<LPK, false>(ow);
-                o[r][e] = ow;
-            }
-            m[r] = mw;
-            l[r] = lw;
-        }
-        if (grp == 0) {
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) sm_o[wave][r][sub * EPC + e] = o[r][e];
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                sm_m[wave][r] = m[r];
-                sm_l[wave][r] = l[r];
-            }
-        }
-        lds_barrier();
-        for (int idx = tid; idx < rows_act * D; idx += kThreads) {
-            const int r = idx / D, d = idx - (idx / D) * D;
-            float M = sm_m[0][r];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][r]);
-            float ov = 0.f, lv = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float f = sm_m[w][r] == -INFINITY ? 0.f : fexp2((sm_m[w][r] - M) * c);
-                ov = fmaf(sm_o[w][r][d], f, ov);
-                lv = fmaf(sm_l[w][r], f, lv);
-            }
-            if (cs.rec < 0) {
-                const int h = cs.g * a.G + a.r0 + r / a.Tc;
-                const int i = a.i0 + r % a.Tc;
-                a.out[((static_cast<int64_t>(a.row0 + cs.b) * a.Hq + h) * a.T + i) * D + d] = ov / lv;
-            } else {
-                const int64_t rr = cs.rec * a.rec_rows + r;
-                a.ws_o[rr * D + d] = ov;
-                if (d == 0) {
-                    a.ws_ml[rr * 2] = M;
-                    a.ws_ml[rr * 2 + 1] = lv;
-                }
-            }
-        }
-        lds_barrier();
-    };
-
-    // -- the loop: stage t sits in slot t % NS; NS - 1 stages are issued ahead.
-    //    Wave 0 loads the first segment's queries before them; every wave
-    //    reads them once they have landed --
-    if (wave == 0) issue_q(is, 0);
-    static_for<NS - 1>([&](auto k) { issue(k); });
-    if (wave == 0) wait_vm<(NS - 1) * 2 * U>();    // the query loads precede every stage load
-    lds_barrier();
-    start_segment();
-    bool done = false;
-    auto step = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(slot_c)::value;
-        issue(std::integral_constant<int, (S + NS - 1) % NS>{});
-        wait_vm<(NS - 1) * 2 * U>();      // this stage's loads have landed
-        consume(slot_c);
-        if (++cs_t == cs.nbat) {
-            // the next segment's queries were loaded before its first stage,
-            // which the wait above covers for wave 0; the barriers in
-            // finish_segment make them visible to every wave
-            finish_segment();
-            if (cs.x_end >= x_end) {
-                done = true;
-            } else {
-                cs = next_seg(cs);
-                cs_t = 0;
-                ++cs_sn;
-                start_segment();
-            }
-        }
-    };
-    while (!done) {
-        static_for<NS>([&](auto k) {
-            if (!done) step(k);
-        });
-    }
-    wait_vm<0>();   // the ring's trailing reloads land before the work-group ends
-}
-
-// ---- slabs of 9 to 32 query rows: row-split work-groups --------------------
-// A KV head with more query rows than one lane group holds (for example 8 heads
-// x a 4-token draft block) is served by RS waves of 8 rows each over the same
-// keys, so the cache is streamed once for all of them. The work-group shares
-// one LDS ring: each wave loads its share of a stage (UB 1 KB blocks of K and
-// of V), waits for its own loads, and one barrier per stage makes the stage
-// visible to all waves and frees the one read before. Each wave merges only its
-// lane groups and writes its own rows; there is no cross-wave merge.
-
-#ifndef KVC_DECODE_ROWS_UB
-#define KVC_DECODE_ROWS_UB 2          // 1 KB blocks per tensor each wave loads per stage
-#endif
-#ifndef KVC_DECODE_ROWS_STAGES
-#define KVC_DECODE_ROWS_STAGES 3
-#endif
-
-template <int D, int ST, int RS>
-struct RCfg {
-    static constexpr int ESZ = ST == F32 ? 4 : 2;
-    static constexpr int EPC = 16 / ESZ;
-    static constexpr int LPK = D / EPC;
-    static constexpr int KPW = 64 / LPK;               // keys per 1 KB block
-    static constexpr int R = 8;                        // query rows per wave
-    static constexpr int ROWS = RS * R;
-    static constexpr int THREADS = 64 * RS;
-    static constexpr int UB = KVC_DECODE_ROWS_UB;
-    static constexpr int BLOCKS = RS * UB;             // blocks per tensor per stage
-    static constexpr int KPS = BLOCKS * KPW;           // keys per stage
-    static constexpr int STAGE_BYTES = BLOCKS * 2048;
-    static constexpr int QSEGS = 2;                    // segments the query table holds
-    static constexpr int QROW_WORDS = D * ESZ / 4;
-    static constexpr int FIXED_BYTES = QSEGS * ROWS * D * ESZ;
-    static constexpr int fit_stages() {
-        int ns = KVC_DECODE_ROWS_STAGES;
-        while (ns > 2 && (ns * STAGE_BYTES + FIXED_BYTES) * 2 > kLdsLimit) --ns;
-        return ns;
-    }
-    static constexpr int NS = fit_stages();
-    static constexpr int LDS_BYTES = NS * STAGE_BYTES + FIXED_BYTES;
-    static_assert(LDS_BYTES <= kLdsLimit, "decode LDS budget");
-    static_assert(NS * STAGE_BYTES < 65536, "ring offsets fit the LDS immediate");
-};
-
-template <int D, int ST, int RS, bool PAGED>
-__global__ __launch_bounds__((RCfg<D, ST, RS>::THREADS)) __attribute__((amdgpu_waves_per_eu(1)))
-void decode_rows(DecodeArgs a) {
-    using C = RCfg<D, ST, RS>;
-    constexpr int EPC = C::EPC, LPK = C::LPK, KPW = C::KPW, UB = C::UB, NS = C::NS, R = C::R;
-    constexpr int KPS = C::KPS, ESZ = C::ESZ, ROWS = C::ROWS;
-
-    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * C::STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) uint32_t qtab[C::QSEGS][ROWS][C::QROW_WORDS];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = lane / LPK;
-    const int sub = lane % LPK;
-    const int rows_act = a.Gc * a.Tc;
-    const float c = a.scale_log2;
-    const float thresh = kRescaleLog2 / c;
-
-    const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
-    int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
-    if (x_end > a.total_keys) x_end = a.total_keys;
-    if (x_begin >= x_end) return;
-
-    const char* kc = static_cast<const char*>(a.k_cache);
-    const char* vc = static_cast<const char*>(a.v_cache);
-
-    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
-        int lo = 0, hi = a.rows;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (a.prefix[mid] <= x) lo = mid; else hi = mid;
-        }
-        Seg sg;
-        sg.b = lo;
-        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
-        sg.g = static_cast<int>((x - a.prefix[lo]) / n_b);
-        const int64_t unit_start = a.prefix[lo] + static_cast<int64_t>(sg.g) * n_b;
-        int64_t seg_end = unit_start + n_b;
-        if (seg_end > x_end) seg_end = x_end;
-        sg.j0 = static_cast<int>(x - unit_start);
-        sg.j1 = static_cast<int>(seg_end - unit_start);
-        sg.n_b = static_cast<int>(n_b);
-        sg.nbat = (sg.j1 - sg.j0 + KPS - 1) / KPS;
-        sg.head = a.layer_off + sg.b * a.row_stride + sg.g * a.head_stride;
-        sg.x_end = seg_end;
-        sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
-        return sg;
-    };
-
-    auto load_qtab = [&](int64_t x) __attribute__((always_inline)) {
-        for (int sgi = 0; sgi < C::QSEGS && x < x_end; ++sgi) {
-            const Seg sg = locate(x);
-            for (int idx = tid; idx < ROWS * D; idx += C::THREADS) {
-                const int r = idx / D, e = idx - (idx / D) * D;
-                float val = 0.f;
-                if (r < rows_act) {
-                    const int h = sg.g * a.G + a.r0 + r / a.Tc;
-                    const int i = a.i0 + r % a.Tc;
-                    const int64_t qe = ((static_cast<int64_t>(a.row0 + sg.b) * a.Hq + h) * a.T + i) * D + e;
-                    if (a.q_dtype == F32) val = static_cast<const float*>(a.q)[qe];
-                    else if (a.q_dtype == BF16) val = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
-                    else val = f16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
-                }
-                if constexpr (ST == F32) {
-                    reinterpret_cast<float*>(qtab[sgi][r])[e] = val;
-                } else {
-                    const uint32_t h16 = ST == BF16 ? f32_to_bf16_rne(val) : f32_to_f16_rne(val);
-                    reinterpret_cast<uint16_t*>(qtab[sgi][r])[e] = static_cast<uint16_t>(h16);
-                }
-            }
-            x = sg.x_end;
-        }
-        __syncthreads();
-    };
-
-    // -- issue side: this wave's UB blocks of the next stage --
-    Seg is = locate(x_begin);
-    int is_t = 0;
-    bool is_live = true;
-    // paged storage: pool offsets of head is.g's rows in the blocks of logical
-    // blocks pg_blk and pg_blk + 1 of the issue cursor's unit (a stage of KPS
-    // keys spans at most these two); the next block's entry is read by a
-    // scalar load when the cursor enters a block
-    int pg_blk = 0;
-    int64_t pg_base = 0, pg_next = 0;
-    auto pg_phys = [&](int blk) __attribute__((always_inline)) -> int64_t {
-        const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
-        const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
-        int p = tab[static_cast<int64_t>(is.b) * a.btab_stride + bi];
-        p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
-        return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + is.g) << a.bshift) * D;
-    };
-    auto pg_enter = [&]() __attribute__((always_inline)) {
-        pg_blk = is.j0 >> a.bshift;
-        pg_base = pg_phys(pg_blk);
-        pg_next = pg_phys(pg_blk + 1);
-    };
-    if constexpr (PAGED) pg_enter();
-    auto issue = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(slot_c)::value;
-        if constexpr (PAGED) {
-            const int blk = (is.j0 + is_t * KPS) >> a.bshift;
-            if (is_live && blk != pg_blk) {       // the stage starts in the next block
-                pg_blk = blk;
-                pg_base = pg_next;
-                pg_next = pg_phys(blk + 1);
-            }
-        }
-#pragma unroll
-        for (int ub = 0; ub < UB; ++ub) {
-            const int bi = wave * UB + ub;
-            int j = is.j0 + is_t * KPS + bi * KPW + grp;
-            j = j < is.j1 ? j : is.j1 - 1;
-            int64_t off;
-            if constexpr (PAGED)
-                off = (((j >> a.bshift) == pg_blk ? pg_base : pg_next) +
-                       static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D + sub * EPC) * ESZ;
-            else
-                off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
-            uint8_t* dst = ring + S * C::STAGE_BYTES + bi * 2048;
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kc + off),
-                                             (void __attribute__((address_space(3)))*)(dst), 16, 0,
-                                             KVC_DECODE_KV_CPOL);
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vc + off),
-                                             (void __attribute__((address_space(3)))*)(dst + 1024), 16, 0,
-                                             KVC_DECODE_KV_CPOL);
-        }
-        if (is_live && ++is_t == is.nbat) {
-            if (is.x_end >= x_end) {
-                is_live = false;
-            } else {
-                is = locate(is.x_end);
-                is_t = 0;
-                if constexpr (PAGED) pg_enter();
-            }
-        }
-    };
-
-    // -- consume side: this wave's rows wave * R .. wave * R + R - 1 of the slab --
-    const uint32_t rd_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-                                 (__attribute__((address_space(3))) uint8_t*)ring)) + lane * 16;
-    Seg cs = locate(x_begin);
-    int cs_t = 0, cs_q = 0;
-    uint32_t qp[R][4];
-    int qpos[R];
-    float m[R], l[R], o[R][EPC];
-    auto start_segment = [&]() __attribute__((always_inline)) {
-        const int qpos0 = cs.n_b - a.Tc;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int rr = wave * R + r;
-            const u32x4 w = *reinterpret_cast<const u32x4*>(&qtab[cs_q][rr][sub * 4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) qp[r][e] = w[e];
-            qpos[r] = rr < rows_act ? qpos0 + rr % a.Tc : -1;
-            m[r] = -INFINITY;
-            l[r] = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) o[r][e] = 0.f;
-        }
-    };
-
-    auto consume = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(slot_c)::value;
-        const int kb = cs.j0 + cs_t * KPS;               // first key of the stage
-        const bool plain = kb + KPS - 1 < cs.j1 && kb + KPS - 1 <= cs.n_b - a.Tc;
-        static_for<C::BLOCKS>([&](auto bi_c) {
-            constexpr int bi = decltype(bi_c)::value;
-            u32x4 kx, vx;
-            read_kv<S * C::STAGE_BYTES + bi * 2048>(kx, vx, rd_addr);
-            float s[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                float acc = 0.f;
-                if constexpr (ST == F32) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(qp[r][e]), __uint_as_float(kx[e]), acc);
-                } else {
-                    acc = dot16<ST>(qp[r], kx, acc);
-                }
-                s[r] = acc;
-            }
-            lane_group_sum<LPK, R>(s);
-            if (!plain) {
-                const int j = kb + bi * KPW + grp;
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    if (!(j < cs.j1 && j <= qpos[r])) s[r] = -INFINITY;
-            }
-            bool need = false;
-#pragma unroll
-            for (int r = 0; r < R; ++r) need |= s[r] - m[r] > thresh;
-            if (__any(need)) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    if (s[r] - m[r] > thresh) {
-                        const float alpha = m[r] == -INFINITY ? 0.f : fexp2((m[r] - s[r]) * c);
-                        m[r] = s[r];
-                        l[r] *= alpha;
-#pragma unroll
-                        for (int e = 0; e < EPC; ++e) o[r][e] *= alpha;
-                    }
-                }
-            }
-            float vf[EPC];
-            unpack_v<ST, EPC>(vx, vf);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float p = fexp2(fmaf(s[r], c, m[r] == -INFINITY ? 0.f : -m[r] * c));
-                l[r] += p;
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
-            }
-        });
-    };
-
-    // -- end of a segment: merge this wave's lane groups, write its rows --
-    auto finish_segment = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float mw = m[r];
-            mw = across_groups<LPK, true>(mw);
-            const float w = mw == -INFINITY ? 0.f : fexp2((m[r] - mw) * c);
-            float lw = l[r] * w;
-            lw = across_groups<LPK, false>(lw);
-            float ow[EPC];
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                ow[e] = o[r][e] * w;
-                ow[e] = across_groups<LPK, false>(ow[e]);
-            }
-            const int rr = wave * R + r;
-            if (grp == 0 && rr < rows_act) {
-                if (cs.rec < 0) {
-                    const int h = cs.g * a.G + a.r0 + rr / a.Tc;
-                    const int i = a.i0 + rr % a.Tc;
-                    float* dst = a.out + ((static_cast<int64_t>(a.row0 + cs.b) * a.Hq + h) * a.T + i) * D + sub * EPC;
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) dst[e] = ow[e] / lw;
-                } else {
-                    const int64_t rec = cs.rec * a.rec_rows + rr;
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) a.ws_o[rec * D + sub * EPC + e] = ow[e];
-                    if (sub == 0) {
-                        a.ws_ml[rec * 2] = mw;
-                        a.ws_ml[rec * 2 + 1] = lw;
-                    }
-                }
-            }
-        }
-    };
-
-    // -- the loop: stage t in slot t % NS, NS - 1 stages issued ahead --
-    static_for<NS - 1>([&](auto k) { issue(k); });
-    load_qtab(x_begin);
-    start_segment();
-    bool done = false;
-    auto step = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(slot_c)::value;
-        wait_vm<(NS - 2) * 2 * UB>();   // this wave's part of stage t has landed
-        lds_barrier();                   // every wave's part has; every wave is done with stage t - 1
-        issue(std::integral_constant<int, (S + NS - 1) % NS>{});
-        consume(slot_c);
-        if (++cs_t == cs.nbat) {
-            finish_segment();
-            if (cs.x_end >= x_end) {
-                done = true;
-            } else {
-                cs = locate(cs.x_end);
-                cs_t = 0;
-                if (++cs_q == C::QSEGS) {    // more segments than the table holds: reload it
-                    load_qtab(cs.x_end - (cs.j1 - cs.j0));
-                    cs_q = 0;
-                }
-                start_segment();
-            }
-        }
-    };
-    while (!done) {
-        static_for<NS>([&](auto k) {
-            if (!done) step(k);
-        });
-    }
-    wait_vm<0>();
-}
-
-// ---- slabs of 5 to 32 query rows, 16-bit caches: matrix cores --------------
-// With 8 heads x a 4-token draft (or any G*T in 5..32) one KV head serves up to
-// 32 query rows, up to 32 flops per byte: the vector ALUs do not keep up with
-// HBM (at 8 rows they already trail the matrix-core kernel by a third), so
-// the two products run as MFMA tiles, the same S^T = K Q^T and O^T = V^T P^T
-// tiles as the prefill kernel, with the slab's rows as the 32 columns. One wave
-// per work-group streams 32-key K and V tiles of its slice through a private
-// LDS ring (LDS-DMA, explicit vmcnt waits, no barrier); the slab queries of its
-// first segments sit in an LDS table; each segment ends in a partial record
-// (or the output) per column, merged by decode_combine.
-
-#ifndef KVC_DECODE_MFMA_STAGES
-#define KVC_DECODE_MFMA_STAGES 2       // one tile in flight per wave ...
-#endif
-#ifndef KVC_DECODE_MFMA_BLOCKS_PER_CU
-#define KVC_DECODE_MFMA_BLOCKS_PER_CU 3   // ... and three waves per CU (measured best)
-#endif
-#ifndef KVC_DECODE_MFMA_QSEGS
-#define KVC_DECODE_MFMA_QSEGS 2
-#endif
-#ifndef KVC_DECODE_MFMA_MIN_ROWS
-#define KVC_DECODE_MFMA_MIN_ROWS 5    // 16-bit slabs with at least this many rows use the matrix cores
-#endif
-
-template <int D>
-struct MCfg : TileLayout<D> {
-    using L = TileLayout<D>;
-    static constexpr int QSEGS = KVC_DECODE_MFMA_QSEGS;      // segments the query table holds
-    static constexpr int QT_BYTES = QSEGS * 32 * D * 2;      // 32 columns of D 16-bit elements each
-    static constexpr int fit_stages() {
-        int ns = KVC_DECODE_MFMA_STAGES;
-        while (ns > 2 && ((ns * 2 * L::TILE_BYTES + QT_BYTES) * KVC_DECODE_MFMA_BLOCKS_PER_CU > kLdsLimit ||
-                          ns * 2 * L::TILE_BYTES + 24 * D * 2 > 65535))
-            --ns;
-        return ns;
-    }
-    static constexpr int NS = fit_stages();
-    static constexpr int STAGE_BYTES = 2 * L::TILE_BYTES;    // K tile, then V tile
-    static constexpr int LDS_BYTES = NS * STAGE_BYTES;
-    static_assert((NS - 1) * 2 * L::NLD < 64, "vmcnt field");
-    static_assert((NS - 1) * STAGE_BYTES + L::TILE_BYTES + 24 * D * 2 < 65536, "LDS read offsets fit 16 bits");
-};
-
-template <int D, int ST, bool PAGED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
-void decode_mfma(DecodeArgs a) {
-    using P = MCfg<D>;
-    constexpr int NS = P::NS, DS = P::DS, DT = P::DT, NLD = P::NLD;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[P::LDS_BYTES / 2];
-    __shared__ __attribute__((aligned(16))) uint16_t qtab[P::QSEGS][32][D];
-
-    const int lane = threadIdx.x;
-    const int col32 = lane & 31;                 // this lane's column: slab row col32
-    const int hl = lane >> 5;
-    const int rows_act = a.Gc * a.Tc;
-    const float c = a.scale_log2;
-    const float thresh = kRescaleLog2 / c;
-
-    const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
-    int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
-    if (x_end > a.total_keys) x_end = a.total_keys;
-    if (x_begin >= x_end) return;
-
-    const uint16_t* kg = static_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* vg = static_cast<const uint16_t*>(a.v_cache);
-
-    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
-        int lo = 0, hi = a.rows;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (a.prefix[mid] <= x) lo = mid; else hi = mid;
-        }
-        Seg sg;
-        sg.b = lo;
-        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
-        sg.g = static_cast<int>((x - a.prefix[lo]) / n_b);
-        const int64_t unit_start = a.prefix[lo] + static_cast<int64_t>(sg.g) * n_b;
-        int64_t seg_end = unit_start + n_b;
-        if (seg_end > x_end) seg_end = x_end;
-        sg.j0 = static_cast<int>(x - unit_start);
-        sg.j1 = static_cast<int>(seg_end - unit_start);
-        sg.n_b = static_cast<int>(n_b);
-        sg.nbat = (sg.j1 - sg.j0 + kBN - 1) / kBN;
-        sg.head = a.layer_off + sg.b * a.row_stride + sg.g * a.head_stride;
-        sg.x_end = seg_end;
-        sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
-        return sg;
-    };
-
-    // -- the query table: 32 columns (slab rows; past the slab zero) per segment,
-    //    rounded to the storage type --
-    auto load_qtab = [&](int64_t x) __attribute__((always_inline)) {
-        for (int sgi = 0; sgi < P::QSEGS && x < x_end; ++sgi) {
-            const Seg sg = locate(x);
-            if (a.q_dtype == ST) {
-                // q already in the storage type: 8 elements (16 bytes) at a time
-                for (int c8 = lane; c8 < 4 * D; c8 += 64) {
-                    const int r = c8 / (D / 8), e = (c8 - r * (D / 8)) * 8;
-                    u32x4 w = {0u, 0u, 0u, 0u};
-                    if (r < rows_act) {
-                        const int h = sg.g * a.G + a.r0 + r / a.Tc;
-                        const int i = a.i0 + r % a.Tc;
-                        const int64_t qe = ((static_cast<int64_t>(a.row0 + sg.b) * a.Hq + h) * a.T + i) * D + e;
-                        w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + qe);
-                    }
-                    *reinterpret_cast<u32x4*>(&qtab[sgi][r][e]) = w;
-                }
-                x = sg.x_end;
-                continue;
-            }
-            for (int idx = lane; idx < 32 * D; idx += 64) {
-                const int r = idx / D, e = idx - (idx / D) * D;
-                float val = 0.f;
-                if (r < rows_act) {
-                    const int h = sg.g * a.G + a.r0 + r / a.Tc;
-                    const int i = a.i0 + r % a.Tc;
-                    const int64_t qe = ((static_cast<int64_t>(a.row0 + sg.b) * a.Hq + h) * a.T + i) * D + e;
-                    if (a.q_dtype == F32) val = static_cast<const float*>(a.q)[qe];
-                    else if (a.q_dtype == BF16) val = bf16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
-                    else val = f16_to_f32(static_cast<const uint16_t*>(a.q)[qe]);
-                }
-                qtab[sgi][r][e] = static_cast<uint16_t>(ST == BF16 ? f32_to_bf16_rne(val) : f32_to_f16_rne(val));
-            }
-            x = sg.x_end;
-        }
-        __syncthreads();
-    };
-
-    // -- issue side: the next 32-key tile, K chunks XOR-swizzled, V chunks
-    //    permuted for the transposed reads; past the slice's end the last key
-    //    is reloaded (never used) --
-    Seg is = locate(x_begin);
-    int is_t = 0;
-    bool is_live = true;
-    // paged storage: pool offsets of head is.g's rows in the blocks of logical
-    // blocks pg_blk and pg_blk + 1 of the issue cursor's unit (a 32-key tile
-    // spans at most these two); the next block's entry is read by a scalar load
-    // when the cursor enters a block
-    int pg_blk = 0;
-    int64_t pg_base = 0, pg_next = 0;
-    auto pg_phys = [&](int blk) __attribute__((always_inline)) -> int64_t {
-        const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
-        const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
-        int p = tab[static_cast<int64_t>(is.b) * a.btab_stride + bi];
-        p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
-        return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + is.g) << a.bshift) * D;
-    };
-    auto pg_enter = [&]() __attribute__((always_inline)) {
-        pg_blk = is.j0 >> a.bshift;
-        pg_base = pg_phys(pg_blk);
-        pg_next = pg_phys(pg_blk + 1);
-    };
-    if constexpr (PAGED) pg_enter();
-    auto issue = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(slot_c)::value;
-        uint16_t* kd = smem + S * P::STAGE_BYTES / 2;
-        uint16_t* vd = kd + P::TILE;
-        if constexpr (PAGED) {
-            const int blk = (is.j0 + is_t * kBN) >> a.bshift;
-            if (is_live && blk != pg_blk) {       // the tile starts in the next block
-                pg_blk = blk;
-                pg_base = pg_next;
-                pg_next = pg_phys(blk + 1);
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            const int e = n * 512 + lane * 8;    // element offset inside the tile
-            const int r = e / D;
-            const int sl = (e % D) >> 3;
-            int j = is.j0 + is_t * kBN + r;
-            j = j < is.j1 ? j : is.j1 - 1;
-            int64_t row;
-            if constexpr (PAGED)
-                row = ((j >> a.bshift) == pg_blk ? pg_base : pg_next) +
-                      static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D;
-            else
-                row = is.head + static_cast<int64_t>(j) * D;
-            __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(kg + row + P::kslot(r, sl) * 8),
-                (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, KVC_DECODE_MFMA_KV_CPOL);
-            __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(vg + row + P::vchunk(r, sl) * 8),
-                (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0, KVC_DECODE_MFMA_KV_CPOL);
-        }
-        if (is_live && ++is_t == is.nbat) {
-            if (is.x_end >= x_end) {
-                is_live = false;
-            } else {
-                is = locate(is.x_end);
-                is_t = 0;
-                if constexpr (PAGED) pg_enter();
-            }
-        }
-    };
-
-    // -- LDS read addresses of this lane (stage offsets are immediates) --
-    const uint32_t lds0 = static_cast<uint32_t>(
-        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t*)smem));
-    uint32_t kaddr[DS];
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) kaddr[ds] = lds0 + (col32 * D + P::kslot(col32, 2 * ds + hl) * 8) * 2;
-    uint32_t vaddr[DT];
-    {
-        const int grp = lane >> 4, ii = (lane >> 2) & 3, aa = lane & 3;
-        const int rv = (grp >> 1) * 4 + ii;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int cv = dt * 4 + 2 * (grp & 1) + (aa >> 1);
-            vaddr[dt] = lds0 + P::TILE_BYTES + (rv * D + P::vslot(rv, cv) * 8) * 2 + (aa & 1) * 8;
-        }
-    }
-
-    // -- consume side --
-    Seg cs = locate(x_begin);
-    int cs_t = 0, cs_q = 0;
-    u32x4 qb[DS];
-    int qpos;
-    float m, lsum;
-    f32x16_t o[DT];
-    auto start_segment = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-            qb[ds] = *reinterpret_cast<const u32x4*>(&qtab[cs_q][col32][ds * 16 + hl * 8]);
-        qpos = col32 < rows_act ? cs.n_b - a.Tc + col32 % a.Tc : -1;
-        m = -INFINITY;
-        lsum = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
-    };
-
-    auto consume = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(slot_c)::value;
-        const int j0 = cs.j0 + cs_t * kBN;
-        const bool plain = j0 + kBN <= cs.j1 && j0 + kBN - 1 <= cs.n_b - a.Tc;
-        u32x4 ka[DS];
-        read_k<DS, S * P::STAGE_BYTES>(ka, kaddr);
-        f32x16_t sacc = f32x16_t{};
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) sacc = mfma32<ST>(ka[ds], qb[ds], sacc);
-        u32x2 vt[DT][2][2];
-        read_vt<DT, S * P::STAGE_BYTES, D * 2>(vt, vaddr);
-
-        // scores -> probabilities; value jj is key j0 + (jj / 4) * 8 + hl * 4 + jj % 4
-        float sv_[16];
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) sv_[jj] = sacc[jj];
-        if (!plain) {
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int j = j0 + (jj >> 2) * 8 + hl * 4 + (jj & 3);
-                if (!(j < cs.j1 && j <= qpos)) sv_[jj] = -INFINITY;
-            }
-        }
-        float mt = sv_[0];
-#pragma unroll
-        for (int jj = 1; jj < 16; ++jj) mt = fmaxf(mt, sv_[jj]);
-        if (__any(mt - m > thresh)) {
-            mt = xor_op<32, true>(mt);
-            if (mt - m > thresh) {
-                const float alpha = m == -INFINITY ? 0.f : fexp2((m - mt) * c);
-                m = mt;
-                lsum *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-            }
-        }
-        const float nmc = m == -INFINITY ? 0.f : -m * c;
-        uint32_t w[8];
-        float ls[2] = {0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            w[e] = pack_p<ST>(fexp2(fmaf(sv_[2 * e], c, nmc)), fexp2(fmaf(sv_[2 * e + 1], c, nmc)));
-            ls[e & 1] = add_pair<ST>(w[e], ls[e & 1]);
-        }
-        lsum += ls[0] + ls[1];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const u32x4 va = {vt[dt][kk][0][0], vt[dt][kk][0][1], vt[dt][kk][1][0], vt[dt][kk][1][1]};
-                const u32x4 pb = {w[kk * 4 + 0], w[kk * 4 + 1], w[kk * 4 + 2], w[kk * 4 + 3]};
-                o[dt] = mfma32<ST>(va, pb, o[dt]);
-            }
-    };
-
-    // -- end of a segment: column col32's (max, sum, output); the lane holds
-    //    head elements dt * 32 + (jj / 4) * 8 + hl * 4 + jj % 4 --
-    auto finish_segment = [&]() __attribute__((always_inline)) {
-        const float l_all = xor_op<32, false>(lsum);
-        if (col32 < rows_act) {
-            if (cs.rec < 0) {
-                const float inv = 1.f / l_all;
-                const int h = cs.g * a.G + a.r0 + col32 / a.Tc;
-                const int i = a.i0 + col32 % a.Tc;
-                float* dst = a.out + ((static_cast<int64_t>(a.row0 + cs.b) * a.Hq + h) * a.T + i) * D;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        *reinterpret_cast<float4*>(dst + dt * 32 + q4 * 8 + hl * 4) =
-                            make_float4(o[dt][q4 * 4 + 0] * inv, o[dt][q4 * 4 + 1] * inv,
-                                        o[dt][q4 * 4 + 2] * inv, o[dt][q4 * 4 + 3] * inv);
-            } else {
-                const int64_t rr = cs.rec * a.rec_rows + col32;
-                float* dst = a.ws_o + rr * D;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        *reinterpret_cast<float4*>(dst + dt * 32 + q4 * 8 + hl * 4) =
-                            make_float4(o[dt][q4 * 4 + 0], o[dt][q4 * 4 + 1], o[dt][q4 * 4 + 2], o[dt][q4 * 4 + 3]);
-                if (hl == 0) {
-                    a.ws_ml[rr * 2] = m;
-                    a.ws_ml[rr * 2 + 1] = l_all;
-                }
-            }
-        }
-    };
-
-    // -- the loop: tile t in slot t % NS, NS - 1 tiles issued ahead --
-    static_for<NS - 1>([&](auto k) { issue(k); });
-    load_qtab(x_begin);
-    start_segment();
-    bool done = false;
-    auto step = [&](auto slot_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(slot_c)::value;
-        issue(std::integral_constant<int, (S + NS - 1) % NS>{});
-        wait_vm<(NS - 1) * 2 * NLD>();   // this tile's loads have landed
-        consume(slot_c);
-        if (++cs_t == cs.nbat) {
-            finish_segment();
-            if (cs.x_end >= x_end) {
-                done = true;
-            } else {
-                cs = locate(cs.x_end);
-                cs_t = 0;
-                if (++cs_q == P::QSEGS) {    // more segments than the table holds: reload it
-                    load_qtab(cs.x_end - (cs.j1 - cs.j0));
-                    cs_q = 0;
-                }
-                start_segment();
-            }
-        }
-    };
-    while (!done) {
-        static_for<NS>([&](auto k) {
-            if (!done) step(k);
-        });
-    }
-    wait_vm<0>();
-}
-
-// Merge the partial records of units whose keys span several work-groups
-// (units held by one work-group were written by the attention kernel and are
-// skipped). Work-group (u, y) covers outputs y*256 .. y*256+255 of unit u's
-// slab, one (row, element) per thread.
-template <int D>
-__global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
-    constexpr int kMaxSeg = 16;
-    const int u = blockIdx.x;
-    const int b = u / a.Hkv;
-    const int g = u - b * a.Hkv;
-    const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
-    if (a.k_new != nullptr && blockIdx.y == gridDim.y - 1) {
-        // fused append: store unit (b, g)'s T new keys and values at slots
-        // n_b - T .. n_b - 1 (bit copies, the input has the storage type)
-        const int esz = a.st_dtype == F32 ? 4 : 2;
-        const int64_t src0 = ((static_cast<int64_t>(a.row0 + b) * a.Hkv + g) * a.T) * D;
-        for (int e = threadIdx.x; e < a.T * D; e += 256) {
-            const int t = e / D, d = e - (e / D) * D;
-            const int64_t p = n_b - a.T + t;
-            int64_t dst;
-            if (a.btab != nullptr) {
-                int blk = a.btab[static_cast<int64_t>(b) * a.btab_stride + (p >> a.bshift)];
-                blk = blk < 0 ? 0 : (blk >= a.pool_blocks ? a.pool_blocks - 1 : blk);
-                dst = a.layer_off + (((static_cast<int64_t>(blk) * a.Hkv + g) << a.bshift) + (p & ((1 << a.bshift) - 1))) * D + d;
-            } else {
-                dst = a.layer_off + b * a.row_stride + g * a.head_stride + p * D + d;
-            }
-            if (esz == 4) {
-                static_cast<float*>(const_cast<void*>(a.k_cache))[dst] = static_cast<const float*>(a.k_new)[src0 + e];
-                static_cast<float*>(const_cast<void*>(a.v_cache))[dst] = static_cast<const float*>(a.v_new)[src0 + e];
-            } else {
-                static_cast<uint16_t*>(const_cast<void*>(a.k_cache))[dst] = static_cast<const uint16_t*>(a.k_new)[src0 + e];
-                static_cast<uint16_t*>(const_cast<void*>(a.v_cache))[dst] = static_cast<const uint16_t*>(a.v_new)[src0 + e];
-            }
-        }
-        return;
-    }
-    const int64_t ustart = a.prefix[b] + g * n_b;
-    const int k_first = static_cast<int>(decode_slice_of(a, ustart));
-    const int k_last = static_cast<int>(decode_slice_of(a, ustart + n_b - 1));
-    if (k_first == k_last) return;
-    const int idx = static_cast<int>(blockIdx.y) * 256 + static_cast<int>(threadIdx.x);
-    if (idx >= a.Gc * a.Tc * D) return;
-    const float c = a.scale_log2;
-    const int r = idx / D, d = idx - (idx / D) * D;
-    float M = -INFINITY, ov = 0.f, lv = 0.f;
-    for (int k0 = k_first; k0 <= k_last; k0 += kMaxSeg) {
-        float mk[kMaxSeg], lk[kMaxSeg], okv[kMaxSeg];
-#pragma unroll
-        for (int t = 0; t < kMaxSeg; ++t) {
-            const int k = k0 + t;
-            const int64_t rec = static_cast<int64_t>((k <= k_last ? k : k_last) + u) * a.rec_rows + r;
-            mk[t] = k <= k_last ? a.ws_ml[rec * 2] : -INFINITY;
-            lk[t] = a.ws_ml[rec * 2 + 1];
-            okv[t] = a.ws_o[rec * D + d];
-        }
-        float Mn = M;
-#pragma unroll
-        for (int t = 0; t < kMaxSeg; ++t) Mn = fmaxf(Mn, mk[t]);
-        const float sc = M == -INFINITY ? 0.f : fexp2((M - Mn) * c);
-        ov *= sc;
-        lv *= sc;
-#pragma unroll
-        for (int t = 0; t < kMaxSeg; ++t) {
-            const float f = mk[t] == -INFINITY ? 0.f : fexp2((mk[t] - Mn) * c);
-            ov = fmaf(okv[t], f, ov);
-            lv = fmaf(lk[t], f, lv);
-        }
-        M = Mn;
-    }
-    const int h = g * a.G + a.r0 + r / a.Tc;
-    const int i = a.i0 + r % a.Tc;
-    a.out[((static_cast<int64_t>(a.row0 + b) * a.Hq + h) * a.T + i) * D + d] = ov / lv;
-}
-
-// CUs of the current device (cached per device).
-hipError_t device_cus(int& n_cu) {
-    static int cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (cus[dev & 63] == 0) {
-        int n = 0;
-        const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        cus[dev & 63] = n > 0 ? n : 1;
-    }
-    n_cu = cus[dev & 63];
-    return hipSuccess;
-}
-
-// Cut the key axis into work-group slices: up to per_cu work-groups per CU, at
-// least min_keys keys each, and no more records than the workspace holds.
-// Work-groups beyond the first dispatch round (one per CU) share a CU with an
-// older one, which the memory system serves first; they get a smaller slice,
-// KVC_DECODE_LATE_PCT percent of a first-round one.
-void split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min_keys) {
-    int64_t nb = static_cast<int64_t>(n_cu) * per_cu;
-    if (nb > kMaxDecodeBlocks) nb = kMaxDecodeBlocks;
-    const int64_t by_ws = a.ws_rows_cap / a.rec_rows - static_cast<int64_t>(a.rows) * a.Hkv;
-    if (nb > by_ws) nb = by_ws;
-    const int64_t by_size = (a.total_keys + min_keys - 1) / min_keys;
-    if (nb > by_size) nb = by_size;
-    if (nb < 1) nb = 1;
-    int64_t n1 = nb < n_cu ? nb : n_cu;
-    int64_t n2 = nb - n1;
-    const int64_t denom = n1 * 100 + n2 * KVC_DECODE_LATE_PCT;
-    int64_t kpb = (a.total_keys * 100 + denom - 1) / denom;
-    int64_t kpb2 = kpb * KVC_DECODE_LATE_PCT / 100;
-    if (kpb2 < 1) kpb2 = 1;
-    if (a.total_keys <= n1 * kpb) {
-        n1 = (a.total_keys + kpb - 1) / kpb;
-        n2 = 0;
-    } else {
-        n2 = (a.total_keys - n1 * kpb + kpb2 - 1) / kpb2;
-    }
-    if (n1 + n2 > nb) {   // rounding pushed past the cap: equal slices
-        kpb = kpb2 = (a.total_keys + nb - 1) / nb;
-        n1 = (a.total_keys + kpb - 1) / kpb;
-        n2 = 0;
-    }
-    a.keys_per_block = kpb;
-    a.keys_per_block2 = kpb2;
-    a.n_first = static_cast<int32_t>(n1);
-    a.n_blocks = static_cast<int32_t>(n1 + n2);
-}
-
-// The merge pass, if some unit spans several work-groups.
-template <int D>
-hipError_t combine_if_split(DecodeArgs& a, hipStream_t s) {
-    bool split = false;
-    for (int b = 0; b < a.rows && !split; ++b) {
-        const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
-        for (int g = 0; g < a.Hkv && !split; ++g) {
-            const int64_t us = a.prefix[b] + g * n_b;
-            split = decode_slice_of(a, us) != decode_slice_of(a, us + n_b - 1);
-        }
-    }
-    // a fused append adds one row of work-groups that store the new keys and values
-    if (!split && a.k_new == nullptr) return hipSuccess;
-    const unsigned merge_rows = split ? (a.Gc * a.Tc * D + 255) / 256 : 0;
-    const dim3 grid(a.rows * a.Hkv, merge_rows + (a.k_new != nullptr ? 1 : 0));
-    decode_combine<D><<<grid, 256, 0, s>>>(a);
-    return hipGetLastError();
-}
-
-template <int D, int ST, int R>
-hipError_t run(DecodeArgs& a, hipStream_t s) {
-    int n_cu = 0;
-    hipError_t e = device_cus(n_cu);
-    if (e != hipSuccess) return e;
-    a.rec_rows = R;
-    split_slices(a, n_cu, KVC_DECODE_BLOCKS_PER_CU, 2 * Cfg<D, ST, R>::KPB);
-    if (a.btab) {
-        if ((1 << a.bshift) < Cfg<D, ST, R>::KPB) return hipErrorInvalidValue;   // a batch within two blocks
-        decode_attn<D, ST, R, true><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
-    } else {
-        decode_attn<D, ST, R, false><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
-    }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return combine_if_split<D>(a, s);
-}
-
-template <int D, int ST, int RS>
-hipError_t run_rows(DecodeArgs& a, hipStream_t s) {
-    int n_cu = 0;
-    hipError_t e = device_cus(n_cu);
-    if (e != hipSuccess) return e;
-    a.rec_rows = RCfg<D, ST, RS>::ROWS;
-    split_slices(a, n_cu, 2, 2 * RCfg<D, ST, RS>::KPS);
-    if (a.btab) {
-        if ((1 << a.bshift) < RCfg<D, ST, RS>::KPS) return hipErrorInvalidValue;   // a stage within two blocks
-        decode_rows<D, ST, RS, true><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
-    } else {
-        decode_rows<D, ST, RS, false><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
-    }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return combine_if_split<D>(a, s);
-}
-
-template <int D, int ST>
-hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
-    int n_cu = 0;
-    hipError_t e = device_cus(n_cu);
-    if (e != hipSuccess) return e;
-    a.rec_rows = 32;
-    split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN);
-    if (a.btab) {
-        if ((1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks
-        decode_mfma<D, ST, true><<<a.n_blocks, 64, 0, s>>>(a);
-    } else {
-        decode_mfma<D, ST, false><<<a.n_blocks, 64, 0, s>>>(a);
-    }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return combine_if_split<D>(a, s);
-}
-
-template <int D, int ST>
-hipError_t run_r(DecodeArgs& a, hipStream_t s) {
-    const int rows = a.Gc * a.Tc;
-    if (a.k_new != nullptr) {     // fused append: one slab on the vector kernel
-        if (rows > (ST == F32 ? 8 : KVC_DECODE_MFMA_MIN_ROWS - 1) || a.Gc != a.G || a.Tc != a.T || a.r0 || a.i0)
-            return hipErrorInvalidValue;
-        return rows <= 4 ? run<D, ST, 4>(a, s) : run<D, ST, 8>(a, s);
-    }
-    if constexpr (ST != F32) {
-        if (rows >= KVC_DECODE_MFMA_MIN_ROWS) return run_mfma<D, ST>(a, s);
-    }
-    if (rows <= 4) return run<D, ST, 4>(a, s);
-    if (rows <= 8) return run<D, ST, 8>(a, s);
-    if constexpr (ST != F32) return run_mfma<D, ST>(a, s);
-    if (rows <= 16) return run_rows<D, ST, 2>(a, s);
-    return run_rows<D, ST, 4>(a, s);
-}
-
-template <int D>
-hipError_t run_d(DecodeArgs& a, hipStream_t s) {
-    switch (a.st_dtype) {
-        case F32: return run_r<D, F32>(a, s);
-        case F16: return run_r<D, F16>(a, s);
-        case BF16: return run_r<D, BF16>(a, s);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-}  // namespace
 
 int decode_vector_batch_keys(int D, int st_dtype, int rows) {
     auto pick = [&](auto d_c) -> int {
         constexpr int DD = decltype(d_c)::value;
         switch (st_dtype) {
-            case F32: return rows <= 4 ? Cfg<DD, F32, 4>::KPB : Cfg<DD, F32, 8>::KPB;
-            case F16: return rows <= 4 ? Cfg<DD, F16, 4>::KPB : Cfg<DD, F16, 8>::KPB;
-            default: return rows <= 4 ? Cfg<DD, BF16, 4>::KPB : Cfg<DD, BF16, 8>::KPB;
+            case F32: return decode_batch_keys<DD, F32>(rows);
+            case F16: return decode_batch_keys<DD, F16>(rows);
+            default: return decode_batch_keys<DD, BF16>(rows);
         }
     };
     switch (D) {
@@ -1568,6 +25,20 @@ int decode_vector_batch_keys(int D, int st_dtype, int rows) {
 bool decode_supported(int D, int st_dtype) {
     return (D == 32 || D == 64 || D == 128) && (st_dtype == F32 || st_dtype == F16 || st_dtype == BF16);
 }
+
+namespace {
+
+template <int D>
+hipError_t run_d(DecodeArgs& a, hipStream_t s) {
+    switch (a.st_dtype) {
+        case F32: return decode_run<D, F32>(a, s);
+        case F16: return decode_run<D, F16>(a, s);
+        case BF16: return decode_run<D, BF16>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
 
 hipError_t launch_decode(DecodeArgs& a, hipStream_t s) {
     if (a.Gc * a.Tc < 1 || a.Gc * a.Tc > kMaxDecodeRows) return hipErrorInvalidValue;

@@ -1,0 +1,7 @@
+// Split-K decode kernels for head dimension 64, bf16 storage.
+#include "kvc_decode_impl.h"
+
+namespace kvc {
+template hipError_t decode_run<64, BF16>(DecodeArgs& a, hipStream_t s);
+template int decode_batch_keys<64, BF16>(int rows);
+}  // namespace kvc

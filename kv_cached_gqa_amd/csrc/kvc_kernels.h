@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kvc {
 
 // Rows of the batch one launch covers; larger batches are split into several
@@ -156,6 +158,12 @@ __host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t 
 
 // Fills in the work split (n_blocks, slice sizes) from the device's resident capacity.
 hipError_t launch_decode(DecodeArgs& a, hipStream_t stream);
+// The decode kernels of one (head dimension, storage type), and their key batch
+// for a slab of `rows` query rows (one instantiation per translation unit).
+template <int D, int ST>
+hipError_t decode_run(DecodeArgs& a, hipStream_t stream);
+template <int D, int ST>
+int decode_batch_keys(int rows);
 // Keys per work-group batch of the vector decode kernel for a slab of `rows`
 // query rows (a paged cache's block must hold a whole number of batches).
 int decode_vector_batch_keys(int D, int st_dtype, int rows);

@@ -26,8 +26,8 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 # Sources whose change invalidates a stored decode traffic figure.
-DECODE_SOURCES = ("csrc/kvc_decode.hip", "csrc/kvc_kernels.h", "csrc/kvc_device.h", "csrc/kvc_mfma.h",
-                  "csrc/kvc_api.cpp")
+DECODE_SOURCES = tuple(sorted(os.path.relpath(f, PKG) for f in glob.glob(os.path.join(PKG, "csrc", "kvc_decode*")))) + (
+    "csrc/kvc_kernels.h", "csrc/kvc_device.h", "csrc/kvc_mfma.h", "csrc/kvc_api.cpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attend_c3_bf16_traffic.md")
 COPY_KERNEL_TAG = "MulFunctor"          # the calibration copy: torch.mul(src, 1, out=dst)
 
