@@ -989,6 +989,12 @@ void decode_rows(DecodeArgs a) {
 #ifndef KVC_DECODE_MFMA_QSEGS
 #define KVC_DECODE_MFMA_QSEGS 2
 #endif
+#ifndef KVC_DECODE_MFMA_LATE_PCT
+// equal slices: with three single-wave work-groups per CU an uneven split
+// measured slower on the long-context workload (e.g. 193 against 180 us at a
+// 4-token draft with 70%)
+#define KVC_DECODE_MFMA_LATE_PCT 100
+#endif
 #ifndef KVC_DECODE_MFMA_MIN_ROWS
 #define KVC_DECODE_MFMA_MIN_ROWS 5    // 16-bit slabs with at least this many rows use the matrix cores
 #endif
@@ -1416,8 +1422,8 @@ hipError_t device_cus(int& n_cu) {
 // least min_keys keys each, and no more records than the workspace holds.
 // Work-groups beyond the first dispatch round (one per CU) share a CU with an
 // older one, which the memory system serves first; they get a smaller slice,
-// KVC_DECODE_LATE_PCT percent of a first-round one.
-void split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min_keys) {
+// late_pct percent of a first-round one.
+void split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min_keys, int late_pct) {
     int64_t nb = static_cast<int64_t>(n_cu) * per_cu;
     if (nb > kMaxDecodeBlocks) nb = kMaxDecodeBlocks;
     const int64_t by_ws = a.ws_rows_cap / a.rec_rows - static_cast<int64_t>(a.rows) * a.Hkv;
@@ -1427,9 +1433,12 @@ void split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min_keys) {
     if (nb < 1) nb = 1;
     int64_t n1 = nb < n_cu ? nb : n_cu;
     int64_t n2 = nb - n1;
-    const int64_t denom = n1 * 100 + n2 * KVC_DECODE_LATE_PCT;
+    const int64_t denom = n1 * 100 + n2 * late_pct;
     int64_t kpb = (a.total_keys * 100 + denom - 1) / denom;
-    int64_t kpb2 = kpb * KVC_DECODE_LATE_PCT / 100;
+    // rounded up, so that n1 slices of kpb and n2 of kpb2 always cover the axis
+    // (rounded down, a last key or so spilled into one work-group more than the
+    // grid holds, and the split fell back to equal slices)
+    int64_t kpb2 = (kpb * late_pct + 99) / 100;
     if (kpb2 < 1) kpb2 = 1;
     if (a.total_keys <= n1 * kpb) {
         n1 = (a.total_keys + kpb - 1) / kpb;
@@ -1473,7 +1482,7 @@ hipError_t run(DecodeArgs& a, hipStream_t s) {
     hipError_t e = device_cus(n_cu);
     if (e != hipSuccess) return e;
     a.rec_rows = R;
-    split_slices(a, n_cu, KVC_DECODE_BLOCKS_PER_CU, 2 * Cfg<D, ST, R>::KPB);
+    split_slices(a, n_cu, KVC_DECODE_BLOCKS_PER_CU, 2 * Cfg<D, ST, R>::KPB, KVC_DECODE_LATE_PCT);
     if (a.btab) {
         if ((1 << a.bshift) < Cfg<D, ST, R>::KPB) return hipErrorInvalidValue;   // a batch within two blocks
         decode_attn<D, ST, R, true><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
@@ -1491,7 +1500,7 @@ hipError_t run_rows(DecodeArgs& a, hipStream_t s) {
     hipError_t e = device_cus(n_cu);
     if (e != hipSuccess) return e;
     a.rec_rows = RCfg<D, ST, RS>::ROWS;
-    split_slices(a, n_cu, 2, 2 * RCfg<D, ST, RS>::KPS);
+    split_slices(a, n_cu, 2, 2 * RCfg<D, ST, RS>::KPS, KVC_DECODE_LATE_PCT);
     if (a.btab) {
         if ((1 << a.bshift) < RCfg<D, ST, RS>::KPS) return hipErrorInvalidValue;   // a stage within two blocks
         decode_rows<D, ST, RS, true><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
@@ -1509,7 +1518,7 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
     hipError_t e = device_cus(n_cu);
     if (e != hipSuccess) return e;
     a.rec_rows = 32;
-    split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN);
+    split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT);
     if (a.btab) {
         if ((1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks
         decode_mfma<D, ST, true><<<a.n_blocks, 64, 0, s>>>(a);
