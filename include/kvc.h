@@ -71,9 +71,12 @@ typedef struct kvc_cache kvc_cache;
  *    store_bytes_each must be >= nbytes / 2. The caller keeps ownership and
  *    must keep both buffers alive for the life of the handle.
  *  out: receives the handle. Every fill count starts at 0.
- * The library also owns a device workspace for split-K partial results,
- * allocated on the storage's device at the first kvc_attend and freed by
- * kvc_destroy. No device work is done here.
+ * The library also owns a device workspace for split-K partial results: when
+ * the storage is device memory it is allocated here, on the storage's device
+ * (so no later call allocates), and freed by kvc_destroy. Storage that is not
+ * device memory gives a handle that keeps metadata (seq_len, truncate, nbytes)
+ * but launches nothing: every call that would enqueue device work on it
+ * returns KVC_ERR_STORAGE. No device work is done here.
  * Errors: KVC_ERR_ARG (null cfg/out, nonpositive dims, n_q_heads not a multiple
  * of n_kv_heads, max_len * d_head >= 2^31), KVC_ERR_DTYPE, KVC_ERR_UNSUPPORTED,
  * KVC_ERR_STORAGE, KVC_ERR_NOMEM. */
@@ -96,7 +99,11 @@ void kvc_destroy(kvc_cache* cache);
  *  The committed length (kvc_seq_len with layer -1) moves only when every
  *  layer has appended ("KV cache, ...", section 2.3).
  * Errors: KVC_ERR_ARG (null handle or pointer, layer out of range, T < 1),
- * KVC_ERR_DTYPE, KVC_ERR_CAPACITY (fill + T > max_len for some row), KVC_ERR_HIP. */
+ * KVC_ERR_DTYPE, KVC_ERR_CAPACITY (fill + T > max_len for some row),
+ * KVC_ERR_STORAGE (the handle's storage is not device memory), KVC_ERR_HIP.
+ * On an error the fills and block accounting are unchanged; when a launch
+ * fails (a batch above 256 rows takes several), slots past the fills may have
+ * been written. */
 int kvc_append(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
                int32_t in_dtype, int32_t T, void* stream);
 
@@ -138,7 +145,8 @@ int kvc_rope_q(const kvc_cache* cache, int32_t layer, void* q, int32_t q_dtype, 
  *  h reads KV head h / G. out = softmax(q K^T / sqrt(d_head)) V with float32
  *  accumulation. Read-only on the cache; fills are unchanged.
  * Errors: KVC_ERR_ARG (null pointer, layer out of range, T < 1), KVC_ERR_DTYPE,
- * KVC_ERR_STATE (fill[layer][b] < T for some row), KVC_ERR_NOMEM, KVC_ERR_HIP. */
+ * KVC_ERR_STATE (fill[layer][b] < T for some row), KVC_ERR_STORAGE (storage
+ * not device memory), KVC_ERR_HIP. Allocates nothing. */
 int kvc_attend(kvc_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
                int32_t T, float* out, void* stream);
 
@@ -148,18 +156,32 @@ int kvc_attend(kvc_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
  * section 2.3: a pass appends its chunk, then attends over all stored
  * positions; "kv-cache-decoding", steps 5-6).
  *  When in_dtype is the storage dtype and T * (n_q_heads / n_kv_heads) is at
- *  most 4 (8 for an fp32 cache), a decode step, the attention kernel reads the
+ *  most 32 (8 for an fp32 cache), a decode step, the attention kernel reads the
  *  chunk's keys and values from k_new and v_new and the merge pass that
  *  follows it stores them in the cache, so no separate append launch runs.
  *  Otherwise the call runs kvc_append, then kvc_attend. Either way k_new, v_new
- *  and q must stay valid until the stream has passed the call. A NaN input is
- *  stored as the canonical quiet NaN by kvc_append but copied bit for bit by
- *  the fused path; every other value is stored the same way.
- * Errors: those of kvc_append and kvc_attend; on an argument, dtype or
- * capacity error nothing changes. */
+ *  and q must stay valid until the stream has passed the call, and the cache
+ *  ends with the bits kvc_append stores (a 16-bit NaN input becomes the
+ *  canonical quiet NaN of its sign on both paths).
+ * Errors: those of kvc_append and kvc_attend. On any error the fills and the
+ *  paged block accounting are as before the call: the fused path advances the
+ *  fills only once its launches are enqueued, and the two-call path undoes its
+ *  append when the attention launch fails (slots past the fills may then hold
+ *  the chunk). */
 int kvc_append_attend(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
                       int32_t in_dtype, const void* q, int32_t q_dtype, int32_t T, float* out,
                       void* stream);
+
+/* Copy out what one layer stores ("KV cache, ...", section 4: update returns
+ * all stored keys and values, the new chunk included; for a paged cache they
+ * are not one contiguous run, so this call assembles them).
+ *  k_out, v_out: device [batch][n_kv_heads][n][d_head] of the storage dtype,
+ *    16-byte aligned, written on `stream`: position p of row b is the stored
+ *    value when p < fill[layer][b], zero otherwise. 1 <= n <= max_len.
+ *  Read-only on the cache. Works on contiguous and paged handles.
+ * Errors: KVC_ERR_ARG (null, layer out of range, n out of range, misaligned),
+ * KVC_ERR_STORAGE (storage not device memory), KVC_ERR_HIP. */
+int kvc_gather(const kvc_cache* cache, int32_t layer, int64_t n, void* k_out, void* v_out, void* stream);
 
 /* Per-row lengths ("KV cache, ...", section 2.3, seq_len).
  *  layer = -1: the committed length s_b = min over layers of fill[layer][b];
@@ -194,8 +216,9 @@ int kvc_nbytes(const kvc_cache* cache, uint64_t* out);
 
 /* Create a paged handle over caller-owned block pools.
  *  block_size: positions per block, a power of two from 64 to 4096 (at least
- *    the decode kernel's key batch for this d_head and dtype, else
- *    KVC_ERR_UNSUPPORTED; 128 and above always qualifies).
+ *    the decode kernels' key batch for this d_head and dtype, else
+ *    KVC_ERR_UNSUPPORTED; every supported shape's batch is at most 64 keys).
+ *  cfg->max_len * d_head must be below 2^31, as for kvc_create.
  *  n_blocks: blocks in the pool, shared by all rows.
  *  k_pool, v_pool: device buffers, each at least pool_bytes_each bytes, holding
  *    [n_layers][n_blocks][n_kv_heads][block_size][d_head] elements of

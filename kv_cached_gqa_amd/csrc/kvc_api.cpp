@@ -39,7 +39,8 @@ struct kvc_cache {
     void* k_store;
     void* v_store;
     std::vector<int64_t> fill;    // [n_layers][batch]
-    // split-K workspace, allocated on first attend on the storage's device
+    // split-K workspace, allocated at create on the storage's device (null when
+    // the storage is not device memory: such a handle launches nothing)
     int device;
     float* ws_o;
     float* ws_ml;
@@ -91,10 +92,17 @@ int64_t workspace_segments(const kvc_config& c) {
     return kMaxDecodeBlocks + (kMaxDecodeRows / kWsRecordRows) * units;
 }
 
-int ensure_workspace(kvc_cache* c) {
-    if (c->ws_o) return KVC_OK;
+// The split-K workspace on the device that holds the storage, allocated when
+// the handle is created. Storage that is not device memory (or no GPU runtime)
+// leaves the handle without one: KVC_OK, and every call that would launch
+// device work on it returns KVC_ERR_STORAGE. KVC_ERR_NOMEM if the allocation
+// fails.
+int alloc_workspace(kvc_cache* c) {
     hipPointerAttribute_t attr;
-    if (hipPointerGetAttributes(&attr, c->k_store) != hipSuccess) return KVC_ERR_HIP;
+    if (hipPointerGetAttributes(&attr, c->k_store) != hipSuccess || attr.type != hipMemoryTypeDevice) {
+        (void)hipGetLastError();
+        return KVC_OK;
+    }
     int prev = 0;
     if (hipGetDevice(&prev) != hipSuccess) return KVC_ERR_HIP;
     const int dev = attr.device;
@@ -119,6 +127,9 @@ int ensure_workspace(kvc_cache* c) {
     c->ws_segments = segs;
     return KVC_OK;
 }
+
+// Whether the handle can launch device work (its storage is device memory).
+bool on_device(const kvc_cache* c) { return c->ws_o != nullptr; }
 
 }  // namespace
 
@@ -167,6 +178,11 @@ int kvc_create(const kvc_config* cfg, void* k_store, void* v_store, uint64_t sto
     h->ws_segments = 0;
     h->block_size = 0;
     h->d_table = nullptr;
+    const int rw = alloc_workspace(h);
+    if (rw != KVC_OK) {
+        delete h;
+        return rw;
+    }
     *out = h;
     return KVC_OK;
 }
@@ -181,6 +197,8 @@ int kvc_create_paged(const kvc_config* cfg, int32_t block_size, int32_t n_blocks
     if (block_size < 64 || (block_size & (block_size - 1)) || block_size > 4096 || n_blocks < 1) return KVC_ERR_ARG;
     const int64_t width = (c.max_len + block_size - 1) / block_size;
     if (width * c.batch >= (int64_t(1) << 31) || c.max_len >= (int64_t(1) << 31)) return KVC_ERR_ARG;
+    // as for a contiguous cache: a chunk's T * d_head elements index in 32 bits
+    if (c.max_len * static_cast<int64_t>(c.d_head) >= (int64_t(1) << 31)) return KVC_ERR_ARG;
     if (!dtype_ok(c.dtype)) return KVC_ERR_DTYPE;
     if (!kvc::decode_supported(c.d_head, c.dtype)) return KVC_ERR_UNSUPPORTED;
     // a decode batch of keys spans at most two blocks
@@ -240,6 +258,11 @@ int kvc_create_paged(const kvc_config* cfg, int32_t block_size, int32_t n_blocks
         return KVC_ERR_NOMEM;
     }
     h->d_table = static_cast<int32_t*>(t);
+    const int rw = alloc_workspace(h);
+    if (rw != KVC_OK) {
+        kvc_destroy(h);
+        return rw;
+    }
     *out = h;
     return KVC_OK;
 }
@@ -280,6 +303,8 @@ int32_t blocks_for(const kvc_cache* c, int64_t n) {
     return static_cast<int32_t>((n + c->block_size - 1) >> c->bshift);
 }
 
+void release_unused(kvc_cache* c);
+
 // Paged cache: give every row the blocks that positions [0, f[b] + T) need,
 // and enqueue the table entries that change. All or nothing: KVC_ERR_CAPACITY
 // (pool exhausted) before anything changes.
@@ -298,16 +323,22 @@ int grow_blocks(kvc_cache* c, const int64_t* f, int32_t T, hipStream_t s) {
             const int32_t id = c->free_ids.back();
             c->free_ids.pop_back();
             c->table[static_cast<size_t>(b) * c->width + k] = id;
-            c->held[b] = k + 1;            // held at once: a failed launch below leaks no block
+            c->held[b] = k + 1;
             a.index[a.n] = b * c->width + k;
             a.value[a.n] = id;
             if (++a.n == kvc::kMaxTableSets) {
-                if (kvc::launch_table_set(a, s) != hipSuccess) return KVC_ERR_HIP;
+                if (kvc::launch_table_set(a, s) != hipSuccess) {
+                    release_unused(c);
+                    return KVC_ERR_HIP;
+                }
                 a.n = 0;
             }
         }
     }
-    if (a.n > 0 && kvc::launch_table_set(a, s) != hipSuccess) return KVC_ERR_HIP;
+    if (a.n > 0 && kvc::launch_table_set(a, s) != hipSuccess) {
+        release_unused(c);
+        return KVC_ERR_HIP;
+    }
     return KVC_OK;
 }
 
@@ -322,6 +353,19 @@ void shrink_blocks(kvc_cache* c, int b, int64_t n) {
     c->held[b] = std::min(c->held[b], keep);
 }
 
+// Paged cache: give back every block no layer's fill reaches (a row holds
+// exactly the blocks of its longest layer). Used when a call that took blocks
+// fails, so that the call leaves the block accounting as it found it.
+void release_unused(kvc_cache* c) {
+    if (!c->block_size) return;
+    for (int b = 0; b < c->cfg.batch; ++b) {
+        int64_t longest = 0;
+        for (int l = 0; l < c->cfg.n_layers; ++l)
+            longest = std::max(longest, c->fill[static_cast<size_t>(l) * c->cfg.batch + b]);
+        shrink_blocks(c, b, longest);
+    }
+}
+
 // Append with or without the rotary embedding of K (rope_base > 0).
 int append_impl(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new, int32_t in_dtype, int32_t T,
                 double rope_base, void* stream) {
@@ -333,6 +377,7 @@ int append_impl(kvc_cache* c, int32_t layer, const void* k_new, const void* v_ne
     int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
     for (int b = 0; b < cf.batch; ++b)
         if (f[b] + T > cf.max_len) return KVC_ERR_CAPACITY;
+    if (!on_device(c)) return KVC_ERR_STORAGE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (c->block_size) {
         const int rc = grow_blocks(c, f, T, s);
@@ -369,7 +414,11 @@ int append_impl(kvc_cache* c, int32_t layer, const void* k_new, const void* v_ne
         }
         if (a.rope) rope_freqs(rope_base, cf.d_head, a.inv_freq);
         for (int b = 0; b < a.rows; ++b) a.fill[b] = static_cast<int32_t>(f[row0 + b]);
-        if (kvc::launch_append(a, s) != hipSuccess) return KVC_ERR_HIP;
+        if (kvc::launch_append(a, s) != hipSuccess) {
+            // fills unchanged: launches that did run wrote only past the fills
+            release_unused(c);
+            return KVC_ERR_HIP;
+        }
     }
     for (int b = 0; b < cf.batch; ++b) f[b] += T;
     return KVC_OK;
@@ -400,6 +449,7 @@ int kvc_rope_q(const kvc_cache* c, int32_t layer, void* q, int32_t q_dtype, int3
     const int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
     for (int b = 0; b < cf.batch; ++b)
         if (f[b] < T) return KVC_ERR_STATE;
+    if (!on_device(c)) return KVC_ERR_STORAGE;
     const int64_t row_bytes = static_cast<int64_t>(cf.n_q_heads) * T * cf.d_head * kvc::itemsize(q_dtype);
     for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
         kvc::RopeArgs a;
@@ -421,15 +471,14 @@ int kvc_rope_q(const kvc_cache* c, int32_t layer, void* q, int32_t q_dtype, int3
 
 namespace {
 
-// Attention of the last T positions of `layer` (arguments checked by the caller).
-// k_new, v_new non-null: a fused append whose chunk the decode kernel reads
-// from the input (one slab on the vector kernel; the fills already count it).
+// Attention of the last T positions of `layer` (arguments checked by the caller),
+// each row's fill taken as fill + pending. k_new, v_new non-null: a fused
+// append whose chunk (pending = T positions, not yet counted in the fills) the
+// decode kernel reads from the input and its merge pass stores (one slab).
 int attend_impl(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int32_t T, float* out, void* stream,
-                const void* k_new, const void* v_new) {
+                const void* k_new, const void* v_new, int64_t pending) {
     const kvc_config& cf = c->cfg;
     const int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
-    const int rc = ensure_workspace(c);
-    if (rc != KVC_OK) return rc;
 
     const int G = cf.n_q_heads / cf.n_kv_heads;
     const int64_t head_stride = cf.max_len * cf.d_head;
@@ -480,7 +529,7 @@ int attend_impl(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
                     a.bshift = c->bshift;
                     a.pool_blocks = c->n_blocks;
                 }
-                for (int b = 0; b < rows; ++b) a.offset[b] = static_cast<int32_t>(f[row0 + b] - T);
+                for (int b = 0; b < rows; ++b) a.offset[b] = static_cast<int32_t>(f[row0 + b] + pending - T);
                 if (kvc::launch_prefill(a, s) != hipSuccess) return KVC_ERR_HIP;
             }
         }
@@ -533,7 +582,7 @@ int attend_impl(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
                 int64_t acc = 0;
                 for (int b = 0; b < rows; ++b) {
                     a.prefix[b] = acc;
-                    const int64_t n_b = f[row0 + b] - T + i0 + a.Tc;   // keys the slab's last query sees
+                    const int64_t n_b = f[row0 + b] + pending - T + i0 + a.Tc;   // keys the slab's last query sees
                     acc += n_b * cf.n_kv_heads;
                 }
                 a.prefix[rows] = acc;
@@ -548,11 +597,13 @@ int attend_impl(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
 }
 
 // Whether append + attend of a chunk can run as one decode launch: the input
-// already has the storage type and the chunk is one slab of the vector kernel.
+// already has the storage type and the chunk is one decode slab (at most 32
+// query rows per KV head on a 16-bit cache, the matrix-core kernel; at most 8
+// on an fp32 cache, the vector kernel).
 bool fusable(const kvc_cache* c, int32_t in_dtype, int32_t T) {
     const kvc_config& cf = c->cfg;
     const int64_t rows = static_cast<int64_t>(T) * (cf.n_q_heads / cf.n_kv_heads);
-    return in_dtype == cf.dtype && rows <= (cf.dtype == KVC_F32 ? 8 : 4);
+    return in_dtype == cf.dtype && rows <= (cf.dtype == KVC_F32 ? 8 : kMaxDecodeRows);
 }
 
 }  // namespace
@@ -568,7 +619,8 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
     const int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
     for (int b = 0; b < cf.batch; ++b)
         if (f[b] < T) return KVC_ERR_STATE;
-    return attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr);
+    if (!on_device(c)) return KVC_ERR_STORAGE;
+    return attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr, 0);
 }
 
 int kvc_append_attend(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new, int32_t in_dtype,
@@ -581,23 +633,70 @@ int kvc_append_attend(kvc_cache* c, int32_t layer, const void* k_new, const void
     int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
     for (int b = 0; b < cf.batch; ++b)
         if (f[b] + T > cf.max_len) return KVC_ERR_CAPACITY;
+    if (!on_device(c)) return KVC_ERR_STORAGE;
     if (!fusable(c, in_dtype, T)) {
-        // the workspace first, so that past the append only a launch can fail
-        const int rw = ensure_workspace(c);
-        if (rw != KVC_OK) return rw;
         const int rc = append_impl(c, layer, k_new, v_new, in_dtype, T, 0.0, stream);
         if (rc != KVC_OK) return rc;
-        return attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr);
+        const int ra = attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr, 0);
+        if (ra != KVC_OK) {
+            // undo the append: fills back, blocks it took given back (its slots
+            // now lie past the fills)
+            for (int b = 0; b < cf.batch; ++b) f[b] -= T;
+            release_unused(c);
+        }
+        return ra;
     }
-    const int rc = ensure_workspace(c);
-    if (rc != KVC_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (c->block_size) {
         const int rg = grow_blocks(c, f, T, s);
         if (rg != KVC_OK) return rg;
     }
+    const int ra = attend_impl(c, layer, q, q_dtype, T, out, stream, k_new, v_new, T);
+    if (ra != KVC_OK) {
+        release_unused(c);
+        return ra;
+    }
     for (int b = 0; b < cf.batch; ++b) f[b] += T;
-    return attend_impl(c, layer, q, q_dtype, T, out, stream, k_new, v_new);
+    return KVC_OK;
+}
+
+int kvc_gather(const kvc_cache* c, int32_t layer, int64_t n, void* k_out, void* v_out, void* stream) {
+    if (!c || !k_out || !v_out) return KVC_ERR_ARG;
+    const kvc_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || n < 1 || n > cf.max_len) return KVC_ERR_ARG;
+    if (!aligned16(k_out) || !aligned16(v_out)) return KVC_ERR_ARG;
+    if (!on_device(c)) return KVC_ERR_STORAGE;
+    const int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
+    const int64_t head_stride = cf.max_len * cf.d_head;
+    const int64_t row_stride = head_stride * cf.n_kv_heads;
+    const int64_t out_row = static_cast<int64_t>(cf.n_kv_heads) * n * cf.d_head * kvc::itemsize(cf.dtype);
+    for (int row0 = 0; row0 < cf.batch; row0 += kMaxRowsPerLaunch) {
+        kvc::GatherArgs a;
+        std::memset(&a, 0, sizeof(a));
+        kvc::AppendArgs& l = a.loc;
+        l.rows = std::min(kMaxRowsPerLaunch, cf.batch - row0);
+        l.k_cache = c->k_store;
+        l.v_cache = c->v_store;
+        l.layer_off = (static_cast<int64_t>(layer) * cf.batch + row0) * row_stride;
+        l.row_stride = row_stride;
+        l.head_stride = head_stride;
+        l.H = cf.n_kv_heads;
+        l.T = static_cast<int32_t>(n);
+        l.D = cf.d_head;
+        l.st_dtype = cf.dtype;
+        if (c->block_size) {
+            l.layer_off = layer * pool_layer_elems(c);
+            l.btab = c->d_table + static_cast<int64_t>(row0) * c->width;
+            l.btab_stride = c->width;
+            l.bshift = c->bshift;
+            l.pool_blocks = c->n_blocks;
+        }
+        for (int b = 0; b < l.rows; ++b) l.fill[b] = static_cast<int32_t>(f[row0 + b]);
+        a.k_out = static_cast<char*>(k_out) + row0 * out_row;
+        a.v_out = static_cast<char*>(v_out) + row0 * out_row;
+        if (kvc::launch_gather(a, static_cast<hipStream_t>(stream)) != hipSuccess) return KVC_ERR_HIP;
+    }
+    return KVC_OK;
 }
 
 int kvc_seq_len(const kvc_cache* c, int32_t layer, int64_t* out_lens) {

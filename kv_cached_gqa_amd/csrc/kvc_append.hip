@@ -105,6 +105,28 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
     }
 }
 
+// One 16-byte vector per thread and step; blockIdx.y selects K or V.
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+    const AppendArgs& l = a.loc;
+    const int esz = l.st_dtype == F32 ? 4 : 2;
+    const int vpp = l.D * esz / 16;                         // 16-byte vectors per position
+    const int64_t n_vec = static_cast<int64_t>(l.rows) * l.H * l.T * vpp;
+    const char* src = static_cast<const char*>(blockIdx.y == 0 ? l.k_cache : l.v_cache);
+    char* dst = static_cast<char*>(blockIdx.y == 0 ? a.k_out : a.v_out);
+    for (int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; v < n_vec;
+         v += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t pos_run = v / vpp;                    // (row, head, position)
+        const int within = static_cast<int>(v - pos_run * vpp);
+        const int64_t run = pos_run / l.T;
+        const int64_t p = pos_run - run * l.T;
+        const int b = static_cast<int>(run / l.H);
+        const int g = static_cast<int>(run - static_cast<int64_t>(b) * l.H);
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (p < l.fill[b]) x = *reinterpret_cast<const uint4*>(src + slot_offset(l, b, g, p) * esz + within * 16);
+        *reinterpret_cast<uint4*>(dst + v * 16) = x;
+    }
+}
+
 __global__ __launch_bounds__(256) void table_set_kernel(TableSetArgs a) {
     for (int i = threadIdx.x; i < a.n; i += 256) a.table[a.index[i]] = a.value[i];
 }
@@ -128,6 +150,16 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
         case BF16: rope_kernel<BF16><<<static_cast<unsigned>(blocks), 256, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
+    const int esz = a.loc.st_dtype == F32 ? 4 : 2;
+    const int64_t n_vec = static_cast<int64_t>(a.loc.rows) * a.loc.H * a.loc.T * (a.loc.D * esz / 16);
+    int64_t blocks = (n_vec + 255) / 256;
+    if (blocks > 8192) blocks = 8192;   // grid-stride beyond this
+    if (blocks < 1) blocks = 1;
+    gather_kernel<<<dim3(static_cast<unsigned>(blocks), 2), 256, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -989,14 +989,17 @@ void decode_rows(DecodeArgs a) {
 #ifndef KVC_DECODE_MFMA_QSEGS
 #define KVC_DECODE_MFMA_QSEGS 2
 #endif
+#ifndef KVC_DECODE_MFMA_PSPLIT
+#define KVC_DECODE_MFMA_PSPLIT 1      // 1: P as a 16-bit hi + lo pair (two products with V); 0: P rounded once
+#endif
+#ifndef KVC_DECODE_MFMA_MIN_ROWS
+#define KVC_DECODE_MFMA_MIN_ROWS 1    // 16-bit slabs with fewer rows run on the vector kernel
+#endif
 #ifndef KVC_DECODE_MFMA_LATE_PCT
 // equal slices: with three single-wave work-groups per CU an uneven split
 // measured slower on the long-context workload (e.g. 193 against 180 us at a
 // 4-token draft with 70%)
 #define KVC_DECODE_MFMA_LATE_PCT 100
-#endif
-#ifndef KVC_DECODE_MFMA_MIN_ROWS
-#define KVC_DECODE_MFMA_MIN_ROWS 5    // 16-bit slabs with at least this many rows use the matrix cores
 #endif
 
 template <int D>
@@ -1153,11 +1156,22 @@ void decode_mfma(DecodeArgs a) {
                       static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D;
             else
                 row = is.head + static_cast<int64_t>(j) * D;
+            const uint16_t* kp = kg;
+            const uint16_t* vp = vg;
+            if (a.k_new != nullptr) {
+                // fused append: the chunk's new keys come from the caller's input
+                const int jn = j - (is.n_b - a.T);
+                if (jn >= 0) {
+                    kp = static_cast<const uint16_t*>(a.k_new);
+                    vp = static_cast<const uint16_t*>(a.v_new);
+                    row = ((static_cast<int64_t>(a.row0 + is.b) * a.Hkv + is.g) * a.T + jn) * D;
+                }
+            }
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(kg + row + P::kslot(r, sl) * 8),
+                (const void __attribute__((address_space(1)))*)(kp + row + P::kslot(r, sl) * 8),
                 (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0, KVC_DECODE_MFMA_KV_CPOL);
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(vg + row + P::vchunk(r, sl) * 8),
+                (const void __attribute__((address_space(1)))*)(vp + row + P::vchunk(r, sl) * 8),
                 (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0, KVC_DECODE_MFMA_KV_CPOL);
         }
         if (is_live && ++is_t == is.nbat) {
@@ -1243,12 +1257,22 @@ void decode_mfma(DecodeArgs a) {
             }
         }
         const float nmc = m == -INFINITY ? 0.f : -m * c;
-        uint32_t w[8];
+        // each probability as a 16-bit pair hi + lo: hi = p rounded to the
+        // storage type, lo = the (exact) residual p - hi rounded again, so
+        // hi + lo carries p to ~2^-17 relative (bf16) and the product with V
+        // runs twice; the normaliser sums the same hi and lo values
+        uint32_t w[8], wl[8];
         float ls[2] = {0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            w[e] = pack_p<ST>(fexp2(fmaf(sv_[2 * e], c, nmc)), fexp2(fmaf(sv_[2 * e + 1], c, nmc)));
+            const float p0 = fexp2(fmaf(sv_[2 * e], c, nmc));
+            const float p1 = fexp2(fmaf(sv_[2 * e + 1], c, nmc));
+            w[e] = pack_p<ST>(p0, p1);
             ls[e & 1] = add_pair<ST>(w[e], ls[e & 1]);
+            if constexpr (KVC_DECODE_MFMA_PSPLIT) {
+                wl[e] = pack_p<ST>(p0 - low_half<ST>(w[e]), p1 - high_half<ST>(w[e]));
+                ls[e & 1] = add_pair<ST>(wl[e], ls[e & 1]);
+            }
         }
         lsum += ls[0] + ls[1];
 #pragma unroll
@@ -1258,6 +1282,10 @@ void decode_mfma(DecodeArgs a) {
                 const u32x4 va = {vt[dt][kk][0][0], vt[dt][kk][0][1], vt[dt][kk][1][0], vt[dt][kk][1][1]};
                 const u32x4 pb = {w[kk * 4 + 0], w[kk * 4 + 1], w[kk * 4 + 2], w[kk * 4 + 3]};
                 o[dt] = mfma32<ST>(va, pb, o[dt]);
+                if constexpr (KVC_DECODE_MFMA_PSPLIT) {
+                    const u32x4 pl = {wl[kk * 4 + 0], wl[kk * 4 + 1], wl[kk * 4 + 2], wl[kk * 4 + 3]};
+                    o[dt] = mfma32<ST>(va, pl, o[dt]);
+                }
             }
     };
 
@@ -1341,7 +1369,9 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
     if (a.k_new != nullptr && blockIdx.y == gridDim.y - 1) {
         // fused append: store unit (b, g)'s T new keys and values at slots
-        // n_b - T .. n_b - 1 (bit copies, the input has the storage type)
+        // n_b - T .. n_b - 1 (the input has the storage type: bit copies, with a
+        // 16-bit NaN stored as the canonical quiet NaN of its sign, as the
+        // append kernel's rounding stores it)
         const int esz = a.st_dtype == F32 ? 4 : 2;
         const int64_t src0 = ((static_cast<int64_t>(a.row0 + b) * a.Hkv + g) * a.T) * D;
         for (int e = threadIdx.x; e < a.T * D; e += 256) {
@@ -1359,8 +1389,15 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
                 static_cast<float*>(const_cast<void*>(a.k_cache))[dst] = static_cast<const float*>(a.k_new)[src0 + e];
                 static_cast<float*>(const_cast<void*>(a.v_cache))[dst] = static_cast<const float*>(a.v_new)[src0 + e];
             } else {
-                static_cast<uint16_t*>(const_cast<void*>(a.k_cache))[dst] = static_cast<const uint16_t*>(a.k_new)[src0 + e];
-                static_cast<uint16_t*>(const_cast<void*>(a.v_cache))[dst] = static_cast<const uint16_t*>(a.v_new)[src0 + e];
+                const uint32_t inf = a.st_dtype == BF16 ? 0x7F80u : 0x7C00u;
+                const uint32_t qnan = a.st_dtype == BF16 ? 0x7FC0u : 0x7E00u;
+                auto canon = [&](uint32_t h) -> uint16_t {
+                    return static_cast<uint16_t>((h & 0x7FFFu) > inf ? (h & 0x8000u) | qnan : h);
+                };
+                static_cast<uint16_t*>(const_cast<void*>(a.k_cache))[dst] =
+                    canon(static_cast<const uint16_t*>(a.k_new)[src0 + e]);
+                static_cast<uint16_t*>(const_cast<void*>(a.v_cache))[dst] =
+                    canon(static_cast<const uint16_t*>(a.v_new)[src0 + e]);
             }
         }
         return;
@@ -1517,7 +1554,7 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
     int n_cu = 0;
     hipError_t e = device_cus(n_cu);
     if (e != hipSuccess) return e;
-    a.rec_rows = 32;
+    a.rec_rows = (a.Gc * a.Tc + 3) & ~3;   // records as wide as the slab (rounded up to 4 rows)
     split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT);
     if (a.btab) {
         if ((1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks
@@ -1533,19 +1570,25 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
 template <int D, int ST>
 hipError_t run_r(DecodeArgs& a, hipStream_t s) {
     const int rows = a.Gc * a.Tc;
-    if (a.k_new != nullptr) {     // fused append: one slab on the vector kernel
-        if (rows > (ST == F32 ? 8 : KVC_DECODE_MFMA_MIN_ROWS - 1) || a.Gc != a.G || a.Tc != a.T || a.r0 || a.i0)
-            return hipErrorInvalidValue;
-        return rows <= 4 ? run<D, ST, 4>(a, s) : run<D, ST, 8>(a, s);
-    }
+    // a fused append is one slab covering the whole chunk
+    if (a.k_new != nullptr && (a.Gc != a.G || a.Tc != a.T || a.r0 || a.i0)) return hipErrorInvalidValue;
     if constexpr (ST != F32) {
-        if (rows >= KVC_DECODE_MFMA_MIN_ROWS) return run_mfma<D, ST>(a, s);
+        // 16-bit caches: the matrix-core kernel for every slab (it streams the
+        // cache faster than the vector kernel even at one query row)
+        if constexpr (KVC_DECODE_MFMA_MIN_ROWS > 1) {
+            if (rows < KVC_DECODE_MFMA_MIN_ROWS) {
+                if (rows > 8) return hipErrorInvalidValue;
+                return rows <= 4 ? run<D, ST, 4>(a, s) : run<D, ST, 8>(a, s);
+            }
+        }
+        return run_mfma<D, ST>(a, s);
+    } else {
+        if (a.k_new != nullptr && rows > 8) return hipErrorInvalidValue;
+        if (rows <= 4) return run<D, ST, 4>(a, s);
+        if (rows <= 8) return run<D, ST, 8>(a, s);
+        if (rows <= 16) return run_rows<D, ST, 2>(a, s);
+        return run_rows<D, ST, 4>(a, s);
     }
-    if (rows <= 4) return run<D, ST, 4>(a, s);
-    if (rows <= 8) return run<D, ST, 8>(a, s);
-    if constexpr (ST != F32) return run_mfma<D, ST>(a, s);
-    if (rows <= 16) return run_rows<D, ST, 2>(a, s);
-    return run_rows<D, ST, 4>(a, s);
 }
 
 }  // namespace
@@ -1560,7 +1603,9 @@ hipError_t decode_run(DecodeArgs& a, hipStream_t s) {
 
 template <int D, int ST>
 int decode_batch_keys(int rows) {
-    return rows <= 4 ? Cfg<D, ST, 4>::KPB : Cfg<D, ST, 8>::KPB;
+    const int vec = rows <= 4 ? Cfg<D, ST, 4>::KPB : Cfg<D, ST, 8>::KPB;
+    if constexpr (ST == F32) return vec;
+    else return KVC_DECODE_MFMA_MIN_ROWS > 1 && vec > kBN ? vec : kBN;
 }
 
 }  // namespace kvc

@@ -134,6 +134,19 @@ struct PrefillArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Copy-out of positions [0, loc.T) of every row of one layer into dense
+// [rows][H_kv][T][D] buffers of the storage type; position p of row b reads the
+// stored value when p < loc.fill[b] and zero otherwise. loc gives the storage
+// (contiguous or paged) exactly as for an append of the same rows.
+// ---------------------------------------------------------------------------
+struct GatherArgs {
+    AppendArgs loc;
+    void* k_out;             // output base for row `row0`
+    void* v_out;
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 
 // Entries of a device block table set in stream order (n <= kMaxTableSets).

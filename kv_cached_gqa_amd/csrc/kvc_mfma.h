@@ -47,6 +47,18 @@ __device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
     }
 }
 
+// The float values of the low and high element of a packed 16-bit pair.
+template <int ST>
+__device__ __forceinline__ float low_half(uint32_t w) {
+    if constexpr (ST == BF16) return __uint_as_float(w << 16);
+    else return f16_to_f32(w & 0xFFFFu);
+}
+template <int ST>
+__device__ __forceinline__ float high_half(uint32_t w) {
+    if constexpr (ST == BF16) return __uint_as_float(w & 0xFFFF0000u);
+    else return f16_to_f32(w >> 16);
+}
+
 // acc + the two values of a packed pair, as stored: a dot product with (1, 1)
 // (exact products, float32 sum) in one instruction.
 template <int ST>

@@ -37,7 +37,7 @@ ERR_ARG, ERR_CAPACITY, ERR_STATE, ERR_DTYPE = -1, -2, -3, -4
 ERR_STORAGE, ERR_HIP, ERR_NOMEM, ERR_UNSUPPORTED = -5, -6, -7, -8
 
 EXPORTED = ("kvc_create", "kvc_destroy", "kvc_append", "kvc_append_rope", "kvc_rope_q", "kvc_attend",
-            "kvc_append_attend",
+            "kvc_append_attend", "kvc_gather",
             "kvc_seq_len", "kvc_truncate", "kvc_nbytes", "kvc_strerror",
             "kvc_create_paged", "kvc_paged_blocks", "kvc_block_table",
             "kvc_latent_create", "kvc_latent_destroy", "kvc_latent_append", "kvc_latent_seq_len",
@@ -71,6 +71,8 @@ _lib.kvc_attend.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp, _vp]
 _lib.kvc_attend.restype = ctypes.c_int
 _lib.kvc_append_attend.argtypes = [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp]
 _lib.kvc_append_attend.restype = ctypes.c_int
+_lib.kvc_gather.argtypes = [_vp, _i32, _i64, _vp, _vp, _vp]
+_lib.kvc_gather.restype = ctypes.c_int
 _lib.kvc_seq_len.argtypes = [_vp, _i32, ctypes.POINTER(_i64)]
 _lib.kvc_seq_len.restype = ctypes.c_int
 _lib.kvc_truncate.argtypes = [_vp, _vp, _i32]        # int64 lengths, by address
@@ -312,6 +314,21 @@ class KVCache:
         _check(_lib.kvc_nbytes(self._h, ctypes.byref(out)), "kvc_nbytes")
         return int(out.value)
 
+    def gather(self, layer: int, n: Optional[int] = None, stream=None):
+        """Copies [B, H_kv, n, d_h] of K and V of `layer` in position order
+        (kvc_gather; n defaults to the longest row's fill; positions at or past
+        a row's fill read as zero)."""
+        torch = _torch()
+        n = int(self.seq_len(layer).max()) if n is None else int(n)
+        shape = (self.batch, self.n_kv_heads, max(n, 1), self.d_head)
+        k = torch.empty(shape, dtype=torch_dtype(self.dtype), device=self._dev)
+        v = torch.empty_like(k)
+        if n < 1:
+            return k[:, :, :0], v[:, :, :0]
+        _check(_lib.kvc_gather(self._h, int(layer), n, k.data_ptr(), v.data_ptr(), _stream_ptr(stream, self._dev)),
+               "kvc_gather")
+        return k, v
+
     # -- helpers --
     def _check_chunk(self, t, heads: int, name: str) -> None:
         if t.dim() != 4 or t.shape[0] != self.batch or t.shape[1] != heads or t.shape[3] != self.d_head:
@@ -367,24 +384,6 @@ class PagedKVCache(KVCache):
         used, total = _i32(), _i32()
         _check(_lib.kvc_paged_blocks(self._h, ctypes.byref(used), ctypes.byref(total)), "kvc_paged_blocks")
         return int(used.value), int(total.value)
-
-    def gather(self, layer: int, n: Optional[int] = None):
-        """Copies [B, H_kv, n, d_h] of K and V of `layer` in position order
-        (n defaults to the longest row's fill; positions a row has no block
-        for read as zero)."""
-        torch = _torch()
-        n = int(self.seq_len(layer).max()) if n is None else int(n)
-        tab = torch.from_numpy(self.block_table().astype(np.int64)).to(self._dev)
-        p = torch.arange(n, device=self._dev)
-        blk = tab[:, p // self.block_size]                            # [B, n]
-        have = (blk >= 0)[:, None, :, None]
-        blk = blk.clamp(min=0)
-        out = []
-        for pool in (self.k_pool[layer], self.v_pool[layer]):      # [n_blocks, H, bs, D]
-            x = pool[blk, :, (p % self.block_size)[None, :].expand_as(blk)]   # [B, n, H, D]
-            x = x.permute(0, 2, 1, 3)
-            out.append(torch.where(have, x, torch.zeros((), dtype=x.dtype, device=x.device)).contiguous())
-        return out[0], out[1]
 
     def update(self, layer: int, k_new, v_new, stream=None):
         """Append, then return copies of everything the layer stores."""

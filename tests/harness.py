@@ -32,6 +32,7 @@ class Report:
     worst_rel: float = 0.0
     worst_tag: str = ""
     failures: list = field(default_factory=list)
+    row_errors: list = None      # (tag, layer, worst per-row relative error) per 16-bit call, when asked for
 
     def ok(self) -> bool:
         return not self.failures
@@ -68,6 +69,20 @@ def compare_out(got: np.ndarray, want: np.ndarray, dtype: str, rows=None):
     return max_abs, rel
 
 
+def worst_row_error(got: np.ndarray, want: np.ndarray, rows=None) -> float:
+    """The largest per-row relative error ||o_gpu - o_ref|| / ||o_ref|| over the
+    call's query rows (b, h, i), each row a d_h vector: the diagnostic reported
+    beside the per-call Frobenius figure for 16-bit caches."""
+    if rows is not None:
+        idx = tuple(np.array(rows).T)
+        got, want = got[idx], want[idx]
+    g = got.reshape(-1, got.shape[-1]).astype(np.float64)
+    w = want.reshape(-1, want.shape[-1])
+    num = np.linalg.norm(g - w, axis=1)
+    den = np.linalg.norm(w, axis=1)
+    return float(np.max(num / np.where(den > 0, den, 1.0))) if num.size else 0.0
+
+
 def sample_rows(rng, B, Hq, T, n):
     rows = {(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(n)}
     rows |= {(0, 0, T - 1), (B - 1, Hq - 1, 0)}
@@ -76,7 +91,7 @@ def sample_rows(rng, B, Hq, T, n):
 
 def run_script(shape, calls, *, device="cuda", q_dtype="fp32", kv_dtype="fp32", sample=None,
                compare_cache=True, check_every_call=True, verbose=True, cache=None, oracle=None,
-               out_log=None):
+               out_log=None, full_rows_at=None, row_errors=False):
     """Run `calls` on both sides. sample=n compares n random rows per attend
     (all rows when None). Returns (report, cache, oracle)."""
     from kv_cached_gqa_amd.kvc import KVCache
@@ -89,7 +104,10 @@ def run_script(shape, calls, *, device="cuda", q_dtype="fp32", kv_dtype="fp32", 
         oracle = OracleCache(shape.n_layers, shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.d_head,
                              shape.max_len, shape.dtype)
     rep = Report()
+    if row_errors:
+        rep.row_errors = []
     rng = np.random.default_rng(12345)
+    n_pass = 0
     t0 = time.time()
     for call in calls:
         rep.calls += 1
@@ -102,14 +120,19 @@ def run_script(shape, calls, *, device="cuda", q_dtype="fp32", kv_dtype="fp32", 
             qd = to_device(call.q, q_dtype, device)
             got = cache.attend(call.layer, qd).cpu().numpy()
             rows = None
-            if sample is not None:
+            if sample is not None and not (full_rows_at is not None and full_rows_at(n_pass, call)):
                 rows = sample_rows(rng, shape.batch, shape.n_q_heads, call.T, sample)
+            n_pass += 1
             want = oracle.attend(call.layer, input_values(call.q, q_dtype), rows=rows)
             mabs, rel = compare_out(got, want, shape.dtype, rows)
             rep.attends += 1
-            bad = (mabs > FP32_MAX_ABS) if shape.dtype == "fp32" else (rel > HALF_REL_FROB)
-            if not np.isfinite(got if rows is None else got[tuple(np.array(rows).T)]).all():
+            # written so that a NaN anywhere (either side, or the error itself) fails
+            bad = not (mabs <= FP32_MAX_ABS) if shape.dtype == "fp32" else not (rel <= HALF_REL_FROB)
+            sel = tuple(np.array(rows).T) if rows is not None else slice(None)
+            if not np.isfinite(got[sel]).all() or not np.isfinite(want[sel]).all():
                 bad = True
+            if rep.row_errors is not None and shape.dtype != "fp32":
+                rep.row_errors.append((call.tag, call.layer, worst_row_error(got, want, rows)))
             if mabs > rep.worst_abs:
                 rep.worst_abs = mabs
             if rel > rep.worst_rel:

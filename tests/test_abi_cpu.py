@@ -239,9 +239,17 @@ def test_paged_create_validation(kvc):
     assert create(128, 0) == kvc.ERR_ARG
     assert create(128, 8, dtype=7) == kvc.ERR_DTYPE
     assert create(128, 8, D=48) == kvc.ERR_UNSUPPORTED
-    # d_head 32 in 16 bits reads 128 keys per work-group batch: a 64-position
-    # block would let one batch span three blocks
-    assert create(64, 8, D=32) == kvc.ERR_UNSUPPORTED
+    # the decode kernels read at most 32 keys per batch at d_head 32 (16-bit
+    # caches: 32-key tiles; fp32: 4 waves x 8 keys), so 64-position blocks pass
+    # the shape checks; the host buffer then fails as a pool
+    for dt in (kvc.F32, kvc.F16, kvc.BF16):
+        assert create(64, 8, D=32, dtype=dt) == kvc.ERR_STORAGE
+    # max_len * d_head must stay below 2^31, as for a contiguous cache
+    def create_long(max_len, D):
+        c = kvc.KVCConfig(1, 1, 2, 2, D, kvc.BF16, max_len)
+        return lib.kvc_create_paged(ctypes.byref(c), 4096, 8, p, p, 1 << 40, ctypes.byref(h))
+    assert create_long((1 << 24), 128) == kvc.ERR_ARG
+    assert create_long((1 << 24) - 1, 128) == kvc.ERR_STORAGE
     assert create(128, 8, pool=None) == kvc.ERR_STORAGE
     assert create(128, 8, pool=p + 4) == kvc.ERR_STORAGE
     need_each = 2 * 8 * 2 * 128 * 128 * 2               # L * n_blocks * H_kv * block * d_head * 2 bytes
@@ -271,3 +279,45 @@ def test_append_attend_rejects_before_any_launch(kvc):
     lens = (ctypes.c_int64 * 3)()
     assert lib.kvc_seq_len(h, 0, lens) == kvc.OK and list(lens) == [0, 0, 0]
     lib.kvc_destroy(h)
+
+
+def test_host_storage_launches_nothing(kvc):
+    """A handle over storage that is not device memory keeps metadata but every
+    call that would enqueue device work returns KVC_ERR_STORAGE, after its
+    argument checks, and changes nothing (no kernel can touch host memory)."""
+    rc, h = _create(kvc, L=2, B=3, Hq=4, Hkv=2, D=32, max_len=8, dtype=2)
+    assert rc == kvc.OK
+    lib = kvc.lib()
+    p = _BASE
+    lens = (ctypes.c_int64 * 3)()
+    try:
+        assert lib.kvc_append(h, 0, p, p, 2, 1, None) == kvc.ERR_STORAGE
+        assert lib.kvc_append(h, 0, p, p, 2, 9, None) == kvc.ERR_CAPACITY     # argument checks come first
+        assert lib.kvc_append_rope(h, 0, p, p, 2, 1, ctypes.c_double(1e4), None) == kvc.ERR_STORAGE
+        assert lib.kvc_append_attend(h, 0, p, p, 2, p, 2, 1, ctypes.c_void_p(p), None) == kvc.ERR_STORAGE
+        assert lib.kvc_append_attend(h, 0, p, p, 0, p, 2, 1, ctypes.c_void_p(p), None) == kvc.ERR_STORAGE
+        assert lib.kvc_gather(h, 0, 4, p, p, None) == kvc.ERR_STORAGE
+        assert lib.kvc_seq_len(h, 0, lens) == kvc.OK and list(lens) == [0, 0, 0]
+        used = ctypes.c_uint64()
+        assert lib.kvc_nbytes(h, ctypes.byref(used)) == kvc.OK
+        n0 = (ctypes.c_int64 * 1)(0)
+        assert lib.kvc_truncate(h, n0, 1) == kvc.OK
+    finally:
+        lib.kvc_destroy(h)
+
+
+def test_gather_rejects_bad_arguments(kvc):
+    rc, h = _create(kvc, L=2, B=3, Hq=4, Hkv=2, D=32, max_len=8, dtype=2)
+    assert rc == kvc.OK
+    lib = kvc.lib()
+    p = _BASE
+    try:
+        assert lib.kvc_gather(None, 0, 4, p, p, None) == kvc.ERR_ARG
+        assert lib.kvc_gather(h, 2, 4, p, p, None) == kvc.ERR_ARG          # layer out of range
+        assert lib.kvc_gather(h, -1, 4, p, p, None) == kvc.ERR_ARG
+        assert lib.kvc_gather(h, 0, 0, p, p, None) == kvc.ERR_ARG          # n < 1
+        assert lib.kvc_gather(h, 0, 9, p, p, None) == kvc.ERR_ARG          # n > max_len
+        assert lib.kvc_gather(h, 0, 4, None, p, None) == kvc.ERR_ARG
+        assert lib.kvc_gather(h, 0, 4, p, p + 8, None) == kvc.ERR_ARG      # misaligned
+    finally:
+        lib.kvc_destroy(h)

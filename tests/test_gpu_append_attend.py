@@ -5,9 +5,8 @@ section 2.3: a pass appends its chunk, then attends over all stored positions).
 A decode step whose input has the storage dtype runs as one decode launch that
 reads the chunk from the input; the merge pass stores it. Every other call runs
 append, then attend. Both are compared bit for bit with a second cache driven
-by the two separate calls: outputs, fills and stored bits. Inputs are finite
-(a NaN input is the one documented difference: canonicalised by append, copied
-by the fused path).
+by the two separate calls: outputs, fills and stored bits, NaN inputs
+included (both paths store a 16-bit NaN as the canonical quiet NaN of its sign).
 """
 import numpy as np
 import pytest
@@ -67,7 +66,7 @@ def test_append_attend_equals_append_then_attend(paged, dtype, D):
         lens = np.array([0, 1, 127, 128, 555])
         fused_c.truncate(lens)
         ref_c.truncate(lens)
-        for step, T in enumerate((1, 1, 2, 1, 9, 1)):
+        for step, T in enumerate((1, 1, 2, 1, 9, 4, 1)):
             inp = dtype if step != 3 else ("fp32" if dtype != "fp32" else "bf16")   # one call not fusable
             for layer in range(L):
                 k, v = (rng.standard_normal((B, Hkv, T, D), dtype=np.float32) for _ in range(2))
@@ -120,3 +119,76 @@ def test_append_attend_batched_decode_full_size_and_wide_batch():
         assert np.array_equal(gpu_bits(caches[0].v_storage), gpu_bits(caches[1].v_storage))
         for c in caches:
             c.close()
+
+
+def _nan_bits(rng, dtype, shape):
+    """Standard-normal values in `dtype` with a third of them replaced by NaNs
+    of both signs and assorted payloads (signalling and quiet)."""
+    import torch
+    from kv_cached_gqa_amd.kvc import torch_dtype
+    x = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch_dtype(dtype))
+    if dtype == "fp32":
+        bits = x.view(torch.int32)
+        payload = torch.from_numpy(rng.integers(1, 1 << 23, size=shape).astype(np.int32))
+        nan = (payload | 0x7F800000) | torch.from_numpy((rng.integers(0, 2, size=shape) << 31).astype(np.int64)).to(torch.int32)
+    else:
+        bits = x.view(torch.int16)
+        exp, mant = (0x7F80, 7) if dtype == "bf16" else (0x7C00, 10)
+        payload = torch.from_numpy(rng.integers(1, 1 << mant, size=shape).astype(np.int64))
+        sign = torch.from_numpy(rng.integers(0, 2, size=shape).astype(np.int64)) << 15
+        nan = ((payload | exp | sign) & 0xFFFF).to(torch.int32)
+        nan = torch.where(nan >= 0x8000, nan - 0x10000, nan).to(torch.int16)
+    pick = torch.from_numpy(rng.random(shape) < 0.33)
+    bits = torch.where(pick, nan, bits)
+    return bits.view(x.dtype).to(DEV)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_append_attend_nan_inputs_store_the_append_bits(dtype):
+    """NaN inputs of every payload: the fused call and kvc_append store the same
+    bits, and the outputs are NaN in the same places and equal elsewhere."""
+    import torch
+    log(f"append_attend NaN inputs dtype={dtype}")
+    rng = np.random.default_rng(1300)
+    L, B, Hkv, D, max_len = 1, 3, 2, 64, 64
+    for G in (2, 8):
+        Hq = G * Hkv
+        fused_c, ref_c = _caches(False, L, B, Hq, Hkv, D, max_len, dtype)
+        for T in (1, 4, 1):
+            kd, vd = _nan_bits(rng, dtype, (B, Hkv, T, D)), _nan_bits(rng, dtype, (B, Hkv, T, D))
+            qd = to_device(rng.standard_normal((B, Hq, T, D), dtype=np.float32), dtype, DEV)
+            of = fused_c.append_attend(0, kd, vd, qd)
+            ref_c.append(0, kd, vd)
+            orf = ref_c.attend(0, qd)
+            torch.cuda.synchronize()
+            assert torch.equal(torch.isnan(of), torch.isnan(orf)), (G, T)
+            fin = ~torch.isnan(of)
+            assert torch.equal(of[fin], orf[fin]), (G, T)
+        for a_, b_ in zip(_storage(fused_c, 0), _storage(ref_c, 0)):
+            assert np.array_equal(gpu_bits(a_), gpu_bits(b_)), G
+        fused_c.close()
+        ref_c.close()
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_gather_copies_the_stored_positions(paged):
+    """kvc_gather: positions below each row's fill are the stored bits (read
+    through the block table on a paged cache), the rest are zero."""
+    import torch
+    log(f"gather paged={paged}")
+    rng = np.random.default_rng(1400)
+    L, B, Hq, Hkv, D, max_len = 2, 4, 4, 2, 128, 400
+    c, _ = _caches(paged, L, B, Hq, Hkv, D, max_len, "bf16")
+    k = torch.randn((B, Hkv, 300, D), device=DEV, dtype=torch.bfloat16)
+    v = torch.randn((B, Hkv, 300, D), device=DEV, dtype=torch.bfloat16)
+    lens = np.array([0, 1, 129, 300])
+    for layer in range(L):
+        c.append(layer, k, v)
+    c.truncate(lens)            # slots past each length keep stale values: gather must not show them
+    gk, gv = c.gather(1, 350)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        assert torch.equal(gk[b, :, :n].view(torch.int16), k[b, :, :n].view(torch.int16)), b
+        assert torch.equal(gv[b, :, :n].view(torch.int16), v[b, :, :n].view(torch.int16)), b
+        assert not gk[b, :, n:].view(torch.int16).any() and not gv[b, :, n:].view(torch.int16).any(), b
+    c.close()

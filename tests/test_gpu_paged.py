@@ -83,7 +83,9 @@ def test_paged_equals_contiguous_bit_exact(dtype, D):
     import torch
     rng = np.random.default_rng(900 + D)
     for G in ((8,) if dtype == "fp32" else (4, 8)):
-        for bs in (128, 256):
+        # 64-position blocks at d_head 32: one block per stage of the fp32
+        # row-split kernel (T=3 x G=8 = 24 rows) and two matrix-core tiles
+        for bs in ((64, 128, 256) if D == 32 else (128, 256)):
             log(f"paged vs contiguous dtype={dtype} D={D} G={G} block={bs}")
             L, B, Hkv, max_len = 2, 5, 2, 1500
             Hq = G * Hkv

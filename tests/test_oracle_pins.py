@@ -246,6 +246,31 @@ def test_attend_brute_force_tiny(shift, G, T):
     assert np.max(np.abs(got - want)) < 1e-13
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_attend_on_sampled_rows_equals_the_full_call(dtype):
+    """attend(rows=R) computes exactly the rows R of the full call (to float64
+    rounding: BLAS may group a product over fewer rows differently) and leaves
+    every other row NaN, on ragged rows, groups that share a KV head, rows of
+    one KV head only, and the first/last query of the chunk."""
+    rng = np.random.default_rng(2024)
+    B, Hkv, G, D, T = 3, 2, 4, 16, 5
+    oc = OracleCache(1, B, Hkv * G, Hkv, D, 64, dtype)
+    oc.append(0, _rand(rng, B, Hkv, 40, D), _rand(rng, B, Hkv, 40, D))
+    oc.truncate(np.array([0, 17, 33]))
+    oc.append(0, _rand(rng, B, Hkv, T, D), _rand(rng, B, Hkv, T, D))
+    q = _rand(rng, B, Hkv * G, T, D)
+    full = oc.attend(0, q)
+    assert np.isfinite(full).all()
+    for rows in ([(0, 0, 0)], [(2, 7, 4), (2, 4, 0), (1, 3, 2)], [(b, h, i) for b in range(B) for h in (1, 2)
+                                                                  for i in range(T)]):
+        got = oc.attend(0, q, rows=rows)
+        idx = tuple(np.array(rows).T)
+        assert np.max(np.abs(got[idx] - full[idx])) <= 1e-13, rows
+        mask = np.ones(got.shape[:3], bool)
+        mask[idx] = False
+        assert np.isnan(got[mask]).all()
+
+
 def test_attend_matches_torch_sdpa_with_explicit_mask():
     rng = np.random.default_rng(3)
     B, Hq, Hkv, D, s, T = 2, 6, 2, 16, 5, 3
