@@ -127,39 +127,56 @@ def gpu_bench(args, lengths):
         cache.attend(0, qs[i % n_in], out=outs[c])
 
     stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        step_two_calls(i)
-    ms_step_two = event_time(lambda i: step_two_calls(args.warmup + i), args.steps, stream)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    warm_up(step_two_calls, args.warmup)
+    ms_step_two = block_times(lambda i: step_two_calls(args.warmup + i), max(50, args.steps), stream)["median"]
+    warm_up(step, args.warmup)
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    ms_step = event_time(lambda i: step(args.warmup + i), args.steps, stream)     # the timed region: K steps
     wall = time.perf_counter() - t_wall
-    ms_step = e0.elapsed_time(e1) / args.steps
+    blocks = block_times(lambda i: step(args.warmup + args.steps + i), max(50, args.steps), stream)
 
-    # decode attention alone (split-K partial + combine), events on the same stream
+    # decode attention alone, events on the same stream
     for c in caches:
         c.truncate(lengths)
         c.append(0, ks[0], vs[0])
-    torch.cuda.synchronize()
-    reps = max(50, args.steps)
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    for i in range(reps):
-        c = i % args.instances
-        caches[c].attend(0, qs[i % n_in], out=outs[c])
-    a1.record(stream)
-    torch.cuda.synchronize()
-    us_attend = a0.elapsed_time(a1) * 1e3 / reps
+    warm_up(lambda i: caches[i % args.instances].attend(0, qs[i % n_in], out=outs[i % args.instances]), 0)
+    at = block_times(lambda i: caches[i % args.instances].attend(0, qs[i % n_in], out=outs[i % args.instances]),
+                     max(50, args.steps), stream)
     for c in caches:
         c.close()
-    return ms_step, us_attend, wall, ms_step_two
+    return ms_step, blocks, at["median"] * 1e3, wall, ms_step_two
+
+
+# Warm-up by wall time as well as by count: the GPU clocks ramp up from idle
+# over the first milliseconds of work.
+WARMUP_S = 0.3
+# Steps are timed in back-to-back blocks bracketed by two events: an event
+# recorded after every step costs ~2.5 us of GPU time per step (measured on the
+# batched-decode step: 67.5 us bracketed, 70.2 us with an event per step).
+BLOCKS = 5
+
+
+def warm_up(fn, n, seconds=WARMUP_S):
+    """n calls, then more until `seconds` of wall time have passed (the GPU
+    clocks ramp up from idle over the first few milliseconds of work, so a
+    count alone does not bring them to a steady state), then synchronise."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < n or time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def block_times(fn, reps, stream, blocks=BLOCKS) -> dict:
+    """`blocks` blocks of `reps` back-to-back calls, each block bracketed by
+    two events and synchronised: ms per call of each block, their median,
+    minimum and maximum."""
+    per = sorted(event_time(lambda i, b=b: fn(b * reps + i), reps, stream) for b in range(blocks))
+    return {"median": per[len(per) // 2], "min": per[0], "max": per[-1], "blocks": blocks, "reps": reps}
 
 
 def pmc_workload(lengths):
@@ -545,7 +562,7 @@ def main():
         prefill_bench(runs=1)
         return
     att, app = step_bytes(lengths)
-    ms_step, us_attend, wall, ms_step_two = gpu_bench(args, lengths)
+    ms_step, blocks, us_attend, wall, ms_step_two = gpu_bench(args, lengths)
     from kv_cached_gqa_amd.measure import stored_traffic
     traffic = stored_traffic()
     gbs = (att + app) / (ms_step * 1e-3) / 1e9
@@ -568,6 +585,11 @@ def main():
                    "mean_context": float(np.mean(lengths) + 1)},
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "step": "truncate to the drawn lengths, then kvc_append_attend (append and attention in one call)",
+        "timing": {"ms_per_step": f"{args.steps} back-to-back steps between two events, after {args.warmup} "
+                                  f"warm-up steps and at least {WARMUP_S:.1f} s of warm-up",
+                   "blocks_median_ms": round(blocks["median"], 5), "blocks_min_ms": round(blocks["min"], 5),
+                   "blocks_max_ms": round(blocks["max"], 5),
+                   "blocks": f"{blocks['blocks']} further blocks of {blocks['reps']} steps, each between two events"},
         "ms_per_step_append_then_attend": round(ms_step_two, 5),
         "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
         "bytes_per_step": att + app,
