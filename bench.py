@@ -274,25 +274,26 @@ def prefill_bench(block=None, runs=3):
 
 
 def tiny_decoder_bench():
-    """The tiny decoder of "kv-cache-decoding" (vocab 96, d_model 128, 4 heads,
-    4 layers; 48-token prompt, 160 greedy steps) on the GPU, attention through
-    the C ABI with an fp32 cache: wall time of the cached and of the uncached
-    generation (one warm-up run of each first) and their work counters."""
+    """The random-weight decoder of "kv-cache-decoding" (vocab 96, width 128,
+    4 heads, 4 layers; 48-token prompt, 160 greedy steps) on the GPU, attention
+    through the C ABI with an fp32 cache: wall time of the cached and of the
+    uncached generation (one warm-up run of each first) and their work
+    counters."""
     import torch
-    from kv_cached_gqa_amd.tiny_decoder import TinyDecoder, generate_no_cache, generate_with_cache
-    from kv_cached_gqa_amd.workloads import TinyDecoderSpec, tiny_decoder_prompt, tiny_decoder_weights
-    spec = TinyDecoderSpec()
-    model = TinyDecoder(tiny_decoder_weights(0, spec), spec)
-    prompt, n_new = tiny_decoder_prompt(1, 48, spec), 160
-    res = {"workload": "tiny decoder: vocab 96, d_model 128, 4 heads, 4 layers, fp32 cache; "
+    from kv_cached_gqa_amd.decoder import GpuDecoder, greedy_cached, greedy_uncached
+    from kv_cached_gqa_amd.workloads import DecoderShape, decoder_params, decoder_prompt
+    shape = DecoderShape()
+    model = GpuDecoder(decoder_params(0, shape), shape)
+    prompt, n_new = decoder_prompt(1, 48, shape), 160
+    res = {"workload": "random-weight decoder: vocab 96, width 128, 4 heads, 4 layers, fp32 cache; "
                        "48-token prompt, 160 greedy steps"}
-    for name, run in (("cached", lambda: generate_with_cache(model, prompt, n_new)),
-                      ("uncached", lambda: generate_no_cache(model, prompt, n_new))):
+    for name, run in (("cached", lambda: greedy_cached(model, prompt, n_new)),
+                      ("uncached", lambda: greedy_uncached(model, prompt, n_new))):
         out = run()
         if name == "cached":
             out[2].close()
         torch.cuda.synchronize()
-        model.scores = model.positions = 0
+        model.scores_computed = model.positions_processed = 0
         t0 = time.perf_counter()
         out = run()
         torch.cuda.synchronize()
@@ -300,7 +301,8 @@ def tiny_decoder_bench():
         if name == "cached":
             out[2].close()
         res[name] = {"ms": round(dt * 1e3, 2), "tokens_per_s": round(n_new / dt, 1),
-                     "attention_scores": model.scores, "positions": model.positions, "ids": out[0]}
+                     "attention_scores": model.scores_computed, "positions": model.positions_processed,
+                     "ids": out[0]}
     res["same_ids"] = res["cached"].pop("ids") == res["uncached"].pop("ids")
     res["speedup"] = round(res["uncached"]["ms"] / res["cached"]["ms"], 2)
     model.close()

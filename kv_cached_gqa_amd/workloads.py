@@ -199,52 +199,75 @@ def script_long_ctx_spec(seed: int = 0, n_cycles: int = 64, s0: int = 32768, dra
     return shape, calls()
 
 
-# ---- tiny decoder-only model ("kv-cache-decoding": the benchmark spec and
-#      "Correctness tests": vocab 96, d_model 128, 4 heads, 4 layers, max_len
-#      256, a 48-token prompt and 160 greedy steps) ------------------------------
+# ---- a random-weight decoder-only model ("kv-cache-decoding": the task
+#      statement (vocab 96, width 128, 4 heads, 4 layers, 256 positions, learned
+#      position rows) and "Correctness tests" (a 48-token prompt, 160 greedy
+#      steps)). Only the shapes and the random draw live here; the model's
+#      arithmetic is in its float64 twin (oracle/) and its GPU version. -------
 
 @dataclass(frozen=True)
-class TinyDecoderSpec:
+class DecoderShape:
     vocab: int = 96
-    d_model: int = 128
-    n_heads: int = 4
-    n_layers: int = 4
-    max_len: int = 256
+    width: int = 128
+    heads: int = 4
+    layers: int = 4
+    positions: int = 256
+    mlp_ratio: int = 4
 
     @property
-    def d_head(self) -> int:
-        return self.d_model // self.n_heads
+    def head_width(self) -> int:
+        return self.width // self.heads
 
 
-def tiny_decoder_weights(seed: int = 0, spec: TinyDecoderSpec = TinyDecoderSpec()) -> dict:
-    """Random float32 weights of the tiny decoder: token and position tables
-    N(0, 1); every projection [rows, cols] N(0, 1/rows) (so activations keep
-    unit scale); layer-norm gains 1 and biases 0. Draw order: tok_emb, pos_emb,
-    then per layer w_q, w_k, w_v, w_o, w_1 [d, 4d], w_2 [4d, d], then w_out."""
+@dataclass
+class BlockParams:
+    """One layer: pre-attention norm (gain, shift), the fused query/key/value
+    projection [width, 3 width] (columns: queries, keys, values, each head's
+    slice contiguous), the head-merge projection [width, width], the pre-MLP
+    norm, and the MLP's expand [width, r width] and contract [r width, width]."""
+    attn_gain: np.ndarray
+    attn_shift: np.ndarray
+    qkv: np.ndarray
+    merge: np.ndarray
+    mlp_gain: np.ndarray
+    mlp_shift: np.ndarray
+    expand: np.ndarray
+    contract: np.ndarray
+
+
+@dataclass
+class DecoderParams:
+    token_rows: np.ndarray      # [vocab, width]
+    position_rows: np.ndarray   # [positions, width]
+    blocks: list
+    out_gain: np.ndarray
+    out_shift: np.ndarray
+    readout: np.ndarray         # [width, vocab]
+
+
+def decoder_params(seed: int = 0, shape: DecoderShape = DecoderShape()) -> DecoderParams:
+    """Random float32 parameters: the readout and both tables first, then each
+    layer's matrices in the order qkv, merge, expand, contract. Tables are
+    N(0, 1); a matrix with `fan_in` input rows is N(0, 1/fan_in), which keeps
+    activations at unit scale through the stack; norm gains 1, shifts 0."""
     rng = np.random.default_rng(seed)
-    d = spec.d_model
+    w, r = shape.width, shape.mlp_ratio
 
-    def proj(rows, cols):
-        return _normal(rng, (rows, cols), float(1.0 / np.sqrt(rows)))
+    def matrix(fan_in, fan_out):
+        return _normal(rng, (fan_in, fan_out), float(1.0 / np.sqrt(fan_in)))
 
-    w = {"tok_emb": _normal(rng, (spec.vocab, d), 1.0), "pos_emb": _normal(rng, (spec.max_len, d), 1.0),
-         "layers": []}
-    for _ in range(spec.n_layers):
-        lw = {}
-        for name, shape in (("w_q", (d, d)), ("w_k", (d, d)), ("w_v", (d, d)), ("w_o", (d, d)),
-                            ("w_1", (d, 4 * d)), ("w_2", (4 * d, d))):
-            lw[name] = proj(*shape)
-        for name in ("g1", "g2"):
-            lw[name] = np.ones(d, np.float32)
-        for name in ("b1", "b2"):
-            lw[name] = np.zeros(d, np.float32)
-        w["layers"].append(lw)
-    w["g_out"] = np.ones(d, np.float32)
-    w["b_out"] = np.zeros(d, np.float32)
-    w["w_out"] = proj(d, spec.vocab)
-    return w
+    readout = matrix(w, shape.vocab)
+    tokens = _normal(rng, (shape.vocab, w), 1.0)
+    positions = _normal(rng, (shape.positions, w), 1.0)
+    ones, zeros = np.ones(w, np.float32), np.zeros(w, np.float32)
+    blocks = []
+    for _ in range(shape.layers):
+        qkv, merge = matrix(w, 3 * w), matrix(w, w)
+        expand, contract = matrix(w, r * w), matrix(r * w, w)
+        blocks.append(BlockParams(ones.copy(), zeros.copy(), qkv, merge, ones.copy(), zeros.copy(), expand, contract))
+    return DecoderParams(tokens, positions, blocks, ones.copy(), zeros.copy(), readout)
 
 
-def tiny_decoder_prompt(seed: int = 1, length: int = 48, spec: TinyDecoderSpec = TinyDecoderSpec()) -> list:
+def decoder_prompt(seed: int = 1, length: int = 48, shape: DecoderShape = DecoderShape()) -> list:
     """A prompt of `length` token ids drawn uniformly from the vocabulary."""
-    return [int(x) for x in np.random.default_rng(seed).integers(0, spec.vocab, size=length)]
+    return [int(x) for x in np.random.default_rng(seed).integers(0, shape.vocab, size=length)]

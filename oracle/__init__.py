@@ -12,7 +12,7 @@ from .kvc_oracle import (  # noqa: F401
     bf16_bits_to_f32,
     causal_mask,
     f16_bits_to_f32,
-    kv_bytes,
+    storage_bytes,
     round_bf16_bits,
     round_f16_bits,
     round_to_storage,

@@ -174,12 +174,13 @@ def causal_mask(T: int, n_keys: int, q_offset: int) -> np.ndarray:
     return j <= q_offset + i
 
 
-def kv_bytes(layers: int, heads: int, head_dim: int, seq_len: int,
-             batch: int = 1, bytes_per_value: int = 2) -> int:
-    """2 * layers * batch * heads * seq_len * head_dim * bytes: K and V of every
-    layer and KV head ("kv-cache-decoding", "What is cached, what is not, and
-    what it costs"; "Heads, GQA and K/V cache", "Memory and the window limit")."""
-    return 2 * layers * batch * heads * seq_len * head_dim * bytes_per_value
+def storage_bytes(n_layers: int, n_rows: int, n_kv_heads: int, n_positions: int, d_head: int,
+                  itemsize: int) -> int:
+    """Bytes of a cache's K and V: two tensors of n_layers x n_rows x n_kv_heads
+    x n_positions x d_head values ("kv-cache-decoding", "What is cached, what is
+    not, and what it costs"; "Heads, GQA and K/V cache", "Memory and the window
+    limit"; with grouped-query attention only the KV heads count)."""
+    return 2 * n_layers * n_rows * n_kv_heads * n_positions * d_head * itemsize
 
 
 # ---------------------------------------------------------------------------
@@ -248,7 +249,7 @@ class OracleCache:
         self.fill[:, :] = n[None, :]
 
     def nbytes(self) -> int:
-        return kv_bytes(self.L, self.Hkv, self.D, self.max_len, self.B, _ITEMSIZE[self.dtype])
+        return storage_bytes(self.L, self.B, self.Hkv, self.max_len, self.D, _ITEMSIZE[self.dtype])
 
     # -- append ("KV cache, ...", sections 2.5 and 4; "kv-cache-decoding", step 5)
 

@@ -83,15 +83,26 @@ def worst_row_error(got: np.ndarray, want: np.ndarray, rows=None) -> float:
     return float(np.max(num / np.where(den > 0, den, 1.0))) if num.size else 0.0
 
 
-def sample_rows(rng, B, Hq, T, n):
-    rows = {(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(n)}
+def sample_rows(rng, B, Hq, T, n, groups=None, G=1):
+    """About n query rows (b, h, i), always including (0, 0, T-1) and (B-1,
+    Hq-1, 0). With groups = k, the rows are drawn inside k random (row, KV
+    head) units, query heads h of group g = h // G, so the oracle reads the
+    keys of only a few units per call."""
+    if groups is None:
+        rows = {(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(n)}
+    else:
+        units = [(int(rng.integers(B)), int(rng.integers(Hq // G))) for _ in range(groups)]
+        rows = set()
+        for _ in range(n):
+            b, g = units[int(rng.integers(len(units)))]
+            rows.add((b, g * G + int(rng.integers(G)), int(rng.integers(T))))
     rows |= {(0, 0, T - 1), (B - 1, Hq - 1, 0)}
     return sorted(rows)
 
 
 def run_script(shape, calls, *, device="cuda", q_dtype="fp32", kv_dtype="fp32", sample=None,
                compare_cache=True, check_every_call=True, verbose=True, cache=None, oracle=None,
-               out_log=None, full_rows_at=None, row_errors=False):
+               out_log=None, full_rows_at=None, row_errors=False, sample_groups=None):
     """Run `calls` on both sides. sample=n compares n random rows per attend
     (all rows when None). Returns (report, cache, oracle)."""
     from kv_cached_gqa_amd.kvc import KVCache
@@ -121,7 +132,8 @@ def run_script(shape, calls, *, device="cuda", q_dtype="fp32", kv_dtype="fp32", 
             got = cache.attend(call.layer, qd).cpu().numpy()
             rows = None
             if sample is not None and not (full_rows_at is not None and full_rows_at(n_pass, call)):
-                rows = sample_rows(rng, shape.batch, shape.n_q_heads, call.T, sample)
+                rows = sample_rows(rng, shape.batch, shape.n_q_heads, call.T, sample, sample_groups,
+                                   shape.n_q_heads // shape.n_kv_heads)
             n_pass += 1
             want = oracle.attend(call.layer, input_values(call.q, q_dtype), rows=rows)
             mabs, rel = compare_out(got, want, shape.dtype, rows)

@@ -167,15 +167,29 @@ def test_chunked_prefill_bf16_reduced():
     assert rep.ok(), rep.failures[:5]
 
 
+@pytest.mark.timeout(1200)
 def test_long_context_speculative_cycles():
-    """B=8, H_q=64, H_kv=8, d_h=128, bf16, s0=32768: three draft/accept/reset cycles."""
-    log("long context bf16 s0=32768: 3 speculative cycles, sampled rows")
-    shape, calls = W.script_long_ctx_spec(n_cycles=3)
-    rep, cache, orc = run_script(shape, calls, sample=24, compare_cache=False)
-    log(f"  attends={rep.attends} worst rel={rep.worst_rel:.3e}")
+    """B=8, H_q=64, H_kv=8, d_h=128, bf16, s0=32768: all 64 draft / accept /
+    reset cycles of the configuration. Every row of every call of the first
+    and the last cycle, 24 sampled rows (in 4 (row, KV head) units) of every
+    other call, fills after every call, and the whole cache bit for bit at the
+    end (every slot a cycle wrote past s0 included)."""
+    log("long context bf16 s0=32768: 64 speculative cycles")
+    shape, calls = W.script_long_ctx_spec(n_cycles=64)
+    def first_or_last_cycle(tag):
+        return tag in ("draft0", "draft63") or tag.startswith(("decode0.", "decode63."))
+
+    full = lambda n, call: first_or_last_cycle(call.tag)  # noqa: E731
+    per_call = []
+    rep, cache, orc = run_script(shape, calls, sample=24, sample_groups=4, full_rows_at=full, compare_cache=True,
+                                 out_log=per_call, row_errors=True)
+    fulls = [c for c in per_call if first_or_last_cycle(c[0])]
+    log(f"  attends={rep.attends} (all rows on {len(fulls)}) worst rel={rep.worst_rel:.3e} ({rep.worst_tag}); "
+        f"worst per-row rel={max(e for _, _, e in rep.row_errors):.3e}")
     assert rep.ok(), rep.failures[:5]
+    assert rep.attends == sum(1 for _ in W.script_long_ctx_spec(n_cycles=64)[1] if _.op == "pass")
     assert cache.seq_len().tolist() == [32768] * 8
-    assert cache_bits_equal(cache, orc, layer_slice=(slice(None), slice(None), slice(None), slice(32760, 32776)))
+    assert len(fulls) >= 4
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
@@ -347,9 +361,13 @@ def test_prefill_chunks_matrix_core_path(dtype, D):
             assert rel <= HALF_REL_FROB, (Hq, Hkv, T, rel)
 
 
+@pytest.mark.timeout(900)
 def test_chunked_prefill_bf16_full_size():
     """All 32 chunks of T=512 (offsets 0 .. 15872) at B=4, H_q=32, H_kv=8, d_h=128:
-    sampled query rows of two (row, head) pairs per chunk against the oracle."""
+    every query row of chunks 0, 15 and 31, sampled rows of two (row, head)
+    pairs per other chunk; the per-call Frobenius bound and the worst per-row
+    error reported."""
+    from tests.harness import worst_row_error
     log("chunked prefill bf16 full size: 32 chunks of 512")
     shape, calls = W.script_chunked_prefill()
     from kv_cached_gqa_amd.kvc import KVCache
@@ -358,20 +376,27 @@ def test_chunked_prefill_bf16_full_size():
     orc = OracleCache(shape.n_layers, shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.d_head,
                       shape.max_len, shape.dtype)
     rng = np.random.default_rng(7)
-    worst = 0.0
+    worst, worst_row = 0.0, 0.0
     for n, call in enumerate(calls):
         cache.append(0, to_device(call.k, "fp32", DEV), to_device(call.v, "fp32", DEV))
         orc.append(0, call.k, call.v)
         got = cache.attend(0, to_device(call.q, "bf16", DEV)).cpu().numpy()
-        pairs = [(int(rng.integers(shape.batch)), int(rng.integers(shape.n_q_heads))) for _ in range(2)]
-        rows = sorted({(b, h, int(i)) for (b, h) in pairs for i in rng.integers(0, call.T, 24)} |
-                      {(b, h, call.T - 1) for (b, h) in pairs})
+        if n in (0, 15, 31):
+            rows = None
+        else:
+            pairs = [(int(rng.integers(shape.batch)), int(rng.integers(shape.n_q_heads))) for _ in range(2)]
+            rows = sorted({(b, h, int(i)) for (b, h) in pairs for i in rng.integers(0, call.T, 24)} |
+                          {(b, h, call.T - 1) for (b, h) in pairs})
         want = orc.attend(0, input_values(call.q, "bf16"), rows=rows)
         mabs, rel = compare_out(got, want, "bf16", rows)
-        worst = max(worst, rel)
+        row_err = worst_row_error(got, want, rows)
+        worst, worst_row = max(worst, rel), max(worst_row, row_err)
+        if rows is None:
+            log(f"  chunk {n}: all rows, rel {rel:.3e}, worst row {row_err:.3e}")
         assert rel <= HALF_REL_FROB, (n, rel)
-        assert np.isfinite(got).all()
-    log(f"  worst rel {worst:.3e}")
+        sel = tuple(np.array(rows).T) if rows is not None else slice(None)
+        assert np.isfinite(got[sel]).all() and np.isfinite(want[sel]).all()
+    log(f"  worst rel {worst:.3e}, worst per-row rel {worst_row:.3e}")
 
 
 def _ulp_gap(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:

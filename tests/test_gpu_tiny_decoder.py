@@ -1,5 +1,5 @@
-"""The tiny decoder on the GPU (attention through the C ABI, fp32 cache)
-against the float64 oracle model of the same weights ("kv-cache-decoding",
+"""The decoder model on the GPU (attention through the C ABI, fp32 cache)
+against the float64 reference model of the same parameters ("kv-cache-decoding",
 "Correctness tests"), with the oracle's token sequence fed to both so every
 step compares the same inputs.
 
@@ -14,13 +14,13 @@ differently chunked prefills: measured 2.4e-6, bound 2e-5.
 import numpy as np
 import pytest
 
-from kv_cached_gqa_amd.workloads import TinyDecoderSpec, tiny_decoder_prompt, tiny_decoder_weights
-from oracle.tiny_decoder import OracleTinyDecoder, generate_with_cache as oracle_generate_with_cache
+from kv_cached_gqa_amd.workloads import DecoderShape, decoder_params, decoder_prompt
+from oracle.reference_decoder import ReferenceDecoder, greedy_cached as reference_greedy_cached
 from tests.harness import log
 
 pytestmark = pytest.mark.gpu
 
-SPEC = TinyDecoderSpec()
+SHAPE = DecoderShape()
 P, N = 48, 160
 TOL_LOGITS = 1e-4
 TOL_CACHE = 2e-5
@@ -38,10 +38,10 @@ def _gpu():
 
 @pytest.fixture(scope="module")
 def reference():
-    weights = tiny_decoder_weights(0, SPEC)
-    prompt = tiny_decoder_prompt(1, P, SPEC)
-    ids, logits, _ = oracle_generate_with_cache(OracleTinyDecoder(weights, SPEC), prompt, N)
-    return weights, prompt, ids, logits
+    params = decoder_params(0, SHAPE)
+    prompt = decoder_prompt(1, P, SHAPE)
+    ids, logits, _ = reference_greedy_cached(ReferenceDecoder(params, SHAPE), prompt, N)
+    return params, prompt, ids, logits
 
 
 def _forced(model, ids, cached: bool):
@@ -53,32 +53,32 @@ def _forced(model, ids, cached: bool):
     for i in range(N):
         if cached:
             new = ids[:P] if i == 0 else [ids[P + i - 1]]
-            out.append(model.forward(new, cache)[-1])
+            out.append(model.step(new, cache)[-1])
         else:
-            out.append(model.forward(ids[:P + i])[-1])
+            out.append(model.step(ids[:P + i])[-1])
     torch.cuda.synchronize()
     return torch.stack(out).cpu().numpy(), cache
 
 
 def test_tiny_decoder_through_the_c_abi(reference):
-    from kv_cached_gqa_amd.tiny_decoder import TinyDecoder, generate_with_cache
-    weights, prompt, ids_ref, l_ref = reference
+    from kv_cached_gqa_amd.decoder import GpuDecoder, greedy_cached
+    params, prompt, ids_ref, l_ref = reference
     log("tiny decoder: 48-token prompt, 160 steps, cached and uncached, against the float64 model")
-    gm = TinyDecoder(weights, SPEC)
+    gm = GpuDecoder(params, SHAPE)
     l_c, cache = _forced(gm, ids_ref, cached=True)
-    assert gm.scores == 362496 and gm.positions == P + N - 1
+    assert gm.scores_computed == 362496 and gm.positions_processed == P + N - 1
     assert cache.seq_len().tolist() == [P + N - 1]
     err_ref = float(np.abs(l_c - l_ref).max())
-    gm.scores = gm.positions = 0
+    gm.scores_computed = gm.positions_processed = 0
     l_n, _ = _forced(gm, ids_ref, cached=False)
-    assert gm.scores == 47077120 and gm.positions == sum(P + i for i in range(N))
+    assert gm.scores_computed == 47077120 and gm.positions_processed == sum(P + i for i in range(N))
     err_self = float(np.abs(l_c - l_n).max())
     log(f"  max |logit diff| vs float64 {err_ref:.2e}, cached vs uncached {err_self:.2e}, "
         f"logit spread {l_ref.max() - l_ref.min():.2f}")
     assert err_ref <= TOL_LOGITS and err_self <= TOL_LOGITS
     # free-running greedy decoding picks the oracle's token wherever its top-2
     # margin exceeds twice the tolerance (the page's margin-gated equality)
-    ids_g, l_g, c2 = generate_with_cache(gm, prompt, N)
+    ids_g, l_g, c2 = greedy_cached(gm, prompt, N)
     top2 = np.sort(l_ref, axis=1)[:, -2:]
     sure = (top2[:, 1] - top2[:, 0]) > 2 * TOL_LOGITS
     first_unsure = int(np.argmin(sure)) if not sure.all() else N
@@ -92,15 +92,15 @@ def test_tiny_decoder_prefill_in_chunks(reference):
     """One pass over the prompt, 30 + 18, and 48 single-token passes: caches and
     last-token logits agree (to fp32 summation order)."""
     import torch
-    from kv_cached_gqa_amd.tiny_decoder import TinyDecoder
-    weights, prompt, _, _ = reference
-    gm = TinyDecoder(weights, SPEC)
+    from kv_cached_gqa_amd.decoder import GpuDecoder
+    params, prompt, _, _ = reference
+    gm = GpuDecoder(params, SHAPE)
     res = []
     for chunks in ([P], [30, 18], [1] * P):
         cache = gm.new_cache()
         at = 0
         for c in chunks:
-            last = gm.forward(prompt[at:at + c], cache)[-1]
+            last = gm.step(prompt[at:at + c], cache)[-1]
             at += c
         torch.cuda.synchronize()
         res.append((cache.k_storage.float().cpu().numpy(), cache.v_storage.float().cpu().numpy(),

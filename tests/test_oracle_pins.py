@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from oracle import (OracleCache, OracleCapacityError, OracleError, bf16_bits_to_f32, causal_mask,
-                    f16_bits_to_f32, kv_bytes, round_bf16_bits, round_f16_bits, round_to_storage)
+                    f16_bits_to_f32, storage_bytes, round_bf16_bits, round_f16_bits, round_to_storage)
 from kv_cached_gqa_amd import work
 
 
@@ -58,13 +58,13 @@ def test_memory_figures(golden_dir):
                      c0["positions"], "fp32")
     assert oc.nbytes() == c0["bytes"]["fp32"]
     assert oc.nbytes() // 4 == c0["elements"]
-    assert kv_bytes(c0["layers"], c0["kv_heads"], c0["head_dim"], c0["positions"], 1, 8) == c0["bytes"]["fp64"]
-    b = kv_bytes(c1["layers"], c1["kv_heads"], c1["head_dim"], c1["positions"], 1, 4)
+    assert storage_bytes(c0["layers"], 1, c0["kv_heads"], c0["positions"], c0["head_dim"], 8) == c0["bytes"]["fp64"]
+    b = storage_bytes(c1["layers"], 1, c1["kv_heads"], c1["positions"], c1["head_dim"], 4)
     assert int(b // 10 ** 6) == c1["bytes_fp32_megabytes_floor"]
     oc16 = OracleCache(c1["layers"], 1, 9, c1["kv_heads"], c1["head_dim"], c1["positions"], "fp16")
     assert 2 * oc16.nbytes() == b                     # "a float16 cache halves it"
-    assert kv_bytes(c2["layers"], c2["kv_heads"], c2["head_dim"], 1, 1, 8) == c2["bytes"]
-    per_tok = kv_bytes(c3["layers"], c3["kv_heads"], c3["head_dim"], 1, 1, 2)
+    assert storage_bytes(c2["layers"], 1, c2["kv_heads"], 1, c2["head_dim"], 8) == c2["bytes"]
+    per_tok = storage_bytes(c3["layers"], 1, c3["kv_heads"], 1, c3["head_dim"], 2)
     assert per_tok == c3["bytes"]
     assert round(per_tok * 4000 / 1e9, 1) == c3["positions_4000_gigabytes_rounded"]
     oc4 = OracleCache(1, 1, 1, 1, 2, 4, "fp32")
