@@ -31,6 +31,10 @@
 
 #include "kvc_mfma.h"
 
+#ifndef KVC_PREFILL_PSPLIT
+#define KVC_PREFILL_PSPLIT 0   // 1: P as a 16-bit hi + lo pair (two products with V)
+#endif
+
 namespace kvc {
 namespace {
 
@@ -264,6 +268,7 @@ void prefill_attn(PrefillArgs a) {
         // scores -> probabilities, in the C layout: value jj is key
         // j0 + (jj / 4) * 8 + hl * 4 + jj % 4 of this lane's column
         u32x4 pb[kNT][2];
+        u32x4 pl[kNT][2];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
             float sv_[16];
@@ -294,16 +299,27 @@ void prefill_attn(PrefillArgs a) {
                 }
             }
             const float nmc = m[nt] == -INFINITY ? 0.f : -m[nt] * c;
-            uint32_t w[8];
+            uint32_t w[8], wl[8];
             float ls[2] = {0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                w[e] = pack_p<ST>(fexp2(fmaf(sv_[2 * e], c, nmc)), fexp2(fmaf(sv_[2 * e + 1], c, nmc)));
+                const float p0 = fexp2(fmaf(sv_[2 * e], c, nmc)), p1 = fexp2(fmaf(sv_[2 * e + 1], c, nmc));
+                w[e] = pack_p<ST>(p0, p1);
                 ls[e & 1] = add_pair<ST>(w[e], ls[e & 1]);
+                if constexpr (KVC_PREFILL_PSPLIT) {
+                    // the rounding residual of each probability, rounded again: P = hi + lo
+                    wl[e] = pack_p<ST>(p0 - low_half<ST>(w[e]), p1 - high_half<ST>(w[e]));
+                    ls[e & 1] = add_pair<ST>(wl[e], ls[e & 1]);
+                }
             }
             lsum[nt] += ls[0] + ls[1];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) pb[nt][kk] = u32x4{w[kk * 4 + 0], w[kk * 4 + 1], w[kk * 4 + 2], w[kk * 4 + 3]};
+            if constexpr (KVC_PREFILL_PSPLIT) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    pl[nt][kk] = u32x4{wl[kk * 4 + 0], wl[kk * 4 + 1], wl[kk * 4 + 2], wl[kk * 4 + 3]};
+            }
         }
 
         // O^T += V^T P^T: for key step kk, A element e of the lane is key
@@ -314,7 +330,10 @@ void prefill_attn(PrefillArgs a) {
             for (int kk = 0; kk < 2; ++kk) {
                 const u32x4 va = {vt[dt][kk][0][0], vt[dt][kk][0][1], vt[dt][kk][1][0], vt[dt][kk][1][1]};
 #pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) o[nt][dt] = mfma32<ST>(va, pb[nt][kk], o[nt][dt]);
+                for (int nt = 0; nt < kNT; ++nt) {
+                    o[nt][dt] = mfma32<ST>(va, pb[nt][kk], o[nt][dt]);
+                    if constexpr (KVC_PREFILL_PSPLIT) o[nt][dt] = mfma32<ST>(va, pl[nt][kk], o[nt][dt]);
+                }
             }
     };
     for (int t0 = 0; t0 < n_tiles; t0 += kNB) {
