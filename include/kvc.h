@@ -45,7 +45,8 @@ typedef enum kvc_status {
     KVC_ERR_STORAGE = -5,     /* storage null, too small or not 16-byte aligned */
     KVC_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
     KVC_ERR_NOMEM = -7,       /* host or device allocation failed */
-    KVC_ERR_UNSUPPORTED = -8  /* a shape outside what the kernels handle (d_head not 32, 64 or 128) */
+    KVC_ERR_UNSUPPORTED = -8, /* a shape outside what the kernels handle (d_head not 32, 64 or 128) */
+    KVC_ERR_SCRATCH = -9      /* kvc_attend_static: the call needs more scratch than its static array */
 } kvc_status;
 
 /* Shape of a cache. n_q_heads must be a multiple of n_kv_heads (G = n_q_heads /
@@ -149,6 +150,22 @@ int kvc_rope_q(const kvc_cache* cache, int32_t layer, void* q, int32_t q_dtype, 
  * not device memory), KVC_ERR_HIP. Allocates nothing. */
 int kvc_attend(kvc_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
                int32_t T, float* out, void* stream);
+
+/* kvc_attend without any allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid it): the same arguments, semantics, kernels and results, except that
+ * the split-K partial records live in a file-scope device array of the library
+ * (16 MiB, kStaticScratchFloats floats, one per device, held until the process
+ * ends) instead of the handle's workspace. The array's device address is looked
+ * up once per device at the first call on it (hipGetSymbolAddress; no
+ * allocation). Every call on one device shares that device's array: calls that
+ * overlap on a device (several streams, threads or handles) race and must be
+ * ordered by the caller. The call allocates nothing, host or device.
+ * Errors: as kvc_attend; KVC_ERR_SCRATCH when min(batch, 256) * n_kv_heads
+ * units of 32-row records (d_head + 2 floats a row), plus one, exceed the
+ * array; nothing is enqueued then. */
+int kvc_attend_static(kvc_cache* cache, int32_t layer, const void* q, int32_t q_dtype, int32_t T, float* out,
+                      void* stream);
 
 /* Append a chunk, then attend to everything the layer holds, in one call: the
  * same state change and bit-identical results as kvc_append(k_new, v_new,

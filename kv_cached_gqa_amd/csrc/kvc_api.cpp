@@ -146,6 +146,7 @@ const char* kvc_strerror(int status) {
         case KVC_ERR_HIP: return "HIP runtime error";
         case KVC_ERR_NOMEM: return "out of memory";
         case KVC_ERR_UNSUPPORTED: return "shape not supported by the kernels";
+        case KVC_ERR_SCRATCH: return "call needs more split-K scratch than the static array holds";
         default: return "unknown status";
     }
 }
@@ -475,8 +476,25 @@ namespace {
 // each row's fill taken as fill + pending. k_new, v_new non-null: a fused
 // append whose chunk (pending = T positions, not yet counted in the fills) the
 // decode kernel reads from the input and its merge pass stores (one slab).
+struct Workspace {
+    float* o;
+    float* ml;
+    int64_t rows_cap;    // records x rows the two regions hold
+};
+
+Workspace handle_workspace(const kvc_cache* c) {
+    return {c->ws_o, c->ws_ml, c->ws_segments * kWsRecordRows};
+}
+
+// Rows of split-K records a call's largest launch may need: one slab of up to
+// kMaxDecodeRows rows per (row, KV head) unit of a launch, plus one record.
+int64_t workspace_rows_needed(const kvc_config& cf) {
+    return static_cast<int64_t>(kMaxDecodeRows) * (static_cast<int64_t>(std::min(cf.batch, kMaxRowsPerLaunch)) *
+                                                   cf.n_kv_heads + 1);
+}
+
 int attend_impl(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int32_t T, float* out, void* stream,
-                const void* k_new, const void* v_new, int64_t pending) {
+                const void* k_new, const void* v_new, int64_t pending, const Workspace& ws) {
     const kvc_config& cf = c->cfg;
     const int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
 
@@ -550,9 +568,9 @@ int attend_impl(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
                 a.v_cache = c->v_store;
                 a.q = q;
                 a.out = out;
-                a.ws_o = c->ws_o;
-                a.ws_ml = c->ws_ml;
-                a.ws_rows_cap = c->ws_segments * kWsRecordRows;
+                a.ws_o = ws.o;
+                a.ws_ml = ws.ml;
+                a.ws_rows_cap = ws.rows_cap;
                 a.layer_off = (static_cast<int64_t>(layer) * cf.batch + row0) * row_stride;
                 a.row_stride = row_stride;
                 a.head_stride = head_stride;
@@ -620,7 +638,28 @@ int kvc_attend(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int3
     for (int b = 0; b < cf.batch; ++b)
         if (f[b] < T) return KVC_ERR_STATE;
     if (!on_device(c)) return KVC_ERR_STORAGE;
-    return attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr, 0);
+    return attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr, 0, handle_workspace(c));
+}
+
+int kvc_attend_static(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int32_t T, float* out,
+                      void* stream) {
+    if (!c || !q || !out) return KVC_ERR_ARG;
+    const kvc_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || T < 1) return KVC_ERR_ARG;
+    if (!dtype_ok(q_dtype)) return KVC_ERR_DTYPE;
+    if (!aligned16(q) || !aligned16(out)) return KVC_ERR_ARG;
+    const int64_t* f = &c->fill[static_cast<size_t>(layer) * cf.batch];
+    for (int b = 0; b < cf.batch; ++b)
+        if (f[b] < T) return KVC_ERR_STATE;
+    if (!on_device(c)) return KVC_ERR_STORAGE;
+    float* base = nullptr;
+    int64_t n_floats = 0;
+    if (kvc::static_scratch(c->device, &base, &n_floats) != hipSuccess) return KVC_ERR_HIP;
+    // records of d_head outputs plus a (max, sum) pair per row
+    const int64_t rows_cap = n_floats / (cf.d_head + 2);
+    if (rows_cap < workspace_rows_needed(cf)) return KVC_ERR_SCRATCH;
+    const Workspace ws{base, base + rows_cap * cf.d_head, rows_cap};
+    return attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr, 0, ws);
 }
 
 int kvc_append_attend(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new, int32_t in_dtype,
@@ -637,7 +676,7 @@ int kvc_append_attend(kvc_cache* c, int32_t layer, const void* k_new, const void
     if (!fusable(c, in_dtype, T)) {
         const int rc = append_impl(c, layer, k_new, v_new, in_dtype, T, 0.0, stream);
         if (rc != KVC_OK) return rc;
-        const int ra = attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr, 0);
+        const int ra = attend_impl(c, layer, q, q_dtype, T, out, stream, nullptr, nullptr, 0, handle_workspace(c));
         if (ra != KVC_OK) {
             // undo the append: fills back, blocks it took given back (its slots
             // now lie past the fills)
@@ -651,7 +690,7 @@ int kvc_append_attend(kvc_cache* c, int32_t layer, const void* k_new, const void
         const int rg = grow_blocks(c, f, T, s);
         if (rg != KVC_OK) return rg;
     }
-    const int ra = attend_impl(c, layer, q, q_dtype, T, out, stream, k_new, v_new, T);
+    const int ra = attend_impl(c, layer, q, q_dtype, T, out, stream, k_new, v_new, T, handle_workspace(c));
     if (ra != KVC_OK) {
         release_unused(c);
         return ra;

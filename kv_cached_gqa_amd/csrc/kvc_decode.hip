@@ -2,9 +2,44 @@
 // kernels (kvc_decode_impl.h) for a cache's head dimension and storage type.
 // The instantiations live in kvc_decode_d<D>_<type>.hip, one translation unit
 // each, so that they compile in parallel.
+#include <mutex>
+
 #include "kvc_kernels.h"
 
 namespace kvc {
+
+namespace {
+
+// The allocation-free attention call's split-K scratch: partial records and
+// their (max, sum) pairs, carved by the caller. Every call on a device shares
+// this device's copy (calls that overlap on one device race); it needs no
+// clearing, since a launch writes every record it reads.
+static __device__ __align__(256) float scratch[kStaticScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float* scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t static_scratch(int device, float** ptr, int64_t* n_floats) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[device] == nullptr) {
+        int prev = 0;
+        hipError_t e = hipGetDevice(&prev);
+        if (e != hipSuccess) return e;
+        if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (prev != device) (void)hipSetDevice(prev);
+        if (e != hipSuccess) return e;
+        scratch_ptr[device] = static_cast<float*>(p);
+    }
+    *ptr = scratch_ptr[device];
+    *n_floats = kStaticScratchFloats;
+    return hipSuccess;
+}
 
 int decode_vector_batch_keys(int D, int st_dtype, int rows) {
     auto pick = [&](auto d_c) -> int {

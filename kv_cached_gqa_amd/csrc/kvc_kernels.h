@@ -171,6 +171,14 @@ __host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t 
 
 // Fills in the work split (n_blocks, slice sizes) from the device's resident capacity.
 hipError_t launch_decode(DecodeArgs& a, hipStream_t stream);
+// Scratch of the allocation-free attention call: a file-scope device array of
+// kStaticScratchFloats floats (16 MiB) in the decode dispatcher's source, one
+// copy per device. static_scratch gives its device address on `device`, taken
+// once per device with hipGetSymbolAddress (the array's host-side name is not a
+// device address and must never reach a kernel).
+constexpr int64_t kStaticScratchFloats = int64_t(4) << 20;
+hipError_t static_scratch(int device, float** ptr, int64_t* n_floats);
+
 // The decode kernels of one (head dimension, storage type), and their key batch
 // for a slab of `rows` query rows (one instantiation per translation unit).
 template <int D, int ST>

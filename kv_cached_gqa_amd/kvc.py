@@ -34,10 +34,10 @@ ITEMSIZE = {"fp32": 4, "fp16": 2, "bf16": 2}
 
 OK = 0
 ERR_ARG, ERR_CAPACITY, ERR_STATE, ERR_DTYPE = -1, -2, -3, -4
-ERR_STORAGE, ERR_HIP, ERR_NOMEM, ERR_UNSUPPORTED = -5, -6, -7, -8
+ERR_STORAGE, ERR_HIP, ERR_NOMEM, ERR_UNSUPPORTED, ERR_SCRATCH = -5, -6, -7, -8, -9
 
 EXPORTED = ("kvc_create", "kvc_destroy", "kvc_append", "kvc_append_rope", "kvc_rope_q", "kvc_attend",
-            "kvc_append_attend", "kvc_gather",
+            "kvc_append_attend", "kvc_gather", "kvc_attend_static",
             "kvc_seq_len", "kvc_truncate", "kvc_nbytes", "kvc_strerror",
             "kvc_create_paged", "kvc_paged_blocks", "kvc_block_table",
             "kvc_latent_create", "kvc_latent_destroy", "kvc_latent_append", "kvc_latent_seq_len",
@@ -71,6 +71,8 @@ _lib.kvc_attend.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp, _vp]
 _lib.kvc_attend.restype = ctypes.c_int
 _lib.kvc_append_attend.argtypes = [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp]
 _lib.kvc_append_attend.restype = ctypes.c_int
+_lib.kvc_attend_static.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp, _vp]
+_lib.kvc_attend_static.restype = ctypes.c_int
 _lib.kvc_gather.argtypes = [_vp, _i32, _i64, _vp, _vp, _vp]
 _lib.kvc_gather.restype = ctypes.c_int
 _lib.kvc_seq_len.argtypes = [_vp, _i32, ctypes.POINTER(_i64)]
@@ -313,6 +315,18 @@ class KVCache:
         out = _u64()
         _check(_lib.kvc_nbytes(self._h, ctypes.byref(out)), "kvc_nbytes")
         return int(out.value)
+
+    def attend_static(self, layer: int, q, out, stream=None):
+        """attend() through kvc_attend_static: split-K scratch from the library's
+        static device array, nothing allocated (out must be given)."""
+        torch = _torch()
+        self._check_chunk(q, self.n_q_heads, "q")
+        if out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
+            raise KVCArgumentError(ERR_ARG, "out must be contiguous float32 shaped like q")
+        _check(_lib.kvc_attend_static(self._h, int(layer), q.data_ptr(), DTYPE_CODES[dtype_name(q)],
+                                      int(q.shape[2]), out.data_ptr(), _stream_ptr(stream, self._dev)),
+               "kvc_attend_static")
+        return out
 
     def gather(self, layer: int, n: Optional[int] = None, stream=None):
         """Copies [B, H_kv, n, d_h] of K and V of `layer` in position order
