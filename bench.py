@@ -25,7 +25,7 @@ wall time of the cached and the uncached generation and their work counters;
 the rotary append and query rotation; and latent-cache appends.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-    python bench.py --pmc-workload      # calibration copy + attention calls, for rocprofv3 --pmc
+    python bench.py --pmc-workload c3_attend|c3_step|c5_t1|c5_t4   # for rocprofv3 --pmc
 """
 from __future__ import annotations
 
@@ -50,6 +50,9 @@ WORKLOAD = ("batched decode, one Llama-3-8B-shaped layer: B=32, H_q=32, H_kv=8, 
             "bf16 cache max_len 4096, lengths U{1024..4095} seed 0, T=1")
 
 
+PMC_WORKLOADS_ARG = ("c3_attend", "c3_step", "c5_t1", "c5_t4")
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,8 +63,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time budget of the oracle sample")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the prefill, long-context and tiny-decoder figures")
-    ap.add_argument("--pmc-workload", action="store_true",
-                    help="run the counter workload (calibration copy, then attention calls) and exit")
+    ap.add_argument("--pmc-workload", choices=PMC_WORKLOADS_ARG, default=None,
+                    help="run one counter workload (calibration copy, then 40 calls) and exit")
     ap.add_argument("--pmc-prefill", action="store_true",
                     help="run the chunked-prefill workload once (32 chunks) for counter passes and exit")
     return ap.parse_args()
@@ -179,10 +182,12 @@ def block_times(fn, reps, stream, blocks=BLOCKS) -> dict:
     return {"median": per[len(per) // 2], "min": per[0], "max": per[-1], "blocks": blocks, "reps": reps}
 
 
-def pmc_workload(lengths):
+def pmc_workload(lengths, which: str):
     """What the traffic counters are collected on: a calibration copy of known
-    size (PMC_COPY_BYTES read and written), then 40 attention calls on the
-    batched-decode workload over 4 cache instances."""
+    size (PMC_COPY_BYTES read and written), then 40 calls of one workload:
+    c3_attend, attention calls of the batched-decode workload over 4 cache
+    instances; c3_step, its whole step (truncate, kvc_append_attend); c5_t1 /
+    c5_t4, attention calls of the long-context workload at T=1 / T=4."""
     import torch
     src = torch.ones(PMC_COPY_BYTES // 4, device="cuda:0")
     dst = torch.empty_like(src)
@@ -190,14 +195,25 @@ def pmc_workload(lengths):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     del src, dst
-    caches, gen, dev = make_caches(4, lengths)
-    for c in caches:
-        c.append(0, torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.bfloat16),
-                 torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.bfloat16))
-    q = torch.randn((B, HQ, 1, D), generator=gen, device=dev, dtype=torch.bfloat16)
-    out = torch.empty((B, HQ, 1, D), device=dev, dtype=torch.float32)
-    for i in range(40):
-        caches[i % 4].attend(0, q, out=out)
+    if which.startswith("c3"):
+        caches, gen, dev = make_caches(4, lengths)
+        kv = torch.randn((B, HKV, 1, D), generator=gen, device=dev, dtype=torch.bfloat16)
+        q = torch.randn((B, HQ, 1, D), generator=gen, device=dev, dtype=torch.bfloat16)
+        out = torch.empty((B, HQ, 1, D), device=dev, dtype=torch.float32)
+        if which == "c3_attend":
+            for c in caches:
+                c.append(0, kv, kv)
+            for i in range(40):
+                caches[i % 4].attend(0, q, out=out)
+        else:
+            for i in range(40):
+                caches[i % 4].truncate(lengths)
+                caches[i % 4].append_attend(0, kv, kv, q, out=out)
+    else:
+        t = 1 if which == "c5_t1" else 4
+        cache, q, out = long_ctx_cache(t)
+        for _ in range(40):
+            cache.attend(0, q, out=out)
     torch.cuda.synchronize()
 
 
@@ -470,35 +486,43 @@ def small_configs_bench():
     return res
 
 
-def long_ctx_bench(block=None):
-    """Long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys;
-    attention calls with T=1 and T=4 (a draft block) after one append; on a
-    paged cache with blocks of `block` positions when given."""
+def long_ctx_cache(t, block=None, seed=13):
+    """The long-context workload (B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768
+    cached keys) with a chunk of t positions appended: (cache, q, out)."""
     import torch
-    from kv_cached_gqa_amd import work
     b, hq, hkv, d, s0, ml = 8, 64, 8, 128, 32768, 32776
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
-    gen.manual_seed(13)
+    gen.manual_seed(seed)
     cache = new_cache(hkv, d, ml, b, hq, dev, block)
     for _ in range(4):
         k = torch.randn((b, hkv, s0 // 4, d), generator=gen, device=dev, dtype=torch.bfloat16)
         cache.append(0, k, k)
         del k
+    kv = torch.randn((b, hkv, t, d), generator=gen, device=dev, dtype=torch.bfloat16)
+    cache.append(0, kv, kv)
+    q = torch.randn((b, hq, t, d), generator=gen, device=dev, dtype=torch.bfloat16)
+    out = torch.empty((b, hq, t, d), device=dev, dtype=torch.float32)
+    return cache, q, out
+
+
+def long_ctx_bench(block=None):
+    """Long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys;
+    attention calls with T=1 and T=4 (a draft block) after one append, each
+    timed over 20 back-to-back calls after a warm-up; on a paged cache with
+    blocks of `block` positions when given."""
+    import torch
+    from kv_cached_gqa_amd import work
+    b, hq, hkv, d, s0 = 8, 64, 8, 128, 32768
     res = {"workload": "long-context decode: B=8, H_q=64, H_kv=8, d_h=128, bf16, 32768 cached keys"}
     for t in (1, 4):
-        cache.truncate(s0)
-        kv = torch.randn((b, hkv, t, d), generator=gen, device=dev, dtype=torch.bfloat16)
-        cache.append(0, kv, kv)
-        q = torch.randn((b, hq, t, d), generator=gen, device=dev, dtype=torch.bfloat16)
-        out = torch.empty((b, hq, t, d), device=dev, dtype=torch.float32)
-        for _ in range(3):
-            cache.attend(0, q, out=out)
-        ms = event_time(lambda i: cache.attend(0, q, out=out), 20, torch.cuda.current_stream())
+        cache, q, out = long_ctx_cache(t, block)
+        warm_up(lambda i: cache.attend(0, q, out=out), 3)
+        ms = block_times(lambda i: cache.attend(0, q, out=out), 20, torch.cuda.current_stream())["median"]
         byt = work.attend_bytes([s0] * b, t, hq, hkv, d, "bf16", "bf16")
         res[f"T{t}"] = {"us_per_attend": round(ms * 1e3, 2), "gbs": round(byt / (ms * 1e-3) / 1e9, 1),
                         "pct_peak_hbm": round(100 * byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
-    cache.close()
+        cache.close()
     return res
 
 
@@ -548,6 +572,70 @@ def cpu_baseline(lengths, seconds: float, threads=1) -> dict:
             "tokens_per_s": round(B / t_step, 2), "s_per_step": round(t_step, 4)}
 
 
+def oracle_config_timings(budget_s: float = 8.0) -> dict:
+    """The oracle, as it stands, on the other configurations' call scripts,
+    all BLAS threads, each bounded to about `budget_s` seconds of timed calls
+    (the set-up and input draws are not timed): seconds, calls timed, tokens/s
+    (query positions per second) or TFLOP/s, and effective GB/s (the same
+    algorithmic bytes the GPU figures use, divided by the oracle's time)."""
+    from threadpoolctl import threadpool_info
+    from oracle import OracleCache
+    from kv_cached_gqa_amd import work
+    from kv_cached_gqa_amd import workloads as W
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+
+    def timed_script(shape, calls, timed_tag, stop_after=None):
+        orc = OracleCache(shape.n_layers, shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.d_head,
+                          shape.max_len, shape.dtype)
+        el, n_calls, queries, byt, flops = 0.0, 0, 0, 0, 0
+        for call in calls:
+            timed = call.op != "truncate" and timed_tag(call)
+            t0 = time.perf_counter()
+            if call.op in ("append", "pass"):
+                orc.append(call.layer, call.k, call.v)
+            if call.op == "pass":
+                orc.attend(call.layer, call.q)
+            if call.op == "truncate":
+                orc.truncate(call.n)
+            dt = time.perf_counter() - t0
+            if timed and call.op == "pass":
+                el += dt
+                n_calls += 1
+                offs = orc.seq_len(call.layer) - call.T
+                if call.layer == shape.n_layers - 1:
+                    queries += shape.batch * call.T
+                byt += (work.attend_bytes(offs, call.T, shape.n_q_heads, shape.n_kv_heads, shape.d_head,
+                                          shape.dtype, "fp32")
+                        + work.append_bytes(shape.batch, shape.n_kv_heads, call.T, shape.d_head, "fp32", shape.dtype))
+                flops += work.attend_flops(offs, call.T, shape.n_q_heads, shape.d_head)
+                if el >= budget_s or (stop_after is not None and n_calls >= stop_after):
+                    break
+        return {"seconds": round(el, 3), "calls_timed": n_calls, "tokens_per_s": round(queries / el, 2),
+                "gbs": round(byt / el / 1e9, 3), "tflops": round(flops / el / 1e12, 4)}
+
+    res = {"cores": threads, "kind": "oracle",
+           "method": "float64 NumPy oracle on the configuration's own call script; timed: the pass "
+                     "calls named in each entry (append + attend), until the budget"}
+    shape, calls = W.script_tiny_gqa()
+    r = timed_script(shape, calls, lambda c: c.tag != "prefill")
+    res["tiny_gqa_fp32"] = {"sample": f"decode passes (T=1, 4 layers) of the 112-step script: {r['calls_timed']} calls",
+                            **r}
+    shape, calls = W.script_smollm2(rollback=0)
+    r = timed_script(shape, calls, lambda c: c.tag != "prefill")
+    res["smollm2_135m_fp16"] = {"sample": f"decode passes (T=1, 30 layers, after the 512-token prefill): "
+                                          f"{r['calls_timed']} calls", **r}
+    shape, calls = W.script_chunked_prefill()
+    r = timed_script(shape, calls, lambda c: True)
+    res["chunked_prefill_bf16"] = {"sample": f"the first {r['calls_timed']} chunks of T=512 (keys up to "
+                                             f"{512 * r['calls_timed']}), all rows", **r}
+    shape, calls = W.script_long_ctx_spec(n_cycles=1)
+    r = timed_script(shape, calls, lambda c: c.op == "pass")
+    res["long_ctx_spec_bf16"] = {"sample": f"one speculative cycle after the 32768-key preload: "
+                                           f"{r['calls_timed']} passes (a T=4 draft, then T=1 steps), all rows",
+                                 **r}
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -558,7 +646,7 @@ def main():
         sys.exit(2)
     lengths = lengths_seed0()
     if args.pmc_workload:
-        pmc_workload(lengths)
+        pmc_workload(lengths, args.pmc_workload)
         return
     if args.pmc_prefill:
         prefill_bench(runs=1)
@@ -595,7 +683,7 @@ def main():
         "ms_per_step_append_then_attend": round(ms_step_two, 5),
         "pct_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
         "bytes_per_step": att + app,
-        "roofline": {"bound": "hbm", "kernel": "decode attention: decode_attn + decode_combine",
+        "roofline": {"bound": "hbm", "kernel": "decode attention: decode_mfma + decode_combine",
                      "achieved": round(att_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(att_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": att, "launch_us": round(us_attend, 3)},
@@ -608,6 +696,7 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(lengths, args.cpu_seconds)
         rec["cpu_baseline"]["all_cores"] = cpu_baseline(lengths, args.cpu_seconds / 2, threads=None)
+        rec["cpu_baseline"]["other_configs"] = oracle_config_timings()
     print(json.dumps(rec), flush=True)
 
 

@@ -63,7 +63,10 @@ def _mean_for(counters, tag: str, counter: str) -> tuple[float, int]:
 
 
 def summarize(fetch_dir: str, write_dir: str, copy_bytes: int, out: str, cmd_fetch: str, cmd_write: str,
-              kernels=("decode_attn", "decode_combine")) -> int:
+              kernels=("decode_mfma", "decode_combine"),
+              title: str = "HBM traffic of one decode attention call, batched decode (B=32, H_q=32, H_kv=8, "
+                           "d_h=128, bf16, lengths U{1024..4095} seed 0, T=1)",
+              workload: str = "c3_attend", unit: str = "attend") -> int:
     fc, wc = read_counters(fetch_dir), read_counters(write_dir)
     cf, ncf = _mean_for(fc, COPY_KERNEL_TAG, "FETCH_SIZE")
     cw, ncw = _mean_for(wc, COPY_KERNEL_TAG, "WRITE_SIZE")
@@ -76,11 +79,10 @@ def summarize(fetch_dir: str, write_dir: str, copy_bytes: int, out: str, cmd_fet
         total += rb + wb
         rows.append(f"| {k} | {nf} | {f:,.1f} | {rb / 1e6:,.2f} | {w:,.1f} | {wb / 1e6:,.2f} |")
     text = [
-        "# HBM traffic of one decode attention call, batched decode (B=32, H_q=32, H_kv=8, d_h=128, bf16, "
-        "lengths U{1024..4095} seed 0, T=1)",
+        f"# {title}",
         "",
-        "Two rocprofv3 counter runs of `bench.py --pmc-workload` (a calibration copy, then attention calls on "
-        "the batched-decode workload over 4 cache instances), one counter each:",
+        f"Two rocprofv3 counter runs of `bench.py --pmc-workload {workload}` (a calibration copy, then 40 calls "
+        "of the workload), one counter each:",
         "",
         f"    {cmd_fetch}",
         f"    {cmd_write}",
@@ -93,7 +95,7 @@ def summarize(fetch_dir: str, write_dir: str, copy_bytes: int, out: str, cmd_fet
         "|---|---|---|---|---|---|",
         *rows,
         "",
-        f"traffic_bytes_per_attend: {int(round(total))}",
+        f"traffic_bytes_per_{unit}: {int(round(total))}",
         f"decode_sources_sha256: {source_digest()}",
         "",
     ]
@@ -134,8 +136,14 @@ def main():
     s.add_argument("--out", default=TRAFFIC_FILE)
     s.add_argument("--cmd-fetch", default="")
     s.add_argument("--cmd-write", default="")
+    s.add_argument("--kernels", default="decode_mfma,decode_combine", help="kernel name tags, comma separated")
+    s.add_argument("--title", default=None)
+    s.add_argument("--workload", default="c3_attend")
+    s.add_argument("--unit", default="attend", help="what one counted call is (attend, step)")
     a = ap.parse_args()
-    total = summarize(a.fetch, a.write, a.copy_bytes, a.out, a.cmd_fetch, a.cmd_write)
+    kw = {"title": a.title} if a.title else {}
+    total = summarize(a.fetch, a.write, a.copy_bytes, a.out, a.cmd_fetch, a.cmd_write,
+                      kernels=tuple(a.kernels.split(",")), workload=a.workload, unit=a.unit, **kw)
     print(f"wrote {a.out}: {total:,} bytes per attention call")
 
 

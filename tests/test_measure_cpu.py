@@ -22,9 +22,9 @@ def test_calibrated_traffic_and_digest_gate(tmp_path):
     copy_k = "void at::native::elementwise_kernel<MulFunctor<float>>"
     # the copy reads 1 MiB but FETCH_SIZE shows half of it (512 KiB); WRITE_SIZE is exact (1024 KiB)
     _write_run(tmp_path / "f", "FETCH_SIZE", [(copy_k, 512.0), (copy_k, 512.0),
-                                             ("decode_attn<128>", 1000.0), ("decode_attn<128>", 1200.0),
+                                             ("decode_mfma<128>", 1000.0), ("decode_mfma<128>", 1200.0),
                                              ("decode_combine<128>", 10.0)])
-    _write_run(tmp_path / "w", "WRITE_SIZE", [(copy_k, 1024.0), ("decode_attn<128>", 50.0),
+    _write_run(tmp_path / "w", "WRITE_SIZE", [(copy_k, 1024.0), ("decode_mfma<128>", 50.0),
                                              ("decode_combine<128>", 4.0), ("decode_combine<128>", 6.0)])
     out = tmp_path / "traffic.md"
     total = measure.summarize(str(tmp_path / "f"), str(tmp_path / "w"), copy, str(out), "cmd f", "cmd w")
