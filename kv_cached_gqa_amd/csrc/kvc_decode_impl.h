@@ -1143,6 +1143,9 @@ void decode_mfma(DecodeArgs a) {
                 pg_next = pg_phys(blk + 1);
             }
         }
+        // a fused append's new keys (the unit's last T) sit in its last tile at
+        // most: only a tile that reaches them selects an address per lane
+        const bool new_keys = a.k_new != nullptr && is.j0 + (is_t + 1) * kBN > is.n_b - a.T;
 #pragma unroll
         for (int n = 0; n < NLD; ++n) {
             const int e = n * 512 + lane * 8;    // element offset inside the tile
@@ -1158,7 +1161,7 @@ void decode_mfma(DecodeArgs a) {
                 row = is.head + static_cast<int64_t>(j) * D;
             const uint16_t* kp = kg;
             const uint16_t* vp = vg;
-            if (a.k_new != nullptr) {
+            if (new_keys) {
                 // fused append: the chunk's new keys come from the caller's input
                 const int jn = j - (is.n_b - a.T);
                 if (jn >= 0) {
