@@ -1,4 +1,5 @@
-"""Measurement helpers: HBM traffic from rocprofv3 counters, calibrated.
+"""Measurement helpers: HBM traffic from rocprofv3 counters, calibrated, and
+per-kernel durations from a rocprofv3 kernel trace.
 
 The TCC counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch) do not read the
 bytes a kernel moves one to one on this GPU. Each is therefore scaled by what
@@ -13,6 +14,14 @@ reads the *_counter_collection.csv files of two rocprofv3 --pmc runs (one
 counter each) and writes a short markdown summary whose last lines hold the
 calibrated bytes per attention call and a digest of the decode sources, which
 bench.py reads back (and ignores once the sources have changed).
+
+    python -m kv_cached_gqa_amd.measure trace --trace FILE [--tags a,b]
+
+prints, from a rocprofv3 --kernel-trace CSV, the calls of the library grouped
+by the kernels and grids they hold (an append, a decode kernel and the merge
+pass that follow one another on the same queue count as one call), with each
+kernel's average duration and the call's span from its first kernel's start to
+its last kernel's end; then the durations of every dispatch per (kernel, grid).
 """
 from __future__ import annotations
 
@@ -21,6 +30,8 @@ import csv
 import glob
 import hashlib
 import os
+import re
+import statistics
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -126,6 +137,84 @@ def stored_traffic(path: str = TRAFFIC_FILE) -> int | None:
         return None
 
 
+# kernels of this library, and which of them start a call (a merge pass only
+# closes one)
+LIB_KERNELS = ("append_kernel", "rope_kernel", "table_set_kernel", "gather_kernel", "decode_attn",
+               "decode_rows", "decode_mfma", "prefill_attn", "decode_combine")
+_NAME_RE = re.compile(r"::([A-Za-z_]\w*(?:<[^()]*>)?)\(")
+
+
+def short_name(name: str) -> str:
+    """'void ns::(anonymous namespace)::decode_mfma<128, 2, false>(Args)' -> 'decode_mfma<128, 2, false>'."""
+    found = _NAME_RE.findall(name)
+    return found[-1] if found else name.split("(")[0][:60]
+
+
+def read_trace(path: str) -> list[dict]:
+    """Dispatches of a rocprofv3 kernel trace in start order: name, grid in
+    work-groups (x, y), work-group size, start and end (ns), queue."""
+    out = []
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            wx, wy = int(r["Workgroup_Size_X"]), int(r["Workgroup_Size_Y"])
+            out.append({
+                "name": short_name(r["Kernel_Name"]),
+                "grid": (int(r["Grid_Size_X"]) // max(wx, 1), int(r["Grid_Size_Y"]) // max(wy, 1)),
+                "wg": wx * wy * int(r["Workgroup_Size_Z"]),
+                "start": int(r["Start_Timestamp"]), "end": int(r["End_Timestamp"]),
+                "queue": r.get("Queue_Id", ""),
+            })
+    out.sort(key=lambda d: d["start"])
+    return out
+
+
+def _stats_ns(v: list[float]) -> str:
+    return (f"{len(v)} | {statistics.fmean(v):,.0f} | {statistics.median(v):,.0f} | {min(v):,.0f} | "
+            f"{max(v):,.0f}")
+
+
+def trace_tables(path: str, tags=LIB_KERNELS) -> str:
+    """Markdown: each call pattern of the library (see the module docstring)
+    with the duration of each of its kernels and its span, then every
+    dispatch of the tagged kernels per (kernel, grid)."""
+    ds = read_trace(path)
+    lib = [d for d in ds if any(d["name"].startswith(t) for t in LIB_KERNELS)]
+    decode = ("decode_attn", "decode_rows", "decode_mfma")
+    calls: dict[tuple, list[list[dict]]] = defaultdict(list)
+    i = 0
+    while i < len(lib):
+        call = [lib[i]]
+        j = i + 1
+        if lib[i]["name"].startswith("append_kernel") and j < len(lib) and \
+                lib[j]["name"].startswith(decode) and lib[j]["queue"] == lib[i]["queue"]:
+            call.append(lib[j])
+            j += 1
+        if call[-1]["name"].startswith(decode) and j < len(lib) and \
+                lib[j]["name"].startswith("decode_combine") and lib[j]["queue"] == call[-1]["queue"]:
+            call.append(lib[j])
+            j += 1
+        calls[tuple((d["name"], d["grid"]) for d in call)].append(call)
+        i = j
+    lines = ["| Call: kernels (grid in work-groups) | Calls | Kernel averages (ns) | Span average (ns) | "
+             "Span median (ns) | Span min (ns) | Span max (ns) |",
+             "|---|---|---|---|---|---|---|"]
+    for key, cs in sorted(calls.items(), key=lambda kv: -len(kv[1])):
+        name = " + ".join(f"{n} ({g[0]}x{g[1]})" for n, g in key)
+        avgs = " + ".join(f"{statistics.fmean(c[k]['end'] - c[k]['start'] for c in cs):,.0f}" for k in range(len(key)))
+        spans = [c[-1]["end"] - c[0]["start"] for c in cs]
+        lines.append(f"| {name} | {len(cs)} | {avgs} | {statistics.fmean(spans):,.0f} | "
+                     f"{statistics.median(spans):,.0f} | {min(spans):,.0f} | {max(spans):,.0f} |")
+    per: dict[tuple, list[float]] = defaultdict(list)
+    for d in ds:
+        if any(d["name"].startswith(t) for t in tags):
+            per[(d["name"], d["grid"], d["wg"])].append(d["end"] - d["start"])
+    lines += ["", "| Kernel | Grid (work-groups) x work-group | Dispatches | Average (ns) | Median (ns) | Min (ns) | Max (ns) |",
+              "|---|---|---|---|---|---|---|"]
+    for (n, g, wg), v in sorted(per.items(), key=lambda kv: -len(kv[1])):
+        lines.append(f"| {n} | {g[0]} x {g[1]} x {wg} | {_stats_ns(v)} |")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -140,7 +229,13 @@ def main():
     s.add_argument("--title", default=None)
     s.add_argument("--workload", default="c3_attend")
     s.add_argument("--unit", default="attend", help="what one counted call is (attend, step)")
+    t = sub.add_parser("trace")
+    t.add_argument("--trace", required=True, help="a rocprofv3 *_kernel_trace.csv")
+    t.add_argument("--tags", default=",".join(LIB_KERNELS), help="kernel name prefixes to tabulate")
     a = ap.parse_args()
+    if a.cmd == "trace":
+        print(trace_tables(a.trace, tuple(a.tags.split(","))))
+        return
     kw = {"title": a.title} if a.title else {}
     total = summarize(a.fetch, a.write, a.copy_bytes, a.out, a.cmd_fetch, a.cmd_write,
                       kernels=tuple(a.kernels.split(",")), workload=a.workload, unit=a.unit, **kw)
