@@ -80,6 +80,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #ifndef KVC_DECODE_LATE_PCT
 #define KVC_DECODE_LATE_PCT 70       // slice of a later-dispatched work-group, % of a first-round one
 #endif
+#ifndef KVC_DECODE_ODD_XCD_PCT
+#define KVC_DECODE_ODD_XCD_PCT 88    // slice of a work-group on an odd XCD, % of one on an even XCD (measured:
+                                     // 90 best for batched decode, 86 for long contexts)
+#endif
 
 // Rescale threshold (log2 units): the running reference max moves only when a
 // score exceeds it by more than this, so p = exp2(s - m) stays below 2^8.
@@ -1462,8 +1466,10 @@ hipError_t device_cus(int& n_cu) {
 // least min_keys keys each, and no more records than the workspace holds.
 // Work-groups beyond the first dispatch round (one per CU) share a CU with an
 // older one, which the memory system serves first; they get a smaller slice,
-// late_pct percent of a first-round one.
-void split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min_keys, int late_pct) {
+// late_pct percent of a first-round one. Work-group k runs on XCD k mod 8, and
+// the odd XCDs read HBM more slowly than the even ones: a work-group with odd
+// k gets odd_pct percent of the slice of its round.
+void split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min_keys, int late_pct, int odd_pct) {
     int64_t nb = static_cast<int64_t>(n_cu) * per_cu;
     if (nb > kMaxDecodeBlocks) nb = kMaxDecodeBlocks;
     const int64_t by_ws = a.ws_rows_cap / a.rec_rows - static_cast<int64_t>(a.rows) * a.Hkv;
@@ -1471,30 +1477,22 @@ void split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min_keys, int lat
     const int64_t by_size = (a.total_keys + min_keys - 1) / min_keys;
     if (nb > by_size) nb = by_size;
     if (nb < 1) nb = 1;
-    int64_t n1 = nb < n_cu ? nb : n_cu;
-    int64_t n2 = nb - n1;
-    const int64_t denom = n1 * 100 + n2 * late_pct;
-    int64_t kpb = (a.total_keys * 100 + denom - 1) / denom;
-    // rounded up, so that n1 slices of kpb and n2 of kpb2 always cover the axis
-    // (rounded down, a last key or so spilled into one work-group more than the
-    // grid holds, and the split fell back to equal slices)
-    int64_t kpb2 = (kpb * late_pct + 99) / 100;
-    if (kpb2 < 1) kpb2 = 1;
-    if (a.total_keys <= n1 * kpb) {
-        n1 = (a.total_keys + kpb - 1) / kpb;
-        n2 = 0;
-    } else {
-        n2 = (a.total_keys - n1 * kpb + kpb2 - 1) / kpb2;
-    }
-    if (n1 + n2 > nb) {   // rounding pushed past the cap: equal slices
-        kpb = kpb2 = (a.total_keys + nb - 1) / nb;
-        n1 = (a.total_keys + kpb - 1) / kpb;
-        n2 = 0;
-    }
+    const int64_t n1 = nb < n_cu ? nb : n_cu;
+    const int64_t n1e = decode_evens_below(n1), n1o = n1 - n1e;
+    const int64_t n2e = decode_evens_below(nb) - n1e, n2o = (nb - n1) - n2e;
+    // slice weights in 1/10000 of a first-round even slice
+    const int64_t w1e = 10000, w1o = 100 * odd_pct, w2e = 100 * late_pct, w2o = late_pct * odd_pct;
+    const int64_t denom = n1e * w1e + n1o * w1o + n2e * w2e + n2o * w2o;
+    const int64_t kpb = (a.total_keys * 10000 + denom - 1) / denom;
+    // each size rounded up, so that the nb slices always cover the axis
+    auto size = [&](int64_t w) { const int64_t v = (kpb * w + 9999) / 10000; return v < 1 ? int64_t(1) : v; };
     a.keys_per_block = kpb;
-    a.keys_per_block2 = kpb2;
+    a.keys_per_block_odd = size(w1o);
+    a.keys_per_block2 = size(w2e);
+    a.keys_per_block2_odd = size(w2o);
     a.n_first = static_cast<int32_t>(n1);
-    a.n_blocks = static_cast<int32_t>(n1 + n2);
+    // work-groups that hold keys (rounding up can leave the last ones empty)
+    a.n_blocks = static_cast<int32_t>(decode_slice_of(a, a.total_keys - 1) + 1);
 }
 
 // The merge pass, if some unit spans several work-groups.
@@ -1522,7 +1520,7 @@ hipError_t run(DecodeArgs& a, hipStream_t s) {
     hipError_t e = device_cus(n_cu);
     if (e != hipSuccess) return e;
     a.rec_rows = R;
-    split_slices(a, n_cu, KVC_DECODE_BLOCKS_PER_CU, 2 * Cfg<D, ST, R>::KPB, KVC_DECODE_LATE_PCT);
+    split_slices(a, n_cu, KVC_DECODE_BLOCKS_PER_CU, 2 * Cfg<D, ST, R>::KPB, KVC_DECODE_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
     if (a.btab) {
         if ((1 << a.bshift) < Cfg<D, ST, R>::KPB) return hipErrorInvalidValue;   // a batch within two blocks
         decode_attn<D, ST, R, true><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
@@ -1540,7 +1538,7 @@ hipError_t run_rows(DecodeArgs& a, hipStream_t s) {
     hipError_t e = device_cus(n_cu);
     if (e != hipSuccess) return e;
     a.rec_rows = RCfg<D, ST, RS>::ROWS;
-    split_slices(a, n_cu, 2, 2 * RCfg<D, ST, RS>::KPS, KVC_DECODE_LATE_PCT);
+    split_slices(a, n_cu, 2, 2 * RCfg<D, ST, RS>::KPS, KVC_DECODE_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
     if (a.btab) {
         if ((1 << a.bshift) < RCfg<D, ST, RS>::KPS) return hipErrorInvalidValue;   // a stage within two blocks
         decode_rows<D, ST, RS, true><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
@@ -1558,7 +1556,7 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
     hipError_t e = device_cus(n_cu);
     if (e != hipSuccess) return e;
     a.rec_rows = (a.Gc * a.Tc + 3) & ~3;   // records as wide as the slab (rounded up to 4 rows)
-    split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT);
+    split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
     if (a.btab) {
         if ((1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks
         decode_mfma<D, ST, true><<<a.n_blocks, 64, 0, s>>>(a);

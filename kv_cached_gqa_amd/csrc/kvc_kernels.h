@@ -83,9 +83,15 @@ struct DecodeArgs {
     int64_t row_stride;
     int64_t head_stride;
     int64_t total_keys;      // sum over rows of n_b * H_kv
-    int64_t keys_per_block;  // slice of the key axis per work-group of the first n_first
-    int64_t keys_per_block2; // slice per later work-group
-    int32_t n_first;         // work-groups with the first slice size
+    // slices of the key axis: work-group k < n_first takes keys_per_block
+    // keys when k is even and keys_per_block_odd when k is odd; a later one
+    // keys_per_block2 or keys_per_block2_odd by the same parity (work-group k
+    // runs on XCD k mod 8, and the odd XCDs read HBM more slowly)
+    int64_t keys_per_block;
+    int64_t keys_per_block_odd;
+    int64_t keys_per_block2;
+    int64_t keys_per_block2_odd;
+    int32_t n_first;
     int32_t row0, rows;      // batch rows of this launch
     int32_t Hq, Hkv, G, T;   // T = query positions in the chunk
     int32_t D;
@@ -159,14 +165,34 @@ struct TableSetArgs {
 };
 hipError_t launch_table_set(const TableSetArgs& a, hipStream_t stream);
 // Decode work-group k's slice of the key axis starts at decode_slice_begin(a, k);
-// key x lies in work-group decode_slice_of(a, x)'s slice.
+// key x lies in work-group decode_slice_of(a, x)'s slice. Slice sizes alternate
+// by the parity of k (even first).
+__host__ __device__ inline int64_t decode_evens_below(int64_t k) { return (k + 1) >> 1; }
 __host__ __device__ inline int64_t decode_slice_begin(const DecodeArgs& a, int64_t k) {
-    return k <= a.n_first ? k * a.keys_per_block
-                          : a.n_first * a.keys_per_block + (k - a.n_first) * a.keys_per_block2;
+    const int64_t n1 = a.n_first;
+    if (k <= n1) {
+        const int64_t ne = decode_evens_below(k);
+        return ne * a.keys_per_block + (k - ne) * a.keys_per_block_odd;
+    }
+    const int64_t ne1 = decode_evens_below(n1);
+    const int64_t x1 = ne1 * a.keys_per_block + (n1 - ne1) * a.keys_per_block_odd;
+    const int64_t ne = decode_evens_below(k) - ne1;
+    return x1 + ne * a.keys_per_block2 + (k - n1 - ne) * a.keys_per_block2_odd;
 }
 __host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t x) {
-    const int64_t x1 = static_cast<int64_t>(a.n_first) * a.keys_per_block;
-    return x < x1 ? x / a.keys_per_block : a.n_first + (x - x1) / a.keys_per_block2;
+    const int64_t n1 = a.n_first;
+    const int64_t x1 = decode_slice_begin(a, n1);
+    int64_t base = 0, first = a.keys_per_block, second = a.keys_per_block_odd;
+    if (x >= x1) {
+        // the later slices start at index n1; a pair is (even, odd) from an even n1
+        base = n1;
+        x -= x1;
+        first = (n1 & 1) ? a.keys_per_block2_odd : a.keys_per_block2;
+        second = (n1 & 1) ? a.keys_per_block2 : a.keys_per_block2_odd;
+    }
+    const int64_t pair = first + second;
+    const int64_t p = x / pair;
+    return base + 2 * p + (x - p * pair >= first ? 1 : 0);
 }
 
 // Fills in the work split (n_blocks, slice sizes) from the device's resident capacity.
