@@ -21,6 +21,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <climits>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -604,6 +605,9 @@ int attend_impl(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
                     acc += n_b * cf.n_kv_heads;
                 }
                 a.prefix[rows] = acc;
+                // entries past the last row stay above every key position (the
+                // kernels find a position's row by counting entries at or below it)
+                for (int b = rows + 1; b <= kMaxRowsPerLaunch; ++b) a.prefix[b] = INT64_MAX;
                 a.total_keys = acc;
                 a.k_new = k_new;
                 a.v_new = v_new;

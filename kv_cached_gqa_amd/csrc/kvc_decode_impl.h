@@ -214,6 +214,62 @@ __device__ __forceinline__ void lane_group_sum(float (&x)[M]) {
 
 // One segment of a work-group's slice: keys [j0, j1) of unit (b, g), whose
 // last slab query sits at position n_b - Tc.
+// The row of key-axis position x, 0 <= x < prefix[rows]: the b with
+// prefix[b] <= x < prefix[b + 1], and those two entries, found with one round
+// of vector loads from the kernel arguments (load_prefix_lanes: lane l reads
+// entries l, l + 64, ...; entries past the last row hold INT64_MAX) and
+// ballots that count the entries at or below x (row_of). A binary search over
+// the arguments waits for one dependent scalar load per step; at a
+// work-group's start that held its first K/V load back by over a microsecond.
+// The whole wave must be active.
+struct RowOf {
+    int b;
+    int64_t p0, p1;
+};
+constexpr int kPrefixSlots = (kMaxRowsPerLaunch + 1 + 63) / 64;
+struct PrefixLanes {
+    int64_t e[kPrefixSlots];   // entries lane, lane + 64, ...
+};
+__device__ __forceinline__ PrefixLanes load_prefix_lanes() {
+    const auto* args = (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+    const auto* pf = reinterpret_cast<const __attribute__((address_space(4))) int64_t*>(args + offsetof(DecodeArgs, prefix));
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    PrefixLanes p;
+#pragma unroll
+    for (int j = 0; j < kPrefixSlots; ++j) {
+        // every lane loads (a vector load: a lane-0-only load would become a
+        // scalar one that the compiler waits for at once)
+        const int i = lane + 64 * j;
+        const int64_t v = pf[i <= kMaxRowsPerLaunch ? i : kMaxRowsPerLaunch];
+        p.e[j] = i <= kMaxRowsPerLaunch ? v : INT64_MAX;
+    }
+    return p;
+}
+__device__ __forceinline__ RowOf row_of(const PrefixLanes& p, int64_t x) {
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kPrefixSlots; ++j) cnt += __popcll(__ballot(p.e[j] <= x));
+    // entry i: read from lane i mod 64 of every slot, then the slot i / 64
+    // picked among the (uniform) results
+    auto entry = [&](int i) __attribute__((always_inline)) -> int64_t {
+        const int j = i >> 6, l = i & 63;
+        int64_t v = 0;
+#pragma unroll
+        for (int jj = 0; jj < kPrefixSlots; ++jj) {
+            const uint64_t u = static_cast<uint64_t>(p.e[jj]);
+            const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
+            const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
+            if (j == jj) v = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+        }
+        return v;
+    };
+    RowOf r;
+    r.b = cnt - 1;
+    r.p0 = entry(r.b);
+    r.p1 = entry(r.b + 1);
+    return r;
+}
+
 struct Seg {
     int b, g;
     int j0, j1, n_b;
@@ -1040,6 +1096,12 @@ void decode_mfma(DecodeArgs a) {
     const float c = a.scale_log2;
     const float thresh = kRescaleLog2 / c;
 
+    const PrefixLanes pfx = load_prefix_lanes();   // in flight while the slice is worked out
+    // one field from each 64-byte line of the arguments' scalar part, needed
+    // together here so that the lines arrive in one round trip instead of one
+    // after another as each is first used
+    asm volatile("" ::"s"(a.k_cache), "s"(a.keys_per_block), "s"(a.n_first), "s"(a.k_new),
+                 "s"(a.prefix[kMaxRowsPerLaunch]));
     const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
     int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
     if (x_end > a.total_keys) x_end = a.total_keys;
@@ -1048,17 +1110,14 @@ void decode_mfma(DecodeArgs a) {
     const uint16_t* kg = static_cast<const uint16_t*>(a.k_cache);
     const uint16_t* vg = static_cast<const uint16_t*>(a.v_cache);
 
-    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
-        int lo = 0, hi = a.rows;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (a.prefix[mid] <= x) lo = mid; else hi = mid;
-        }
+    // the segment at x of row lo, whose units start at p0 (prefix[lo]) and end
+    // at p1 (prefix[lo + 1])
+    auto seg_at = [&](int lo, int64_t p0, int64_t p1, int64_t x) __attribute__((always_inline)) -> Seg {
         Seg sg;
         sg.b = lo;
-        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
-        sg.g = static_cast<int>((x - a.prefix[lo]) / n_b);
-        const int64_t unit_start = a.prefix[lo] + static_cast<int64_t>(sg.g) * n_b;
+        const int64_t n_b = (p1 - p0) / a.Hkv;
+        sg.g = static_cast<int>((x - p0) / n_b);
+        const int64_t unit_start = p0 + static_cast<int64_t>(sg.g) * n_b;
         int64_t seg_end = unit_start + n_b;
         if (seg_end > x_end) seg_end = x_end;
         sg.j0 = static_cast<int>(x - unit_start);
@@ -1070,12 +1129,25 @@ void decode_mfma(DecodeArgs a) {
         sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
         return sg;
     };
+    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
+        int lo = 0, hi = a.rows;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.prefix[mid] <= x) lo = mid; else hi = mid;
+        }
+        return seg_at(lo, a.prefix[lo], a.prefix[lo + 1], x);
+    };
+    // the first segment, found without the search's chain of scalar loads
+    const Seg first = [&]() __attribute__((always_inline)) {
+        const RowOf r = row_of(pfx, x_begin);
+        return seg_at(r.b, r.p0, r.p1, x_begin);
+    }();
 
     // -- the query table: 32 columns (slab rows; past the slab zero) per segment,
     //    rounded to the storage type --
     auto load_qtab = [&](int64_t x) __attribute__((always_inline)) {
         for (int sgi = 0; sgi < P::QSEGS && x < x_end; ++sgi) {
-            const Seg sg = locate(x);
+            const Seg sg = x == x_begin ? first : locate(x);
             if (a.q_dtype == ST) {
                 // q already in the storage type: 8 elements (16 bytes) at a time
                 for (int c8 = lane; c8 < 4 * D; c8 += 64) {
@@ -1113,7 +1185,7 @@ void decode_mfma(DecodeArgs a) {
     // -- issue side: the next 32-key tile, K chunks XOR-swizzled, V chunks
     //    permuted for the transposed reads; past the slice's end the last key
     //    is reloaded (never used) --
-    Seg is = locate(x_begin);
+    Seg is = first;
     int is_t = 0;
     bool is_live = true;
     // paged storage: pool offsets of head is.g's rows in the blocks of logical
@@ -1210,7 +1282,7 @@ void decode_mfma(DecodeArgs a) {
     }
 
     // -- consume side --
-    Seg cs = locate(x_begin);
+    Seg cs = first;
     int cs_t = 0, cs_q = 0;
     u32x4 qb[DS];
     int qpos;
