@@ -1442,11 +1442,16 @@ void decode_mfma(DecodeArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     constexpr int kMaxSeg = 16;
-    const int u = blockIdx.x;
-    const int b = u / a.Hkv;
-    const int g = u - b * a.Hkv;
-    const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
-    if (a.k_new != nullptr && blockIdx.y == gridDim.y - 1) {
+    // grid (H_kv, rows of 256 outputs [+ the store row], batch rows): the row
+    // b is known without the arguments, so its prefix entries and the argument
+    // lines used below are fetched in one round trip
+    const int g = blockIdx.x;
+    const int b = blockIdx.z;
+    const int64_t p0 = a.prefix[b], p1 = a.prefix[b + 1];
+    asm volatile("" ::"s"(p0), "s"(p1), "s"(a.k_cache), "s"(a.keys_per_block), "s"(a.n_first), "s"(a.k_new));
+    const int u = b * a.Hkv + g;
+    const int64_t n_b = (p1 - p0) / a.Hkv;
+    if (a.k_new != nullptr && static_cast<int>(blockIdx.y) == a.merge_rows) {
         // fused append: store unit (b, g)'s T new keys and values at slots
         // n_b - T .. n_b - 1 (the input has the storage type: bit copies, with a
         // 16-bit NaN stored as the canonical quiet NaN of its sign, as the
@@ -1481,7 +1486,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
         }
         return;
     }
-    const int64_t ustart = a.prefix[b] + g * n_b;
+    const int64_t ustart = p0 + g * n_b;
     const int k_first = static_cast<int>(decode_slice_of(a, ustart));
     const int k_last = static_cast<int>(decode_slice_of(a, ustart + n_b - 1));
     if (k_first == k_last) return;
@@ -1581,7 +1586,8 @@ hipError_t combine_if_split(DecodeArgs& a, hipStream_t s) {
     // a fused append adds one row of work-groups that store the new keys and values
     if (!split && a.k_new == nullptr) return hipSuccess;
     const unsigned merge_rows = split ? (a.Gc * a.Tc * D + 255) / 256 : 0;
-    const dim3 grid(a.rows * a.Hkv, merge_rows + (a.k_new != nullptr ? 1 : 0));
+    a.merge_rows = static_cast<int32_t>(merge_rows);
+    const dim3 grid(a.Hkv, merge_rows + (a.k_new != nullptr ? 1 : 0), a.rows);
     decode_combine<D><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }

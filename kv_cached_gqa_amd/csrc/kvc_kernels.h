@@ -98,6 +98,7 @@ struct DecodeArgs {
     int32_t r0, Gc, i0, Tc;  // the slab
     int32_t q_dtype, st_dtype;
     int32_t n_blocks;        // work-groups (set by launch_decode)
+    int32_t merge_rows;      // the merge pass's rows of 256 outputs (its store row, if any, follows them)
     float scale_log2;        // log2(e) / sqrt(D)
     // paged storage (btab non-null): key j of unit (b, g) sits in physical block
     // btab[b * btab_stride + (j >> bshift)] of the layer's pool, at element
