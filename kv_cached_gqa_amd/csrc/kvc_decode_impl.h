@@ -1129,13 +1129,14 @@ void decode_mfma(DecodeArgs a) {
         sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
         return sg;
     };
-    auto locate = [&](int64_t x) __attribute__((always_inline)) -> Seg {
-        int lo = 0, hi = a.rows;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (a.prefix[mid] <= x) lo = mid; else hi = mid;
-        }
-        return seg_at(lo, a.prefix[lo], a.prefix[lo + 1], x);
+    // the segment after sg, which ended at its unit's end inside the slice:
+    // the next KV head of the row, or the first of the next row (whose end is
+    // the one prefix entry read here)
+    auto locate_next = [&](const Seg& sg) __attribute__((always_inline)) -> Seg {
+        const int64_t row_start = sg.x_end - static_cast<int64_t>(sg.g + 1) * sg.n_b;
+        const int64_t row_end = row_start + static_cast<int64_t>(a.Hkv) * sg.n_b;
+        if (sg.g + 1 < a.Hkv) return seg_at(sg.b, row_start, row_end, sg.x_end);
+        return seg_at(sg.b + 1, row_end, a.prefix[sg.b + 2], sg.x_end);
     };
     // the first segment, found without the search's chain of scalar loads
     const Seg first = [&]() __attribute__((always_inline)) {
@@ -1145,9 +1146,13 @@ void decode_mfma(DecodeArgs a) {
 
     // -- the query table: 32 columns (slab rows; past the slab zero) per segment,
     //    rounded to the storage type --
-    auto load_qtab = [&](int64_t x) __attribute__((always_inline)) {
-        for (int sgi = 0; sgi < P::QSEGS && x < x_end; ++sgi) {
-            const Seg sg = x == x_begin ? first : locate(x);
+    auto load_qtab = [&](const Seg& s0) __attribute__((always_inline)) {
+        Seg sg = s0;
+        for (int sgi = 0; sgi < P::QSEGS; ++sgi) {
+            if (sgi > 0) {
+                if (sg.x_end >= x_end) break;
+                sg = locate_next(sg);
+            }
             if (a.q_dtype == ST) {
                 // q already in the storage type: 8 elements (16 bytes) at a time
                 for (int c8 = lane; c8 < 4 * D; c8 += 64) {
@@ -1161,7 +1166,6 @@ void decode_mfma(DecodeArgs a) {
                     }
                     *reinterpret_cast<u32x4*>(&qtab[sgi][r][e]) = w;
                 }
-                x = sg.x_end;
                 continue;
             }
             for (int idx = lane; idx < 32 * D; idx += 64) {
@@ -1177,7 +1181,6 @@ void decode_mfma(DecodeArgs a) {
                 }
                 qtab[sgi][r][e] = static_cast<uint16_t>(ST == BF16 ? f32_to_bf16_rne(val) : f32_to_f16_rne(val));
             }
-            x = sg.x_end;
         }
         __syncthreads();
     };
@@ -1257,7 +1260,7 @@ void decode_mfma(DecodeArgs a) {
             if (is.x_end >= x_end) {
                 is_live = false;
             } else {
-                is = locate(is.x_end);
+                is = locate_next(is);
                 is_t = 0;
                 if constexpr (PAGED) pg_enter();
             }
@@ -1404,7 +1407,7 @@ void decode_mfma(DecodeArgs a) {
 
     // -- the loop: tile t in slot t % NS, NS - 1 tiles issued ahead --
     static_for<NS - 1>([&](auto k) { issue(k); });
-    load_qtab(x_begin);
+    load_qtab(first);
     start_segment();
     bool done = false;
     auto step = [&](auto slot_c) __attribute__((always_inline)) {
@@ -1417,10 +1420,10 @@ void decode_mfma(DecodeArgs a) {
             if (cs.x_end >= x_end) {
                 done = true;
             } else {
-                cs = locate(cs.x_end);
+                cs = locate_next(cs);
                 cs_t = 0;
                 if (++cs_q == P::QSEGS) {    // more segments than the table holds: reload it
-                    load_qtab(cs.x_end - (cs.j1 - cs.j0));
+                    load_qtab(cs);
                     cs_q = 0;
                 }
                 start_segment();
