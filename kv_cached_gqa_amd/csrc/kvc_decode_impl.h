@@ -1186,8 +1186,7 @@ void decode_mfma(DecodeArgs a) {
     };
 
     // -- issue side: the next 32-key tile, K chunks XOR-swizzled, V chunks
-    //    permuted for the transposed reads; past the slice's end the last key
-    //    is reloaded (never used) --
+    //    permuted for the transposed reads; nothing once the slice is done --
     Seg is = first;
     int is_t = 0;
     bool is_live = true;
@@ -1212,6 +1211,7 @@ void decode_mfma(DecodeArgs a) {
     if constexpr (PAGED) pg_enter();
     auto issue = [&](auto slot_c) __attribute__((always_inline)) {
         constexpr int S = decltype(slot_c)::value;
+        if (!is_live) return;
         uint16_t* kd = smem + S * P::STAGE_BYTES / 2;
         uint16_t* vd = kd + P::TILE;
         if constexpr (PAGED) {
@@ -1412,8 +1412,12 @@ void decode_mfma(DecodeArgs a) {
     bool done = false;
     auto step = [&](auto slot_c) __attribute__((always_inline)) {
         constexpr int S = decltype(slot_c)::value;
+        // this tile's loads have landed: NS - 1 tiles stay in flight, or none
+        // at the slice's end (no loads are issued past it)
+        const bool more = is_live;
         issue(std::integral_constant<int, (S + NS - 1) % NS>{});
-        wait_vm<(NS - 1) * 2 * NLD>();   // this tile's loads have landed
+        if (more) wait_vm<(NS - 1) * 2 * NLD>();
+        else wait_vm<0>();
         consume(slot_c);
         if (++cs_t == cs.nbat) {
             finish_segment();
