@@ -214,8 +214,9 @@ __device__ __forceinline__ void lane_group_sum(float (&x)[M]) {
 
 // One segment of a work-group's slice: keys [j0, j1) of unit (b, g), whose
 // last slab query sits at position n_b - Tc.
-// The row of key-axis position x, 0 <= x < prefix[rows]: the b with
-// prefix[b] <= x < prefix[b + 1], and those two entries, found with one round
+// The row of key-axis position x on the padded axis (row b starts at
+// prefix[b] + b * row_pad): the b whose rows start at or before x, and the
+// padded starts of rows b and b + 1, found with one round
 // of vector loads from the kernel arguments (load_prefix_lanes: lane l reads
 // entries l, l + 64, ...; entries past the last row hold INT64_MAX) and
 // ballots that count the entries at or below x (row_of). A binary search over
@@ -245,10 +246,15 @@ __device__ __forceinline__ PrefixLanes load_prefix_lanes() {
     }
     return p;
 }
-__device__ __forceinline__ RowOf row_of(const PrefixLanes& p, int64_t x) {
+__device__ __forceinline__ RowOf row_of(const PrefixLanes& p, int64_t x, int64_t row_pad) {
+    // entry i on the padded axis: prefix[i] + i * row_pad
+    const int lane = static_cast<int>(threadIdx.x) & 63;
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kPrefixSlots; ++j) cnt += __popcll(__ballot(p.e[j] <= x));
+    for (int j = 0; j < kPrefixSlots; ++j) {
+        const int64_t ep = p.e[j] == INT64_MAX ? INT64_MAX : p.e[j] + static_cast<int64_t>(lane + 64 * j) * row_pad;
+        cnt += __popcll(__ballot(ep <= x));
+    }
     // entry i: read from lane i mod 64 of every slot, then the slot i / 64
     // picked among the (uniform) results
     auto entry = [&](int i) __attribute__((always_inline)) -> int64_t {
@@ -265,8 +271,8 @@ __device__ __forceinline__ RowOf row_of(const PrefixLanes& p, int64_t x) {
     };
     RowOf r;
     r.b = cnt - 1;
-    r.p0 = entry(r.b);
-    r.p1 = entry(r.b + 1);
+    r.p0 = entry(r.b) + r.b * row_pad;
+    r.p1 = entry(r.b + 1) + (r.b + 1) * row_pad;
     return r;
 }
 
@@ -1055,6 +1061,13 @@ void decode_rows(DecodeArgs a) {
 #ifndef KVC_DECODE_MFMA_MIN_ROWS
 #define KVC_DECODE_MFMA_MIN_ROWS 1    // 16-bit slabs with fewer rows run on the vector kernel
 #endif
+#ifndef KVC_DECODE_MFMA_UNIT_PAD
+// virtual keys charged to every unit on the key axis: a work-group whose slice
+// holds a unit boundary streams a part tile on each side of it, about one tile
+// more for the same keys (the latest work-groups of the batched-decode call
+// were all such)
+#define KVC_DECODE_MFMA_UNIT_PAD 48   // measured: 0 65.3, 16 65.0, 32 64.8, 48 64.3-64.6, 64-112 64.6-65.1 us per batched-decode call
+#endif
 #ifndef KVC_DECODE_MFMA_LATE_PCT
 // equal slices: with three single-wave work-groups per CU an uneven split
 // measured slower on the long-context workload (e.g. 193 against 180 us at a
@@ -1110,20 +1123,22 @@ void decode_mfma(DecodeArgs a) {
     const uint16_t* kg = static_cast<const uint16_t*>(a.k_cache);
     const uint16_t* vg = static_cast<const uint16_t*>(a.v_cache);
 
-    // the segment at x of row lo, whose units start at p0 (prefix[lo]) and end
-    // at p1 (prefix[lo + 1])
+    // the segment at padded position x of row lo, whose units start at p0 and
+    // end at p1 on the padded axis: each unit is unit_pad virtual keys, then
+    // its n_b real ones; a segment that holds no real key has nbat = 0
+    const int64_t row_pad = static_cast<int64_t>(a.Hkv) * a.unit_pad;
     auto seg_at = [&](int lo, int64_t p0, int64_t p1, int64_t x) __attribute__((always_inline)) -> Seg {
         Seg sg;
         sg.b = lo;
-        const int64_t n_b = (p1 - p0) / a.Hkv;
-        sg.g = static_cast<int>((x - p0) / n_b);
-        const int64_t unit_start = p0 + static_cast<int64_t>(sg.g) * n_b;
-        int64_t seg_end = unit_start + n_b;
+        const int64_t n_e = (p1 - p0) / a.Hkv;
+        sg.g = static_cast<int>((x - p0) / n_e);
+        const int64_t unit_start = p0 + static_cast<int64_t>(sg.g) * n_e + a.unit_pad;   // its first real key
+        int64_t seg_end = unit_start + (n_e - a.unit_pad);
         if (seg_end > x_end) seg_end = x_end;
-        sg.j0 = static_cast<int>(x - unit_start);
+        sg.j0 = x > unit_start ? static_cast<int>(x - unit_start) : 0;
         sg.j1 = static_cast<int>(seg_end - unit_start);
-        sg.n_b = static_cast<int>(n_b);
-        sg.nbat = (sg.j1 - sg.j0 + kBN - 1) / kBN;
+        sg.n_b = static_cast<int>(n_e - a.unit_pad);
+        sg.nbat = sg.j1 > sg.j0 ? (sg.j1 - sg.j0 + kBN - 1) / kBN : 0;
         sg.head = a.layer_off + sg.b * a.row_stride + sg.g * a.head_stride;
         sg.x_end = seg_end;
         sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
@@ -1133,16 +1148,18 @@ void decode_mfma(DecodeArgs a) {
     // the next KV head of the row, or the first of the next row (whose end is
     // the one prefix entry read here)
     auto locate_next = [&](const Seg& sg) __attribute__((always_inline)) -> Seg {
-        const int64_t row_start = sg.x_end - static_cast<int64_t>(sg.g + 1) * sg.n_b;
-        const int64_t row_end = row_start + static_cast<int64_t>(a.Hkv) * sg.n_b;
+        const int64_t n_e = static_cast<int64_t>(sg.n_b) + a.unit_pad;
+        const int64_t row_start = sg.x_end - static_cast<int64_t>(sg.g + 1) * n_e;
+        const int64_t row_end = row_start + static_cast<int64_t>(a.Hkv) * n_e;
         if (sg.g + 1 < a.Hkv) return seg_at(sg.b, row_start, row_end, sg.x_end);
-        return seg_at(sg.b + 1, row_end, a.prefix[sg.b + 2], sg.x_end);
+        return seg_at(sg.b + 1, row_end, a.prefix[sg.b + 2] + (sg.b + 2) * row_pad, sg.x_end);
     };
     // the first segment, found without the search's chain of scalar loads
     const Seg first = [&]() __attribute__((always_inline)) {
-        const RowOf r = row_of(pfx, x_begin);
+        const RowOf r = row_of(pfx, x_begin, row_pad);
         return seg_at(r.b, r.p0, r.p1, x_begin);
     }();
+    if (first.nbat == 0) return;   // a slice of virtual keys only
 
     // -- the query table: 32 columns (slab rows; past the slab zero) per segment,
     //    rounded to the storage type --
@@ -1152,6 +1169,7 @@ void decode_mfma(DecodeArgs a) {
             if (sgi > 0) {
                 if (sg.x_end >= x_end) break;
                 sg = locate_next(sg);
+                if (sg.nbat == 0) break;
             }
             if (a.q_dtype == ST) {
                 // q already in the storage type: 8 elements (16 bytes) at a time
@@ -1262,7 +1280,8 @@ void decode_mfma(DecodeArgs a) {
             } else {
                 is = locate_next(is);
                 is_t = 0;
-                if constexpr (PAGED) pg_enter();
+                if (is.nbat == 0) is_live = false;          // the slice ends in virtual keys
+                else if constexpr (PAGED) pg_enter();
             }
         }
     };
@@ -1425,12 +1444,16 @@ void decode_mfma(DecodeArgs a) {
                 done = true;
             } else {
                 cs = locate_next(cs);
-                cs_t = 0;
-                if (++cs_q == P::QSEGS) {    // more segments than the table holds: reload it
-                    load_qtab(cs);
-                    cs_q = 0;
+                if (cs.nbat == 0) {          // the slice ends in virtual keys
+                    done = true;
+                } else {
+                    cs_t = 0;
+                    if (++cs_q == P::QSEGS) {    // more segments than the table holds: reload it
+                        load_qtab(cs);
+                        cs_q = 0;
+                    }
+                    start_segment();
                 }
-                start_segment();
             }
         }
     };
@@ -1458,6 +1481,8 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     asm volatile("" ::"s"(p0), "s"(p1), "s"(a.k_cache), "s"(a.keys_per_block), "s"(a.n_first), "s"(a.k_new));
     const int u = b * a.Hkv + g;
     const int64_t n_b = (p1 - p0) / a.Hkv;
+    // the unit's first real key on the (padded) key axis
+    const int64_t ustart = p0 + static_cast<int64_t>(b) * a.Hkv * a.unit_pad + g * (n_b + a.unit_pad) + a.unit_pad;
     if (a.k_new != nullptr && static_cast<int>(blockIdx.y) == a.merge_rows) {
         // fused append: store unit (b, g)'s T new keys and values at slots
         // n_b - T .. n_b - 1 (the input has the storage type: bit copies, with a
@@ -1493,7 +1518,6 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
         }
         return;
     }
-    const int64_t ustart = p0 + g * n_b;
     const int k_first = static_cast<int>(decode_slice_of(a, ustart));
     const int k_last = static_cast<int>(decode_slice_of(a, ustart + n_b - 1));
     if (k_first == k_last) return;
@@ -1586,7 +1610,7 @@ hipError_t combine_if_split(DecodeArgs& a, hipStream_t s) {
     for (int b = 0; b < a.rows && !split; ++b) {
         const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
         for (int g = 0; g < a.Hkv && !split; ++g) {
-            const int64_t us = a.prefix[b] + g * n_b;
+            const int64_t us = a.prefix[b] + static_cast<int64_t>(b) * a.Hkv * a.unit_pad + g * (n_b + a.unit_pad) + a.unit_pad;
             split = decode_slice_of(a, us) != decode_slice_of(a, us + n_b - 1);
         }
     }
@@ -1641,6 +1665,9 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
     hipError_t e = device_cus(n_cu);
     if (e != hipSuccess) return e;
     a.rec_rows = (a.Gc * a.Tc + 3) & ~3;   // records as wide as the slab (rounded up to 4 rows)
+    // every unit charged one tile more on the key axis (its part tiles)
+    a.unit_pad = KVC_DECODE_MFMA_UNIT_PAD;
+    a.total_keys += static_cast<int64_t>(a.rows) * a.Hkv * a.unit_pad;
     split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
     if (a.btab) {
         if ((1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks

@@ -82,7 +82,7 @@ struct DecodeArgs {
     int64_t layer_off;       // element offset of (layer, row0, 0, 0, 0)
     int64_t row_stride;
     int64_t head_stride;
-    int64_t total_keys;      // sum over rows of n_b * H_kv
+    int64_t total_keys;      // sum over rows of (n_b + unit_pad) * H_kv
     // slices of the key axis: work-group k < n_first takes keys_per_block
     // keys when k is even and keys_per_block_odd when k is odd; a later one
     // keys_per_block2 or keys_per_block2_odd by the same parity (work-group k
@@ -99,6 +99,12 @@ struct DecodeArgs {
     int32_t q_dtype, st_dtype;
     int32_t n_blocks;        // work-groups (set by launch_decode)
     int32_t merge_rows;      // the merge pass's rows of 256 outputs (its store row, if any, follows them)
+    // The key axis may give every unit unit_pad virtual keys before its real
+    // ones (the matrix-core kernel charges each unit one tile this way: a
+    // slice that holds a unit boundary has a part tile on each side of it).
+    // Positions and total_keys are on that padded axis; prefix counts real
+    // keys, so row b starts at prefix[b] + b * Hkv * unit_pad.
+    int32_t unit_pad;
     float scale_log2;        // log2(e) / sqrt(D)
     // paged storage (btab non-null): key j of unit (b, g) sits in physical block
     // btab[b * btab_stride + (j >> bshift)] of the layer's pool, at element
