@@ -81,8 +81,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define KVC_DECODE_LATE_PCT 70       // slice of a later-dispatched work-group, % of a first-round one
 #endif
 #ifndef KVC_DECODE_ODD_XCD_PCT
-#define KVC_DECODE_ODD_XCD_PCT 88    // slice of a work-group on an odd XCD, % of one on an even XCD (measured:
-                                     // 90 best for batched decode, 86 for long contexts)
+#define KVC_DECODE_ODD_XCD_PCT 90    // slice of a work-group on an odd XCD, % of one on an even XCD (measured on
+                                     // batched decode: 86 65.0, 88 64.6, 90 64.0, 93 64.3 us)
+#endif
+#ifndef KVC_DECODE_MFMA_ODD_XCD_PCT_WIDE
+#define KVC_DECODE_MFMA_ODD_XCD_PCT_WIDE 86   // the same on the matrix-core kernel for slabs of more than 16 query
+                                              // rows (32-row long context: 86 173.8, 88 175.2, 90 176.3 us)
 #endif
 
 // Rescale threshold (log2 units): the running reference max moves only when a
@@ -1668,7 +1672,8 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
     // every unit charged one tile more on the key axis (its part tiles)
     a.unit_pad = KVC_DECODE_MFMA_UNIT_PAD;
     a.total_keys += static_cast<int64_t>(a.rows) * a.Hkv * a.unit_pad;
-    split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
+    const int odd_pct = a.Gc * a.Tc > 16 ? KVC_DECODE_MFMA_ODD_XCD_PCT_WIDE : KVC_DECODE_ODD_XCD_PCT;
+    split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT, odd_pct);
     if (a.btab) {
         if ((1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks
         decode_mfma<D, ST, true><<<a.n_blocks, 64, 0, s>>>(a);

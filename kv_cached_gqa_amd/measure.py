@@ -152,20 +152,26 @@ def short_name(name: str) -> str:
 
 def read_trace(path: str) -> list[dict]:
     """Dispatches of a rocprofv3 kernel trace in start order: name, grid in
-    work-groups (x, y), work-group size, start and end (ns), queue."""
+    work-groups (x, y, z), work-group size, start and end (ns), queue."""
     out = []
     with open(path, newline="") as fh:
         for r in csv.DictReader(fh):
             wx, wy = int(r["Workgroup_Size_X"]), int(r["Workgroup_Size_Y"])
             out.append({
                 "name": short_name(r["Kernel_Name"]),
-                "grid": (int(r["Grid_Size_X"]) // max(wx, 1), int(r["Grid_Size_Y"]) // max(wy, 1)),
+                "grid": (int(r["Grid_Size_X"]) // max(wx, 1), int(r["Grid_Size_Y"]) // max(wy, 1),
+                         int(r["Grid_Size_Z"]) // max(int(r["Workgroup_Size_Z"]), 1)),
                 "wg": wx * wy * int(r["Workgroup_Size_Z"]),
                 "start": int(r["Start_Timestamp"]), "end": int(r["End_Timestamp"]),
                 "queue": r.get("Queue_Id", ""),
             })
     out.sort(key=lambda d: d["start"])
     return out
+
+
+def _grid(g: tuple) -> str:
+    """(768, 1, 1) -> '768x1', (8, 2, 32) -> '8x2x32'."""
+    return "x".join(str(v) for v in (g if g[2] > 1 else g[:2]))
 
 
 def _stats_ns(v: list[float]) -> str:
@@ -199,7 +205,7 @@ def trace_tables(path: str, tags=LIB_KERNELS) -> str:
              "Span median (ns) | Span min (ns) | Span max (ns) |",
              "|---|---|---|---|---|---|---|"]
     for key, cs in sorted(calls.items(), key=lambda kv: -len(kv[1])):
-        name = " + ".join(f"{n} ({g[0]}x{g[1]})" for n, g in key)
+        name = " + ".join(f"{n} ({_grid(g)})" for n, g in key)
         avgs = " + ".join(f"{statistics.fmean(c[k]['end'] - c[k]['start'] for c in cs):,.0f}" for k in range(len(key)))
         spans = [c[-1]["end"] - c[0]["start"] for c in cs]
         lines.append(f"| {name} | {len(cs)} | {avgs} | {statistics.fmean(spans):,.0f} | "
@@ -211,7 +217,7 @@ def trace_tables(path: str, tags=LIB_KERNELS) -> str:
     lines += ["", "| Kernel | Grid (work-groups) x work-group | Dispatches | Average (ns) | Median (ns) | Min (ns) | Max (ns) |",
               "|---|---|---|---|---|---|---|"]
     for (n, g, wg), v in sorted(per.items(), key=lambda kv: -len(kv[1])):
-        lines.append(f"| {n} | {g[0]} x {g[1]} x {wg} | {_stats_ns(v)} |")
+        lines.append(f"| {n} | {_grid(g)} x {wg} | {_stats_ns(v)} |")
     return "\n".join(lines)
 
 

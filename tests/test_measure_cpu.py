@@ -50,20 +50,21 @@ def test_trace_tables_group_calls(tmp_path):
     dec = "void kvc::(anonymous namespace)::decode_mfma<128, 2, false>(kvc::DecodeArgs)"
     comb = "void kvc::(anonymous namespace)::decode_combine<128>(kvc::DecodeArgs)"
     app = "void kvc::(anonymous namespace)::append_kernel<2, 2>(kvc::AppendArgs)"
-    rows = [(dec, 0, 60, 64, 49152, 1), (comb, 61, 65, 256, 65536, 2),      # attention: span 65
-            (dec, 100, 170, 64, 49152, 1), (comb, 171, 175, 256, 65536, 2),  # attention: span 75
-            (app, 200, 204, 256, 4096, 2), (dec, 205, 265, 64, 49152, 1), (comb, 266, 270, 256, 65536, 2)]
+    rows = [(dec, 0, 60, 64, 49152, 1, 1), (comb, 61, 65, 256, 2048, 2, 32),      # attention: span 65
+            (dec, 100, 170, 64, 49152, 1, 1), (comb, 171, 175, 256, 2048, 2, 32),  # attention: span 75
+            (app, 200, 204, 256, 4096, 2, 1), (dec, 205, 265, 64, 49152, 1, 1), (comb, 266, 270, 256, 2048, 2, 32)]
     with open(f, "w", newline="") as fh:
         w = csv.DictWriter(fh, fieldnames=cols)
         w.writeheader()
-        for name, st, en, wg, gx, gy in rows:
+        for name, st, en, wg, gx, gy, gz in rows:
             w.writerow({"Kind": "KERNEL_DISPATCH", "Queue_Id": 1, "Kernel_Name": name, "Start_Timestamp": st,
                         "End_Timestamp": en, "Workgroup_Size_X": wg, "Workgroup_Size_Y": 1, "Workgroup_Size_Z": 1,
-                        "Grid_Size_X": gx, "Grid_Size_Y": gy, "Grid_Size_Z": 1})
+                        "Grid_Size_X": gx, "Grid_Size_Y": gy, "Grid_Size_Z": gz})
     text = measure.trace_tables(str(f))
     lines = text.splitlines()
-    attn = [ln for ln in lines if ln.startswith("| decode_mfma<128, 2, false> (768x1) + decode_combine<128> (256x2)")]
+    attn = [ln for ln in lines if ln.startswith("| decode_mfma<128, 2, false> (768x1) + decode_combine<128> (8x2x32)")]
     assert len(attn) == 1 and "| 2 | 65 + 4 | 70 | 70 | 65 | 75 |" in attn[0]
     step = [ln for ln in lines if ln.startswith("| append_kernel<2, 2> (16x2) + decode_mfma")]
     assert len(step) == 1 and "| 1 | 4 + 60 + 4 | 70 |" in step[0]
-    assert any(ln.startswith("| decode_mfma<128, 2, false> | 768 x 1 x 64 | 3 |") for ln in lines)
+    assert any(ln.startswith("| decode_mfma<128, 2, false> | 768x1 x 64 | 3 |") for ln in lines)
+    assert any(ln.startswith("| decode_combine<128> | 8x2x32 x 256 | 3 |") for ln in lines)
