@@ -78,7 +78,8 @@ hipError_t run_d(DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode(DecodeArgs& a, hipStream_t s) {
     if (a.Gc * a.Tc < 1 || a.Gc * a.Tc > kMaxDecodeRows) return hipErrorInvalidValue;
     if (a.ws_rows_cap < static_cast<int64_t>(kMaxDecodeRows) * (a.rows * a.Hkv + 1)) return hipErrorInvalidValue;
-    if (a.total_keys < 1) return hipErrorInvalidValue;
+    if (a.total_keys < 1 || a.Hkv < 1) return hipErrorInvalidValue;
+    decode_set_hkv_div(a);
     switch (a.D) {
         case 32: return run_d<32>(a, s);
         case 64: return run_d<64>(a, s);

@@ -372,7 +372,7 @@ void decode_attn(DecodeArgs a) {
     const int qrow_bytes = D * (a.q_dtype == F32 ? 4 : 2);
 
     const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
-    int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
+    int64_t x_end = x_begin + decode_slice_size(a, blockIdx.x);
     if (x_end > a.total_keys) x_end = a.total_keys;
     if (x_begin >= x_end) return;
 
@@ -385,7 +385,7 @@ void decode_attn(DecodeArgs a) {
         Seg sg;
         sg.b = b;
         sg.g = g;
-        const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
+        const int64_t n_b = decode_div_hkv(a, a.prefix[b + 1] - a.prefix[b]);
         const int64_t unit_start = a.prefix[b] + static_cast<int64_t>(g) * n_b;
         int64_t seg_end = unit_start + n_b;
         if (seg_end > x_end) seg_end = x_end;
@@ -404,8 +404,8 @@ void decode_attn(DecodeArgs a) {
             const int mid = (lo + hi) >> 1;
             if (a.prefix[mid] <= x) lo = mid; else hi = mid;
         }
-        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
-        return make_seg(lo, static_cast<int>((x - a.prefix[lo]) / n_b), x);
+        const int64_t n_b = decode_div_hkv(a, a.prefix[lo + 1] - a.prefix[lo]);
+        return make_seg(lo, static_cast<int>(decode_quot(x - a.prefix[lo], n_b)), x);
     };
     // the segment after sg (which ended at its unit's end): the next unit
     auto next_seg = [&](const Seg& sg) __attribute__((always_inline)) -> Seg {
@@ -772,7 +772,7 @@ void decode_rows(DecodeArgs a) {
     const float thresh = kRescaleLog2 / c;
 
     const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
-    int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
+    int64_t x_end = x_begin + decode_slice_size(a, blockIdx.x);
     if (x_end > a.total_keys) x_end = a.total_keys;
     if (x_begin >= x_end) return;
 
@@ -787,8 +787,8 @@ void decode_rows(DecodeArgs a) {
         }
         Seg sg;
         sg.b = lo;
-        const int64_t n_b = (a.prefix[lo + 1] - a.prefix[lo]) / a.Hkv;
-        sg.g = static_cast<int>((x - a.prefix[lo]) / n_b);
+        const int64_t n_b = decode_div_hkv(a, a.prefix[lo + 1] - a.prefix[lo]);
+        sg.g = static_cast<int>(decode_quot(x - a.prefix[lo], n_b));
         const int64_t unit_start = a.prefix[lo] + static_cast<int64_t>(sg.g) * n_b;
         int64_t seg_end = unit_start + n_b;
         if (seg_end > x_end) seg_end = x_end;
@@ -1120,7 +1120,7 @@ void decode_mfma(DecodeArgs a) {
     asm volatile("" ::"s"(a.k_cache), "s"(a.keys_per_block), "s"(a.n_first), "s"(a.k_new),
                  "s"(a.prefix[kMaxRowsPerLaunch]));
     const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
-    int64_t x_end = decode_slice_begin(a, blockIdx.x + 1);
+    int64_t x_end = x_begin + decode_slice_size(a, blockIdx.x);
     if (x_end > a.total_keys) x_end = a.total_keys;
     if (x_begin >= x_end) return;
 
@@ -1131,12 +1131,12 @@ void decode_mfma(DecodeArgs a) {
     // end at p1 on the padded axis: each unit is unit_pad virtual keys, then
     // its n_b real ones; a segment that holds no real key has nbat = 0
     const int64_t row_pad = static_cast<int64_t>(a.Hkv) * a.unit_pad;
-    auto seg_at = [&](int lo, int64_t p0, int64_t p1, int64_t x) __attribute__((always_inline)) -> Seg {
+    // (unit (b, g) of a row starting at p0 whose units are n_e long, x inside it)
+    auto seg_make = [&](int b, int g, int64_t n_e, int64_t p0, int64_t x) __attribute__((always_inline)) -> Seg {
         Seg sg;
-        sg.b = lo;
-        const int64_t n_e = (p1 - p0) / a.Hkv;
-        sg.g = static_cast<int>((x - p0) / n_e);
-        const int64_t unit_start = p0 + static_cast<int64_t>(sg.g) * n_e + a.unit_pad;   // its first real key
+        sg.b = b;
+        sg.g = g;
+        const int64_t unit_start = p0 + static_cast<int64_t>(g) * n_e + a.unit_pad;   // its first real key
         int64_t seg_end = unit_start + (n_e - a.unit_pad);
         if (seg_end > x_end) seg_end = x_end;
         sg.j0 = x > unit_start ? static_cast<int>(x - unit_start) : 0;
@@ -1148,15 +1148,18 @@ void decode_mfma(DecodeArgs a) {
         sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
         return sg;
     };
+    auto seg_at = [&](int b, int64_t p0, int64_t p1, int64_t x) __attribute__((always_inline)) -> Seg {
+        const int64_t n_e = decode_div_hkv(a, p1 - p0);
+        return seg_make(b, static_cast<int>(decode_quot(x - p0, n_e)), n_e, p0, x);
+    };
     // the segment after sg, which ended at its unit's end inside the slice:
     // the next KV head of the row, or the first of the next row (whose end is
     // the one prefix entry read here)
     auto locate_next = [&](const Seg& sg) __attribute__((always_inline)) -> Seg {
         const int64_t n_e = static_cast<int64_t>(sg.n_b) + a.unit_pad;
-        const int64_t row_start = sg.x_end - static_cast<int64_t>(sg.g + 1) * n_e;
-        const int64_t row_end = row_start + static_cast<int64_t>(a.Hkv) * n_e;
-        if (sg.g + 1 < a.Hkv) return seg_at(sg.b, row_start, row_end, sg.x_end);
-        return seg_at(sg.b + 1, row_end, a.prefix[sg.b + 2] + (sg.b + 2) * row_pad, sg.x_end);
+        if (sg.g + 1 < a.Hkv) return seg_make(sg.b, sg.g + 1, n_e, sg.x_end - static_cast<int64_t>(sg.g + 1) * n_e, sg.x_end);
+        const int64_t p1 = a.prefix[sg.b + 2] + (sg.b + 2) * row_pad;
+        return seg_make(sg.b + 1, 0, decode_div_hkv(a, p1 - sg.x_end), sg.x_end, sg.x_end);
     };
     // the first segment, found without the search's chain of scalar loads
     const Seg first = [&]() __attribute__((always_inline)) {
@@ -1484,7 +1487,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     const int64_t p0 = a.prefix[b], p1 = a.prefix[b + 1];
     asm volatile("" ::"s"(p0), "s"(p1), "s"(a.k_cache), "s"(a.keys_per_block), "s"(a.n_first), "s"(a.k_new));
     const int u = b * a.Hkv + g;
-    const int64_t n_b = (p1 - p0) / a.Hkv;
+    const int64_t n_b = decode_div_hkv(a, p1 - p0);
     // the unit's first real key on the (padded) key axis
     const int64_t ustart = p0 + static_cast<int64_t>(b) * a.Hkv * a.unit_pad + g * (n_b + a.unit_pad) + a.unit_pad;
     if (a.k_new != nullptr && static_cast<int>(blockIdx.y) == a.merge_rows) {
@@ -1574,45 +1577,12 @@ hipError_t device_cus(int& n_cu) {
     return hipSuccess;
 }
 
-// Cut the key axis into work-group slices: up to per_cu work-groups per CU, at
-// least min_keys keys each, and no more records than the workspace holds.
-// Work-groups beyond the first dispatch round (one per CU) share a CU with an
-// older one, which the memory system serves first; they get a smaller slice,
-// late_pct percent of a first-round one. Work-group k runs on XCD k mod 8, and
-// the odd XCDs read HBM more slowly than the even ones: a work-group with odd
-// k gets odd_pct percent of the slice of its round.
-void split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min_keys, int late_pct, int odd_pct) {
-    int64_t nb = static_cast<int64_t>(n_cu) * per_cu;
-    if (nb > kMaxDecodeBlocks) nb = kMaxDecodeBlocks;
-    const int64_t by_ws = a.ws_rows_cap / a.rec_rows - static_cast<int64_t>(a.rows) * a.Hkv;
-    if (nb > by_ws) nb = by_ws;
-    const int64_t by_size = (a.total_keys + min_keys - 1) / min_keys;
-    if (nb > by_size) nb = by_size;
-    if (nb < 1) nb = 1;
-    const int64_t n1 = nb < n_cu ? nb : n_cu;
-    const int64_t n1e = decode_evens_below(n1), n1o = n1 - n1e;
-    const int64_t n2e = decode_evens_below(nb) - n1e, n2o = (nb - n1) - n2e;
-    // slice weights in 1/10000 of a first-round even slice
-    const int64_t w1e = 10000, w1o = 100 * odd_pct, w2e = 100 * late_pct, w2o = late_pct * odd_pct;
-    const int64_t denom = n1e * w1e + n1o * w1o + n2e * w2e + n2o * w2o;
-    const int64_t kpb = (a.total_keys * 10000 + denom - 1) / denom;
-    // each size rounded up, so that the nb slices always cover the axis
-    auto size = [&](int64_t w) { const int64_t v = (kpb * w + 9999) / 10000; return v < 1 ? int64_t(1) : v; };
-    a.keys_per_block = kpb;
-    a.keys_per_block_odd = size(w1o);
-    a.keys_per_block2 = size(w2e);
-    a.keys_per_block2_odd = size(w2o);
-    a.n_first = static_cast<int32_t>(n1);
-    // work-groups that hold keys (rounding up can leave the last ones empty)
-    a.n_blocks = static_cast<int32_t>(decode_slice_of(a, a.total_keys - 1) + 1);
-}
-
 // The merge pass, if some unit spans several work-groups.
 template <int D>
 hipError_t combine_if_split(DecodeArgs& a, hipStream_t s) {
     bool split = false;
     for (int b = 0; b < a.rows && !split; ++b) {
-        const int64_t n_b = (a.prefix[b + 1] - a.prefix[b]) / a.Hkv;
+        const int64_t n_b = decode_div_hkv(a, a.prefix[b + 1] - a.prefix[b]);
         for (int g = 0; g < a.Hkv && !split; ++g) {
             const int64_t us = a.prefix[b] + static_cast<int64_t>(b) * a.Hkv * a.unit_pad + g * (n_b + a.unit_pad) + a.unit_pad;
             split = decode_slice_of(a, us) != decode_slice_of(a, us + n_b - 1);
@@ -1633,7 +1603,7 @@ hipError_t run(DecodeArgs& a, hipStream_t s) {
     hipError_t e = device_cus(n_cu);
     if (e != hipSuccess) return e;
     a.rec_rows = R;
-    split_slices(a, n_cu, KVC_DECODE_BLOCKS_PER_CU, 2 * Cfg<D, ST, R>::KPB, KVC_DECODE_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
+    decode_split_slices(a, n_cu, KVC_DECODE_BLOCKS_PER_CU, 2 * Cfg<D, ST, R>::KPB, KVC_DECODE_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
     if (a.btab) {
         if ((1 << a.bshift) < Cfg<D, ST, R>::KPB) return hipErrorInvalidValue;   // a batch within two blocks
         decode_attn<D, ST, R, true><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
@@ -1651,7 +1621,7 @@ hipError_t run_rows(DecodeArgs& a, hipStream_t s) {
     hipError_t e = device_cus(n_cu);
     if (e != hipSuccess) return e;
     a.rec_rows = RCfg<D, ST, RS>::ROWS;
-    split_slices(a, n_cu, 2, 2 * RCfg<D, ST, RS>::KPS, KVC_DECODE_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
+    decode_split_slices(a, n_cu, 2, 2 * RCfg<D, ST, RS>::KPS, KVC_DECODE_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
     if (a.btab) {
         if ((1 << a.bshift) < RCfg<D, ST, RS>::KPS) return hipErrorInvalidValue;   // a stage within two blocks
         decode_rows<D, ST, RS, true><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
@@ -1673,7 +1643,7 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
     a.unit_pad = KVC_DECODE_MFMA_UNIT_PAD;
     a.total_keys += static_cast<int64_t>(a.rows) * a.Hkv * a.unit_pad;
     const int odd_pct = a.Gc * a.Tc > 16 ? KVC_DECODE_MFMA_ODD_XCD_PCT_WIDE : KVC_DECODE_ODD_XCD_PCT;
-    split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT, odd_pct);
+    decode_split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT, odd_pct);
     if (a.btab) {
         if ((1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks
         decode_mfma<D, ST, true><<<a.n_blocks, 64, 0, s>>>(a);

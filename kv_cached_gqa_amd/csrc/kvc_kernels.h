@@ -117,6 +117,11 @@ struct DecodeArgs {
     // cache afterwards; null: the cache already holds them
     const void* k_new;
     const void* v_new;
+    // exact division by Hkv of a multiple of it (set by launch_decode):
+    // x / Hkv = (x >> hkv_shift) * hkv_inv mod 2^64, hkv_inv the inverse of
+    // Hkv's odd part modulo 2^64
+    int32_t hkv_shift;
+    uint64_t hkv_inv;
     int64_t prefix[kMaxRowsPerLaunch + 1];  // exclusive prefix of n_b * H_kv
 };
 
@@ -171,9 +176,41 @@ struct TableSetArgs {
     int32_t value[kMaxTableSets];
 };
 hipError_t launch_table_set(const TableSetArgs& a, hipStream_t stream);
-// Decode work-group k's slice of the key axis starts at decode_slice_begin(a, k);
-// key x lies in work-group decode_slice_of(a, x)'s slice. Slice sizes alternate
-// by the parity of k (even first).
+// floor(x / d) for x >= 0, d > 0 and a quotient below 2^31: a double-precision
+// estimate (off by at most one: the operands convert with a relative error of
+// 2^-53 each and the quotient is rounded once), then the exact remainder moves
+// it by one where the estimate rounded across an integer. Some 20 instructions
+// with no branch, against the long expansion of a 64-bit integer division.
+__host__ __device__ inline int64_t decode_quot(int64_t x, int64_t d) {
+    int64_t q = static_cast<int32_t>(static_cast<double>(x) / static_cast<double>(d));
+    const int64_t r = x - q * d;
+    q += r < 0 ? -1 : (r >= d ? 1 : 0);
+    return q;
+}
+// x / Hkv for x >= 0 a multiple of Hkv.
+__host__ __device__ inline int64_t decode_div_hkv(const DecodeArgs& a, int64_t x) {
+    return static_cast<int64_t>((static_cast<uint64_t>(x) >> a.hkv_shift) * a.hkv_inv);
+}
+// hkv_shift and hkv_inv from Hkv (>= 1): Newton's iteration x <- x (2 - m x)
+// doubles the number of correct low bits of m's inverse; m odd is its own
+// inverse modulo 8, so five steps reach 96 bits.
+inline void decode_set_hkv_div(DecodeArgs& a) {
+    uint64_t m = static_cast<uint64_t>(a.Hkv);
+    int s = 0;
+    while ((m & 1) == 0) {
+        m >>= 1;
+        ++s;
+    }
+    uint64_t inv = m;
+    for (int i = 0; i < 5; ++i) inv *= 2 - m * inv;
+    a.hkv_shift = s;
+    a.hkv_inv = inv;
+}
+
+// Decode work-group k's slice of the key axis starts at decode_slice_begin(a, k)
+// and holds decode_slice_size(a, k) keys; key x lies in work-group
+// decode_slice_of(a, x)'s slice. Slice sizes alternate by the parity of k (even
+// first), and change once, at k = n_first.
 __host__ __device__ inline int64_t decode_evens_below(int64_t k) { return (k + 1) >> 1; }
 __host__ __device__ inline int64_t decode_slice_begin(const DecodeArgs& a, int64_t k) {
     const int64_t n1 = a.n_first;
@@ -185,6 +222,10 @@ __host__ __device__ inline int64_t decode_slice_begin(const DecodeArgs& a, int64
     const int64_t x1 = ne1 * a.keys_per_block + (n1 - ne1) * a.keys_per_block_odd;
     const int64_t ne = decode_evens_below(k) - ne1;
     return x1 + ne * a.keys_per_block2 + (k - n1 - ne) * a.keys_per_block2_odd;
+}
+__host__ __device__ inline int64_t decode_slice_size(const DecodeArgs& a, int64_t k) {
+    if (k < a.n_first) return (k & 1) ? a.keys_per_block_odd : a.keys_per_block;
+    return (k & 1) ? a.keys_per_block2_odd : a.keys_per_block2;
 }
 __host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t x) {
     const int64_t n1 = a.n_first;
@@ -198,8 +239,41 @@ __host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t 
         second = (n1 & 1) ? a.keys_per_block2 : a.keys_per_block2_odd;
     }
     const int64_t pair = first + second;
-    const int64_t p = x / pair;
+    const int64_t p = decode_quot(x, pair);
     return base + 2 * p + (x - p * pair >= first ? 1 : 0);
+}
+
+// Cut the key axis into work-group slices: up to per_cu work-groups per CU, at
+// least min_keys keys each, and no more records than the workspace holds.
+// Work-groups beyond the first dispatch round (one per CU) share a CU with an
+// older one, which the memory system serves first; they get a smaller slice,
+// late_pct percent of a first-round one. Work-group k runs on XCD k mod 8, and
+// the odd XCDs read HBM more slowly than the even ones: a work-group with odd
+// k gets odd_pct percent of the slice of its round.
+inline void decode_split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min_keys, int late_pct, int odd_pct) {
+    int64_t nb = static_cast<int64_t>(n_cu) * per_cu;
+    if (nb > kMaxDecodeBlocks) nb = kMaxDecodeBlocks;
+    const int64_t by_ws = a.ws_rows_cap / a.rec_rows - static_cast<int64_t>(a.rows) * a.Hkv;
+    if (nb > by_ws) nb = by_ws;
+    const int64_t by_size = (a.total_keys + min_keys - 1) / min_keys;
+    if (nb > by_size) nb = by_size;
+    if (nb < 1) nb = 1;
+    const int64_t n1 = nb < n_cu ? nb : n_cu;
+    const int64_t n1e = decode_evens_below(n1), n1o = n1 - n1e;
+    const int64_t n2e = decode_evens_below(nb) - n1e, n2o = (nb - n1) - n2e;
+    // slice weights in 1/10000 of a first-round even slice
+    const int64_t w1e = 10000, w1o = 100 * odd_pct, w2e = 100 * late_pct, w2o = late_pct * odd_pct;
+    const int64_t denom = n1e * w1e + n1o * w1o + n2e * w2e + n2o * w2o;
+    const int64_t kpb = (a.total_keys * 10000 + denom - 1) / denom;
+    // each size rounded up, so that the nb slices always cover the axis
+    auto size = [&](int64_t w) { const int64_t v = (kpb * w + 9999) / 10000; return v < 1 ? int64_t(1) : v; };
+    a.keys_per_block = kpb;
+    a.keys_per_block_odd = size(w1o);
+    a.keys_per_block2 = size(w2e);
+    a.keys_per_block2_odd = size(w2o);
+    a.n_first = static_cast<int32_t>(n1);
+    // work-groups that hold keys (rounding up can leave the last ones empty)
+    a.n_blocks = static_cast<int32_t>(decode_slice_of(a, a.total_keys - 1) + 1);
 }
 
 // Fills in the work split (n_blocks, slice sizes) from the device's resident capacity.
