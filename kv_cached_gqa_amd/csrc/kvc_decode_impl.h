@@ -280,6 +280,24 @@ __device__ __forceinline__ RowOf row_of(const PrefixLanes& p, int64_t x, int64_t
     return r;
 }
 
+// row_of for launches of fewer than 64 rows: every entry, the one past the last
+// row included, sits in the first slot.
+__device__ __forceinline__ RowOf row_of_one(int64_t e0, int64_t x, int64_t row_pad) {
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int64_t ep = e0 == INT64_MAX ? INT64_MAX : e0 + static_cast<int64_t>(lane) * row_pad;
+    RowOf r;
+    r.b = static_cast<int>(__popcll(__ballot(ep <= x))) - 1;
+    auto entry = [&](int i) __attribute__((always_inline)) -> int64_t {
+        const uint64_t u = static_cast<uint64_t>(e0);
+        const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), i);
+        const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), i);
+        return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+    };
+    r.p0 = entry(r.b) + r.b * row_pad;
+    r.p1 = entry(r.b + 1) + (r.b + 1) * row_pad;
+    return r;
+}
+
 struct Seg {
     int b, g;
     int j0, j1, n_b;
@@ -1114,14 +1132,21 @@ void decode_mfma(DecodeArgs a) {
     const float thresh = kRescaleLog2 / c;
 
     const PrefixLanes pfx = load_prefix_lanes();   // in flight while the slice is worked out
-    // one field from each 64-byte line of the arguments' scalar part, needed
-    // together here so that the lines arrive in one round trip instead of one
-    // after another as each is first used
-    asm volatile("" ::"s"(a.k_cache), "s"(a.keys_per_block), "s"(a.n_first), "s"(a.k_new),
-                 "s"(a.prefix[kMaxRowsPerLaunch]));
-    const int64_t x_begin = decode_slice_begin(a, blockIdx.x);
-    int64_t x_end = x_begin + decode_slice_size(a, blockIdx.x);
-    if (x_end > a.total_keys) x_end = a.total_keys;
+    // The scalars that locating the first segment needs, read from the
+    // arguments in one round trip and held as opaque copies (the compiler would
+    // otherwise read each again near its use, one dependent wait each), and the
+    // argument lines the first tile's addresses need, fetched in the same trip.
+    int64_t kpb = a.keys_per_block, kpbo = a.keys_per_block_odd, kpb2 = a.keys_per_block2,
+            kpb2o = a.keys_per_block2_odd, total = a.total_keys;
+    int32_t n1 = a.n_first, hkv = a.Hkv, upad = a.unit_pad, hshift = a.hkv_shift, nrows = a.rows;
+    uint64_t hinv = a.hkv_inv;
+    asm volatile("" : "+s"(kpb), "+s"(kpbo), "+s"(kpb2), "+s"(kpb2o), "+s"(total), "+s"(n1), "+s"(hkv), "+s"(upad),
+                 "+s"(hshift), "+s"(hinv), "+s"(nrows)
+                 : "s"(a.k_cache), "s"(a.v_cache), "s"(a.layer_off), "s"(a.row_stride), "s"(a.head_stride),
+                   "s"(a.T), "s"(a.row0), "s"(a.k_new), "s"(a.v_new), "s"(a.prefix[kMaxRowsPerLaunch]));
+    const int64_t x_begin = decode_slice_begin(blockIdx.x, n1, kpb, kpbo, kpb2, kpb2o);
+    int64_t x_end = x_begin + decode_slice_size(blockIdx.x, n1, kpb, kpbo, kpb2, kpb2o);
+    if (x_end > total) x_end = total;
     if (x_begin >= x_end) return;
 
     const uint16_t* kg = static_cast<const uint16_t*>(a.k_cache);
@@ -1130,41 +1155,48 @@ void decode_mfma(DecodeArgs a) {
     // the segment at padded position x of row lo, whose units start at p0 and
     // end at p1 on the padded axis: each unit is unit_pad virtual keys, then
     // its n_b real ones; a segment that holds no real key has nbat = 0
-    const int64_t row_pad = static_cast<int64_t>(a.Hkv) * a.unit_pad;
+    const int64_t row_pad = static_cast<int64_t>(hkv) * upad;
     // (unit (b, g) of a row starting at p0 whose units are n_e long, x inside it)
     auto seg_make = [&](int b, int g, int64_t n_e, int64_t p0, int64_t x) __attribute__((always_inline)) -> Seg {
         Seg sg;
         sg.b = b;
         sg.g = g;
-        const int64_t unit_start = p0 + static_cast<int64_t>(g) * n_e + a.unit_pad;   // its first real key
-        int64_t seg_end = unit_start + (n_e - a.unit_pad);
+        const int64_t unit_start = p0 + static_cast<int64_t>(g) * n_e + upad;   // its first real key
+        int64_t seg_end = unit_start + (n_e - upad);
         if (seg_end > x_end) seg_end = x_end;
         sg.j0 = x > unit_start ? static_cast<int>(x - unit_start) : 0;
         sg.j1 = static_cast<int>(seg_end - unit_start);
-        sg.n_b = static_cast<int>(n_e - a.unit_pad);
+        sg.n_b = static_cast<int>(n_e - upad);
         sg.nbat = sg.j1 > sg.j0 ? (sg.j1 - sg.j0 + kBN - 1) / kBN : 0;
         sg.head = a.layer_off + sg.b * a.row_stride + sg.g * a.head_stride;
         sg.x_end = seg_end;
         sg.rec = (sg.j0 == 0 && sg.j1 == sg.n_b) ? -1 : static_cast<int64_t>(blockIdx.x) + sg.b * a.Hkv + sg.g;
         return sg;
     };
-    auto seg_at = [&](int b, int64_t p0, int64_t p1, int64_t x) __attribute__((always_inline)) -> Seg {
-        const int64_t n_e = decode_div_hkv(a, p1 - p0);
-        return seg_make(b, static_cast<int>(decode_quot(x - p0, n_e)), n_e, p0, x);
-    };
     // the segment after sg, which ended at its unit's end inside the slice:
     // the next KV head of the row, or the first of the next row (whose end is
     // the one prefix entry read here)
     auto locate_next = [&](const Seg& sg) __attribute__((always_inline)) -> Seg {
-        const int64_t n_e = static_cast<int64_t>(sg.n_b) + a.unit_pad;
-        if (sg.g + 1 < a.Hkv) return seg_make(sg.b, sg.g + 1, n_e, sg.x_end - static_cast<int64_t>(sg.g + 1) * n_e, sg.x_end);
+        const int64_t n_e = static_cast<int64_t>(sg.n_b) + upad;
+        if (sg.g + 1 < hkv) return seg_make(sg.b, sg.g + 1, n_e, sg.x_end - static_cast<int64_t>(sg.g + 1) * n_e, sg.x_end);
         const int64_t p1 = a.prefix[sg.b + 2] + (sg.b + 2) * row_pad;
-        return seg_make(sg.b + 1, 0, decode_div_hkv(a, p1 - sg.x_end), sg.x_end, sg.x_end);
+        return seg_make(sg.b + 1, 0, decode_div_exact(p1 - sg.x_end, hshift, hinv), sg.x_end, sg.x_end);
     };
-    // the first segment, found without the search's chain of scalar loads
+    // the first segment, found without a search's chain of scalar loads: its
+    // row from the prefix entries' ballots, its KV head g from a ballot of
+    // l * n_e <= x - p0 over lanes l = 1 .. Hkv - 1 (a division past 64 heads)
     const Seg first = [&]() __attribute__((always_inline)) {
-        const RowOf r = row_of(pfx, x_begin, row_pad);
-        return seg_at(r.b, r.p0, r.p1, x_begin);
+        const RowOf r = nrows < 64 ? row_of_one(pfx.e[0], x_begin, row_pad) : row_of(pfx, x_begin, row_pad);
+        const int64_t n_e = decode_div_exact(r.p1 - r.p0, hshift, hinv);
+        const int64_t dx = x_begin - r.p0;
+        int g;
+        if (hkv <= 64) {
+            const int l = static_cast<int>(threadIdx.x) & 63;
+            g = static_cast<int>(__popcll(__ballot(l >= 1 && l < hkv && static_cast<int64_t>(l) * n_e <= dx)));
+        } else {
+            g = static_cast<int>(decode_quot(dx, n_e));
+        }
+        return seg_make(r.b, g, n_e, r.p0, x_begin);
     }();
     if (first.nbat == 0) return;   // a slice of virtual keys only
 

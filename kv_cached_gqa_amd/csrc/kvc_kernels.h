@@ -188,8 +188,11 @@ __host__ __device__ inline int64_t decode_quot(int64_t x, int64_t d) {
     return q;
 }
 // x / Hkv for x >= 0 a multiple of Hkv.
+__host__ __device__ inline int64_t decode_div_exact(int64_t x, int shift, uint64_t inv) {
+    return static_cast<int64_t>((static_cast<uint64_t>(x) >> shift) * inv);
+}
 __host__ __device__ inline int64_t decode_div_hkv(const DecodeArgs& a, int64_t x) {
-    return static_cast<int64_t>((static_cast<uint64_t>(x) >> a.hkv_shift) * a.hkv_inv);
+    return decode_div_exact(x, a.hkv_shift, a.hkv_inv);
 }
 // hkv_shift and hkv_inv from Hkv (>= 1): Newton's iteration x <- x (2 - m x)
 // doubles the number of correct low bits of m's inverse; m odd is its own
@@ -212,20 +215,30 @@ inline void decode_set_hkv_div(DecodeArgs& a) {
 // decode_slice_of(a, x)'s slice. Slice sizes alternate by the parity of k (even
 // first), and change once, at k = n_first.
 __host__ __device__ inline int64_t decode_evens_below(int64_t k) { return (k + 1) >> 1; }
-__host__ __device__ inline int64_t decode_slice_begin(const DecodeArgs& a, int64_t k) {
-    const int64_t n1 = a.n_first;
+// (the same on the split's five values: n_first and the four slice sizes)
+__host__ __device__ inline int64_t decode_slice_begin(int64_t k, int64_t n1, int64_t kpb, int64_t kpbo, int64_t kpb2,
+                                                      int64_t kpb2o) {
     if (k <= n1) {
         const int64_t ne = decode_evens_below(k);
-        return ne * a.keys_per_block + (k - ne) * a.keys_per_block_odd;
+        return ne * kpb + (k - ne) * kpbo;
     }
     const int64_t ne1 = decode_evens_below(n1);
-    const int64_t x1 = ne1 * a.keys_per_block + (n1 - ne1) * a.keys_per_block_odd;
+    const int64_t x1 = ne1 * kpb + (n1 - ne1) * kpbo;
     const int64_t ne = decode_evens_below(k) - ne1;
-    return x1 + ne * a.keys_per_block2 + (k - n1 - ne) * a.keys_per_block2_odd;
+    return x1 + ne * kpb2 + (k - n1 - ne) * kpb2o;
+}
+__host__ __device__ inline int64_t decode_slice_size(int64_t k, int64_t n1, int64_t kpb, int64_t kpbo, int64_t kpb2,
+                                                     int64_t kpb2o) {
+    if (k < n1) return (k & 1) ? kpbo : kpb;
+    return (k & 1) ? kpb2o : kpb2;
+}
+__host__ __device__ inline int64_t decode_slice_begin(const DecodeArgs& a, int64_t k) {
+    return decode_slice_begin(k, a.n_first, a.keys_per_block, a.keys_per_block_odd, a.keys_per_block2,
+                              a.keys_per_block2_odd);
 }
 __host__ __device__ inline int64_t decode_slice_size(const DecodeArgs& a, int64_t k) {
-    if (k < a.n_first) return (k & 1) ? a.keys_per_block_odd : a.keys_per_block;
-    return (k & 1) ? a.keys_per_block2_odd : a.keys_per_block2;
+    return decode_slice_size(k, a.n_first, a.keys_per_block, a.keys_per_block_odd, a.keys_per_block2,
+                             a.keys_per_block2_odd);
 }
 __host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t x) {
     const int64_t n1 = a.n_first;
