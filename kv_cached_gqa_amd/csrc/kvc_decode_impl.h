@@ -1512,23 +1512,33 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     constexpr int kMaxSeg = 16;
     // grid (H_kv, rows of 256 outputs [+ the store row], batch rows): the row
-    // b is known without the arguments, so its prefix entries and the argument
-    // lines used below are fetched in one round trip
+    // b is known without the arguments, so its prefix entries and every
+    // argument used below are fetched in one round trip, and held as opaque
+    // copies (the compiler would otherwise read some again near their use,
+    // one dependent wait each)
     const int g = blockIdx.x;
     const int b = blockIdx.z;
-    const int64_t p0 = a.prefix[b], p1 = a.prefix[b + 1];
-    asm volatile("" ::"s"(p0), "s"(p1), "s"(a.k_cache), "s"(a.keys_per_block), "s"(a.n_first), "s"(a.k_new));
-    const int u = b * a.Hkv + g;
-    const int64_t n_b = decode_div_hkv(a, p1 - p0);
+    int64_t p0 = a.prefix[b], p1 = a.prefix[b + 1];
+    int64_t kpb = a.keys_per_block, kpbo = a.keys_per_block_odd, kpb2 = a.keys_per_block2,
+            kpb2o = a.keys_per_block2_odd;
+    float pinv = a.pair_inv, pinv2 = a.pair2_inv;
+    int32_t n1 = a.n_first, hkv = a.Hkv, upad = a.unit_pad, hshift = a.hkv_shift, mrows = a.merge_rows;
+    uint64_t hinv = a.hkv_inv;
+    const void* knew = a.k_new;
+    asm volatile("" : "+s"(p0), "+s"(p1), "+s"(kpb), "+s"(kpbo), "+s"(kpb2), "+s"(kpb2o), "+s"(pinv), "+s"(pinv2),
+                 "+s"(n1), "+s"(hkv), "+s"(upad), "+s"(hshift), "+s"(mrows), "+s"(hinv), "+s"(knew)
+                 : "s"(a.ws_o), "s"(a.ws_ml), "s"(a.rec_rows), "s"(a.out), "s"(a.Gc), "s"(a.Tc), "s"(a.scale_log2));
+    const int u = b * hkv + g;
+    const int64_t n_b = decode_div_exact(p1 - p0, hshift, hinv);
     // the unit's first real key on the (padded) key axis
-    const int64_t ustart = p0 + static_cast<int64_t>(b) * a.Hkv * a.unit_pad + g * (n_b + a.unit_pad) + a.unit_pad;
-    if (a.k_new != nullptr && static_cast<int>(blockIdx.y) == a.merge_rows) {
+    const int64_t ustart = p0 + static_cast<int64_t>(b) * hkv * upad + g * (n_b + upad) + upad;
+    if (knew != nullptr && static_cast<int>(blockIdx.y) == mrows) {
         // fused append: store unit (b, g)'s T new keys and values at slots
         // n_b - T .. n_b - 1 (the input has the storage type: bit copies, with a
         // 16-bit NaN stored as the canonical quiet NaN of its sign, as the
         // append kernel's rounding stores it)
         const int esz = a.st_dtype == F32 ? 4 : 2;
-        const int64_t src0 = ((static_cast<int64_t>(a.row0 + b) * a.Hkv + g) * a.T) * D;
+        const int64_t src0 = ((static_cast<int64_t>(a.row0 + b) * hkv + g) * a.T) * D;
         for (int e = threadIdx.x; e < a.T * D; e += 256) {
             const int t = e / D, d = e - (e / D) * D;
             const int64_t p = n_b - a.T + t;
@@ -1536,12 +1546,12 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
             if (a.btab != nullptr) {
                 int blk = a.btab[static_cast<int64_t>(b) * a.btab_stride + (p >> a.bshift)];
                 blk = blk < 0 ? 0 : (blk >= a.pool_blocks ? a.pool_blocks - 1 : blk);
-                dst = a.layer_off + (((static_cast<int64_t>(blk) * a.Hkv + g) << a.bshift) + (p & ((1 << a.bshift) - 1))) * D + d;
+                dst = a.layer_off + (((static_cast<int64_t>(blk) * hkv + g) << a.bshift) + (p & ((1 << a.bshift) - 1))) * D + d;
             } else {
                 dst = a.layer_off + b * a.row_stride + g * a.head_stride + p * D + d;
             }
             if (esz == 4) {
-                static_cast<float*>(const_cast<void*>(a.k_cache))[dst] = static_cast<const float*>(a.k_new)[src0 + e];
+                static_cast<float*>(const_cast<void*>(a.k_cache))[dst] = static_cast<const float*>(knew)[src0 + e];
                 static_cast<float*>(const_cast<void*>(a.v_cache))[dst] = static_cast<const float*>(a.v_new)[src0 + e];
             } else {
                 const uint32_t inf = a.st_dtype == BF16 ? 0x7F80u : 0x7C00u;
@@ -1550,42 +1560,52 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
                     return static_cast<uint16_t>((h & 0x7FFFu) > inf ? (h & 0x8000u) | qnan : h);
                 };
                 static_cast<uint16_t*>(const_cast<void*>(a.k_cache))[dst] =
-                    canon(static_cast<const uint16_t*>(a.k_new)[src0 + e]);
+                    canon(static_cast<const uint16_t*>(knew)[src0 + e]);
                 static_cast<uint16_t*>(const_cast<void*>(a.v_cache))[dst] =
                     canon(static_cast<const uint16_t*>(a.v_new)[src0 + e]);
             }
         }
         return;
     }
-    const int k_first = static_cast<int>(decode_slice_of(a, ustart));
-    const int k_last = static_cast<int>(decode_slice_of(a, ustart + n_b - 1));
+    const int k_first = static_cast<int>(decode_slice_of(ustart, n1, kpb, kpbo, kpb2, kpb2o, pinv, pinv2));
+    const int k_last = static_cast<int>(decode_slice_of(ustart + n_b - 1, n1, kpb, kpbo, kpb2, kpb2o, pinv, pinv2));
     if (k_first == k_last) return;
     const int idx = static_cast<int>(blockIdx.y) * 256 + static_cast<int>(threadIdx.x);
     if (idx >= a.Gc * a.Tc * D) return;
     const float c = a.scale_log2;
     const int r = idx / D, d = idx - (idx / D) * D;
+    // the unit's records k_first + u .. k_last + u, one apart, each rec_rows
+    // rows of D outputs and of a (max, sum) pair
+    const int n = k_last - k_first + 1;
+    const int64_t rec0 = static_cast<int64_t>(k_first + u) * a.rec_rows + r;
+    const float* po = a.ws_o + rec0 * D + d;
+    const float2* pml = reinterpret_cast<const float2*>(a.ws_ml) + rec0;
+    const int64_t so = static_cast<int64_t>(a.rec_rows) * D;
     float M = -INFINITY, ov = 0.f, lv = 0.f;
-    for (int k0 = k_first; k0 <= k_last; k0 += kMaxSeg) {
-        float mk[kMaxSeg], lk[kMaxSeg], okv[kMaxSeg];
+    for (int t0 = 0; t0 < n; t0 += kMaxSeg) {
+        float2 ml[kMaxSeg];
+        float ok[kMaxSeg];
 #pragma unroll
         for (int t = 0; t < kMaxSeg; ++t) {
-            const int k = k0 + t;
-            const int64_t rec = static_cast<int64_t>((k <= k_last ? k : k_last) + u) * a.rec_rows + r;
-            mk[t] = k <= k_last ? a.ws_ml[rec * 2] : -INFINITY;
-            lk[t] = a.ws_ml[rec * 2 + 1];
-            okv[t] = a.ws_o[rec * D + d];
+            if (t0 + t < n) {
+                ml[t] = pml[static_cast<int64_t>(t0 + t) * a.rec_rows];
+                ok[t] = po[(t0 + t) * so];
+            } else {
+                ml[t] = make_float2(-INFINITY, 0.f);
+                ok[t] = 0.f;
+            }
         }
         float Mn = M;
 #pragma unroll
-        for (int t = 0; t < kMaxSeg; ++t) Mn = fmaxf(Mn, mk[t]);
+        for (int t = 0; t < kMaxSeg; ++t) Mn = fmaxf(Mn, ml[t].x);
         const float sc = M == -INFINITY ? 0.f : fexp2((M - Mn) * c);
         ov *= sc;
         lv *= sc;
 #pragma unroll
         for (int t = 0; t < kMaxSeg; ++t) {
-            const float f = mk[t] == -INFINITY ? 0.f : fexp2((mk[t] - Mn) * c);
-            ov = fmaf(okv[t], f, ov);
-            lv = fmaf(lk[t], f, lv);
+            const float f = ml[t].x == -INFINITY ? 0.f : fexp2((ml[t].x - Mn) * c);
+            ov = fmaf(ok[t], f, ov);
+            lv = fmaf(ml[t].y, f, lv);
         }
         M = Mn;
     }

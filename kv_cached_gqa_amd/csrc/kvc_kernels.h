@@ -91,6 +91,9 @@ struct DecodeArgs {
     int64_t keys_per_block_odd;
     int64_t keys_per_block2;
     int64_t keys_per_block2_odd;
+    // 1 / (keys_per_block + keys_per_block_odd) and the same for the later
+    // pair, rounded to float: decode_slice_of's quotient estimates
+    float pair_inv, pair2_inv;
     int32_t n_first;
     int32_t row0, rows;      // batch rows of this launch
     int32_t Hq, Hkv, G, T;   // T = query positions in the chunk
@@ -187,6 +190,17 @@ __host__ __device__ inline int64_t decode_quot(int64_t x, int64_t d) {
     q += r < 0 ? -1 : (r >= d ? 1 : 0);
     return q;
 }
+// floor(x / d) for x >= 0, d > 0 and a quotient below 2^20, from inv = 1 / d
+// rounded to float: the estimate's relative error is at most about 2^-22 (d and
+// x rounded to float, the reciprocal and the product rounded, 2^-24 each),
+// under a quarter at such quotients, and the exact remainder corrects it by
+// one where it fell across an integer.
+__host__ __device__ inline int64_t decode_quot_rcp(int64_t x, int64_t d, float inv) {
+    int64_t q = static_cast<int32_t>(static_cast<float>(x) * inv);
+    const int64_t r = x - q * d;
+    q += r < 0 ? -1 : (r >= d ? 1 : 0);
+    return q;
+}
 // x / Hkv for x >= 0 a multiple of Hkv.
 __host__ __device__ inline int64_t decode_div_exact(int64_t x, int shift, uint64_t inv) {
     return static_cast<int64_t>((static_cast<uint64_t>(x) >> shift) * inv);
@@ -240,20 +254,27 @@ __host__ __device__ inline int64_t decode_slice_size(const DecodeArgs& a, int64_
     return decode_slice_size(k, a.n_first, a.keys_per_block, a.keys_per_block_odd, a.keys_per_block2,
                              a.keys_per_block2_odd);
 }
-__host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t x) {
-    const int64_t n1 = a.n_first;
-    const int64_t x1 = decode_slice_begin(a, n1);
-    int64_t base = 0, first = a.keys_per_block, second = a.keys_per_block_odd;
+__host__ __device__ inline int64_t decode_slice_of(int64_t x, int64_t n1, int64_t kpb, int64_t kpbo, int64_t kpb2,
+                                                   int64_t kpb2o, float pair_inv, float pair2_inv) {
+    const int64_t x1 = decode_slice_begin(n1, n1, kpb, kpbo, kpb2, kpb2o);
+    int64_t base = 0, first = kpb, second = kpbo;
+    float inv = pair_inv;
     if (x >= x1) {
         // the later slices start at index n1; a pair is (even, odd) from an even n1
         base = n1;
         x -= x1;
-        first = (n1 & 1) ? a.keys_per_block2_odd : a.keys_per_block2;
-        second = (n1 & 1) ? a.keys_per_block2 : a.keys_per_block2_odd;
+        first = (n1 & 1) ? kpb2o : kpb2;
+        second = (n1 & 1) ? kpb2 : kpb2o;
+        inv = pair2_inv;
     }
+    // (pairs on the axis: fewer than kMaxDecodeBlocks)
     const int64_t pair = first + second;
-    const int64_t p = decode_quot(x, pair);
+    const int64_t p = decode_quot_rcp(x, pair, inv);
     return base + 2 * p + (x - p * pair >= first ? 1 : 0);
+}
+__host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t x) {
+    return decode_slice_of(x, a.n_first, a.keys_per_block, a.keys_per_block_odd, a.keys_per_block2,
+                           a.keys_per_block2_odd, a.pair_inv, a.pair2_inv);
 }
 
 // Cut the key axis into work-group slices: up to per_cu work-groups per CU, at
@@ -284,6 +305,8 @@ inline void decode_split_slices(DecodeArgs& a, int n_cu, int per_cu, int64_t min
     a.keys_per_block_odd = size(w1o);
     a.keys_per_block2 = size(w2e);
     a.keys_per_block2_odd = size(w2o);
+    a.pair_inv = 1.0f / static_cast<float>(a.keys_per_block + a.keys_per_block_odd);
+    a.pair2_inv = 1.0f / static_cast<float>(a.keys_per_block2 + a.keys_per_block2_odd);
     a.n_first = static_cast<int32_t>(n1);
     // work-groups that hold keys (rounding up can leave the last ones empty)
     a.n_blocks = static_cast<int32_t>(decode_slice_of(a, a.total_keys - 1) + 1);
