@@ -288,6 +288,57 @@ def test_batch_wider_than_one_launch():
     assert cache_bits_equal(cache, orc)
 
 
+def test_decode_more_kv_heads_than_a_wave_has_lanes():
+    """80 and 130 KV heads: a decode work-group finds the KV head of its first
+    key by a division instead of a ballot over the wave's 64 lanes (1 and 8
+    query rows per KV head on the matrix-core kernel, 1 row on the vector
+    kernel of an fp32 cache), on a contiguous and a paged cache (bit-identical
+    to each other), and through the fused call (bit-identical to the two calls)."""
+    from kv_cached_gqa_amd.kvc import KVCache, PagedKVCache
+    rng = np.random.default_rng(1300)
+    #        dtype   D   B  Hq   Hkv  T  context lengths before the chunk
+    cases = (("bf16", 64, 3, 80, 80, 1, (700, 64, 1500)),
+             ("fp16", 64, 2, 260, 130, 4, (900, 333)),
+             ("fp32", 32, 2, 80, 80, 1, (500, 1200)))
+    for (dtype, D, B, Hq, Hkv, T, lens) in cases:
+        log(f"  {dtype} D={D} B={B} Hq={Hq} Hkv={Hkv} T={T}")
+        lens = np.array(lens)
+        max_len = int(lens.max()) + 2 * T
+        n0 = int(lens.max())
+        caches = [KVCache(1, Hkv, D, max_len, batch=B, n_q_heads=Hq, dtype=dtype, device=DEV),
+                  PagedKVCache(1, Hkv, D, max_len, batch=B, n_q_heads=Hq, dtype=dtype, device=DEV, block_size=64),
+                  KVCache(1, Hkv, D, max_len, batch=B, n_q_heads=Hq, dtype=dtype, device=DEV)]
+        orc = OracleCache(1, B, Hq, Hkv, D, max_len, dtype)
+        k, v = (rng.standard_normal((B, Hkv, n0, D), dtype=np.float32) for _ in range(2))
+        for c in caches:
+            c.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
+            c.truncate(lens)
+        orc.append(0, k, v)
+        orc.truncate(lens)
+        q, k, v = (rng.standard_normal(sh, dtype=np.float32) for sh in ((B, Hq, T, D), (B, Hkv, T, D), (B, Hkv, T, D)))
+        q *= 2.0
+        outs = []
+        for c in caches[:2]:
+            c.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
+            outs.append(c.attend(0, to_device(q, "fp32", DEV)).cpu().numpy())
+        # the fused call takes the chunk in the storage type
+        fused = caches[2].append_attend(0, to_device(round_to_storage(k, dtype), dtype, DEV),
+                                        to_device(round_to_storage(v, dtype), dtype, DEV),
+                                        to_device(q, "fp32", DEV)).cpu().numpy()
+        orc.append(0, k, v)
+        want = orc.attend(0, q)
+        mabs, rel = compare_out(outs[0], want, dtype)
+        log(f"    rel {rel:.2e} max abs {mabs:.2e}")
+        assert np.isfinite(outs[0]).all()
+        if dtype == "fp32":
+            assert mabs <= FP32_MAX_ABS, mabs
+        else:
+            assert rel <= HALF_REL_FROB, rel
+        assert np.array_equal(outs[0], outs[1]), "paged differs from contiguous"
+        assert np.array_equal(outs[0], fused), "fused call differs from the two calls"
+        assert cache_bits_equal(caches[0], orc) and cache_bits_equal(caches[2], orc)
+
+
 @pytest.mark.parametrize("st", ["fp16", "bf16"])
 def test_q_dtype_rule(st):
     """An fp32 q for a 16-bit cache is rounded to the storage type first: the
