@@ -1266,6 +1266,19 @@ void decode_mfma(DecodeArgs a) {
         pg_next = pg_phys(pg_blk + 1);
     };
     if constexpr (PAGED) pg_enter();
+    // byte offsets, inside a tile, of this lane's 16 bytes of each load (D =
+    // 128: load n covers rows 4n .. 4n + 3; the K chunks' swizzle repeats
+    // every 4 loads, so ko4[n % 4] + (n / 4) * 4096 is load n's; the V
+    // permutation depends on the row mod 4 only, so vo0 + 1024 n is)
+    uint32_t ko4[4], vo0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int e = m * 512 + lane * 8;
+        const int r = e / D;
+        const int sl = (e % D) >> 3;
+        ko4[m] = static_cast<uint32_t>(r * D + P::kslot(r, sl) * 8) * 2u;
+        if (m == 0) vo0 = static_cast<uint32_t>(r * D + P::vchunk(r, sl) * 8) * 2u;
+    }
     auto issue = [&](auto slot_c) __attribute__((always_inline)) {
         constexpr int S = decltype(slot_c)::value;
         if (!is_live) return;
@@ -1282,12 +1295,50 @@ void decode_mfma(DecodeArgs a) {
         // a fused append's new keys (the unit's last T) sit in its last tile at
         // most: only a tile that reaches them selects an address per lane
         const bool new_keys = a.k_new != nullptr && is.j0 + (is_t + 1) * kBN > is.n_b - a.T;
+        const int j0t = is.j0 + is_t * kBN;
+        bool whole = j0t + kBN <= is.j1 && !new_keys;    // 32 keys of the cache, no row clamped
+        if constexpr (PAGED) whole = whole && ((j0t + kBN - 1) >> a.bshift) == (j0t >> a.bshift);
+        if (whole) {
+            // the tile's rows are consecutive: one uniform base per tensor, and
+            // a 32-bit offset per lane and load (the same for every tile)
+            int64_t tb;
+            if constexpr (PAGED)
+                tb = ((j0t >> a.bshift) == pg_blk ? pg_base : pg_next) +
+                     static_cast<int64_t>(j0t & ((1 << a.bshift) - 1)) * D;
+            else
+                tb = is.head + static_cast<int64_t>(j0t) * D;
+            const char* kb = reinterpret_cast<const char*>(kg + tb);
+            const char* vb = reinterpret_cast<const char*>(vg + tb);
 #pragma unroll
-        for (int n = 0; n < NLD; ++n) {
+            for (int n = 0; n < NLD; ++n) {
+                uint32_t ko, vo;
+                if constexpr (D == 128) {
+                    ko = ko4[n & 3];
+                    vo = vo0;
+                } else {
+                    const int e = n * 512 + lane * 8;
+                    const int r = e / D;
+                    const int sl = (e % D) >> 3;
+                    ko = static_cast<uint32_t>(r * D + P::kslot(r, sl) * 8) * 2u;
+                    vo = static_cast<uint32_t>(r * D + P::vchunk(r, sl) * 8) * 2u;
+                }
+                // (D = 128: the uniform part of each load's address first)
+                const char* kbn = D == 128 ? kb + (n >> 2) * 4096 : kb;
+                const char* vbn = D == 128 ? vb + n * 1024 : vb;
+                __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kbn + ko),
+                                                 (void __attribute__((address_space(3)))*)(kd + n * 512), 16, 0,
+                                                 KVC_DECODE_MFMA_KV_CPOL);
+                __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vbn + vo),
+                                                 (void __attribute__((address_space(3)))*)(vd + n * 512), 16, 0,
+                                                 KVC_DECODE_MFMA_KV_CPOL);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NLD && !whole; ++n) {
             const int e = n * 512 + lane * 8;    // element offset inside the tile
             const int r = e / D;
             const int sl = (e % D) >> 3;
-            int j = is.j0 + is_t * kBN + r;
+            int j = j0t + r;
             j = j < is.j1 ? j : is.j1 - 1;
             int64_t row;
             if constexpr (PAGED)
