@@ -4,7 +4,9 @@
 
 Every HIP source is compiled with packed-FP32 instructions disabled; the
 objects go to kv_cached_gqa_amd/_build/ and the library to
-kv_cached_gqa_amd/libkvc.so.
+kv_cached_gqa_amd/libkvc.so. KVC_BUILD_DEFINES (space-separated NAME=VALUE)
+adds preprocessor definitions to every source (the timestamp probe of
+kv_cached_gqa_amd.probe builds a copy of the package with one).
 """
 from __future__ import annotations
 
@@ -25,7 +27,8 @@ ARCH = "gfx950"
 # the decode kernels compile per (head dimension, storage type), in parallel
 DECODE_UNITS = [f"kvc_decode_d{d}_{t}.hip" for d in (128, 64, 32) for t in ("bf16", "f16", "f32")]
 SOURCES = [*DECODE_UNITS, "kvc_prefill.hip", "kvc_append.hip", "kvc_decode.hip", "kvc_api.cpp", "kvc_latent.cpp"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}",
+          *[f"-D{d}" for d in os.environ.get("KVC_BUILD_DEFINES", "").split()]]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

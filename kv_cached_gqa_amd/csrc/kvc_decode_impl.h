@@ -1083,6 +1083,26 @@ void decode_rows(DecodeArgs a) {
 #ifndef KVC_DECODE_MFMA_MIN_ROWS
 #define KVC_DECODE_MFMA_MIN_ROWS 1    // 16-bit slabs with fewer rows run on the vector kernel
 #endif
+#ifndef KVC_DECODE_TIMESTAMPS
+#define KVC_DECODE_TIMESTAMPS 0   // 1: per-work-group timestamps for kv_cached_gqa_amd.probe (never in the library)
+#endif
+#if KVC_DECODE_TIMESTAMPS
+// Timestamp probe: per matrix-core decode work-group its start, first segment
+// located, first tile issued and end (s_memrealtime, 100 MHz), its XCC and
+// hardware ids and its slice's keys; per merge block its start, contributors
+// known, records merged and end. Each launch overwrites what it records.
+constexpr int kProbeMergeBlocks = 16384;
+static __device__ unsigned long long kvc_probe_wg[kMaxDecodeBlocks * 6];
+static __device__ unsigned long long kvc_probe_merge[kProbeMergeBlocks * 4];
+__device__ __forceinline__ unsigned long long probe_now() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ unsigned long long probe_ids() {
+    unsigned x, h;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(h));
+    return (static_cast<unsigned long long>(x) << 32) | h;
+}
+#endif
+
 #ifndef KVC_DECODE_MFMA_UNIT_PAD
 // virtual keys charged to every unit on the key axis: a work-group whose slice
 // holds a unit boundary streams a part tile on each side of it, about one tile
@@ -1131,6 +1151,9 @@ void decode_mfma(DecodeArgs a) {
     const float c = a.scale_log2;
     const float thresh = kRescaleLog2 / c;
 
+#if KVC_DECODE_TIMESTAMPS
+    const unsigned long long pt_start = probe_now();
+#endif
     const PrefixLanes pfx = load_prefix_lanes();   // in flight while the slice is worked out
     // The scalars that locating the first segment needs, read from the
     // arguments in one round trip and held as opaque copies (the compiler would
@@ -1199,6 +1222,9 @@ void decode_mfma(DecodeArgs a) {
         return seg_make(r.b, g, n_e, r.p0, x_begin);
     }();
     if (first.nbat == 0) return;   // a slice of virtual keys only
+#if KVC_DECODE_TIMESTAMPS
+    const unsigned long long pt_located = probe_now();
+#endif
 
     // -- the query table: 32 columns (slab rows; past the slab zero) per segment,
     //    rounded to the storage type --
@@ -1516,6 +1542,9 @@ void decode_mfma(DecodeArgs a) {
 
     // -- the loop: tile t in slot t % NS, NS - 1 tiles issued ahead --
     static_for<NS - 1>([&](auto k) { issue(k); });
+#if KVC_DECODE_TIMESTAMPS
+    const unsigned long long pt_issued = probe_now();
+#endif
     load_qtab(first);
     start_segment();
     bool done = false;
@@ -1553,6 +1582,17 @@ void decode_mfma(DecodeArgs a) {
         });
     }
     wait_vm<0>();
+#if KVC_DECODE_TIMESTAMPS
+    if (lane == 0) {
+        unsigned long long* w = kvc_probe_wg + static_cast<int64_t>(blockIdx.x) * 6;
+        w[0] = pt_start;
+        w[1] = pt_located;
+        w[2] = pt_issued;
+        w[3] = probe_now();
+        w[4] = probe_ids();
+        w[5] = static_cast<unsigned long long>(x_end - x_begin);
+    }
+#endif
 }
 
 // Merge the partial records of units whose keys span several work-groups
@@ -1567,6 +1607,9 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     // argument used below are fetched in one round trip, and held as opaque
     // copies (the compiler would otherwise read some again near their use,
     // one dependent wait each)
+#if KVC_DECODE_TIMESTAMPS
+    const unsigned long long pt_start = probe_now();
+#endif
     const int g = blockIdx.x;
     const int b = blockIdx.z;
     int64_t p0 = a.prefix[b], p1 = a.prefix[b + 1];
@@ -1620,6 +1663,9 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
     }
     const int k_first = static_cast<int>(decode_slice_of(ustart, n1, kpb, kpbo, kpb2, kpb2o, pinv, pinv2));
     const int k_last = static_cast<int>(decode_slice_of(ustart + n_b - 1, n1, kpb, kpbo, kpb2, kpb2o, pinv, pinv2));
+#if KVC_DECODE_TIMESTAMPS
+    const unsigned long long pt_known = probe_now();
+#endif
     if (k_first == k_last) return;
     const int idx = static_cast<int>(blockIdx.y) * 256 + static_cast<int>(threadIdx.x);
     if (idx >= a.Gc * a.Tc * D) return;
@@ -1660,9 +1706,22 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
         }
         M = Mn;
     }
+#if KVC_DECODE_TIMESTAMPS
+    const unsigned long long pt_merged = probe_now();
+#endif
     const int h = g * a.G + a.r0 + r / a.Tc;
     const int i = a.i0 + r % a.Tc;
     a.out[((static_cast<int64_t>(a.row0 + b) * a.Hq + h) * a.T + i) * D + d] = ov / lv;
+#if KVC_DECODE_TIMESTAMPS
+    const unsigned bid = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    if (threadIdx.x == 0 && bid < kProbeMergeBlocks) {
+        unsigned long long* w = kvc_probe_merge + static_cast<int64_t>(bid) * 4;
+        w[0] = pt_start;
+        w[1] = pt_known;
+        w[2] = pt_merged;
+        w[3] = probe_now();
+    }
+#endif
 }
 
 // CUs of the current device (cached per device).

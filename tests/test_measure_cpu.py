@@ -5,6 +5,8 @@ figure is used only while the decode sources are the ones it was taken on."""
 import csv
 import os
 
+import numpy as np
+
 from kv_cached_gqa_amd import measure
 
 
@@ -68,3 +70,32 @@ def test_trace_tables_group_calls(tmp_path):
     assert len(step) == 1 and "| 1 | 4 + 60 + 4 | 70 |" in step[0]
     assert any(ln.startswith("| decode_mfma<128, 2, false> | 768x1 x 64 | 3 |") for ln in lines)
     assert any(ln.startswith("| decode_combine<128> | 8x2x32 x 256 | 3 |") for ln in lines)
+
+
+def test_probe_summary_on_synthetic_records():
+    """The timestamp probe's summary: phases from the records, per-XCD rates,
+    and the share of the end-time spread the XCD accounts for (here the whole
+    of it: every work-group of XCD x ends x microseconds after the others')."""
+    from kv_cached_gqa_amd import probe
+    rng = np.random.default_rng(0)
+    bursts = []
+    for _ in range(3):
+        wg, merge = [], []
+        for k in range(64):
+            x = k % 8
+            start = 1000 + int(rng.integers(0, 20))
+            end = 1000 + 5000 + 100 * x
+            ids = (x << 32) | ((k // 8) << 8)
+            wg.append([start, start + 50, start + 110, end, ids, 900])
+        for j in range(16):
+            merge.append([6800 + j, 6900 + j, 7000 + j, 7020 + j])
+        bursts.append({"wg": wg, "merge": merge})
+    text = probe.summarize(bursts)
+    lines = text.splitlines()
+    first = [ln for ln in lines if ln.startswith("| 0 | 64 |")]
+    assert len(first) == 1
+    cells = [c.strip() for c in first[0].strip("|").split("|")]
+    assert cells[3] == "0.50" and cells[4] == "1.10"          # located, issued (us after start)
+    assert float(cells[7]) > 0                                 # the merge starts after the last work-group
+    assert any(ln.startswith("| 7 |") for ln in lines)
+    assert "the XCD accounts for 100% of the variance" in text
