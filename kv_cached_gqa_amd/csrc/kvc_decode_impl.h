@@ -307,6 +307,49 @@ struct Seg {
     int64_t rec;             // workspace record, or -1: the whole unit, written directly
 };
 
+// Paged storage, issue side: pool offsets of head g's rows in the physical
+// blocks of an issue cursor's logical blocks blk and blk + 1 (a batch, stage
+// or tile spans at most these two), and the raw table entry of block blk + 2.
+// That entry is read by a scalar load when the cursor enters blk and first used
+// when it enters blk + 1: a value needed at once would make the wave wait for
+// the load at every block, with the next loads not yet issued, while this one
+// arrives under the waits for the loads in flight.
+template <int D>
+struct PagedCursor {
+    int blk;
+    int64_t base, next;
+    int ahead;
+
+    __device__ __forceinline__ static int entry(const DecodeArgs& a, int b, int blk) {
+        const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
+        const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
+        return tab[static_cast<int64_t>(b) * a.btab_stride + bi];
+    }
+    __device__ __forceinline__ static int64_t rows(const DecodeArgs& a, int p, int g) {
+        p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
+        return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + g) << a.bshift) * D;
+    }
+    // the cursor starts unit (b, g) at logical block b0
+    __device__ __forceinline__ void enter(const DecodeArgs& a, int b, int g, int b0) {
+        const int e0 = entry(a, b, b0), e1 = entry(a, b, b0 + 1);    // the three loads, then one wait
+        ahead = entry(a, b, b0 + 2);
+        blk = b0;
+        base = rows(a, e0, g);
+        next = rows(a, e1, g);
+    }
+    // the cursor moves on to block nb = blk + 1
+    __device__ __forceinline__ void step(const DecodeArgs& a, int b, int g, int nb) {
+        blk = nb;
+        base = next;
+        next = rows(a, ahead, g);
+        ahead = entry(a, b, nb + 2);
+    }
+    // element offset of key j (in block blk or blk + 1) of the unit's head
+    __device__ __forceinline__ int64_t row(const DecodeArgs& a, int j) const {
+        return ((j >> a.bshift) == blk ? base : next) + static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D;
+    }
+};
+
 // The slab's query rows, lane's share (EPC elements from element sub * EPC of
 // each row), converted to the storage format, from an LDS slot at byte address
 // `slot` that holds the rows as the caller passed them (row r at r * D * qsize).
@@ -461,25 +504,10 @@ void decode_attn(DecodeArgs a) {
     Seg is = locate(x_begin);
     int is_t = 0, is_sn = 0;
     bool is_live = true;
-    // paged storage: element offsets of head is.g's rows in the physical
-    // blocks of logical blocks pg_blk and pg_blk + 1 of the issue cursor's
-    // unit. A work-group batch (KPB keys, at most one block) spans at most
-    // those two; the next block's entry is read when the cursor enters a
-    // block, with a scalar load, long before a batch needs it.
-    int pg_blk = 0;
-    int64_t pg_base = 0, pg_next = 0;
-    auto pg_phys = [&](int blk) __attribute__((always_inline)) -> int64_t {
-        const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
-        const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
-        int p = tab[static_cast<int64_t>(is.b) * a.btab_stride + bi];
-        p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
-        return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + is.g) << a.bshift) * D;
-    };
-    auto pg_enter = [&]() __attribute__((always_inline)) {
-        pg_blk = is.j0 >> a.bshift;
-        pg_base = pg_phys(pg_blk);
-        pg_next = pg_phys(pg_blk + 1);
-    };
+    // paged storage: the issue cursor's blocks (a work-group batch of KPB
+    // keys, at most one block, spans at most two)
+    PagedCursor<D> pg{};
+    auto pg_enter = [&]() __attribute__((always_inline)) { pg.enter(a, is.b, is.g, is.j0 >> a.bshift); };
     if constexpr (PAGED) pg_enter();
     uint8_t* const ring_w = ring + wave * (NS * C::STAGE_BYTES);
     auto issue = [&](auto slot_c) __attribute__((always_inline)) {
@@ -497,11 +525,7 @@ void decode_attn(DecodeArgs a) {
         }
         if constexpr (PAGED) {
             const int blk = (is.j0 + is_t * KPB) >> a.bshift;
-            if (is_live && blk != pg_blk) {       // the batch starts in the next block
-                pg_blk = blk;
-                pg_base = pg_next;
-                pg_next = pg_phys(blk + 1);
-            }
+            if (is_live && blk != pg.blk) pg.step(a, is.b, is.g, blk);    // the batch starts in the next block
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -509,9 +533,7 @@ void decode_attn(DecodeArgs a) {
             j = j < is.j1 ? j : is.j1 - 1;
             int64_t off;
             if constexpr (PAGED) {
-                const int64_t row = ((j >> a.bshift) == pg_blk ? pg_base : pg_next) +
-                                    static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D;
-                off = (row + sub * EPC) * ESZ;
+                off = (pg.row(a, j) + sub * EPC) * ESZ;
             } else {
                 off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
             }
@@ -850,34 +872,16 @@ void decode_rows(DecodeArgs a) {
     Seg is = locate(x_begin);
     int is_t = 0;
     bool is_live = true;
-    // paged storage: pool offsets of head is.g's rows in the blocks of logical
-    // blocks pg_blk and pg_blk + 1 of the issue cursor's unit (a stage of KPS
-    // keys spans at most these two); the next block's entry is read by a
-    // scalar load when the cursor enters a block
-    int pg_blk = 0;
-    int64_t pg_base = 0, pg_next = 0;
-    auto pg_phys = [&](int blk) __attribute__((always_inline)) -> int64_t {
-        const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
-        const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
-        int p = tab[static_cast<int64_t>(is.b) * a.btab_stride + bi];
-        p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
-        return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + is.g) << a.bshift) * D;
-    };
-    auto pg_enter = [&]() __attribute__((always_inline)) {
-        pg_blk = is.j0 >> a.bshift;
-        pg_base = pg_phys(pg_blk);
-        pg_next = pg_phys(pg_blk + 1);
-    };
+    // paged storage: the issue cursor's blocks (a stage of KPS keys spans at
+    // most two)
+    PagedCursor<D> pg{};
+    auto pg_enter = [&]() __attribute__((always_inline)) { pg.enter(a, is.b, is.g, is.j0 >> a.bshift); };
     if constexpr (PAGED) pg_enter();
     auto issue = [&](auto slot_c) __attribute__((always_inline)) {
         constexpr int S = decltype(slot_c)::value;
         if constexpr (PAGED) {
             const int blk = (is.j0 + is_t * KPS) >> a.bshift;
-            if (is_live && blk != pg_blk) {       // the stage starts in the next block
-                pg_blk = blk;
-                pg_base = pg_next;
-                pg_next = pg_phys(blk + 1);
-            }
+            if (is_live && blk != pg.blk) pg.step(a, is.b, is.g, blk);    // the stage starts in the next block
         }
 #pragma unroll
         for (int ub = 0; ub < UB; ++ub) {
@@ -886,8 +890,7 @@ void decode_rows(DecodeArgs a) {
             j = j < is.j1 ? j : is.j1 - 1;
             int64_t off;
             if constexpr (PAGED)
-                off = (((j >> a.bshift) == pg_blk ? pg_base : pg_next) +
-                       static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D + sub * EPC) * ESZ;
+                off = (pg.row(a, j) + sub * EPC) * ESZ;
             else
                 off = (is.head + static_cast<int64_t>(j) * D + sub * EPC) * ESZ;
             uint8_t* dst = ring + S * C::STAGE_BYTES + bi * 2048;
@@ -1273,24 +1276,10 @@ void decode_mfma(DecodeArgs a) {
     Seg is = first;
     int is_t = 0;
     bool is_live = true;
-    // paged storage: pool offsets of head is.g's rows in the blocks of logical
-    // blocks pg_blk and pg_blk + 1 of the issue cursor's unit (a 32-key tile
-    // spans at most these two); the next block's entry is read by a scalar load
-    // when the cursor enters a block
-    int pg_blk = 0;
-    int64_t pg_base = 0, pg_next = 0;
-    auto pg_phys = [&](int blk) __attribute__((always_inline)) -> int64_t {
-        const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
-        const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
-        int p = tab[static_cast<int64_t>(is.b) * a.btab_stride + bi];
-        p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
-        return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + is.g) << a.bshift) * D;
-    };
-    auto pg_enter = [&]() __attribute__((always_inline)) {
-        pg_blk = is.j0 >> a.bshift;
-        pg_base = pg_phys(pg_blk);
-        pg_next = pg_phys(pg_blk + 1);
-    };
+    // paged storage: the issue cursor's blocks (a 32-key tile spans at most
+    // two)
+    PagedCursor<D> pg{};
+    auto pg_enter = [&]() __attribute__((always_inline)) { pg.enter(a, is.b, is.g, is.j0 >> a.bshift); };
     if constexpr (PAGED) pg_enter();
     // byte offsets, inside a tile, of this lane's 16 bytes of each load (D =
     // 128: load n covers rows 4n .. 4n + 3; the K chunks' swizzle repeats
@@ -1312,11 +1301,7 @@ void decode_mfma(DecodeArgs a) {
         uint16_t* vd = kd + P::TILE;
         if constexpr (PAGED) {
             const int blk = (is.j0 + is_t * kBN) >> a.bshift;
-            if (is_live && blk != pg_blk) {       // the tile starts in the next block
-                pg_blk = blk;
-                pg_base = pg_next;
-                pg_next = pg_phys(blk + 1);
-            }
+            if (is_live && blk != pg.blk) pg.step(a, is.b, is.g, blk);    // the tile starts in the next block
         }
         // a fused append's new keys (the unit's last T) sit in its last tile at
         // most: only a tile that reaches them selects an address per lane
@@ -1329,8 +1314,7 @@ void decode_mfma(DecodeArgs a) {
             // a 32-bit offset per lane and load (the same for every tile)
             int64_t tb;
             if constexpr (PAGED)
-                tb = ((j0t >> a.bshift) == pg_blk ? pg_base : pg_next) +
-                     static_cast<int64_t>(j0t & ((1 << a.bshift) - 1)) * D;
+                tb = pg.row(a, j0t);
             else
                 tb = is.head + static_cast<int64_t>(j0t) * D;
             const char* kb = reinterpret_cast<const char*>(kg + tb);
@@ -1368,8 +1352,7 @@ void decode_mfma(DecodeArgs a) {
             j = j < is.j1 ? j : is.j1 - 1;
             int64_t row;
             if constexpr (PAGED)
-                row = ((j >> a.bshift) == pg_blk ? pg_base : pg_next) +
-                      static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D;
+                row = pg.row(a, j);
             else
                 row = is.head + static_cast<int64_t>(j) * D;
             const uint16_t* kp = kg;

@@ -182,8 +182,9 @@ hipError_t launch_table_set(const TableSetArgs& a, hipStream_t stream);
 // floor(x / d) for x >= 0, d > 0 and a quotient below 2^31: a double-precision
 // estimate (off by at most one: the operands convert with a relative error of
 // 2^-53 each and the quotient is rounded once), then the exact remainder moves
-// it by one where the estimate rounded across an integer. Some 20 instructions
-// with no branch, against the long expansion of a 64-bit integer division.
+// it by one where the estimate rounded across an integer. About 30
+// instructions with no branch, against the long expansion of a 64-bit integer
+// division.
 __host__ __device__ inline int64_t decode_quot(int64_t x, int64_t d) {
     int64_t q = static_cast<int32_t>(static_cast<double>(x) / static_cast<double>(d));
     const int64_t r = x - q * d;
