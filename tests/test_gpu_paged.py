@@ -145,6 +145,40 @@ def test_paged_long_context_and_prefill_chunks_bit_exact():
         pc.close()
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_paged_rows_that_reach_the_last_table_entry(dtype):
+    """Rows whose last key sits in the last entry of their table row, rows that
+    end exactly at a block edge, one-block rows, and long rows over many small
+    blocks: the decode kernels read each block's entry ahead of time (the block
+    after next, clamped to the row's table, -1 past the held blocks), which must
+    change nothing. Attention outputs bit-identical to the contiguous cache for
+    T = 1 and 3 and for 4 and 8 query heads per KV head."""
+    import torch
+    rng = np.random.default_rng(4242)
+    D, Hkv, bs = 128, 2, 64
+    for max_len, lens in ((4 * bs, [4 * bs - 1, 2 * bs - 1, bs - 1, 199]), (4096, [4095, 4032, 2049, 64])):
+        for G in (4, 8):
+            for T in (1, 3):
+                log(f"paged table edges dtype={dtype} max_len={max_len} G={G} T={T}")
+                B, Hq = len(lens), G * Hkv
+                cc, pc = _pair(1, B, Hq, Hkv, D, max_len, dtype, bs)
+                k, v = (rng.standard_normal((B, Hkv, max_len - T, D), dtype=np.float32) for _ in range(2))
+                _both_append(cc, pc, 0, k, v, inp="bf16")
+                cut = np.minimum(np.array(lens) + 1 - T, max_len - T)
+                cc.truncate(cut)
+                pc.truncate(cut)
+                k, v = (rng.standard_normal((B, Hkv, T, D), dtype=np.float32) for _ in range(2))
+                _both_append(cc, pc, 0, k, v)
+                _check_table(pc)
+                q = to_device(rng.standard_normal((B, Hq, T, D), dtype=np.float32), "bf16", DEV)
+                oc, op = cc.attend(0, q), pc.attend(0, q)
+                torch.cuda.synchronize()
+                assert torch.equal(oc.view(torch.int32), op.view(torch.int32)), (max_len, G, T)
+                assert np.isfinite(oc.cpu().numpy()).all()
+                cc.close()
+                pc.close()
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 def test_paged_groups_and_chunks_against_the_oracle(dtype):
     """Group sizes 1..16 and chunks T = 1..9 (slabs of up to 8 query rows per
