@@ -256,10 +256,11 @@ def new_cache(n_kv_heads, d_head, max_len, batch, n_q_heads, dev, block=None):
                         block_size=block)
 
 
-def prefill_bench(block=None, runs=3):
+def prefill_bench(block=None, runs=3, precision="rounded"):
     """Chunked prefill: B=4, H_q=32, H_kv=8, d_h=128, bf16, 32 chunks of T=512
     appended and attended in turn (queries at s = 0, 512, ..., 15872); on a
-    paged cache with blocks of `block` positions when given."""
+    paged cache with blocks of `block` positions when given; `precision` is the
+    cache's prefill precision (kvc_set_prefill_precision)."""
     import torch
     from kv_cached_gqa_amd import work
     b, hq, hkv, d, t, nch = 4, 32, 8, 128, 512, 32
@@ -267,6 +268,7 @@ def prefill_bench(block=None, runs=3):
     gen = torch.Generator(device=dev)
     gen.manual_seed(11)
     cache = new_cache(hkv, d, t * nch, b, hq, dev, block)
+    cache.set_prefill_precision(precision)
     ks = [torch.randn((b, hkv, t, d), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(4)]
     vs = [torch.randn((b, hkv, t, d), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(4)]
     qs = [torch.randn((b, hq, t, d), generator=gen, device=dev, dtype=torch.bfloat16) for _ in range(4)]
@@ -689,7 +691,12 @@ def main():
                      "bytes_per_launch": att, "launch_us": round(us_attend, 3)},
     }
     if not args.no_extra:
-        rec["extra"] = {"chunked_prefill": prefill_bench(), "long_context_decode": long_ctx_bench(),
+        pf_split = prefill_bench(precision="split")
+        rec["extra"] = {"chunked_prefill": prefill_bench(),
+                        "chunked_prefill_split_p": {"precision": "P as a hi + lo pair (kvc_set_prefill_precision)",
+                                                    **{k: pf_split[k] for k in ("ms_per_run", "tflops",
+                                                                                "pct_peak_bf16_mfma")}},
+                        "long_context_decode": long_ctx_bench(),
                         "tiny_decoder": tiny_decoder_bench(), "rope": rope_bench(),
                         "latent_cache": latent_bench(), "paged_decode": paged_bench(lengths, us_attend),
                         "small_configs": small_configs_bench()}

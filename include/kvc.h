@@ -167,6 +167,29 @@ int kvc_attend(kvc_cache* cache, int32_t layer, const void* q, int32_t q_dtype,
 int kvc_attend_static(kvc_cache* cache, int32_t layer, const void* q, int32_t q_dtype, int32_t T, float* out,
                       void* stream);
 
+/* How a prefill chunk's probabilities enter the product with V on the matrix
+ * cores (16-bit caches, chunks of more than 32 query rows per KV head): the
+ * attention computed is the one of kvc_attend ("KV cache, incremental decode,
+ * ...", section 2.3: softmax(q K^T / sqrt(d_head)) V), and this only sets how
+ * closely. */
+typedef enum kvc_prefill_precision {
+    KVC_PREFILL_P_ROUNDED = 0,  /* P rounded once to the storage type (round to nearest even), the
+                                   normaliser summing the rounded values: ~1e-3 relative error per
+                                   call on bf16 caches, ~1.5e-4 on fp16 (the default) */
+    KVC_PREFILL_P_SPLIT = 1     /* P as a hi + lo pair of the storage type (the residual of the first
+                                   rounding rounded again, multiplied with V by a second product):
+                                   ~1e-6, with half again as many matrix products (slower) */
+} kvc_prefill_precision;
+
+/* Select the prefill precision of one handle (every later kvc_attend and
+ * kvc_attend_static on it). Decode calls (32 query rows per KV head or fewer)
+ * and fp32 caches are unaffected: their probabilities are kept in float32, or
+ * as a hi + lo pair on the matrix cores.
+ *  mode: a kvc_prefill_precision value. Host state only; nothing is enqueued.
+ * Errors: KVC_ERR_ARG (null handle, unknown mode); the setting is unchanged
+ * then. */
+int kvc_set_prefill_precision(kvc_cache* cache, int32_t mode);
+
 /* Append a chunk, then attend to everything the layer holds, in one call: the
  * same state change and bit-identical results as kvc_append(k_new, v_new,
  * in_dtype, T) followed by kvc_attend(q, q_dtype, T, out) ("KV cache, ...",

@@ -56,6 +56,7 @@ struct kvc_cache {
     std::vector<int32_t> table;    // host table, -1 = no block
     std::vector<int32_t> held;     // blocks held per row (a prefix of its table row)
     std::vector<int32_t> free_ids; // free blocks, taken from the back
+    int32_t prefill_precision = KVC_PREFILL_P_ROUNDED;   // kvc_set_prefill_precision
 };
 
 namespace {
@@ -539,6 +540,7 @@ int attend_impl(kvc_cache* c, int32_t layer, const void* q, int32_t q_dtype, int
                 a.q_dtype = q_dtype;
                 a.st_dtype = cf.dtype;
                 a.scale_log2 = scale_log2;
+                a.p_split = c->prefill_precision == KVC_PREFILL_P_SPLIT;
                 if (paged) {
                     a.layer_off = layer * pool_layer_elems(c);
                     a.row_stride = 0;
@@ -763,6 +765,12 @@ int kvc_truncate(kvc_cache* c, const int64_t* n, int32_t count) {
         for (int l = 0; l < c->cfg.n_layers; ++l) c->fill[static_cast<size_t>(l) * B + b] = nb;
         if (c->block_size) shrink_blocks(c, b, nb);
     }
+    return KVC_OK;
+}
+
+int kvc_set_prefill_precision(kvc_cache* c, int32_t mode) {
+    if (!c || (mode != KVC_PREFILL_P_ROUNDED && mode != KVC_PREFILL_P_SPLIT)) return KVC_ERR_ARG;
+    c->prefill_precision = mode;
     return KVC_OK;
 }
 

@@ -148,6 +148,7 @@ struct PrefillArgs {
     int32_t q_per_block;     // queries per work-group
     int32_t q_dtype, st_dtype;
     float scale_log2;
+    int32_t p_split;         // 1: P as a 16-bit hi + lo pair (two products with V), 0: rounded once
     // paged storage (btab non-null), as in DecodeArgs
     const int32_t* btab;
     int32_t btab_stride, bshift, pool_blocks;

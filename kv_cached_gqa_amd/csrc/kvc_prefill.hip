@@ -31,9 +31,6 @@
 
 #include "kvc_mfma.h"
 
-#ifndef KVC_PREFILL_PSPLIT
-#define KVC_PREFILL_PSPLIT 0   // 1: P as a 16-bit hi + lo pair (two products with V)
-#endif
 
 namespace kvc {
 namespace {
@@ -75,7 +72,10 @@ struct PCfg : TileLayout<D> {
     static_assert(V_OFF + (kNB - 1) * L::TILE_BYTES + 24 * D * 2 < 65536, "LDS read offsets fit 16 bits");
 };
 
-template <int D, int ST, bool PAGED>
+// PS: P as a 16-bit hi + lo pair, the residual of the first rounding rounded
+// again and multiplied with V by a second product (error ~1e-6 instead of
+// ~1e-3 for a once-rounded P; half again as many products).
+template <int D, int ST, bool PAGED, bool PS>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(KVC_PF_WAVES_PER_EU)))
 void prefill_attn(PrefillArgs a) {
     using P = PCfg<D>;
@@ -306,7 +306,7 @@ void prefill_attn(PrefillArgs a) {
                 const float p0 = fexp2(fmaf(sv_[2 * e], c, nmc)), p1 = fexp2(fmaf(sv_[2 * e + 1], c, nmc));
                 w[e] = pack_p<ST>(p0, p1);
                 ls[e & 1] = add_pair<ST>(w[e], ls[e & 1]);
-                if constexpr (KVC_PREFILL_PSPLIT) {
+                if constexpr (PS) {
                     // the rounding residual of each probability, rounded again: P = hi + lo
                     wl[e] = pack_p<ST>(p0 - low_half<ST>(w[e]), p1 - high_half<ST>(w[e]));
                     ls[e & 1] = add_pair<ST>(wl[e], ls[e & 1]);
@@ -315,7 +315,7 @@ void prefill_attn(PrefillArgs a) {
             lsum[nt] += ls[0] + ls[1];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) pb[nt][kk] = u32x4{w[kk * 4 + 0], w[kk * 4 + 1], w[kk * 4 + 2], w[kk * 4 + 3]};
-            if constexpr (KVC_PREFILL_PSPLIT) {
+            if constexpr (PS) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
                     pl[nt][kk] = u32x4{wl[kk * 4 + 0], wl[kk * 4 + 1], wl[kk * 4 + 2], wl[kk * 4 + 3]};
@@ -332,7 +332,7 @@ void prefill_attn(PrefillArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) {
                     o[nt][dt] = mfma32<ST>(va, pb[nt][kk], o[nt][dt]);
-                    if constexpr (KVC_PREFILL_PSPLIT) o[nt][dt] = mfma32<ST>(va, pl[nt][kk], o[nt][dt]);
+                    if constexpr (PS) o[nt][dt] = mfma32<ST>(va, pl[nt][kk], o[nt][dt]);
                 }
             }
     };
@@ -372,12 +372,17 @@ void prefill_attn(PrefillArgs a) {
     }
 }
 
-template <int D, bool PAGED>
-hipError_t run_pp(const PrefillArgs& a, hipStream_t s, unsigned grid) {
-    if (a.st_dtype == BF16) prefill_attn<D, BF16, PAGED><<<grid, kPThreads, 0, s>>>(a);
-    else if (a.st_dtype == F16) prefill_attn<D, F16, PAGED><<<grid, kPThreads, 0, s>>>(a);
+template <int D, bool PAGED, bool PS>
+hipError_t run_pps(const PrefillArgs& a, hipStream_t s, unsigned grid) {
+    if (a.st_dtype == BF16) prefill_attn<D, BF16, PAGED, PS><<<grid, kPThreads, 0, s>>>(a);
+    else if (a.st_dtype == F16) prefill_attn<D, F16, PAGED, PS><<<grid, kPThreads, 0, s>>>(a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+template <int D, bool PAGED>
+hipError_t run_pp(const PrefillArgs& a, hipStream_t s, unsigned grid) {
+    return a.p_split ? run_pps<D, PAGED, true>(a, s, grid) : run_pps<D, PAGED, false>(a, s, grid);
 }
 
 template <int D>

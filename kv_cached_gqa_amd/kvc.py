@@ -32,12 +32,15 @@ F32, F16, BF16 = 0, 1, 2
 DTYPE_CODES = {"fp32": F32, "fp16": F16, "bf16": BF16}
 ITEMSIZE = {"fp32": 4, "fp16": 2, "bf16": 2}
 
+PREFILL_P_ROUNDED, PREFILL_P_SPLIT = 0, 1      # kvc_prefill_precision
+PREFILL_PRECISION = {"rounded": PREFILL_P_ROUNDED, "split": PREFILL_P_SPLIT}
+
 OK = 0
 ERR_ARG, ERR_CAPACITY, ERR_STATE, ERR_DTYPE = -1, -2, -3, -4
 ERR_STORAGE, ERR_HIP, ERR_NOMEM, ERR_UNSUPPORTED, ERR_SCRATCH = -5, -6, -7, -8, -9
 
 EXPORTED = ("kvc_create", "kvc_destroy", "kvc_append", "kvc_append_rope", "kvc_rope_q", "kvc_attend",
-            "kvc_append_attend", "kvc_gather", "kvc_attend_static",
+            "kvc_append_attend", "kvc_gather", "kvc_attend_static", "kvc_set_prefill_precision",
             "kvc_seq_len", "kvc_truncate", "kvc_nbytes", "kvc_strerror",
             "kvc_create_paged", "kvc_paged_blocks", "kvc_block_table",
             "kvc_latent_create", "kvc_latent_destroy", "kvc_latent_append", "kvc_latent_seq_len",
@@ -73,6 +76,8 @@ _lib.kvc_append_attend.argtypes = [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _
 _lib.kvc_append_attend.restype = ctypes.c_int
 _lib.kvc_attend_static.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp, _vp]
 _lib.kvc_attend_static.restype = ctypes.c_int
+_lib.kvc_set_prefill_precision.argtypes = [_vp, _i32]
+_lib.kvc_set_prefill_precision.restype = ctypes.c_int
 _lib.kvc_gather.argtypes = [_vp, _i32, _i64, _vp, _vp, _vp]
 _lib.kvc_gather.restype = ctypes.c_int
 _lib.kvc_seq_len.argtypes = [_vp, _i32, ctypes.POINTER(_i64)]
@@ -315,6 +320,13 @@ class KVCache:
         out = _u64()
         _check(_lib.kvc_nbytes(self._h, ctypes.byref(out)), "kvc_nbytes")
         return int(out.value)
+
+    def set_prefill_precision(self, mode: str) -> None:
+        """"rounded" (the default: P rounded once to the storage type) or
+        "split" (P as a hi + lo pair) for this cache's prefill chunks."""
+        if mode not in PREFILL_PRECISION:
+            raise KVCArgumentError(ERR_ARG, f"prefill precision must be one of {sorted(PREFILL_PRECISION)}")
+        _check(_lib.kvc_set_prefill_precision(self._h, PREFILL_PRECISION[mode]), "kvc_set_prefill_precision")
 
     def attend_static(self, layer: int, q, out, stream=None):
         """attend() through kvc_attend_static: split-K scratch from the library's

@@ -321,3 +321,23 @@ def test_gather_rejects_bad_arguments(kvc):
         assert lib.kvc_gather(h, 0, 4, p, p + 8, None) == kvc.ERR_ARG      # misaligned
     finally:
         lib.kvc_destroy(h)
+
+
+def test_prefill_precision_setting(kvc):
+    """kvc_set_prefill_precision takes the two declared modes on any handle
+    (host state only) and rejects a null handle or an unknown mode, leaving the
+    setting as it was."""
+    lib = kvc.lib()
+    assert (kvc.PREFILL_P_ROUNDED, kvc.PREFILL_P_SPLIT) == (0, 1)
+    text = open(HEADER).read()
+    assert re.search(r"KVC_PREFILL_P_ROUNDED\s*=\s*0", text) and re.search(r"KVC_PREFILL_P_SPLIT\s*=\s*1", text)
+    rc, h = _create(kvc)
+    assert rc == kvc.OK
+    try:
+        assert lib.kvc_set_prefill_precision(h, kvc.PREFILL_P_SPLIT) == kvc.OK
+        assert lib.kvc_set_prefill_precision(h, kvc.PREFILL_P_ROUNDED) == kvc.OK
+        for bad in (2, -1, 99):
+            assert lib.kvc_set_prefill_precision(h, bad) == kvc.ERR_ARG
+        assert lib.kvc_set_prefill_precision(None, kvc.PREFILL_P_SPLIT) == kvc.ERR_ARG
+    finally:
+        lib.kvc_destroy(h)

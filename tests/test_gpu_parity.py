@@ -167,6 +167,46 @@ def test_chunked_prefill_bf16_reduced():
     assert rep.ok(), rep.failures[:5]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_prefill_split_precision(dtype):
+    """kvc_set_prefill_precision: the first two chunks of the chunked-prefill
+    workload (B=4, H_q=32, H_kv=8, d_h=128, T=512), every row, with P as a hi +
+    lo pair, within 1e-4 of the float64 oracle per call (the once-rounded P of
+    the default is ~1e-3 on bf16); the paged cache, in the same mode, gives the
+    same bits; switching back restores the default kernel's result."""
+    import torch
+    from kv_cached_gqa_amd.kvc import KVCache, PagedKVCache
+    log(f"prefill split precision {dtype}")
+    shape, calls = W.script_chunked_prefill(n_chunks=2)
+    mk = dict(batch=shape.batch, n_q_heads=shape.n_q_heads, dtype=dtype, device="cuda")
+    cache = KVCache(1, shape.n_kv_heads, shape.d_head, shape.max_len, **mk)
+    paged = PagedKVCache(1, shape.n_kv_heads, shape.d_head, shape.max_len, block_size=128, **mk)
+    orc = OracleCache(1, shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.d_head, shape.max_len, dtype)
+    cache.set_prefill_precision("split")
+    paged.set_prefill_precision("split")
+    for n, call in enumerate(c for c in calls if c.op == "pass"):
+        kd, vd = to_device(call.k, "fp32", "cuda"), to_device(call.v, "fp32", "cuda")
+        cache.append(0, kd, vd)
+        paged.append(0, kd, vd)
+        orc.append(0, input_values(call.k, "fp32"), input_values(call.v, "fp32"))
+        q = to_device(call.q, dtype, "cuda")
+        got = cache.attend(0, q)
+        got_paged = paged.attend(0, q)
+        cache.set_prefill_precision("rounded")
+        got_rounded = cache.attend(0, q)
+        cache.set_prefill_precision("split")
+        torch.cuda.synchronize()
+        want = orc.attend(0, input_values(call.q, dtype))
+        _, rel = compare_out(got.cpu().numpy(), want, dtype)
+        _, rel_rounded = compare_out(got_rounded.cpu().numpy(), want, dtype)
+        log(f"  chunk {n}: split rel {rel:.3e}, rounded rel {rel_rounded:.3e}")
+        assert rel <= 1e-4, (n, rel)
+        assert rel_rounded <= HALF_REL_FROB and rel < rel_rounded, (n, rel, rel_rounded)
+        assert torch.equal(got.view(torch.int32), got_paged.view(torch.int32)), n
+    cache.close()
+    paged.close()
+
+
 @pytest.mark.timeout(1200)
 def test_long_context_speculative_cycles():
     """B=8, H_q=64, H_kv=8, d_h=128, bf16, s0=32768: all 64 draft / accept /
