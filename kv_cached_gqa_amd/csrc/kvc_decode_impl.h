@@ -231,31 +231,36 @@ struct RowOf {
     int b;
     int64_t p0, p1;
 };
-constexpr int kPrefixSlots = (kMaxRowsPerLaunch + 1 + 63) / 64;
+template <int S>
 struct PrefixLanes {
-    int64_t e[kPrefixSlots];   // entries lane, lane + 64, ...
+    static constexpr int kSlots = S;
+    int64_t e[S];              // entries lane, lane + 64, ...
 };
-__device__ __forceinline__ PrefixLanes load_prefix_lanes() {
+// the table of argument block A (the kernel's own: A is its parameter type)
+template <class A>
+__device__ __forceinline__ PrefixLanes<(A::kPrefix + 63) / 64> load_prefix_lanes() {
+    constexpr int last = A::kPrefix - 1;
     const auto* args = (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
-    const auto* pf = reinterpret_cast<const __attribute__((address_space(4))) int64_t*>(args + offsetof(DecodeArgs, prefix));
+    const auto* pf = reinterpret_cast<const __attribute__((address_space(4))) int64_t*>(args + offsetof(A, prefix));
     const int lane = static_cast<int>(threadIdx.x) & 63;
-    PrefixLanes p;
+    PrefixLanes<(A::kPrefix + 63) / 64> p;
 #pragma unroll
-    for (int j = 0; j < kPrefixSlots; ++j) {
+    for (int j = 0; j < p.kSlots; ++j) {
         // every lane loads (a vector load: a lane-0-only load would become a
         // scalar one that the compiler waits for at once)
         const int i = lane + 64 * j;
-        const int64_t v = pf[i <= kMaxRowsPerLaunch ? i : kMaxRowsPerLaunch];
-        p.e[j] = i <= kMaxRowsPerLaunch ? v : INT64_MAX;
+        const int64_t v = pf[i <= last ? i : last];
+        p.e[j] = i <= last ? v : INT64_MAX;
     }
     return p;
 }
-__device__ __forceinline__ RowOf row_of(const PrefixLanes& p, int64_t x, int64_t row_pad) {
+template <int S>
+__device__ __forceinline__ RowOf row_of(const PrefixLanes<S>& p, int64_t x, int64_t row_pad) {
     // entry i on the padded axis: prefix[i] + i * row_pad
     const int lane = static_cast<int>(threadIdx.x) & 63;
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kPrefixSlots; ++j) {
+    for (int j = 0; j < S; ++j) {
         const int64_t ep = p.e[j] == INT64_MAX ? INT64_MAX : p.e[j] + static_cast<int64_t>(lane + 64 * j) * row_pad;
         cnt += __popcll(__ballot(ep <= x));
     }
@@ -265,7 +270,7 @@ __device__ __forceinline__ RowOf row_of(const PrefixLanes& p, int64_t x, int64_t
         const int j = i >> 6, l = i & 63;
         int64_t v = 0;
 #pragma unroll
-        for (int jj = 0; jj < kPrefixSlots; ++jj) {
+        for (int jj = 0; jj < S; ++jj) {
             const uint64_t u = static_cast<uint64_t>(p.e[jj]);
             const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
             const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
@@ -320,17 +325,20 @@ struct PagedCursor {
     int64_t base, next;
     int ahead;
 
-    __device__ __forceinline__ static int entry(const DecodeArgs& a, int b, int blk) {
+    template <class A>
+    __device__ __forceinline__ static int entry(const A& a, int b, int blk) {
         const auto* tab = (const __attribute__((address_space(4))) int32_t*)(a.btab);
         const int bi = blk < a.btab_stride ? blk : a.btab_stride - 1;
         return tab[static_cast<int64_t>(b) * a.btab_stride + bi];
     }
-    __device__ __forceinline__ static int64_t rows(const DecodeArgs& a, int p, int g) {
+    template <class A>
+    __device__ __forceinline__ static int64_t rows(const A& a, int p, int g) {
         p = p < 0 ? 0 : (p >= a.pool_blocks ? a.pool_blocks - 1 : p);
         return a.layer_off + ((static_cast<int64_t>(p) * a.Hkv + g) << a.bshift) * D;
     }
     // the cursor starts unit (b, g) at logical block b0
-    __device__ __forceinline__ void enter(const DecodeArgs& a, int b, int g, int b0) {
+    template <class A>
+    __device__ __forceinline__ void enter(const A& a, int b, int g, int b0) {
         const int e0 = entry(a, b, b0), e1 = entry(a, b, b0 + 1);    // the three loads, then one wait
         ahead = entry(a, b, b0 + 2);
         blk = b0;
@@ -338,14 +346,16 @@ struct PagedCursor {
         next = rows(a, e1, g);
     }
     // the cursor moves on to block nb = blk + 1
-    __device__ __forceinline__ void step(const DecodeArgs& a, int b, int g, int nb) {
+    template <class A>
+    __device__ __forceinline__ void step(const A& a, int b, int g, int nb) {
         blk = nb;
         base = next;
         next = rows(a, ahead, g);
         ahead = entry(a, b, nb + 2);
     }
     // element offset of key j (in block blk or blk + 1) of the unit's head
-    __device__ __forceinline__ int64_t row(const DecodeArgs& a, int j) const {
+    template <class A>
+    __device__ __forceinline__ int64_t row(const A& a, int j) const {
         return ((j >> a.bshift) == blk ? base : next) + static_cast<int64_t>(j & ((1 << a.bshift) - 1)) * D;
     }
 };
@@ -406,9 +416,9 @@ __device__ __forceinline__ void load_q_rows(uint32_t (&qp)[R][4], uint32_t slot,
     }
 }
 
-template <int D, int ST, int R, bool PAGED>
+template <class A, int D, int ST, int R, bool PAGED>
 __global__ __launch_bounds__((Cfg<D, ST, R>::THREADS)) __attribute__((amdgpu_waves_per_eu(1)))
-void decode_attn(DecodeArgs a) {
+void decode_attn(A a) {
     using C = Cfg<D, ST, R>;
     constexpr int kWaves = C::WAVES, kThreads = C::THREADS;
     constexpr int EPC = C::EPC, LPK = C::LPK, KPW = C::KPW, U = C::U, NS = C::NS;
@@ -792,9 +802,9 @@ struct RCfg {
     static_assert(NS * STAGE_BYTES < 65536, "ring offsets fit the LDS immediate");
 };
 
-template <int D, int ST, int RS, bool PAGED>
+template <class A, int D, int ST, int RS, bool PAGED>
 __global__ __launch_bounds__((RCfg<D, ST, RS>::THREADS)) __attribute__((amdgpu_waves_per_eu(1)))
-void decode_rows(DecodeArgs a) {
+void decode_rows(A a) {
     using C = RCfg<D, ST, RS>;
     constexpr int EPC = C::EPC, LPK = C::LPK, KPW = C::KPW, UB = C::UB, NS = C::NS, R = C::R;
     constexpr int KPS = C::KPS, ESZ = C::ESZ, ROWS = C::ROWS;
@@ -1139,9 +1149,9 @@ struct MCfg : TileLayout<D> {
     static_assert((NS - 1) * STAGE_BYTES + L::TILE_BYTES + 24 * D * 2 < 65536, "LDS read offsets fit 16 bits");
 };
 
-template <int D, int ST, bool PAGED>
+template <class A, int D, int ST, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
-void decode_mfma(DecodeArgs a) {
+void decode_mfma(A a) {
     using P = MCfg<D>;
     constexpr int NS = P::NS, DS = P::DS, DT = P::DT, NLD = P::NLD;
     __shared__ __attribute__((aligned(16))) uint16_t smem[P::LDS_BYTES / 2];
@@ -1157,7 +1167,7 @@ void decode_mfma(DecodeArgs a) {
 #if KVC_DECODE_TIMESTAMPS
     const unsigned long long pt_start = probe_now();
 #endif
-    const PrefixLanes pfx = load_prefix_lanes();   // in flight while the slice is worked out
+    const auto pfx = load_prefix_lanes<A>();   // in flight while the slice is worked out
     // The scalars that locating the first segment needs, read from the
     // arguments in one round trip and held as opaque copies (the compiler would
     // otherwise read each again near its use, one dependent wait each), and the
@@ -1169,7 +1179,7 @@ void decode_mfma(DecodeArgs a) {
     asm volatile("" : "+s"(kpb), "+s"(kpbo), "+s"(kpb2), "+s"(kpb2o), "+s"(total), "+s"(n1), "+s"(hkv), "+s"(upad),
                  "+s"(hshift), "+s"(hinv), "+s"(nrows)
                  : "s"(a.k_cache), "s"(a.v_cache), "s"(a.layer_off), "s"(a.row_stride), "s"(a.head_stride),
-                   "s"(a.T), "s"(a.row0), "s"(a.k_new), "s"(a.v_new), "s"(a.prefix[kMaxRowsPerLaunch]));
+                   "s"(a.T), "s"(a.row0), "s"(a.k_new), "s"(a.v_new), "s"(a.prefix[A::kPrefix - 1]));
     const int64_t x_begin = decode_slice_begin(blockIdx.x, n1, kpb, kpbo, kpb2, kpb2o);
     int64_t x_end = x_begin + decode_slice_size(blockIdx.x, n1, kpb, kpbo, kpb2, kpb2o);
     if (x_end > total) x_end = total;
@@ -1582,8 +1592,8 @@ void decode_mfma(DecodeArgs a) {
 // (units held by one work-group were written by the attention kernel and are
 // skipped). Work-group (u, y) covers outputs y*256 .. y*256+255 of unit u's
 // slab, one (row, element) per thread.
-template <int D>
-__global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
+template <class A, int D>
+__global__ __launch_bounds__(256) void decode_combine(A a) {
     constexpr int kMaxSeg = 16;
     // grid (H_kv, rows of 256 outputs [+ the store row], batch rows): the row
     // b is known without the arguments, so its prefix entries and every
@@ -1722,6 +1732,21 @@ hipError_t device_cus(int& n_cu) {
     return hipSuccess;
 }
 
+// Launches `f` with the launch's arguments: a copy cut to the short prefix
+// table when the launch has at most kSmallRows rows (less for the runtime to
+// copy), else the full block.
+template <class F>
+hipError_t with_args(const DecodeArgs& a, F&& f) {
+    if (a.rows <= kSmallRows) {
+        DecodeArgsSmall sm;
+        std::memcpy(&sm, &a, sizeof(sm));
+        f(sm);
+    } else {
+        f(a);
+    }
+    return hipGetLastError();
+}
+
 // The merge pass, if some unit spans several work-groups.
 template <int D>
 hipError_t combine_if_split(DecodeArgs& a, hipStream_t s) {
@@ -1738,8 +1763,9 @@ hipError_t combine_if_split(DecodeArgs& a, hipStream_t s) {
     const unsigned merge_rows = split ? (a.Gc * a.Tc * D + 255) / 256 : 0;
     a.merge_rows = static_cast<int32_t>(merge_rows);
     const dim3 grid(a.Hkv, merge_rows + (a.k_new != nullptr ? 1 : 0), a.rows);
-    decode_combine<D><<<grid, 256, 0, s>>>(a);
-    return hipGetLastError();
+    return with_args(a, [&](const auto& args) {
+        decode_combine<std::decay_t<decltype(args)>, D><<<grid, 256, 0, s>>>(args);
+    });
 }
 
 template <int D, int ST, int R>
@@ -1749,13 +1775,12 @@ hipError_t run(DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     a.rec_rows = R;
     decode_split_slices(a, n_cu, KVC_DECODE_BLOCKS_PER_CU, 2 * Cfg<D, ST, R>::KPB, KVC_DECODE_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
-    if (a.btab) {
-        if ((1 << a.bshift) < Cfg<D, ST, R>::KPB) return hipErrorInvalidValue;   // a batch within two blocks
-        decode_attn<D, ST, R, true><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
-    } else {
-        decode_attn<D, ST, R, false><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(a);
-    }
-    e = hipGetLastError();
+    if (a.btab && (1 << a.bshift) < Cfg<D, ST, R>::KPB) return hipErrorInvalidValue;   // a batch within two blocks
+    e = with_args(a, [&](const auto& args) {
+        using A = std::decay_t<decltype(args)>;
+        if (a.btab) decode_attn<A, D, ST, R, true><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(args);
+        else decode_attn<A, D, ST, R, false><<<a.n_blocks, Cfg<D, ST, R>::THREADS, 0, s>>>(args);
+    });
     if (e != hipSuccess) return e;
     return combine_if_split<D>(a, s);
 }
@@ -1767,13 +1792,12 @@ hipError_t run_rows(DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     a.rec_rows = RCfg<D, ST, RS>::ROWS;
     decode_split_slices(a, n_cu, 2, 2 * RCfg<D, ST, RS>::KPS, KVC_DECODE_LATE_PCT, KVC_DECODE_ODD_XCD_PCT);
-    if (a.btab) {
-        if ((1 << a.bshift) < RCfg<D, ST, RS>::KPS) return hipErrorInvalidValue;   // a stage within two blocks
-        decode_rows<D, ST, RS, true><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
-    } else {
-        decode_rows<D, ST, RS, false><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(a);
-    }
-    e = hipGetLastError();
+    if (a.btab && (1 << a.bshift) < RCfg<D, ST, RS>::KPS) return hipErrorInvalidValue;   // a stage within two blocks
+    e = with_args(a, [&](const auto& args) {
+        using A = std::decay_t<decltype(args)>;
+        if (a.btab) decode_rows<A, D, ST, RS, true><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(args);
+        else decode_rows<A, D, ST, RS, false><<<a.n_blocks, RCfg<D, ST, RS>::THREADS, 0, s>>>(args);
+    });
     if (e != hipSuccess) return e;
     return combine_if_split<D>(a, s);
 }
@@ -1789,13 +1813,12 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
     a.total_keys += static_cast<int64_t>(a.rows) * a.Hkv * a.unit_pad;
     const int odd_pct = a.Gc * a.Tc > 16 ? KVC_DECODE_MFMA_ODD_XCD_PCT_WIDE : KVC_DECODE_ODD_XCD_PCT;
     decode_split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT, odd_pct);
-    if (a.btab) {
-        if ((1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks
-        decode_mfma<D, ST, true><<<a.n_blocks, 64, 0, s>>>(a);
-    } else {
-        decode_mfma<D, ST, false><<<a.n_blocks, 64, 0, s>>>(a);
-    }
-    e = hipGetLastError();
+    if (a.btab && (1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks
+    e = with_args(a, [&](const auto& args) {
+        using A = std::decay_t<decltype(args)>;
+        if (a.btab) decode_mfma<A, D, ST, true><<<a.n_blocks, 64, 0, s>>>(args);
+        else decode_mfma<A, D, ST, false><<<a.n_blocks, 64, 0, s>>>(args);
+    });
     if (e != hipSuccess) return e;
     return combine_if_split<D>(a, s);
 }

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <cstddef>
+#include <cstring>
 
 #include <type_traits>
 
@@ -70,7 +72,8 @@ struct RopeArgs {
 // A slab is a set of query rows of one unit: query heads g*G + r0 .. + Gc and
 // query positions i0 .. i0 + Tc of the chunk (Gc * Tc <= kMaxDecodeRows).
 // ---------------------------------------------------------------------------
-struct DecodeArgs {
+template <int PC>
+struct DecodeArgsT {
     const void* k_cache;
     const void* v_cache;
     const void* q;           // [B][Hq][T][D], q_dtype, whole-batch base
@@ -125,8 +128,18 @@ struct DecodeArgs {
     // Hkv's odd part modulo 2^64
     int32_t hkv_shift;
     uint64_t hkv_inv;
-    int64_t prefix[kMaxRowsPerLaunch + 1];  // exclusive prefix of n_b * H_kv
+    int64_t prefix[PC];      // exclusive prefix of n_b * H_kv; INT64_MAX past the launch's rows
+    static constexpr int kPrefix = PC;
 };
+
+// The arguments of a launch of up to kMaxRowsPerLaunch rows, and their first
+// bytes (the prefix table cut to 33 entries) for a launch of at most 32 rows:
+// the runtime copies a kernel's whole argument block at every launch, and the
+// full table's 2 KB cost some 1.5 us more per launch on the host.
+using DecodeArgs = DecodeArgsT<kMaxRowsPerLaunch + 1>;
+constexpr int kSmallRows = 32;
+using DecodeArgsSmall = DecodeArgsT<kSmallRows + 1>;
+static_assert(offsetof(DecodeArgs, prefix) == offsetof(DecodeArgsSmall, prefix), "one layout up to the table");
 
 // ---------------------------------------------------------------------------
 // Prefill-chunk attention on matrix cores (fp16/bf16 caches): one work-group per
@@ -207,7 +220,8 @@ __host__ __device__ inline int64_t decode_quot_rcp(int64_t x, int64_t d, float i
 __host__ __device__ inline int64_t decode_div_exact(int64_t x, int shift, uint64_t inv) {
     return static_cast<int64_t>((static_cast<uint64_t>(x) >> shift) * inv);
 }
-__host__ __device__ inline int64_t decode_div_hkv(const DecodeArgs& a, int64_t x) {
+template <class A>
+__host__ __device__ inline int64_t decode_div_hkv(const A& a, int64_t x) {
     return decode_div_exact(x, a.hkv_shift, a.hkv_inv);
 }
 // hkv_shift and hkv_inv from Hkv (>= 1): Newton's iteration x <- x (2 - m x)
@@ -248,11 +262,13 @@ __host__ __device__ inline int64_t decode_slice_size(int64_t k, int64_t n1, int6
     if (k < n1) return (k & 1) ? kpbo : kpb;
     return (k & 1) ? kpb2o : kpb2;
 }
-__host__ __device__ inline int64_t decode_slice_begin(const DecodeArgs& a, int64_t k) {
+template <class A>
+__host__ __device__ inline int64_t decode_slice_begin(const A& a, int64_t k) {
     return decode_slice_begin(k, a.n_first, a.keys_per_block, a.keys_per_block_odd, a.keys_per_block2,
                               a.keys_per_block2_odd);
 }
-__host__ __device__ inline int64_t decode_slice_size(const DecodeArgs& a, int64_t k) {
+template <class A>
+__host__ __device__ inline int64_t decode_slice_size(const A& a, int64_t k) {
     return decode_slice_size(k, a.n_first, a.keys_per_block, a.keys_per_block_odd, a.keys_per_block2,
                              a.keys_per_block2_odd);
 }
@@ -274,7 +290,8 @@ __host__ __device__ inline int64_t decode_slice_of(int64_t x, int64_t n1, int64_
     const int64_t p = decode_quot_rcp(x, pair, inv);
     return base + 2 * p + (x - p * pair >= first ? 1 : 0);
 }
-__host__ __device__ inline int64_t decode_slice_of(const DecodeArgs& a, int64_t x) {
+template <class A>
+__host__ __device__ inline int64_t decode_slice_of(const A& a, int64_t x) {
     return decode_slice_of(x, a.n_first, a.keys_per_block, a.keys_per_block_odd, a.keys_per_block2,
                            a.keys_per_block2_odd, a.pair_inv, a.pair2_inv);
 }

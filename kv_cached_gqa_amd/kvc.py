@@ -153,12 +153,21 @@ def torch_dtype(name: str):
     return {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[name]
 
 
+_DTYPE_NAMES = {}     # torch dtype -> name, filled at the first call (torch is imported lazily)
+
+
 def dtype_name(t) -> str:
-    torch = _torch()
-    m = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
-    if t.dtype not in m:
+    if not _DTYPE_NAMES:
+        torch = _torch()
+        _DTYPE_NAMES.update({torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"})
+    name = _DTYPE_NAMES.get(t.dtype)
+    if name is None:
         raise KVCArgumentError(ERR_DTYPE, f"dtype {t.dtype}")
-    return m[t.dtype]
+    return name
+
+
+def _dtype_code(t) -> int:
+    return DTYPE_CODES[dtype_name(t)]
 
 
 def _stream_ptr(stream, device=None) -> Optional[int]:
@@ -239,18 +248,18 @@ class KVCache:
             raise KVCArgumentError(ERR_ARG, "k_new and v_new differ in shape or dtype")
         if rope_base is None:
             _check(_lib.kvc_append(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
-                                   DTYPE_CODES[dtype_name(k_new)], int(k_new.shape[2]), _stream_ptr(stream, self._dev)),
+                                   _dtype_code(k_new), int(k_new.shape[2]), _stream_ptr(stream, self._dev)),
                    "kvc_append")
         else:
             _check(_lib.kvc_append_rope(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
-                                        DTYPE_CODES[dtype_name(k_new)], int(k_new.shape[2]), float(rope_base),
+                                        _dtype_code(k_new), int(k_new.shape[2]), float(rope_base),
                                         _stream_ptr(stream, self._dev)), "kvc_append_rope")
 
     def rope_q(self, layer: int, q, rope_base: float, stream=None):
         """Rotate q [B, H_q, T, d_h] (device, contiguous) in place at the
         positions the next attend of `layer` gives the chunk; returns q."""
         self._check_chunk(q, self.n_q_heads, "q")
-        _check(_lib.kvc_rope_q(self._h, int(layer), q.data_ptr(), DTYPE_CODES[dtype_name(q)], int(q.shape[2]),
+        _check(_lib.kvc_rope_q(self._h, int(layer), q.data_ptr(), _dtype_code(q), int(q.shape[2]),
                                float(rope_base), _stream_ptr(stream, self._dev)), "kvc_rope_q")
         return q
 
@@ -263,7 +272,7 @@ class KVCache:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
             raise KVCArgumentError(ERR_ARG, "out must be contiguous float32 shaped like q")
-        _check(_lib.kvc_attend(self._h, int(layer), q.data_ptr(), DTYPE_CODES[dtype_name(q)],
+        _check(_lib.kvc_attend(self._h, int(layer), q.data_ptr(), _dtype_code(q),
                                int(q.shape[2]), out.data_ptr(), _stream_ptr(stream, self._dev)), "kvc_attend")
         return out
 
@@ -282,7 +291,7 @@ class KVCache:
         elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
             raise KVCArgumentError(ERR_ARG, "out must be contiguous float32 shaped like q")
         _check(_lib.kvc_append_attend(self._h, int(layer), k_new.data_ptr(), v_new.data_ptr(),
-                                      DTYPE_CODES[dtype_name(k_new)], q.data_ptr(), DTYPE_CODES[dtype_name(q)],
+                                      _dtype_code(k_new), q.data_ptr(), _dtype_code(q),
                                       int(q.shape[2]), out.data_ptr(), _stream_ptr(stream, self._dev)), "kvc_append_attend")
         return out
 
@@ -335,7 +344,7 @@ class KVCache:
         self._check_chunk(q, self.n_q_heads, "q")
         if out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
             raise KVCArgumentError(ERR_ARG, "out must be contiguous float32 shaped like q")
-        _check(_lib.kvc_attend_static(self._h, int(layer), q.data_ptr(), DTYPE_CODES[dtype_name(q)],
+        _check(_lib.kvc_attend_static(self._h, int(layer), q.data_ptr(), _dtype_code(q),
                                       int(q.shape[2]), out.data_ptr(), _stream_ptr(stream, self._dev)),
                "kvc_attend_static")
         return out
@@ -357,9 +366,10 @@ class KVCache:
 
     # -- helpers --
     def _check_chunk(self, t, heads: int, name: str) -> None:
-        if t.dim() != 4 or t.shape[0] != self.batch or t.shape[1] != heads or t.shape[3] != self.d_head:
+        sh = t.shape          # read once: every access builds a new size object
+        if len(sh) != 4 or sh[0] != self.batch or sh[1] != heads or sh[3] != self.d_head:
             raise KVCArgumentError(ERR_ARG, f"{name} must be [B={self.batch}, H={heads}, T, d_h={self.d_head}], "
-                                            f"got {tuple(t.shape)}")
+                                            f"got {tuple(sh)}")
         if not t.is_contiguous() or t.device != self._dev:
             raise KVCArgumentError(ERR_ARG, f"{name} must be contiguous and on {self._dev}")
 
@@ -471,7 +481,7 @@ class LatentCache:
         if c_new.shape[1] != kr_new.shape[1] or c_new.dtype != kr_new.dtype:
             raise KVCArgumentError(ERR_ARG, "c_new and kr_new differ in T or dtype")
         _check(_lib.kvc_latent_append(self._h, int(layer), c_new.data_ptr(), kr_new.data_ptr(),
-                                      DTYPE_CODES[dtype_name(c_new)], int(c_new.shape[1]), _stream_ptr(stream, self._dev)),
+                                      _dtype_code(c_new), int(c_new.shape[1]), _stream_ptr(stream, self._dev)),
                "kvc_latent_append")
 
     def seq_len(self, layer: Optional[int] = None) -> np.ndarray:
