@@ -306,25 +306,33 @@ def test_decode_slabs_split_over_many_work_groups(dtype, D):
             assert rel <= HALF_REL_FROB, (Hq, Hkv, T, rel)
 
 
-def test_batch_wider_than_one_launch():
-    """B=300 rows (two launches of at most 256 rows each), on the vector (2 and 8
-    query rows per KV head) and matrix-core (6 rows) decode kernels."""
-    log("B=300 rows")
-    rng = np.random.default_rng(300)
-    B, Hq, Hkv, D, max_len = 300, 4, 2, 64, 52
-    cache, orc = _new((1, B, Hq, Hkv, D, max_len), "bf16")
+@pytest.mark.parametrize("B, dtype", [(300, "bf16"), (300, "fp32"), (33, "bf16"), (33, "fp32")])
+def test_batch_wider_than_one_launch(B, dtype):
+    """B=300 rows (two launches of at most 256 rows each) and B=33 (one launch
+    just past the 32 rows whose arguments carry the short row table): the
+    vector (2 and 8 query rows per KV head) and matrix-core (6 rows) decode
+    kernels on bf16, the vector and both row-split kernels (10 and 24 rows) on
+    fp32."""
+    log(f"B={B} rows {dtype}")
+    rng = np.random.default_rng(300 + B)
+    Hq, Hkv, D, max_len = 4, 2, 64, 80
+    cache, orc = _new((1, B, Hq, Hkv, D, max_len), dtype)
     lens = rng.integers(0, 40, size=B)
     k, v = (rng.standard_normal((B, Hkv, 40, D), dtype=np.float32) for _ in range(2))
     cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
     orc.append(0, k, v)
     cache.truncate(lens)
     orc.truncate(lens)
-    for T in (1, 4, 3):
+    for T in ((1, 4, 3) if dtype == "bf16" else (1, 4, 5, 12)):
         q, k, v = (rng.standard_normal(s, dtype=np.float32) for s in ((B, Hq, T, D), (B, Hkv, T, D), (B, Hkv, T, D)))
         cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
         orc.append(0, k, v)
         got = cache.attend(0, to_device(q, "fp32", DEV)).cpu().numpy()
-        assert compare_out(got, orc.attend(0, q), "bf16")[1] <= HALF_REL_FROB
+        want = orc.attend(0, input_values(q, dtype) if dtype != "fp32" else q)
+        if dtype == "fp32":
+            assert compare_out(got, want, dtype)[0] <= FP32_MAX_ABS, T
+        else:
+            assert compare_out(got, want, dtype)[1] <= HALF_REL_FROB, T
     assert cache_bits_equal(cache, orc)
 
 
