@@ -207,6 +207,36 @@ def test_prefill_split_precision(dtype):
     paged.close()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("D", [32, 64])
+def test_prefill_split_precision_small_heads(dtype, D):
+    """The split prefill precision at head dimensions 32 and 64 (the
+    SmolLM2-shaped cache's): ragged rows (fills 0, 37 and 300), two chunks of
+    T=96 with 3 query heads per KV head, every row within 1e-4 of the oracle."""
+    from kv_cached_gqa_amd.kvc import KVCache
+    log(f"prefill split precision D={D} {dtype}")
+    rng = np.random.default_rng(4100 + D)
+    B, Hq, Hkv, T, max_len = 3, 9, 3, 96, 600
+    cache = KVCache(1, Hkv, D, max_len, batch=B, n_q_heads=Hq, dtype=dtype, device=DEV)
+    orc = OracleCache(1, B, Hq, Hkv, D, max_len, dtype)
+    cache.set_prefill_precision("split")
+    k, v = (rng.standard_normal((B, Hkv, 300, D), dtype=np.float32) for _ in range(2))
+    cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
+    orc.append(0, k, v)
+    fills = np.array([0, 37, 300])
+    cache.truncate(fills)
+    orc.truncate(fills)
+    for n in range(2):
+        k, v, q = (rng.standard_normal(s, dtype=np.float32) for s in ((B, Hkv, T, D), (B, Hkv, T, D), (B, Hq, T, D)))
+        cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
+        orc.append(0, k, v)
+        got = cache.attend(0, to_device(q, dtype, DEV)).cpu().numpy()
+        _, rel = compare_out(got, orc.attend(0, input_values(q, dtype)), dtype)
+        log(f"  chunk {n}: split rel {rel:.3e}")
+        assert rel <= 1e-4, (n, rel)
+    cache.close()
+
+
 @pytest.mark.timeout(1200)
 def test_long_context_speculative_cycles():
     """B=8, H_q=64, H_kv=8, d_h=128, bf16, s0=32768: all 64 draft / accept /
