@@ -1085,8 +1085,24 @@ void decode_rows(A a) {
 #define KVC_DECODE_MFMA_STAGES 2       // one tile in flight per wave ...
 #endif
 #ifndef KVC_DECODE_MFMA_BLOCKS_PER_CU
-#define KVC_DECODE_MFMA_BLOCKS_PER_CU 3   // ... and three waves per CU (measured best)
+#define KVC_DECODE_MFMA_BLOCKS_PER_CU 3   // ... and three waves per CU (measured best at d_h 128)
 #endif
+// smaller heads: a wave's chain of waits, products and softmax per 32-key
+// tile serves fewer bytes, so more single-wave work-groups share a CU (their
+// registers allow it). Batched decode (B scaled to the same bytes), % of HBM
+// peak by work-groups per CU: d_h 64: 3 69.7, 4 71.9, 5 68.4, 6 68.9; d_h 32:
+// 3 48.6, 4 61.2, 5 59.8, 6 64.8, 7 67.4, 8 68.0, 10 64.2, 12 68.0
+#ifndef KVC_DECODE_MFMA_BLOCKS_PER_CU_D64
+#define KVC_DECODE_MFMA_BLOCKS_PER_CU_D64 4
+#endif
+#ifndef KVC_DECODE_MFMA_BLOCKS_PER_CU_D32
+#define KVC_DECODE_MFMA_BLOCKS_PER_CU_D32 8
+#endif
+template <int D>
+constexpr int mfma_blocks_per_cu() {
+    return D == 128 ? KVC_DECODE_MFMA_BLOCKS_PER_CU : D == 64 ? KVC_DECODE_MFMA_BLOCKS_PER_CU_D64
+                                                              : KVC_DECODE_MFMA_BLOCKS_PER_CU_D32;
+}
 #ifndef KVC_DECODE_MFMA_QSEGS
 #define KVC_DECODE_MFMA_QSEGS 2
 #endif
@@ -1137,7 +1153,7 @@ struct MCfg : TileLayout<D> {
     static constexpr int QT_BYTES = QSEGS * 32 * D * 2;      // 32 columns of D 16-bit elements each
     static constexpr int fit_stages() {
         int ns = KVC_DECODE_MFMA_STAGES;
-        while (ns > 2 && ((ns * 2 * L::TILE_BYTES + QT_BYTES) * KVC_DECODE_MFMA_BLOCKS_PER_CU > kLdsLimit ||
+        while (ns > 2 && ((ns * 2 * L::TILE_BYTES + QT_BYTES) * mfma_blocks_per_cu<D>() > kLdsLimit ||
                           ns * 2 * L::TILE_BYTES + 24 * D * 2 > 65535))
             --ns;
         return ns;
@@ -1812,7 +1828,7 @@ hipError_t run_mfma(DecodeArgs& a, hipStream_t s) {
     a.unit_pad = KVC_DECODE_MFMA_UNIT_PAD;
     a.total_keys += static_cast<int64_t>(a.rows) * a.Hkv * a.unit_pad;
     const int odd_pct = a.Gc * a.Tc > 16 ? KVC_DECODE_MFMA_ODD_XCD_PCT_WIDE : KVC_DECODE_ODD_XCD_PCT;
-    decode_split_slices(a, n_cu, KVC_DECODE_MFMA_BLOCKS_PER_CU, 2 * kBN, KVC_DECODE_MFMA_LATE_PCT, odd_pct);
+    decode_split_slices(a, n_cu, mfma_blocks_per_cu<D>(), 2 * kBN, KVC_DECODE_MFMA_LATE_PCT, odd_pct);
     if (a.btab && (1 << a.bshift) < kBN) return hipErrorInvalidValue;   // a tile within two blocks
     e = with_args(a, [&](const auto& args) {
         using A = std::decay_t<decltype(args)>;
