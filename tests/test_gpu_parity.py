@@ -158,6 +158,47 @@ def test_batched_decode_bf16_full_size():
     assert rep.ok(), rep.failures[:5]
 
 
+@pytest.mark.parametrize("D, B", [(64, 64), (32, 128)])
+def test_batched_decode_small_heads_full_size(D, B):
+    """Batched decode at head dimensions 64 and 32 with the batch scaled so a
+    call moves the bytes of the d_h 128 workload (H_q=32, H_kv=8, bf16, lengths
+    U{1024..4095}, T=1): the split over every work-group these head dimensions
+    run per CU. One step as append + attend and one as the fused call, every
+    output row against the oracle, the per-row worst error reported."""
+    import torch
+    log(f"batched decode bf16 D={D} B={B} ctx U[1024,4095], all rows")
+    rng = np.random.default_rng(900 + D)
+    Hq, Hkv, max_len = 32, 8, 4096
+    lens = W.batched_lengths(rng, B)
+    cache, orc = _new((1, B, Hq, Hkv, D, max_len), "bf16")
+    k, v = (rng.standard_normal((B, Hkv, max_len - 2, D), dtype=np.float32) for _ in range(2))
+    cache.append(0, to_device(k, "fp32", DEV), to_device(v, "fp32", DEV))
+    orc.append(0, k, v)
+    del k, v
+    cache.truncate(lens)
+    orc.truncate(lens)
+    for step in range(2):
+        q, k, v = (rng.standard_normal(s, dtype=np.float32) for s in ((B, Hq, 1, D), (B, Hkv, 1, D), (B, Hkv, 1, D)))
+        qv = input_values(q, "bf16")
+        qd = torch.from_numpy(qv).to(torch.bfloat16).to(DEV)
+        kd, vd = to_device(k, "fp32", DEV), to_device(v, "fp32", DEV)
+        if step == 0:
+            cache.append(0, kd, vd)
+            got = cache.attend(0, qd).cpu().numpy()
+        else:
+            got = cache.append_attend(0, kd, vd, qd).cpu().numpy()
+        orc.append(0, k, v)
+        want = orc.attend(0, qv)
+        mabs, rel = compare_out(got, want, "bf16")
+        diff = (got.astype(np.float64) - want).reshape(B * Hq, D)
+        row_rel = np.linalg.norm(diff, axis=1) / np.linalg.norm(want.reshape(B * Hq, D), axis=1)
+        log(f"  step {step} ({'append + attend' if step == 0 else 'fused'}): rel {rel:.2e}, "
+            f"worst row {row_rel.max():.2e}, max abs {mabs:.2e}")
+        assert np.isfinite(got).all() and np.isfinite(want).all()
+        assert rel <= HALF_REL_FROB, (D, B, step, rel)
+    assert cache_bits_equal(cache, orc)
+
+
 def test_chunked_prefill_bf16_reduced():
     """B=4, H_q=32, H_kv=8, d_h=128, bf16: four chunks of 512 with the bottom-right mask."""
     log("chunked prefill bf16: 4 chunks of 512")
