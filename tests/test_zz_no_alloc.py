@@ -27,15 +27,16 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_attend_static_equals_attend_on_two_calls(dtype):
+@pytest.mark.parametrize("dtype, D", [("bf16", 128), ("fp32", 128), ("bf16", 64), ("bf16", 32)])
+def test_attend_static_equals_attend_on_two_calls(dtype, D):
     import torch
     from kv_cached_gqa_amd.kvc import KVCache
-    log(f"attend_static vs attend dtype={dtype}")
+    log(f"attend_static vs attend dtype={dtype} D={D}")
     gen = torch.Generator(device=DEV)
     gen.manual_seed(31)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    B, Hq, Hkv, D, max_len = 8, 32, 8, 128, 3000
+    # d_head 64 and 32 run more decode work-groups per CU: a finer split
+    B, Hq, Hkv, max_len = 8, 32, 8, 3000
     cache = KVCache(1, Hkv, D, max_len, batch=B, n_q_heads=Hq, dtype=dtype, device=DEV)
     k = torch.randn((B, Hkv, 2900, D), generator=gen, device=DEV, dtype=tdt)
     v = torch.randn((B, Hkv, 2900, D), generator=gen, device=DEV, dtype=tdt)
