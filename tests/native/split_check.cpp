@@ -50,17 +50,17 @@ static void check_split(int64_t total, int n_cu, int per_cu, int64_t min_keys, i
 
 int main() {
     std::mt19937_64 rng(7);
-    // the launch shapes of the kernels: 256 CUs, 2 or 3 work-groups per CU, the
+    // the launch shapes of the kernels: 256 CUs, 2, 3, 4 or 8 work-groups per CU, the
     // weights in use and around them, axes from a few keys to billions
     const int64_t totals[] = {1, 2, 31, 64, 65, 1000, 4097, 676736 + 256 * 48, 2097216 + 64 * 48,
                               (int64_t(1) << 31) + 12345, (int64_t(1) << 40) + 3};
     for (int64_t t : totals)
-        for (int per_cu : {2, 3})
+        for (int per_cu : {2, 3, 4, 8})
             for (int odd : {86, 88, 90, 100})
                 for (int late : {70, 100}) check_split(t, 256, per_cu, 64, late, odd);
     for (int i = 0; i < 3000; ++i) {
         const int64_t t = 1 + static_cast<int64_t>(rng() % (int64_t(1) << (1 + rng() % 40)));
-        check_split(t, 1 + static_cast<int>(rng() % 304), 1 + static_cast<int>(rng() % 4), 1 + rng() % 128,
+        check_split(t, 1 + static_cast<int>(rng() % 304), 1 + static_cast<int>(rng() % 8), 1 + rng() % 128,
                     50 + static_cast<int>(rng() % 51), 80 + static_cast<int>(rng() % 21));
     }
     // floor division with small quotients: exact at and around multiples
